@@ -1,0 +1,400 @@
+"""CPU oracle for paged KV-cache decode attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call, link
+or execute this module: only the tests, the smoke check of the entry script
+and the bench's CPU-baseline leg use it. It shares no code with the HIP path
+and never imports it.
+
+What it computes, each piece written out plainly in float64 (inputs are
+converted exactly from their fp32 or bf16 bits):
+
+* allocation arithmetic: blocks a sequence needs, last-block slack, and the
+  slot (physical block, offset) of a logical position;
+* a block manager mirror: a free pool handing out blocks in a given order,
+  per-sequence block tables grown one token at a time, reference counts,
+  fork, copy-on-write on a write into a shared block, and freeing;
+* decode attention: for every attended position p the block table is
+  dereferenced at p // block_size and the row read at offset p % block_size,
+  then exact softmax attention over those rows;
+* the same attention split into fixed-length context partitions and combined
+  by the log-sum-exp identity;
+* the slot write of new K/V rows and the whole-block copy, bit for bit.
+
+Sources (page title, then the section used):
+  [Vij]  "PagedAttention Explained: KV Blocks, Allocation, and Sharing"
+         (palashvij.pages.dev)
+  [FP]   "PagedAttention & vLLM" (fp-ai-systems.pages.dev)
+  [ZQ]   "Walk through paged attention end to end, page table, block
+         lookup, and how it enables higher throughput" (zenaique.com)
+  [N4N]  "What is PagedAttention and how does it manage KV cache"
+         (n4n.ai blog)
+
+Readings taken where the pages are silent (all listed with reasons in the
+design notes of the repository):
+  * the caller passes the softmax scale (the pages' pseudo-code applies none);
+  * seq_lens counts every cached token including the one just written, so
+    the new token attends to itself ([ZQ] pseudo-code writes first, then
+    attends over seq_len + 1 positions);
+  * GQA: query head h reads KV head h // (Hq / Hkv);
+  * seq_len 0 gives an all-zero output;
+  * a fork shares every block of the parent including a partial last block,
+    and the first write into a block whose reference count exceeds one
+    copies it first; writers are served in call order, so the last writer
+    keeps the original block;
+  * freed blocks return to the back of the free list, in table order;
+  * a slot < 0 means "no write" (padding).
+
+Every function here is pinned by tests against the pages' worked numbers,
+closed forms, invariants, a library routine or brute force; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from collections import deque
+
+import numpy as np
+
+__all__ = [
+    "blocks_needed", "slack", "slot_of", "kv_bytes_per_token",
+    "OracleNoBlocks", "OracleRefcountError", "OracleBlockManager",
+    "as_f64", "positions_to_rows", "kv_head_of",
+    "decode", "decode_one", "partition_partials", "combine_partials",
+    "decode_partitioned", "reshape_and_cache", "copy_blocks",
+]
+
+
+# --------------------------------------------------------------------------
+# Allocation arithmetic
+# --------------------------------------------------------------------------
+
+def blocks_needed(num_tokens: int, block_size: int) -> int:
+    """Blocks that hold `num_tokens` tokens: the count rounded up to whole
+    blocks. [Vij] "Grow allocation with the sequence": 33 tokens in 16-token
+    blocks take three blocks, 32 tokens take two."""
+    if num_tokens < 0 or block_size <= 0:
+        raise ValueError("num_tokens must be >= 0 and block_size > 0")
+    return -(-int(num_tokens) // int(block_size))
+
+
+def slack(num_tokens: int, block_size: int) -> int:
+    """Unused token positions in the last block. [FP] "The insight: KV cache
+    as virtual memory": the only waste left is in the last block, below one
+    block's worth."""
+    return blocks_needed(num_tokens, block_size) * block_size - int(num_tokens)
+
+
+def slot_of(table, pos: int, block_size: int) -> int:
+    """Flat slot of logical position `pos`: physical block table[pos // bs]
+    at offset pos % bs, encoded as block * bs + offset. [ZQ] pseudo-code of
+    the single decode step (the physical block and offset of a position)."""
+    return int(table[pos // block_size]) * block_size + pos % block_size
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int,
+                       elem_bytes: int) -> int:
+    """K and V bytes one token occupies across all layers: layers x 2 (K,V)
+    x heads x head_dim x element bytes. [FP] "Worked example: naive vs
+    paged" uses this for a 40-layer, 40-head, 128-dim model (~0.78 MB)."""
+    return num_layers * 2 * num_kv_heads * head_dim * elem_bytes
+
+
+# --------------------------------------------------------------------------
+# Block manager mirror
+# --------------------------------------------------------------------------
+
+class OracleNoBlocks(RuntimeError):
+    """The free pool cannot satisfy the request; nothing was changed."""
+
+
+class OracleRefcountError(RuntimeError):
+    """A block was released more often than it was referenced."""
+
+
+class OracleBlockManager:
+    """Free pool + per-sequence block tables + reference counts.
+
+    [FP] "The insight": fixed-size blocks are taken from one shared pool on
+    demand and mapped per request by a block table. [ZQ] pseudo-code: a new
+    physical block is taken exactly when the position to write starts a
+    block. [N4N] "How PagedAttention works" (BlockTable listing): the table
+    maps logical block index to physical id and grows by one entry when the
+    logical index reaches its length. [N4N] "Prefix sharing" and [FP]
+    "Copy-on-write sharing": forks share physical blocks; a write into a
+    shared block first duplicates that block. [N4N] chat example: freed
+    blocks go straight back to the pool.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of range(num_blocks)")
+        self.free = deque(order)
+        self.ref = [0] * self.num_blocks
+        self.tables: dict[int, list[int]] = {}
+        self.ntok: dict[int, int] = {}
+
+    # -- helpers ----------------------------------------------------------
+    def _take(self) -> int:
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def refcount(self, block: int) -> int:
+        return self.ref[block]
+
+    def table(self, seq: int) -> list[int]:
+        return list(self.tables[seq])
+
+    def num_tokens(self, seq: int) -> int:
+        return self.ntok[seq]
+
+    # -- operations -------------------------------------------------------
+    def add_seq(self, seq: int, num_tokens: int) -> None:
+        """A new sequence holding `num_tokens` tokens gets exactly the blocks
+        it needs, taken from the front of the free list."""
+        if seq in self.tables:
+            raise ValueError(f"sequence {seq} exists")
+        need = blocks_needed(num_tokens, self.block_size)
+        if need > len(self.free):
+            raise OracleNoBlocks(f"need {need}, free {len(self.free)}")
+        self.tables[seq] = [self._take() for _ in range(need)]
+        self.ntok[seq] = int(num_tokens)
+
+    def _append_needs_block(self, seq: int) -> bool:
+        p = self.ntok[seq]
+        if p % self.block_size == 0:
+            return True
+        return self.ref[self.tables[seq][p // self.block_size]] > 1
+
+    def append_slot(self, seq: int):
+        """Reserve the slot of the next token of `seq`.
+
+        Returns (slot, cow) where cow is None or (src, dst): the shared block
+        src must be copied to the fresh block dst before the write."""
+        return self.append_slots([seq])[0]
+
+    def append_slots(self, seqs):
+        """append_slot for each listed sequence in order; all or nothing."""
+        need = sum(1 for s in seqs if self._append_needs_block(s)) if len(set(seqs)) == len(seqs) else None
+        if need is None:
+            raise ValueError("a sequence may appear once per batch")
+        if need > len(self.free):
+            raise OracleNoBlocks(f"need {need}, free {len(self.free)}")
+        out = []
+        bs = self.block_size
+        for s in seqs:
+            p = self.ntok[s]
+            t = self.tables[s]
+            lblk, off = p // bs, p % bs
+            cow = None
+            if off == 0:
+                # the position starts a new logical block: take one now
+                assert lblk == len(t)
+                t.append(self._take())
+            elif self.ref[t[lblk]] > 1:
+                # writing into a shared block: duplicate it, then write
+                src = t[lblk]
+                dst = self._take()
+                self.ref[src] -= 1
+                t[lblk] = dst
+                cow = (src, dst)
+            self.ntok[s] = p + 1
+            out.append((t[lblk] * bs + off, cow))
+        return out
+
+    def fork(self, parent: int, child: int) -> None:
+        """The child shares every block of the parent (partial last block
+        included) and the parent's token count."""
+        if child in self.tables:
+            raise ValueError(f"sequence {child} exists")
+        self.tables[child] = list(self.tables[parent])
+        self.ntok[child] = self.ntok[parent]
+        for b in self.tables[child]:
+            self.ref[b] += 1
+
+    def free_seq(self, seq: int) -> None:
+        """Drop a sequence; blocks whose count reaches zero rejoin the back
+        of the free list in table order."""
+        t = self.tables[seq]
+        for b in t:
+            if self.ref[b] <= 0:
+                raise OracleRefcountError(f"block {b}")
+        for b in t:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.tables[seq]
+        del self.ntok[seq]
+
+    def export(self, seqs, max_blocks: int):
+        """Block tables padded with -1 (the [N4N] BlockTable's "unallocated"
+        marker) and token counts, for the listed sequences."""
+        tab = np.full((len(seqs), max_blocks), -1, dtype=np.int32)
+        lens = np.zeros(len(seqs), dtype=np.int32)
+        for r, s in enumerate(seqs):
+            t = self.tables[s]
+            if len(t) > max_blocks:
+                raise ValueError("table longer than max_blocks")
+            tab[r, :len(t)] = t
+            lens[r] = self.ntok[s]
+        return tab, lens
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of fp32 data or of bf16 bit patterns (uint16):
+    a bf16 value is the upper half of the fp32 with the same bits."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(x).view(np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def positions_to_rows(table, seq_len: int, block_size: int):
+    """Per attended position p < seq_len: the physical block table[p // bs]
+    and the offset p % bs inside it ([ZQ] pseudo-code, per-position
+    dereference in the attention loop)."""
+    pos = np.arange(int(seq_len))
+    phys = np.asarray(table, dtype=np.int64)[pos // block_size]
+    off = pos % block_size
+    return phys, off
+
+
+def kv_head_of(q_head: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """KV head read by query head h: heads are grouped contiguously,
+    h // (Hq / Hkv)."""
+    return q_head // (num_q_heads // num_kv_heads)
+
+
+def _gather(pool: np.ndarray, phys, off, kv_head: int) -> np.ndarray:
+    return pool[phys, kv_head, off, :]
+
+
+def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """Exact softmax of `scores` applied to the rows of `values`."""
+    m = scores.max()
+    w = np.exp(scores - m)
+    return (w @ values) / w.sum()
+
+
+def decode_one(q_row, k_pool, v_pool, table, seq_len, scale, kv_head, block_size):
+    """Decode output of one query row (float64 [D]) attending to the first
+    seq_len positions of one sequence through its block table."""
+    d = k_pool.shape[-1]
+    if seq_len == 0:
+        return np.zeros(d, dtype=np.float64)
+    phys, off = positions_to_rows(table, seq_len, block_size)
+    keys = _gather(k_pool, phys, off, kv_head)
+    vals = _gather(v_pool, phys, off, kv_head)
+    scores = float(scale) * (keys @ q_row)
+    return _softmax_weighted_sum(scores, vals)
+
+
+def decode(q, k_pool, v_pool, block_tables, seq_lens, scale):
+    """Paged decode attention, float64.
+
+    q [B, Hq, D]; k_pool, v_pool [NB, Hkv, bs, D]; block_tables [B, maxb]
+    (row i lists sequence i's physical blocks in logical order); seq_lens [B].
+    Output [B, Hq, D]. [ZQ] pseudo-code and "Red flags" (the attention math
+    is that of ordinary attention; only where K/V live changes); [Vij]
+    "Borrow the abstraction" (logical order is kept, physical blocks are
+    scattered)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, hq, d = q.shape
+    hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    out = np.zeros((B, hq, d), dtype=np.float64)
+    for i in range(B):
+        for h in range(hq):
+            out[i, h] = decode_one(q[i, h], k_pool, v_pool, block_tables[i],
+                                   int(seq_lens[i]), scale,
+                                   kv_head_of(h, hq, hkv), bs)
+    return out
+
+
+def partition_partials(q_row, k_pool, v_pool, table, seq_len, scale, kv_head,
+                       block_size, partition_tokens):
+    """Split the context into partitions of `partition_tokens` positions and
+    return, per partition j, (m_j, l_j, o_j): the max score, the sum of
+    exp(score - m_j), and the partition's own normalised output."""
+    parts = []
+    for start in range(0, int(seq_len), int(partition_tokens)):
+        stop = min(int(seq_len), start + int(partition_tokens))
+        pos = np.arange(start, stop)
+        phys = np.asarray(table, dtype=np.int64)[pos // block_size]
+        off = pos % block_size
+        keys = _gather(k_pool, phys, off, kv_head)
+        vals = _gather(v_pool, phys, off, kv_head)
+        s = float(scale) * (keys @ q_row)
+        m = s.max()
+        w = np.exp(s - m)
+        parts.append((m, w.sum(), (w @ vals) / w.sum()))
+    return parts
+
+
+def combine_partials(parts, d):
+    """Log-sum-exp combine: M = max m_j, weights l_j exp(m_j - M), output
+    = sum_j weight_j o_j / sum_j weight_j."""
+    if not parts:
+        return np.zeros(d, dtype=np.float64)
+    big_m = max(p[0] for p in parts)
+    wts = np.array([p[1] * math.exp(p[0] - big_m) for p in parts])
+    outs = np.stack([p[2] for p in parts])
+    return (wts @ outs) / wts.sum()
+
+
+def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale,
+                       partition_tokens):
+    """decode() computed partition by partition and combined (must equal the
+    unsplit result up to rounding)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, hq, d = q.shape
+    hkv, bs = k_pool.shape[1], k_pool.shape[2]
+    out = np.zeros((B, hq, d), dtype=np.float64)
+    for i in range(B):
+        for h in range(hq):
+            parts = partition_partials(q[i, h], k_pool, v_pool, block_tables[i],
+                                       int(seq_lens[i]), scale,
+                                       kv_head_of(h, hq, hkv), bs, partition_tokens)
+            out[i, h] = combine_partials(parts, d)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Cache writes
+# --------------------------------------------------------------------------
+
+def reshape_and_cache(k_new, v_new, slot_mapping, k_pool, v_pool):
+    """Write token t's K and V rows (every KV head) into slot slot_mapping[t]
+    = block * bs + offset of the pools, bit for bit; slot < 0 writes nothing.
+    In place on numpy arrays of any element type. [ZQ] pseudo-code: the new
+    token's K/V go to the last block at offset pos % bs; [ZQ] comparison
+    table: generation writes into the current block."""
+    bs = k_pool.shape[2]
+    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        b, o = slot // bs, slot % bs
+        k_pool[b, :, o, :] = k_new[t]
+        v_pool[b, :, o, :] = v_new[t]
+
+
+def copy_blocks(k_pool, v_pool, pairs):
+    """For each (src, dst): both pools' block dst becomes a bit copy of block
+    src. [FP] "Copy-on-write sharing": the diverging sequence gets a copy of
+    the one shared block before it writes."""
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        k_pool[dst] = k_pool[src]
+        v_pool[dst] = v_pool[src]
