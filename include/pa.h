@@ -1,0 +1,243 @@
+/*
+ * pa.h — C ABI of libpa: paged KV-cache decode attention for gfx950.
+ *
+ * Sources (page title, then the section that defines the operation):
+ *   [Vij] "PagedAttention Explained: KV Blocks, Allocation, and Sharing"
+ *   [FP]  "PagedAttention & vLLM"
+ *   [ZQ]  "Walk through paged attention end to end, page table, block lookup,
+ *         and how it enables higher throughput"
+ *   [N4N] "What is PagedAttention and how does it manage KV cache"
+ *
+ * Conventions for every call below
+ *   - Pointers marked [dev] are device memory on the current HIP device;
+ *     [host] pointers are host memory. All buffers are owned by the caller;
+ *     libpa never allocates, frees or retains device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GPU calls only enqueue work on it and return; stream order makes a
+ *     write (pa_reshape_and_cache, pa_copy_blocks) visible to a later
+ *     pa_decode on the same stream.
+ *   - Every call returns a pa_status_t. Host-visible arguments are checked
+ *     before anything is enqueued; on any error nothing is enqueued.
+ *   - Device-resident indices (block ids, slots, copy pairs, lengths) cannot
+ *     be checked on the host without a sync. The kernels check each one
+ *     against the sizes passed here, never access memory outside the
+ *     buffers described, skip the offending work item and raise a bit in a
+ *     per-device error word read by pa_device_errors().
+ *   - Element types: PA_F32 (float) or PA_BF16 (bfloat16 bit patterns).
+ *     q, the pools, new k/v and out share one type. Pointers must be
+ *     16-byte aligned; head_dim * element size must be a multiple of 16.
+ *
+ * KV pool layout (one pool for K and one for V, per layer):
+ *   pool[num_blocks][num_kv_heads][block_size][head_dim], row-major.
+ *   A block holds block_size consecutive token positions of one sequence;
+ *   inside a block the tokens of one head are contiguous ([FP] "The
+ *   insight: KV cache as virtual memory"; [N4N] "How PagedAttention works").
+ *   Slot s names position (block s / block_size, offset s % block_size).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,        /* bad argument (null pointer, size, alignment)        */
+  PA_EUNSUPPORTED = 2,  /* valid but not built (dtype/head_dim/block_size/G)   */
+  PA_EWORKSPACE = 3,    /* workspace missing or smaller than required          */
+  PA_ENOBLOCKS = 4,     /* block manager: free pool exhausted, state unchanged */
+  PA_EREFCOUNT = 5,     /* block manager: release of an unreferenced block     */
+  PA_EHIP = 6,          /* a HIP runtime call failed                           */
+  PA_EDEVICE = 7        /* a kernel met an out-of-range device index           */
+} pa_status_t;
+
+/* Bits of the device error word (pa_device_errors). */
+#define PA_DEVERR_BLOCK_ID 0x1u   /* block table entry outside [0, num_blocks) */
+#define PA_DEVERR_SEQ_LEN 0x2u    /* seq_len < 0, > max_seq_len, or > table   */
+#define PA_DEVERR_SLOT 0x4u       /* slot >= num_blocks * block_size          */
+#define PA_DEVERR_COPY_PAIR 0x8u  /* copy pair id outside [0, num_blocks)     */
+
+/* Decode kernel variants (pa_decode_shape_t.variant). */
+#define PA_VARIANT_AUTO 0   /* library's choice for the shape                     */
+#define PA_VARIANT_VALU 1   /* q.K and P.V on the vector ALUs                     */
+#define PA_VARIANT_MFMA 2   /* q.K on matrix cores, P.V on the vector ALUs; bf16,
+                               head_dim 128, group size 1, 2 or 4 only            */
+
+/* Shape of one pa_decode call. */
+typedef struct {
+  int32_t num_seqs;           /* B                                             */
+  int32_t num_q_heads;        /* Hq                                            */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0, group G = Hq / Hkv         */
+  int32_t head_dim;           /* D: 64 or 128                                  */
+  int32_t block_size;         /* tokens per block: 16 or 32                    */
+  int32_t num_blocks;         /* physical blocks in each pool                  */
+  int32_t max_blocks_per_seq; /* row stride (entries) of block_tables          */
+  int32_t max_seq_len;        /* host bound on every seq_lens[i]; sizes the
+                                 grid and the workspace                        */
+  int32_t partition_tokens;   /* context partition length: 0 = 512, -1 = one
+                                 partition per sequence, else a positive
+                                 multiple of block_size                        */
+  int32_t dtype;              /* pa_dtype_t                                    */
+  int32_t variant;            /* PA_VARIANT_*                                  */
+} pa_decode_shape_t;
+
+/* Bytes of scratch workspace pa_decode needs for `shape` (partial softmax
+ * statistics and partial outputs, fp32). 0 if the shape is invalid. */
+size_t pa_decode_workspace_bytes(const pa_decode_shape_t* shape);
+
+/*
+ * pa_decode — paged decode attention (one new query token per sequence).
+ *
+ * [ZQ] single-decode-step pseudo-code and "Red flags"; [Vij] "Borrow the
+ * abstraction"; [N4N] "How PagedAttention works". For sequence i and query
+ * head h (KV head g = h / G):
+ *     for p < seq_lens[i]:  b = block_tables[i][p / bs], o = p % bs
+ *                           s_p = scale * dot(q[i][h], k_pool[b][g][o])
+ *     out[i][h] = sum_p softmax(s)_p * v_pool[b][g][o]
+ * seq_lens counts every cached token including the one just written; a
+ * length of 0 gives zeros. Positions >= seq_lens[i] and table entries past
+ * ceil(seq_lens[i] / bs) are never read, so slack slots and -1 padding are
+ * harmless. The context is processed in partitions of partition_tokens
+ * positions whose softmax statistics are merged by the log-sum-exp identity
+ * (pa_decode_partition then pa_decode_reduce).
+ *
+ *   q             [dev] [B][Hq][D]
+ *   k_pool,v_pool [dev] [num_blocks][Hkv][bs][D]
+ *   block_tables  [dev] int32 [B][max_blocks_per_seq], -1 = unallocated
+ *   seq_lens      [dev] int32 [B]
+ *   scale         softmax scale applied to q.k (e.g. 1/sqrt(D))
+ *   out           [dev] [B][Hq][D], written; rounded to nearest-even for bf16
+ *   workspace     [dev] >= pa_decode_workspace_bytes(shape) bytes
+ */
+pa_status_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                      void* out, const pa_decode_shape_t* shape, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* First half of pa_decode: one workgroup per (sequence, KV head, partition)
+ * writes that partition's max score, exp-sum and normalised partial output
+ * to `workspace`; a sequence with a single partition gets its final `out`
+ * row directly. Same arguments as pa_decode. */
+pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                float scale, void* out, const pa_decode_shape_t* shape,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Second half of pa_decode: for every sequence with more than one partition,
+ * out[i][h] = sum_j w_j o_j / sum_j w_j with w_j = l_j * exp(m_j - max_j m_j),
+ * read from the workspace pa_decode_partition filled. */
+pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out,
+                             const pa_decode_shape_t* shape, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * pa_reshape_and_cache — write new tokens' K and V rows into their slots.
+ *
+ * [ZQ] pseudo-code (the new token's K/V go to block table[-1] at offset
+ * pos % bs) and comparison table (generation writes into the current
+ * block). For t < num_tokens with slot_mapping[t] >= 0:
+ *     k_pool[slot / bs][h][slot % bs][:] = k[t][h][:]   for every h < Hkv
+ * and the same for v. Bitwise copy. slot < 0 means "no write" (padding).
+ * Slots must be distinct; two tokens writing one slot race.
+ *
+ *   k, v          [dev] [num_tokens][Hkv][D]
+ *   slot_mapping  [dev] int64 [num_tokens]
+ *   k_pool,v_pool [dev] [num_blocks][Hkv][bs][D]
+ */
+pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                                 void* k_pool, void* v_pool, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * pa_copy_blocks — copy-on-write duplication of whole physical blocks.
+ *
+ * [FP] "Copy-on-write sharing": a sequence about to write into a block it
+ * shares gets a private copy of that one block first. For each pair n:
+ *     k_pool[dst] = k_pool[src],  v_pool[dst] = v_pool[src]   (bitwise)
+ * where (src, dst) = (pairs[2n], pairs[2n+1]). Destinations must be distinct
+ * and must not appear as sources in the same call (pairs run concurrently).
+ *
+ *   k_pool,v_pool [dev] num_blocks blocks of block_bytes bytes each
+ *   pairs         [dev] int64 [num_pairs][2]
+ *   block_bytes   Hkv * bs * D * element size; a multiple of 16
+ */
+pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,
+                           int64_t block_bytes, int32_t num_blocks, void* stream);
+
+/* Waits for `stream`, then returns the current device's error word in
+ * *flags (PA_DEVERR_* bits, 0 = clean) and clears it. Returns PA_EDEVICE if
+ * any bit was set, PA_EHIP if a HIP call failed. */
+pa_status_t pa_device_errors(uint32_t* flags, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_str(pa_status_t status);
+
+/* ------------------------------------------------------------------------
+ * Host block manager: free pool, block tables, reference counts, fork and
+ * copy-on-write decisions. Host memory only, no GPU calls, not thread-safe.
+ *
+ * [FP] "The insight: KV cache as virtual memory" (blocks taken from one
+ * shared pool on demand, per-request block table); [ZQ] pseudo-code (a new
+ * block exactly when the position to write starts a block); [N4N]
+ * "How PagedAttention works" (BlockTable.append_token), "Prefix sharing"
+ * (fork_block_table) and the chat example (finished requests return their
+ * blocks at once); [Vij] "Shared blocks need ownership rules" and [FP]
+ * "Copy-on-write sharing" (reference counts, copy before writing into a
+ * shared block).
+ *
+ * Readings: a fork shares every parent block including a partial last
+ * block; within one batch, writers are served in order, so the last writer
+ * into a shared block keeps the original; freed blocks rejoin the back of
+ * the free list in table order; the free list hands out blocks front first.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_bm pa_bm_t;
+
+/* Creates a manager for `num_blocks` blocks of `block_size` tokens.
+ * free_order [host]: a permutation of 0..num_blocks-1 giving the order in
+ * which blocks are handed out, or NULL for 0, 1, 2, ... */
+pa_status_t pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                         pa_bm_t** out);
+void pa_bm_destroy(pa_bm_t* bm);
+
+/* Registers sequence `seq_id` already holding `num_tokens` tokens and gives
+ * it ceil(num_tokens / block_size) blocks. PA_ENOBLOCKS leaves state as is. */
+pa_status_t pa_bm_add_seq(pa_bm_t* bm, int32_t seq_id, int32_t num_tokens);
+
+/* Reserves the next token position of each of the n sequences (each listed
+ * at most once), in order. slots [host] int64[n] receives block * bs +
+ * offset. cow_pairs [host] int64[2n] receives the (src, dst) block copies
+ * that must run (pa_copy_blocks) before the slots are written; *num_cow is
+ * their count. All or nothing: PA_ENOBLOCKS if the pool cannot cover the
+ * whole batch, with no state change. */
+pa_status_t pa_bm_append_slots(pa_bm_t* bm, const int32_t* seq_ids, int32_t n, int64_t* slots,
+                               int64_t* cow_pairs, int32_t* num_cow);
+
+/* Child `child_id` shares every block of `parent_id` (count + 1 each). */
+pa_status_t pa_bm_fork(pa_bm_t* bm, int32_t parent_id, int32_t child_id);
+
+/* Drops a sequence; blocks whose count reaches 0 return to the free list. */
+pa_status_t pa_bm_free_seq(pa_bm_t* bm, int32_t seq_id);
+
+/* Writes the block tables [host] int32[n][max_blocks] (-1 padded) and token
+ * counts [host] int32[n] of the listed sequences. PA_EINVAL if a table is
+ * longer than max_blocks. Either output may be NULL. */
+pa_status_t pa_bm_export(const pa_bm_t* bm, const int32_t* seq_ids, int32_t n,
+                         int32_t max_blocks, int32_t* tables, int32_t* lens);
+
+int32_t pa_bm_num_free(const pa_bm_t* bm);
+/* Reference count of `block`, or -1 if out of range. */
+int32_t pa_bm_refcount(const pa_bm_t* bm, int32_t block);
+/* Token count of `seq_id`, or -1 if unknown. */
+int32_t pa_bm_num_tokens(const pa_bm_t* bm, int32_t seq_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

@@ -1,0 +1,334 @@
+"""Python binding of libpa, the gfx950 paged decode attention library.
+
+Argument marshalling only: every computation runs in libpa.so (HIP kernels
+for the GPU calls, C++ for the host block manager). torch tensors supply
+device memory and the current stream. There is no fallback: if libpa.so has
+not been built, importing the binding's functions raises.
+
+Calls mirror the C ABI in include/pa.h:
+    pa_decode, pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes,
+    pa_reshape_and_cache, pa_copy_blocks, pa_device_errors, BlockManager (pa_bm_*).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16",
+    "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
+    "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_device_errors", "BlockManager",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_F32, PA_BF16 = 0, 1
+PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
+_STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
+           4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
+
+# Every function include/pa.h declares.
+EXPORTED_SYMBOLS = (
+    "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_device_errors", "pa_status_str",
+    "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
+    "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
+)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        super().__init__(f"{what}: {self.name}" if what else self.name)
+
+
+class DecodeShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
+        "max_blocks_per_seq", "max_seq_len", "partition_tokens", "dtype", "variant")]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(DecodeShape)]),
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                         ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+    "pa_decode_partition": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                   ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+    "pa_decode_reduce": (_i32, [_vp, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _vp]),
+    "pa_device_errors": (_i32, [ctypes.POINTER(ctypes.c_uint32), _vp]),
+    "pa_status_str": (ctypes.c_char_p, [_i32]),
+    "pa_bm_create": (_i32, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add_seq": (_i32, [_vp, _i32, _i32]),
+    "pa_bm_append_slots": (_i32, [_vp, _vp, _i32, _vp, _vp, ctypes.POINTER(_i32)]),
+    "pa_bm_fork": (_i32, [_vp, _i32, _i32]),
+    "pa_bm_free_seq": (_i32, [_vp, _i32]),
+    "pa_bm_export": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "pa_bm_num_free": (_i32, [_vp]),
+    "pa_bm_refcount": (_i32, [_vp, _i32]),
+    "pa_bm_num_tokens": (_i32, [_vp, _i32]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise PaError(status, what)
+
+
+# --------------------------------------------------------------------------
+# GPU calls (torch tensors in, pointers out)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(stream, device) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _need(t, name, dtype=None, dim=None, device=None):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, variant):
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_pool.shape
+    if d2 != d:
+        raise ValueError("head_dim mismatch between q and the pools")
+    return DecodeShape(B, hq, hkv, d, bs, nb, block_tables.shape[1], int(max_seq_len),
+                       int(partition_tokens), _dtype_code(q), int(variant))
+
+
+def pa_decode_workspace_bytes(shape: DecodeShape) -> int:
+    return int(lib().pa_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def _decode_call(fn_name, q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
+                 max_seq_len, partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None,
+                 stream=None):
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", dim=3)
+    _need(k_pool, "k_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(v_pool, "v_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if block_tables.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise ValueError("batch mismatch")
+    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, variant)
+    need = pa_decode_workspace_bytes(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = getattr(lib(), fn_name)(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
+        workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+    _check(st, fn_name)
+    return out
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,
+              partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None, stream=None):
+    """Paged decode attention (include/pa.h pa_decode). q [B,Hq,D]; pools
+    [NB,Hkv,bs,D]; block_tables int32 [B,maxb]; seq_lens int32 [B]; out
+    [B,Hq,D]. Enqueues on `stream` (default: torch's current stream)."""
+    return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, seq_lens, scale, out,
+                        max_seq_len=max_seq_len, partition_tokens=partition_tokens,
+                        variant=variant, workspace=workspace, stream=stream)
+
+
+def pa_decode_partition(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,
+                        partition_tokens=0, variant=PA_VARIANT_AUTO, workspace, stream=None):
+    """First half of pa_decode (per-partition kernel)."""
+    return _decode_call("pa_decode_partition", q, k_pool, v_pool, block_tables, seq_lens, scale,
+                        out, max_seq_len=max_seq_len, partition_tokens=partition_tokens,
+                        variant=variant, workspace=workspace, stream=stream)
+
+
+def pa_decode_reduce(q, k_pool, block_tables, seq_lens, out, *, max_seq_len, partition_tokens=0,
+                     variant=PA_VARIANT_AUTO, workspace, stream=None):
+    """Second half of pa_decode (partition merge). q/k_pool/block_tables only
+    describe the shape."""
+    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, variant)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().pa_decode_reduce(seq_lens.data_ptr(), out.data_ptr(), ctypes.byref(shape),
+                                workspace.data_ptr(), ws_bytes, _stream_ptr(stream, out.device))
+    _check(st, "pa_decode_reduce")
+    return out
+
+
+def pa_reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None):
+    """Write k/v [T,Hkv,D] into the pools at slot_mapping (int64 [T]);
+    slot < 0 writes nothing."""
+    torch = _torch()
+    dev = k_pool.device
+    _need(k, "k", dtype=k_pool.dtype, dim=3, device=dev)
+    _need(v, "v", dtype=k_pool.dtype, dim=3, device=dev)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, dim=1, device=dev)
+    _need(k_pool, "k_pool", dim=4)
+    _need(v_pool, "v_pool", dtype=k_pool.dtype, device=dev)
+    nb, hkv, bs, d = k_pool.shape
+    T = k.shape[0]
+    if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d) or slot_mapping.shape[0] != T:
+        raise ValueError("shape mismatch")
+    st = lib().pa_reshape_and_cache(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                    k_pool.data_ptr(), v_pool.data_ptr(), T, hkv, d, bs, nb,
+                                    _dtype_code(k_pool), _stream_ptr(stream, dev))
+    _check(st, "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(k_pool, v_pool, pairs, stream=None):
+    """Copy whole blocks (src, dst) = pairs[n] in both pools; pairs int64 [N,2]."""
+    torch = _torch()
+    dev = k_pool.device
+    _need(k_pool, "k_pool", dim=4)
+    _need(v_pool, "v_pool", dtype=k_pool.dtype, device=dev)
+    _need(pairs, "pairs", dtype=torch.int64, device=dev)
+    n = pairs.numel() // 2
+    block_bytes = k_pool[0].numel() * k_pool.element_size()
+    st = lib().pa_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(), n,
+                              block_bytes, k_pool.shape[0], _stream_ptr(stream, dev))
+    _check(st, "pa_copy_blocks")
+
+
+def pa_device_errors(stream=None, device=None) -> int:
+    """Synchronise the stream and return (and clear) the device error word."""
+    torch = _torch()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    flags = ctypes.c_uint32(0)
+    st = lib().pa_device_errors(ctypes.byref(flags), _stream_ptr(stream, dev))
+    if st not in (0, 7):
+        raise PaError(st, "pa_device_errors")
+    return int(flags.value)
+
+
+# --------------------------------------------------------------------------
+# Host block manager
+# --------------------------------------------------------------------------
+
+class BlockManager:
+    """pa_bm_*: free pool, block tables, reference counts, fork, CoW."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self._l = lib()
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("free_order must list every block once")
+        st = self._l.pa_bm_create(num_blocks, block_size,
+                                  None if order is None else order.ctypes.data, ctypes.byref(h))
+        _check(st, "pa_bm_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._l.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_seq(self, seq_id: int, num_tokens: int) -> None:
+        _check(self._l.pa_bm_add_seq(self._h, seq_id, num_tokens), "pa_bm_add_seq")
+
+    def append_slots(self, seq_ids):
+        """Returns (slots int64 [n], cow_pairs int64 [k, 2])."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        n = ids.shape[0]
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pairs = np.empty(max(2 * n, 2), dtype=np.int64)
+        ncow = ctypes.c_int32(0)
+        st = self._l.pa_bm_append_slots(self._h, ids.ctypes.data, n, slots.ctypes.data,
+                                        pairs.ctypes.data, ctypes.byref(ncow))
+        _check(st, "pa_bm_append_slots")
+        return slots[:n], pairs[: 2 * ncow.value].reshape(-1, 2)
+
+    def append_slots_into(self, seq_ids, slots_out, pairs_out) -> int:
+        """append_slots writing into caller arrays (e.g. pinned host memory);
+        returns the number of copy pairs."""
+        ncow = ctypes.c_int32(0)
+        st = self._l.pa_bm_append_slots(self._h, seq_ids.ctypes.data, seq_ids.shape[0],
+                                        slots_out.ctypes.data, pairs_out.ctypes.data,
+                                        ctypes.byref(ncow))
+        _check(st, "pa_bm_append_slots")
+        return ncow.value
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._l.pa_bm_fork(self._h, parent, child), "pa_bm_fork")
+
+    def free_seq(self, seq_id: int) -> None:
+        _check(self._l.pa_bm_free_seq(self._h, seq_id), "pa_bm_free_seq")
+
+    def export(self, seq_ids, max_blocks: int, tables_out=None, lens_out=None):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        n = ids.shape[0]
+        tab = tables_out if tables_out is not None else np.empty((n, max_blocks), dtype=np.int32)
+        lens = lens_out if lens_out is not None else np.empty(n, dtype=np.int32)
+        st = self._l.pa_bm_export(self._h, ids.ctypes.data, n, max_blocks, tab.ctypes.data,
+                                  lens.ctypes.data)
+        _check(st, "pa_bm_export")
+        return tab, lens
+
+    def num_free(self) -> int:
+        return int(self._l.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._l.pa_bm_refcount(self._h, block))
+
+    def num_tokens(self, seq_id: int) -> int:
+        return int(self._l.pa_bm_num_tokens(self._h, seq_id))

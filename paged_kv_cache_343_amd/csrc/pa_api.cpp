@@ -1,0 +1,255 @@
+// C ABI of libpa: argument validation and kernel dispatch. Every check on a
+// host-visible argument happens before anything is enqueued; on error the
+// call returns a status and enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kDefaultPartitionTokens = 512;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 0; }
+
+// Resolved layout of a decode call.
+struct Plan {
+  int part_tokens = 0;
+  int max_parts = 0;
+  int len_cap = 0;
+  int group = 0;
+  size_t ml_bytes = 0;    // partial (max, sum) region
+  size_t o_bytes = 0;     // partial output region
+  pa::DecodeKey key{};
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int auto_variant(const pa_decode_shape_t& s, int group) {
+  if (s.dtype == PA_BF16 && s.head_dim == 128 && (group == 1 || group == 2 || group == 4))
+    return PA_VARIANT_MFMA;
+  return PA_VARIANT_VALU;
+}
+
+pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan) {
+  if (!s) return PA_EINVAL;
+  if (s->num_seqs < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_blocks <= 0 ||
+      s->max_blocks_per_seq <= 0 || s->max_seq_len < 0 || s->block_size <= 0 ||
+      s->head_dim <= 0)
+    return PA_EINVAL;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_EINVAL;
+  if (elem_bytes(s->dtype) == 0) return PA_EINVAL;
+  if ((s->head_dim * elem_bytes(s->dtype)) % 16 != 0) return PA_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return PA_EUNSUPPORTED;
+  if (s->block_size != 16 && s->block_size != 32) return PA_EUNSUPPORTED;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  int pt = s->partition_tokens;
+  if (pt == 0) pt = kDefaultPartitionTokens;
+  if (pt == -1) {
+    // one partition per sequence
+    pt = s->max_seq_len > 0 ? (int)round_up((size_t)s->max_seq_len, (size_t)s->block_size)
+                            : s->block_size;
+  }
+  if (pt <= 0 || pt % s->block_size != 0) return PA_EINVAL;
+  plan->part_tokens = pt;
+  plan->max_parts = s->max_seq_len == 0 ? 1 : (s->max_seq_len + pt - 1) / pt;
+  const int64_t table_cap = (int64_t)s->max_blocks_per_seq * s->block_size;
+  plan->len_cap = (int)(table_cap < s->max_seq_len ? table_cap : s->max_seq_len);
+  plan->group = group;
+  int variant = s->variant == PA_VARIANT_AUTO ? auto_variant(*s, group) : s->variant;
+  if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
+  plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant};
+  if (!pa::decode_partition_supported(plan->key)) return PA_EUNSUPPORTED;
+  const size_t rows = (size_t)s->num_seqs * s->num_q_heads * plan->max_parts;
+  if (plan->max_parts > 1) {
+    plan->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+    plan->o_bytes = round_up(rows * (size_t)s->head_dim * sizeof(float), 256);
+  }
+  return PA_OK;
+}
+
+pa_status_t fill_args(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale, void* out,
+                      const pa_decode_shape_t* s, const Plan& plan, void* workspace,
+                      size_t workspace_bytes, pa::DecodeArgs* a) {
+  if (s->num_seqs > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out))
+    return PA_EINVAL;
+  if (s->num_seqs > 0 &&
+      (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)))
+    return PA_EINVAL;
+  if (!std::isfinite(scale)) return PA_EINVAL;
+  const size_t need = plan.ml_bytes + plan.o_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_EWORKSPACE;
+  a->q = q;
+  a->k_pool = k_pool;
+  a->v_pool = v_pool;
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->out = out;
+  a->part_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a->part_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes)
+                       : nullptr;
+  a->qscale = scale * 1.4426950408889634f;  // log2(e): scores kept in log2 units
+  a->num_seqs = s->num_seqs;
+  a->num_q_heads = s->num_q_heads;
+  a->num_kv_heads = s->num_kv_heads;
+  a->num_blocks = s->num_blocks;
+  a->max_blocks = s->max_blocks_per_seq;
+  a->max_seq_len = s->max_seq_len;
+  a->len_cap = plan.len_cap;
+  a->part_tokens = plan.part_tokens;
+  a->max_parts = plan.max_parts;
+  return PA_OK;
+}
+
+pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_workspace_bytes(const pa_decode_shape_t* shape) {
+  Plan plan;
+  if (make_plan(shape, &plan) != PA_OK) return 0;
+  return plan.ml_bytes + plan.o_bytes;
+}
+
+static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                               void* out, const pa_decode_shape_t* shape, void* workspace,
+                               size_t workspace_bytes, void* stream, bool do_partition,
+                               bool do_reduce) {
+  Plan plan;
+  pa_status_t st = make_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  pa::DecodeArgs a{};
+  st = fill_args(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, plan, workspace,
+                 workspace_bytes, &a);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (do_partition) {
+    st = from_hip(pa::launch_decode_partition(plan.key, a, s));
+    if (st != PA_OK) return st;
+  }
+  if (do_reduce) st = from_hip(pa::launch_decode_reduce(shape->dtype, shape->head_dim, a, s));
+  return st;
+}
+
+pa_status_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                      void* out, const pa_decode_shape_t* shape, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, true);
+}
+
+pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                float scale, void* out, const pa_decode_shape_t* shape,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, false);
+}
+
+pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode_shape_t* shape,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Plan plan;
+  pa_status_t st = make_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0 || plan.max_parts <= 1) return PA_OK;
+  if (!seq_lens || !out || !aligned16(out)) return PA_EINVAL;
+  const size_t need = plan.ml_bytes + plan.o_bytes;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_EWORKSPACE;
+  pa::DecodeArgs a{};
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_ml = static_cast<float*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes);
+  a.num_seqs = shape->num_seqs;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.num_blocks = shape->num_blocks;
+  a.max_blocks = shape->max_blocks_per_seq;
+  a.max_seq_len = shape->max_seq_len;
+  a.len_cap = plan.len_cap;
+  a.part_tokens = plan.part_tokens;
+  a.max_parts = plan.max_parts;
+  return from_hip(pa::launch_decode_reduce(shape->dtype, shape->head_dim, a,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                                 void* k_pool, void* v_pool, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t dtype, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (eb == 0 || num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return PA_EINVAL;
+  if ((head_dim * eb) % 16 != 0) return PA_EINVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PA_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_EINVAL;
+  pa::CacheArgs a{};
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_slots = (int64_t)num_blocks * block_size;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.row_chunks = head_dim * eb / 16;
+  a.block_size = block_size;
+  return from_hip(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,
+                           int64_t block_bytes, int32_t num_blocks, void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 16 != 0 || num_blocks <= 0)
+    return PA_EINVAL;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !pairs || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_EINVAL;
+  pa::CopyArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.pairs = pairs;
+  a.block_chunks = block_bytes / 16;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_device_errors(uint32_t* flags, void* stream) {
+  if (!flags) return PA_EINVAL;
+  *flags = 0;
+  hipError_t e = pa::read_and_clear_errors(flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return PA_EHIP;
+  return *flags ? PA_EDEVICE : PA_OK;
+}
+
+const char* pa_status_str(pa_status_t status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_EINVAL: return "PA_EINVAL: invalid argument";
+    case PA_EUNSUPPORTED: return "PA_EUNSUPPORTED: shape not built";
+    case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
+    case PA_ENOBLOCKS: return "PA_ENOBLOCKS: free pool exhausted";
+    case PA_EREFCOUNT: return "PA_EREFCOUNT: block released more than referenced";
+    case PA_EHIP: return "PA_EHIP: HIP runtime call failed";
+    case PA_EDEVICE: return "PA_EDEVICE: out-of-range device index";
+  }
+  return "unknown pa_status_t";
+}
+
+}  // extern "C"

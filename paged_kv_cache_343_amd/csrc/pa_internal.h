@@ -1,0 +1,76 @@
+// Internal interface between the C ABI (pa_api.cpp) and the gfx950 kernels
+// (pa_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one decode launch needs, passed by value as the kernel argument.
+struct DecodeArgs {
+  const void* q;              // [B][Hq][D]
+  const void* k_pool;         // [NB][Hkv][bs][D]
+  const void* v_pool;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* seq_lens;      // [B]
+  void* out;                    // [B][Hq][D]
+  float* part_ml;               // [B][Hq][max_parts][2]: max score (log2 units), exp-sum
+  float* part_o;                // [B][Hq][max_parts][D]: normalised partial output
+  float qscale;                 // softmax scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t max_seq_len;
+  int32_t len_cap;              // min(max_seq_len, max_blocks * bs)
+  int32_t part_tokens;          // partition length in positions (multiple of bs)
+  int32_t max_parts;            // ceil(max_seq_len / part_tokens)
+};
+
+struct CacheArgs {
+  const void* k;                // [T][Hkv][D]
+  const void* v;
+  const int64_t* slots;         // [T]
+  void* k_pool;
+  void* v_pool;
+  int64_t num_slots;            // num_blocks * block_size
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t row_chunks;           // 16-byte chunks per (token, head) row = D * elem / 16
+  int32_t block_size;
+};
+
+struct CopyArgs {
+  void* k_pool;
+  void* v_pool;
+  const int64_t* pairs;         // [N][2]
+  int64_t block_chunks;         // 16-byte chunks per block
+  int32_t num_pairs;
+  int32_t num_blocks;
+};
+
+// Kernel selection key for pa_decode_partition.
+struct DecodeKey {
+  int dtype;       // 0 f32, 1 bf16
+  int head_dim;    // 64, 128
+  int block_size;  // 16, 32
+  int group;       // 1, 2, 4, 8
+  int variant;     // 1 VALU, 2 MFMA
+};
+
+// Returns hipErrorInvalidValue (and launches nothing) if `key` has no kernel.
+hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
+                                   hipStream_t stream);
+bool decode_partition_supported(const DecodeKey& key);
+hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
+                                hipStream_t stream);
+hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream);
+// Synchronises `stream`, returns the device error word and clears it.
+hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);
+
+// Workgroup size (waves) of the partition kernels.
+constexpr int kDecodeWaves = 4;
+
+}  // namespace pa

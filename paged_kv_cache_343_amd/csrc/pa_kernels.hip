@@ -1,0 +1,700 @@
+// gfx950 kernels for paged decode attention, the slot write and the block
+// copy.
+//
+// The decode computes, for every sequence i and query head h (KV head
+// g = h / G), softmax-weighted V over the positions p < seq_len[i], where
+// position p lives in physical block block_tables[i][p / bs] at offset
+// p % bs (the per-position lookup of the single decode step pseudo-code on
+// the zenaique.com page "Walk through paged attention end to end ..."; the
+// attention itself is ordinary attention, as its "Red flags" section
+// stresses). Tokens of one head are contiguous inside a block ("PagedAttention
+// & vLLM", "The insight: KV cache as virtual memory"; n4n.ai "How
+// PagedAttention works"), so each block is one contiguous bs x D tile per
+// head and is read with full 16-byte, fully used loads.
+//
+// Work decomposition (one workgroup = 4 wave64s per (sequence, KV head,
+// context partition)):
+//   * a partition covers part_tokens consecutive positions; its blocks are
+//     dealt round-robin to the 4 waves; all G query heads of the KV head
+//     share every K/V load;
+//   * inside a wave, lanes are split into "rows"; each row is an independent
+//     online-softmax stream over a fixed subset of the positions, so no
+//     cross-row communication happens in the main loop;
+//   * at the end the streams are merged with the log-sum-exp identity
+//     (shuffles across rows, LDS across waves). A sequence with a single
+//     partition writes its output directly; otherwise the partition's
+//     (max, exp-sum, normalised output) go to the workspace and a second
+//     kernel merges the partitions.
+// Scores are kept in log2 units: q.k * scale * log2(e), exponentiated with
+// v_exp_f32 (2^x).
+//
+// Two partition kernels:
+//   VALU: 16-byte lane loads of K rows, per-lane partial dot products
+//         reduced across the row's lanes with DPP; P.V on the VALU.
+//   MFMA: q.K on the matrix cores (v_mfma_f32_16x16x32_bf16) with K as the
+//         A operand and the group's query rows, replicated over the 16
+//         columns, as B; the result leaves each lane with the scores of its
+//         own row's 4 positions, and a quad-level DPP broadcast hands each
+//         lane the other heads' probabilities; P.V on the VALU.
+// Every device-resident index is range-checked; a bad one is replaced by an
+// in-range value, its work is masked, and a bit is set in g_error_word.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+__device__ uint32_t g_error_word;
+
+namespace {
+
+constexpr uint32_t kErrBlockId = 0x1u;
+constexpr uint32_t kErrSeqLen = 0x2u;
+constexpr uint32_t kErrSlot = 0x4u;
+constexpr uint32_t kErrCopyPair = 0x8u;
+
+__device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_word, bit); }
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kPerLoad = 4;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kPerLoad = 8;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* f) {
+    f[0] = lo_bf16(v.x);
+    f[1] = hi_bf16(v.x);
+    f[2] = lo_bf16(v.y);
+    f[3] = hi_bf16(v.y);
+    f[4] = lo_bf16(v.z);
+    f[5] = hi_bf16(v.z);
+    f[6] = lo_bf16(v.w);
+    f[7] = hi_bf16(v.w);
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, float x) { *p = to_bf16(x); }
+};
+
+__device__ __forceinline__ uint4 ld16(const char* base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint4*>(base + byte_off);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of LPR consecutive lanes (LPR in 8, 16, 32); every
+// lane of the group receives the total.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror: lane k <- 7-k within 8
+  if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror: lane k <- 15-k
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Value held by lane (k & ~(G-1)) + h of this lane's quad, for every lane k.
+template <int G, int H>
+__device__ __forceinline__ float quad_pick(float x) {
+  static_assert(G == 1 || G == 2 || G == 4, "quad group");
+  if constexpr (G == 1) {
+    return x;
+  } else {
+    constexpr int s0 = (0 & ~(G - 1)) | H, s1 = (1 & ~(G - 1)) | H;
+    constexpr int s2 = (2 & ~(G - 1)) | H, s3 = (3 & ~(G - 1)) | H;
+    return dpp<s0 | (s1 << 2) | (s2 << 4) | (s3 << 6)>(x);
+  }
+}
+
+// out[h] = the value held by the lane of this quad that owns head h.
+template <int G>
+__device__ __forceinline__ void quad_spread(float x, float (&out)[G]) {
+  if constexpr (G == 1) {
+    out[0] = x;
+  } else if constexpr (G == 2) {
+    out[0] = quad_pick<2, 0>(x);
+    out[1] = quad_pick<2, 1>(x);
+  } else {
+    out[0] = quad_pick<4, 0>(x);
+    out[1] = quad_pick<4, 1>(x);
+    out[2] = quad_pick<4, 2>(x);
+    out[3] = quad_pick<4, 3>(x);
+  }
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a softmax stream with running max m when merged under max M.
+__device__ __forceinline__ float merge_weight(float m, float big_m) {
+  return m == -INFINITY ? 0.0f : exp2_fast(m - big_m);
+}
+
+// Validated view of one sequence / partition for a workgroup.
+struct PartitionWork {
+  int i, g, j;       // sequence, KV head, partition
+  int len;           // validated sequence length
+  int nparts;        // partitions of this sequence
+  int tok0, tok1;    // positions [tok0, tok1) of partition j
+};
+
+// Sequence length checked against the host bound (len_cap = min(max_seq_len,
+// max_blocks * bs)); out-of-range values are clamped and flagged.
+__device__ __forceinline__ int checked_len(const DecodeArgs& a, int i) {
+  int len = a.seq_lens[i];
+  if (len < 0 || len > a.len_cap) {
+    if (threadIdx.x == 0) flag_error(kErrSeqLen);
+    len = len < 0 ? 0 : a.len_cap;
+  }
+  return len;
+}
+
+__device__ __forceinline__ int checked_block(const DecodeArgs& a, int i, int logical_block) {
+  int b = a.block_tables[(int64_t)i * a.max_blocks + logical_block];
+  b = __builtin_amdgcn_readfirstlane(b);
+  if ((unsigned)b >= (unsigned)a.num_blocks) {
+    if ((threadIdx.x & 63) == 0) flag_error(kErrBlockId);
+    b = 0;
+  }
+  return b;
+}
+
+// Writes zeros for the G query heads of KV head g of a sequence with no
+// cached tokens.
+template <typename T, int D, int G, int NW>
+__device__ void write_zero_rows(const DecodeArgs& a, int i, int g) {
+  T* out = reinterpret_cast<T*>(a.out);
+  for (int t = threadIdx.x; t < G * D; t += NW * 64) {
+    const int h = t / D, d = t % D;
+    Elem<T>::store(out + ((int64_t)i * a.num_q_heads + g * G + h) * D + d, 0.0f);
+  }
+}
+
+// Merges the per-row softmax streams of every wave and writes either the
+// final output (single-partition sequence) or the partition's partials.
+// Inputs per lane: m[h], l[h] of the lane's row stream (log2 units) and
+// acc[h][e] = unnormalised output for dims c*EPL + e, where c = lane % LPR.
+template <typename T, int D, int G, int NW, int LPR, int EPL>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const PartitionWork& wk,
+                                                 float (&m)[G], float (&l)[G],
+                                                 float (&acc)[G][EPL]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane % LPR;
+  // rows of one wave: butterfly over the lane bits above the row
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float big = fmaxf(m[h], mo);
+      const float f1 = merge_weight(m[h], big), f2 = merge_weight(mo, big);
+      l[h] = f1 * l[h] + f2 * lo;
+      m[h] = big;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[h][e], off);
+        acc[h][e] = f1 * acc[h][e] + f2 * ao;
+      }
+    }
+  }
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ float s_acc[NW][G][D];
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[w][h][c * EPL + e] = acc[h][e];
+      if (c == 0) {
+        s_m[w][h] = m[h];
+        s_l[w][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  T* out = reinterpret_cast<T*>(a.out);
+  for (int t = threadIdx.x; t < G * D; t += NW * 64) {
+    const int h = t / D, d = t % D;
+    float big = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float f = merge_weight(s_m[k][h], big);
+      lsum += f * s_l[k][h];
+      o += f * s_acc[k][h][d];
+    }
+    const int hq = wk.g * G + h;
+    const int64_t row = (int64_t)wk.i * a.num_q_heads + hq;
+    const float val = lsum > 0.0f ? o / lsum : 0.0f;
+    if (wk.nparts == 1) {
+      Elem<T>::store(out + row * D + d, val);
+    } else {
+      const int64_t prow = row * a.max_parts + wk.j;
+      a.part_o[prow * D + d] = val;
+      if (d == 0) {
+        a.part_ml[prow * 2 + 0] = big;
+        a.part_ml[prow * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// Decodes blockIdx.x into (KV head, sequence, partition); returns false if
+// the workgroup has nothing to do (after writing zeros for empty sequences).
+template <typename T, int D, int BS, int G, int NW>
+__device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk) {
+  int id = blockIdx.x;
+  wk.g = id % a.num_kv_heads;
+  id /= a.num_kv_heads;
+  wk.i = id % a.num_seqs;
+  wk.j = id / a.num_seqs;
+  wk.len = checked_len(a, wk.i);
+  wk.nparts = (wk.len + a.part_tokens - 1) / a.part_tokens;
+  if (wk.len == 0) {
+    if (wk.j == 0) write_zero_rows<T, D, G, NW>(a, wk.i, wk.g);
+    return false;
+  }
+  if (wk.j >= wk.nparts) return false;
+  wk.tok0 = wk.j * a.part_tokens;
+  wk.tok1 = min(wk.len, wk.tok0 + a.part_tokens);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// VALU partition kernel
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_partition_valu(DecodeArgs a) {
+  constexpr int S = sizeof(T);
+  constexpr int EPL = Elem<T>::kPerLoad;  // elements per 16-byte lane load
+  constexpr int LPR = D / EPL;            // lanes holding one token row
+  constexpr int RPI = 64 / LPR;           // token rows per wave-wide load
+  constexpr int NLB = BS / RPI;           // loads per block per lane
+  static_assert(LPR * 16 == D * S, "row must split into 16-byte lane chunks");
+  constexpr int64_t kHeadBytes = (int64_t)BS * D * S;
+
+  PartitionWork wk;
+  if (!setup_partition<T, D, BS, G, NW>(a, wk)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane / LPR, c = lane % LPR;
+  const int64_t blk_bytes = kHeadBytes * a.num_kv_heads;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + wk.g * kHeadBytes;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + wk.g * kHeadBytes;
+
+  float qf[G][EPL];
+  {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)wk.i * a.num_q_heads + wk.g * G) * D + c * EPL) * S;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      Elem<T>::unpack(ld16(qp, h * D * S), qf[h]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] *= a.qscale;
+    }
+  }
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+  }
+
+  const int blk0 = wk.tok0 / BS;
+  const int nblk = (wk.tok1 - wk.tok0 + BS - 1) / BS;
+  for (int b = w; b < nblk; b += NW) {
+    const int lb = blk0 + b;
+    const int phys = checked_block(a, wk.i, lb);
+    const char* kb = kbase + (int64_t)phys * blk_bytes;
+    const char* vb = vbase + (int64_t)phys * blk_bytes;
+    uint4 kr[NLB], vr[NLB];
+#pragma unroll
+    for (int n = 0; n < NLB; ++n) kr[n] = ld16(kb, n * RPI * D * S + lane * 16);
+#pragma unroll
+    for (int n = 0; n < NLB; ++n) vr[n] = ld16(vb, n * RPI * D * S + lane * 16);
+
+    const int pos0 = lb * BS + r;  // position of this row's first token
+    const bool full = lb * BS + BS <= wk.tok1;
+    float s[NLB][G];
+#pragma unroll
+    for (int n = 0; n < NLB; ++n) {
+      float kf[EPL];
+      Elem<T>::unpack(kr[n], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) t = fmaf(qf[h][e], kf[e], t);
+        s[n][h] = group_sum<LPR>(t);
+      }
+    }
+    bool ok[NLB];
+#pragma unroll
+    for (int n = 0; n < NLB; ++n) ok[n] = full || (pos0 + n * RPI < wk.tok1);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float bm = -INFINITY;
+#pragma unroll
+      for (int n = 0; n < NLB; ++n) bm = ok[n] ? fmaxf(bm, s[n][h]) : bm;
+      const float mn = fmaxf(m[h], bm);
+      const float alpha = mn == m[h] ? 1.0f : exp2_fast(m[h] - mn);
+      m[h] = mn;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int n = 0; n < NLB; ++n) {
+      float vf[EPL];
+      Elem<T>::unpack(vr[n], vf);
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = ok[n] ? vf[e] : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = ok[n] ? exp2_fast(s[n][h] - m[h]) : 0.0f;
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  }
+  finish_partition<T, D, G, NW, LPR, EPL>(a, wk, m, l, acc);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA partition kernel (bf16, D = 128, G in {1, 2, 4})
+// ---------------------------------------------------------------------------
+// Positions are taken 16 at a time ("chunk"; a 16-token block, or half of a
+// 32-token block). Lane l: R = l / 16 (row), c = l % 16.
+//   K load s (s = 0..3): token (l % 16), dims [32 s + 8 R, +8)  -> A operand
+//   q operand step s:    query row (l % 16) % G, same dims        -> B operand
+//   MFMA result reg r:   score of token 4 R + r for head (l % G)
+//   V load jj (0..3):    token 4 R + jj, dims [8 c, +8), coalesced 256 B rows
+// Row R is one softmax stream over tokens {4R .. 4R+3} of every chunk.
+template <int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
+  constexpr int D = 128;
+  constexpr int ROW = D * 2;                      // bytes per token row
+  constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
+  static_assert(BS % 16 == 0, "block must hold whole 16-token chunks");
+
+  PartitionWork wk;
+  if (!setup_partition<uint16_t, D, BS, G, NW>(a, wk)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = lane >> 4, c = lane & 15;
+  const int64_t blk_bytes = kHeadBytes * a.num_kv_heads;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + wk.g * kHeadBytes;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + wk.g * kHeadBytes;
+
+  bf16x8_t qop[4];
+  {
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)wk.i * a.num_q_heads + wk.g * G + (lane % G)) * D + 8 * R) * 2;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8_t, ld16(qp, s * 64));
+  }
+  const uint32_t k_off = (uint32_t)(c * ROW + R * 16);       // + s * 64
+  const uint32_t v_off = (uint32_t)(4 * R * ROW + c * 16);   // + jj * ROW
+
+  float m = -INFINITY, lsum = 0.0f;  // stream of row R, head lane % G
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+
+  const int nch = (wk.tok1 - wk.tok0 + 15) / 16;
+  for (int cc = w; cc < nch; cc += NW) {
+    const int tokc = wk.tok0 + cc * 16;
+    const int lb = tokc / BS;
+    const int phys = checked_block(a, wk.i, lb);
+    const int64_t base = (int64_t)phys * blk_bytes + (int64_t)(tokc % BS) * ROW;
+    const char* kb = kbase + base;
+    const char* vb = vbase + base;
+    uint4 kr[4], vr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kr[s] = ld16(kb, k_off + s * 64);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) vr[jj] = ld16(vb, v_off + jj * ROW);
+
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[s],
+                                                   sc, 0, 0, 0);
+    const bool full = tokc + 16 <= wk.tok1;
+    float sv[4];
+    bool ok[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = sc[r] * a.qscale;
+      ok[r] = full || (tokc + 4 * R + r < wk.tok1);
+      bm = ok[r] ? fmaxf(bm, sv[r]) : bm;
+    }
+    const float mn = fmaxf(m, bm);
+    const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
+    m = mn;
+    float p[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = ok[r] ? exp2_fast(sv[r] - mn) : 0.0f;
+      psum += p[r];
+    }
+    lsum = lsum * alpha + psum;
+    float al[G], ph[4][G];
+    quad_spread<G>(alpha, al);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) quad_spread<G>(p[r], ph[r]);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float vf[8];
+      Elem<uint16_t>::unpack(vr[jj], vf);
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[e] = ok[jj] ? vf[e] : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[jj][h], vf[e], acc[h][e]);
+    }
+  }
+  float mh[G], lh[G];
+  quad_spread<G>(m, mh);
+  quad_spread<G>(lsum, lh);
+  finish_partition<uint16_t, D, G, NW, 16, 8>(a, wk, mh, lh, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Partition merge
+// ---------------------------------------------------------------------------
+// One wave per (sequence, query head); only sequences with more than one
+// partition have anything to merge.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
+  const int hq = blockIdx.x % a.num_q_heads;
+  const int i = blockIdx.x / a.num_q_heads;
+  int len = a.seq_lens[i];
+  len = len < 0 ? 0 : min(len, a.len_cap);
+  const int np = (len + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+  const int64_t prow = ((int64_t)i * a.num_q_heads + hq) * a.max_parts;
+  const float* ml = a.part_ml + prow * 2;
+  const float* po = a.part_o + prow * D;
+  const int lane = threadIdx.x;
+  float big = -INFINITY;
+  for (int j = lane; j < np; j += 64) big = fmaxf(big, ml[2 * j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
+  float wsum = 0.0f;
+  float o[D / 64];
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) o[k] = 0.0f;
+  for (int j = 0; j < np; ++j) {
+    const float wj = ml[2 * j + 1] * merge_weight(ml[2 * j], big);
+    wsum += wj;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) o[k] = fmaf(wj, po[(int64_t)j * D + lane + 64 * k], o[k]);
+  }
+  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)i * a.num_q_heads + hq) * D;
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) Elem<T>::store(out + lane + 64 * k, o[k] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Slot write and block copy
+// ---------------------------------------------------------------------------
+// One thread per 16-byte chunk of a (token, head) row, K and V together.
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)a.num_kv_heads * a.row_chunks;
+  if (idx >= per_token * a.num_tokens) return;
+  const int64_t t = idx / per_token;
+  const int64_t rem = idx - t * per_token;
+  const int h = (int)(rem / a.row_chunks);
+  const int c = (int)(rem - (int64_t)h * a.row_chunks);
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    if (rem == 0) flag_error(kErrSlot);
+    return;
+  }
+  const int64_t b = slot / a.block_size, o = slot - b * a.block_size;
+  const int64_t dst = ((b * a.num_kv_heads + h) * a.block_size + o) * a.row_chunks + c;
+  const int64_t src = idx;  // [T][Hkv][row_chunks] is exactly the thread order
+  reinterpret_cast<uint4*>(a.k_pool)[dst] = reinterpret_cast<const uint4*>(a.k)[src];
+  reinterpret_cast<uint4*>(a.v_pool)[dst] = reinterpret_cast<const uint4*>(a.v)[src];
+}
+
+// grid.x = pair, grid.z = pool (0 K, 1 V); grid.y strides over the block.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+  const int n = blockIdx.x;
+  const int64_t src = a.pairs[2 * n], dst = a.pairs[2 * n + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) {
+    if (blockIdx.y == 0 && threadIdx.x == 0 && blockIdx.z == 0) flag_error(kErrCopyPair);
+    return;
+  }
+  uint4* pool = reinterpret_cast<uint4*>(blockIdx.z == 0 ? a.k_pool : a.v_pool);
+  const uint4* s = pool + src * a.block_chunks;
+  uint4* d = pool + dst * a.block_chunks;
+  for (int64_t k = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; k < a.block_chunks;
+       k += (int64_t)gridDim.y * blockDim.x)
+    d[k] = s[k];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+using PartitionKernel = void (*)(DecodeArgs);
+
+template <typename T, int D, int BS>
+static PartitionKernel pick_valu(int group) {
+  switch (group) {
+    case 1: return decode_partition_valu<T, D, BS, 1, kDecodeWaves>;
+    case 2: return decode_partition_valu<T, D, BS, 2, kDecodeWaves>;
+    case 4: return decode_partition_valu<T, D, BS, 4, kDecodeWaves>;
+    case 8: return decode_partition_valu<T, D, BS, 8, kDecodeWaves>;
+    default: return nullptr;
+  }
+}
+
+template <typename T>
+static PartitionKernel pick_valu_t(int d, int bs, int group) {
+  if (d == 64 && bs == 16) return pick_valu<T, 64, 16>(group);
+  if (d == 64 && bs == 32) return pick_valu<T, 64, 32>(group);
+  if (d == 128 && bs == 16) return pick_valu<T, 128, 16>(group);
+  if (d == 128 && bs == 32) return pick_valu<T, 128, 32>(group);
+  return nullptr;
+}
+
+template <int BS>
+static PartitionKernel pick_mfma(int group) {
+  switch (group) {
+    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves>;
+    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves>;
+    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves>;
+    default: return nullptr;
+  }
+}
+
+static PartitionKernel pick_partition(const DecodeKey& k) {
+  if (k.variant == 1) {
+    if (k.dtype == 0) return pick_valu_t<float>(k.head_dim, k.block_size, k.group);
+    if (k.dtype == 1) return pick_valu_t<uint16_t>(k.head_dim, k.block_size, k.group);
+    return nullptr;
+  }
+  if (k.variant == 2) {
+    if (k.dtype != 1 || k.head_dim != 128) return nullptr;
+    if (k.block_size == 16) return pick_mfma<16>(k.group);
+    if (k.block_size == 32) return pick_mfma<32>(k.group);
+  }
+  return nullptr;
+}
+
+bool decode_partition_supported(const DecodeKey& key) { return pick_partition(key) != nullptr; }
+
+hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
+                                   hipStream_t stream) {
+  PartitionKernel kern = pick_partition(key);
+  if (!kern) return hipErrorInvalidValue;
+  const int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
+  if (groups <= 0) return hipSuccess;
+  if (groups > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kDecodeWaves * 64), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
+                                hipStream_t stream) {
+  if (args.max_parts <= 1) return hipSuccess;
+  const int64_t groups = (int64_t)args.num_seqs * args.num_q_heads;
+  if (groups <= 0) return hipSuccess;
+  if (groups > 0x7fffffff) return hipErrorInvalidValue;
+  PartitionKernel kern = nullptr;
+  if (dtype == 0 && head_dim == 64) kern = decode_reduce<float, 64>;
+  if (dtype == 0 && head_dim == 128) kern = decode_reduce<float, 128>;
+  if (dtype == 1 && head_dim == 64) kern = decode_reduce<uint16_t, 64>;
+  if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
+  if (!kern) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(64), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream) {
+  const int64_t total = (int64_t)args.num_tokens * args.num_kv_heads * args.row_chunks;
+  if (total <= 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream) {
+  if (args.num_pairs <= 0) return hipSuccess;
+  const int64_t per_wg = 256 * 4;  // 16-byte chunks per workgroup sweep
+  int64_t gy = (args.block_chunks + per_wg - 1) / per_wg;
+  if (gy < 1) gy = 1;
+  if (gy > 1024) gy = 1024;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)args.num_pairs, (unsigned)gy, 2),
+                     dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  uint32_t v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_error_word), sizeof(v), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  if (v != 0) {
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_error_word), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+  }
+  *flags = v;
+  return hipSuccess;
+}
+
+}  // namespace pa

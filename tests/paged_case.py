@@ -1,0 +1,262 @@
+"""Builds one paged-decode case on both sides from the same seeded draws.
+
+HIP side: libpa's block manager allocates, the pools live on the GPU, the new
+tokens go through pa_copy_blocks / pa_reshape_and_cache and the step ends
+with pa_decode. Oracle side: the oracle's own block manager mirror and its
+own slot write / block copy on host copies of the initial pools, then the
+float64 decode. The two share only the draws from `workloads`.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import paged_kv_cache_343_amd as P
+import workloads as W
+from oracle import pa_oracle as O
+
+TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}   # (abs, rel): |d| <= abs + rel*|ref|
+
+
+def torch_dtype(dtype):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def to_storage_np(t: torch.Tensor) -> np.ndarray:
+    """Host numpy copy in storage form (float32, or uint16 bf16 bits)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Device tensor from storage form (float32, or uint16 bf16 bits)."""
+    x = np.ascontiguousarray(x)
+    if dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(x).to(device)
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    atol, rtol = TOL[dtype]
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    big = np.abs(ref) >= 1e-3
+    max_abs = float(err.max()) if err.size else 0.0
+    max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
+                           f"max_abs={max_abs:.3g} max_rel={max_rel:.3g}")
+    return max_abs, max_rel
+
+
+@dataclass
+class Case:
+    w: W.Workload
+    dtype: str
+    B: int
+    hq: int
+    hkv: int
+    d: int
+    bs: int
+    nb: int
+    maxb: int
+    scale: float
+    device: object
+    # HIP side
+    q: torch.Tensor = None
+    k_pool: torch.Tensor = None
+    v_pool: torch.Tensor = None
+    tables: torch.Tensor = None
+    lens: torch.Tensor = None
+    bm: P.BlockManager = None
+    # oracle side (host)
+    oq: np.ndarray = None
+    ok_pool: np.ndarray = None
+    ov_pool: np.ndarray = None
+    otables: np.ndarray = None
+    olens: np.ndarray = None
+    obm: O.OracleBlockManager = None
+    max_len: int = 0
+    extra: dict = field(default_factory=dict)
+
+    def decode(self, *, variant=P.PA_VARIANT_AUTO, partition_tokens=0, max_seq_len=None):
+        out = torch.empty_like(self.q)
+        P.pa_decode(self.q, self.k_pool, self.v_pool, self.tables, self.lens, self.scale, out,
+                    max_seq_len=max_seq_len or self.max_len, partition_tokens=partition_tokens,
+                    variant=variant)
+        return out
+
+    def oracle_rows(self, pairs):
+        """Oracle outputs (float64) for the listed (seq, q_head) pairs."""
+        q64 = O.as_f64(self.oq, self.dtype)
+        res = []
+        for i, h in pairs:
+            g = O.kv_head_of(h, self.hq, self.hkv)
+            L = int(self.olens[i])
+            phys, off = O.positions_to_rows(self.otables[i], L, self.bs)
+            kk = O.as_f64(self.ok_pool[phys, g, off, :], self.dtype)
+            vv = O.as_f64(self.ov_pool[phys, g, off, :], self.dtype)
+            if L == 0:
+                res.append(np.zeros(self.d))
+                continue
+            s = self.scale * (kk @ q64[i, h])
+            e = np.exp(s - s.max())
+            res.append((e @ vv) / e.sum())
+        return np.stack(res)
+
+    def oracle_all(self):
+        q64 = O.as_f64(self.oq, self.dtype)
+        return O.decode(q64, O.as_f64(self.ok_pool, self.dtype), O.as_f64(self.ov_pool, self.dtype),
+                        self.otables, self.olens, self.scale)
+
+
+def scale_for(d: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def build(w: W.Workload, device, *, lens=None, pool_on_device=False, append=True,
+          prefix=None, max_blocks=None, nb=None):
+    """Draw inputs for workload `w`, allocate on both sides, append one token
+    per sequence (unless append=False) through pa_reshape_and_cache, and
+    return a Case ready to decode. `lens` overrides the drawn lengths (the
+    draws still happen, to keep the generator order)."""
+    rng = np.random.default_rng(w.seed)
+    drawn = W.draw_lengths(w, rng)
+    ctx = np.asarray(drawn if lens is None else lens, dtype=np.int64)
+    B = len(ctx)
+    bs, hq, hkv, d = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
+    final = ctx + (1 if append else 0)
+    occupied = int(sum(O.blocks_needed(int(L), bs) for L in final))
+    nb = nb or W.pool_blocks(w, occupied)
+    nb = max(nb, occupied)
+    order = W.free_order(nb, rng)
+    dtype = w.dtype
+    q_np = W.normal_values((B, hq, d), rng, dtype)
+    knew = W.normal_values((B, hkv, d), rng, dtype)
+    vnew = W.normal_values((B, hkv, d), rng, dtype)
+    if pool_on_device:
+        kp_t = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 1, dtype, device)
+        vp_t = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 2, dtype, device)
+        kp_np, vp_np = to_storage_np(kp_t), to_storage_np(vp_t)
+    else:
+        kp_np = W.normal_values((nb, hkv, bs, d), rng, dtype)
+        vp_np = W.normal_values((nb, hkv, bs, d), rng, dtype)
+        kp_t, vp_t = to_device(kp_np, dtype, device), to_device(vp_np, dtype, device)
+    maxb = max_blocks or max(1, max(O.blocks_needed(int(L), bs) for L in final))
+    c = Case(w=w, dtype=dtype, B=B, hq=hq, hkv=hkv, d=d, bs=bs, nb=nb, maxb=maxb,
+             scale=scale_for(d), device=device)
+    # HIP side
+    c.bm = P.BlockManager(nb, bs, order)
+    for i, L in enumerate(ctx):
+        c.bm.add_seq(i, int(L))
+    c.k_pool, c.v_pool = kp_t, vp_t
+    c.q = to_device(q_np, dtype, device)
+    # oracle side
+    c.obm = O.OracleBlockManager(nb, bs, order)
+    for i, L in enumerate(ctx):
+        c.obm.add_seq(i, int(L))
+    c.oq, c.ok_pool, c.ov_pool = q_np, kp_np.copy(), vp_np.copy()
+    if append:
+        slots, pairs = c.bm.append_slots(list(range(B)))
+        ores = c.obm.append_slots(list(range(B)))
+        assert slots.tolist() == [s for s, _ in ores], "slot mapping differs from the oracle"
+        assert pairs.shape[0] == 0
+        P.pa_reshape_and_cache(to_device(knew, dtype, device), to_device(vnew, dtype, device),
+                               torch.from_numpy(slots).to(device), c.k_pool, c.v_pool)
+        O.reshape_and_cache(knew, vnew, np.array([s for s, _ in ores]), c.ok_pool, c.ov_pool)
+        c.extra["slots"] = slots
+    tab, ln = c.bm.export(list(range(B)), maxb)
+    otab, oln = c.obm.export(list(range(B)), maxb)
+    assert np.array_equal(tab, otab) and np.array_equal(ln, oln), "block tables differ"
+    c.tables = torch.from_numpy(tab).to(device)
+    c.lens = torch.from_numpy(ln).to(device)
+    c.otables, c.olens = otab, oln
+    c.max_len = int(max(1, ln.max()))
+    return c
+
+
+def build_shared_prefix(w: W.Workload, device, *, prefix_len=None, groups=None, long_seqs=None,
+                        pool_on_device=True):
+    """Shared-prefix workload: per group, one parent holds the prompt, the
+    other samples fork it; every sample then appends its private suffix
+    (copy-on-write on the first write into the shared partial block), and a
+    final decode step appends one token per sequence."""
+    rng = np.random.default_rng(w.seed)
+    suffix = W.draw_lengths(w, rng)
+    samples = w.extra["samples"]
+    ngroups = groups or w.extra["groups"]
+    prefix_len = prefix_len or w.lengths[1]
+    n_samp = ngroups * samples
+    n_long = (long_seqs if long_seqs is not None else w.extra.get("long_seqs", 0))
+    long_len = w.extra.get("long_len", 0)
+    suffix_s = suffix[:n_samp] if "long_seqs" not in w.extra else suffix[:w.extra["groups"] * samples][:n_samp]
+    bs, hq, hkv, d, dtype = w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype
+    B = n_samp + n_long
+    final = [prefix_len + int(s) + 1 for s in suffix_s] + [long_len + 1] * n_long
+    shared_blocks = ngroups * O.blocks_needed(prefix_len, bs)
+    private = sum(O.blocks_needed(L, bs) - prefix_len // bs for L in final[:n_samp])
+    occupied = shared_blocks + private + n_long * O.blocks_needed(long_len + 1, bs)
+    nb = W.pool_blocks(w, occupied)
+    order = W.free_order(nb, rng)
+    q_np = W.normal_values((B, hq, d), rng, dtype)
+    n_new = int(suffix_s.sum()) + B
+    knew = W.normal_values((n_new, hkv, d), rng, dtype)
+    vnew = W.normal_values((n_new, hkv, d), rng, dtype)
+    if pool_on_device:
+        kp_t = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 1, dtype, device)
+        vp_t = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 2, dtype, device)
+        kp_np, vp_np = to_storage_np(kp_t), to_storage_np(vp_t)
+    else:
+        kp_np = W.normal_values((nb, hkv, bs, d), rng, dtype)
+        vp_np = W.normal_values((nb, hkv, bs, d), rng, dtype)
+        kp_t, vp_t = to_device(kp_np, dtype, device), to_device(vp_np, dtype, device)
+    maxb = max(O.blocks_needed(L, bs) for L in final)
+    c = Case(w=w, dtype=dtype, B=B, hq=hq, hkv=hkv, d=d, bs=bs, nb=nb, maxb=maxb,
+             scale=scale_for(d), device=device)
+    c.bm, c.obm = P.BlockManager(nb, bs, order), O.OracleBlockManager(nb, bs, order)
+    for m in (c.bm, c.obm):
+        for gi in range(ngroups):
+            m.add_seq(gi * samples, prefix_len)
+            for s in range(1, samples):
+                m.fork(gi * samples, gi * samples + s)
+        for k in range(n_long):
+            m.add_seq(n_samp + k, long_len)
+    c.k_pool, c.v_pool, c.q = kp_t, vp_t, to_device(q_np, dtype, device)
+    c.oq, c.ok_pool, c.ov_pool = q_np, kp_np.copy(), vp_np.copy()
+    # private suffixes, token by token on the host side; one copy + one write
+    all_slots, all_pairs, oslots, opairs = [], [], [], []
+    for step in range(int(suffix_s.max()) if n_samp else 0):
+        batch = [s for s in range(n_samp) if suffix_s[s] > step]
+        slots, pairs = c.bm.append_slots(batch)
+        ores = c.obm.append_slots(batch)
+        all_slots += slots.tolist()
+        all_pairs += pairs.tolist()
+        oslots += [s for s, _ in ores]
+        opairs += [list(cw) for _, cw in ores if cw is not None]
+    slots, pairs = c.bm.append_slots(list(range(B)))
+    ores = c.obm.append_slots(list(range(B)))
+    all_slots += slots.tolist(); all_pairs += pairs.tolist()
+    oslots += [s for s, _ in ores]; opairs += [list(cw) for _, cw in ores if cw is not None]
+    assert all_slots == oslots and all_pairs == opairs, "allocation differs from the oracle"
+    c.extra["cow_pairs"] = np.array(all_pairs, dtype=np.int64).reshape(-1, 2)
+    if all_pairs:
+        P.pa_copy_blocks(c.k_pool, c.v_pool, torch.tensor(all_pairs, dtype=torch.int64, device=device))
+        O.copy_blocks(c.ok_pool, c.ov_pool, np.array(opairs))
+    P.pa_reshape_and_cache(to_device(knew, dtype, device), to_device(vnew, dtype, device),
+                           torch.tensor(all_slots, dtype=torch.int64, device=device),
+                           c.k_pool, c.v_pool)
+    O.reshape_and_cache(knew, vnew, np.array(oslots), c.ok_pool, c.ov_pool)
+    tab, ln = c.bm.export(list(range(B)), maxb)
+    otab, oln = c.obm.export(list(range(B)), maxb)
+    assert np.array_equal(tab, otab) and np.array_equal(ln, oln)
+    c.tables, c.lens = torch.from_numpy(tab).to(device), torch.from_numpy(ln).to(device)
+    c.otables, c.olens = otab, oln
+    c.max_len = int(ln.max())
+    c.extra["prefix_len"] = prefix_len
+    c.extra["samples"] = samples
+    c.extra["groups"] = ngroups
+    return c
