@@ -4,12 +4,13 @@ One step = one decode step of the whole batch through one layer:
   host   libpa block manager reserves each sequence's next slot (a new block
          when the position starts one) and exports tables / lengths into a
          pinned staging buffer;
-  H2D    slots, lengths and block tables (one async copy each);
+  H2D    slots, lengths and block tables, packed, in one async copy on a
+         side stream (ordered before the step's kernels by an event);
   GPU    pa_reshape_and_cache (new K/V rows into their slots),
          pa_decode_partition (one workgroup per sequence x KV head x 512-token
          partition), pa_decode_reduce (log-sum-exp merge of partitions).
-The host work of step s+1 overlaps the GPU work of step s (double-buffered
-staging). Inputs (pools, q, new k/v) are resident in HBM before timing.
+The host work and the H2D copy of step s+1 overlap the GPU work of step s
+(double-buffered staging). Inputs (pools, q, new k/v) are resident in HBM before timing.
 
 Metric: effective KV GB/s = sum over steps of (sum_i L_i * 2 * Hkv * D * 2 B)
 divided by the timed wall time; L_i counts the tokens each decode attends to.
@@ -18,6 +19,7 @@ The roofline line uses the partition kernel's own time from HIP events.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -76,9 +78,22 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--block-order", default="shuffled", choices=["shuffled", "identity"],
+                    help="free-list order: a seeded permutation (scattered blocks, the "
+                         "default) or 0, 1, 2, ... (each sequence's blocks contiguous)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run pa_copy_blocks over this many MiB per "
+                         "pool (read and written) so that rocprofv3 counters of the decode "
+                         "kernel can be scaled by those of a copy of known size")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                         "this script with --copy-calibration-mib into a traffic record")
+    ap.add_argument("--traffic-out", default=None)
     args = ap.parse_args()
+    if args.traffic_from:
+        return summarise_traffic(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by sequence or KV head with no exchange, see the design notes.",
@@ -112,6 +127,8 @@ def main() -> int:
     occupied = int(sum(-(-int(L) // bs) for L in ctx + 1))
     nb = max(W.pool_blocks(w, occupied), int(sum(-(-int(L) // bs) for L in final)))
     order = W.free_order(nb, rng)
+    if args.block_order == "identity":
+        order = np.arange(nb, dtype=np.int32)
     maxb = int(-(-int(final.max()) // bs))
     max_len = int(final.max())
     k_pool = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 1, w.dtype, dev)
@@ -130,58 +147,131 @@ def main() -> int:
     for i, L in enumerate(ctx):
         bm.add_seq(i, int(L))
     seq_ids = np.arange(B, dtype=np.int32)
-    # double-buffered pinned staging and device copies
-    stage = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
-                  pairs=torch.empty(2 * B, dtype=torch.int64, pin_memory=True),
-                  tables=torch.empty((B, maxb), dtype=torch.int32, pin_memory=True),
-                  lens=torch.empty(B, dtype=torch.int32, pin_memory=True)) for _ in range(2)]
-    devbuf = [dict(slots=torch.empty(B, dtype=torch.int64, device=dev),
-                   tables=torch.empty((B, maxb), dtype=torch.int32, device=dev),
-                   lens=torch.empty(B, dtype=torch.int32, device=dev)) for _ in range(2)]
-    copied = [None, None]
+    # Per step the host produces slots (int64 [B]), lengths (int32 [B]) and
+    # block tables (int32 [B, maxb]); they travel in one packed pinned buffer
+    # and one H2D copy on a side stream. NBUF staging/device buffer pairs let
+    # the host run up to NBUF - 1 steps ahead, so host jitter never leaves the
+    # GPU waiting, and the copy of step s+1 overlaps the kernels of step s.
+    NBUF = 4
+    n_slots, n_lens, n_tab = 8 * B, 4 * B, 4 * B * maxb
+    pack_bytes = n_slots + n_lens + n_tab
+
+    def views(buf):
+        return dict(slots=buf[:n_slots].view(torch.int64),
+                    lens=buf[n_slots:n_slots + n_lens].view(torch.int32),
+                    tables=buf[n_slots + n_lens:].view(torch.int32).view(B, maxb))
+
+    stage_raw = [torch.empty(pack_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(NBUF)]
+    dev_raw = [torch.empty(pack_bytes, dtype=torch.uint8, device=dev) for _ in range(NBUF)]
+    stage = [views(x) for x in stage_raw]
+    devbuf = [views(x) for x in dev_raw]
+    pairs_host = np.empty(2 * B, dtype=np.int64)
+    # Two non-default streams (default priority): on ROCm an H2D copy issued
+    # on the null stream, or ordered after null-stream work, blocks the host
+    # until the GPU drains, which would serialise host and GPU work.
+    compute = torch.cuda.Stream(dev)
+    copier = torch.cuda.Stream(dev)
+    torch.cuda.synchronize(dev)      # inputs drawn on the null stream are ready
+    copied = [None] * NBUF    # H2D copy of staging buffer b done
+    done = [None] * NBUF      # kernels reading device buffer b done
     shape = P.DecodeShape(B, hq, hkv, d, bs, nb, maxb, max_len, ptok,
                           P.PA_BF16 if w.dtype == "bf16" else P.PA_F32, variant)
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     step_bytes = []
+    host_s = [0.0]  # host time per timed step, waits excluded
     ev = []  # per step: (reshape start, partition start, partition end, reduce end)
+
+    # Host side of a step through the raw C ABI (block manager: append one
+    # token per sequence, then export tables and lengths straight into the
+    # pinned staging buffer), pointers resolved once.
+    Lh = P.lib()
+    ids_ptr = seq_ids.ctypes.data
+    pairs_ptr = pairs_host.ctypes.data
+    ncow = ctypes.c_int32(0)
+    stage_ptr = [{k: v.data_ptr() for k, v in st.items()} for st in stage]
+    lens_np = [st["lens"].numpy() for st in stage]
 
     def host_step(s: int, b: int):
         if copied[b] is not None:
+            w0 = time.perf_counter()
             copied[b].synchronize()          # the staging buffer's last copy has landed
-        st = stage[b]
-        ncow = bm.append_slots_into(seq_ids, st["slots"].numpy(), st["pairs"].numpy())
-        if ncow:
+            host_s[0] -= time.perf_counter() - w0
+        sp = stage_ptr[b]
+        st = Lh.pa_bm_append_slots(bm._h, ids_ptr, B, sp["slots"], pairs_ptr, ctypes.byref(ncow))
+        if st != 0:
+            raise P.PaError(st, "pa_bm_append_slots")
+        if ncow.value:
             raise RuntimeError("no copy-on-write expected in this workload")
-        bm.export(seq_ids, maxb, st["tables"].numpy(), st["lens"].numpy())
-        step_bytes.append(int(st["lens"].numpy().astype(np.int64).sum()) * 2 * hkv * d * eb)
+        st = Lh.pa_bm_export(bm._h, ids_ptr, B, maxb, sp["tables"], sp["lens"])
+        if st != 0:
+            raise P.PaError(st, "pa_bm_export")
+        step_bytes.append(int(lens_np[b].sum(dtype=np.int64)) * 2 * hkv * d * eb)
+
+    # Raw C-ABI calls with pointers resolved once: the step's host cost stays
+    # far below its GPU time, so the GPU never waits for the host.
+    L = P.lib()
+    c_scale = ctypes.c_float(scale)
+    shape_ref = ctypes.byref(shape)
+    ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    kp_ptr, vp_ptr, out_ptr = k_pool.data_ptr(), v_pool.data_ptr(), out.data_ptr()
+    dt_code = P.PA_BF16 if w.dtype == "bf16" else P.PA_F32
+    cs = compute.cuda_stream
+    dptr = [{k: v.data_ptr() for k, v in db.items()} for db in devbuf]
+    def check(st, what):
+        if st != 0:
+            raise P.PaError(st, what)
+
+    copy_ev = [torch.cuda.Event() for _ in range(NBUF)]
+    done_ev = [torch.cuda.Event() for _ in range(NBUF)]
+    time_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    # The upload is one hipMemcpyAsync on the side stream, called directly
+    # (torch's stream-switching context costs tens of microseconds per use).
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
+    HIP_H2D = 1
+    copier_handle = copier.cuda_stream
+    stage_base = [x.data_ptr() for x in stage_raw]
+    dev_base = [x.data_ptr() for x in dev_raw]
 
     def gpu_step(s: int, b: int, timed: bool):
-        st, db = stage[b], devbuf[b]
-        for k in ("slots", "tables", "lens"):
-            db[k].copy_(st[k], non_blocking=True)
-        e = torch.cuda.Event()
-        e.record()
-        copied[b] = e
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        db = dptr[b]
+        if done[b] is not None:
+            # step s-NBUF no longer reads device buffer b; waited on the host
+            # (a GPU-side wait would make the runtime run the copy
+            # synchronously), normally long since complete
+            done[b].synchronize()
+        if hip.hipMemcpyAsync(dev_base[b], stage_base[b], pack_bytes, HIP_H2D, copier_handle):
+            raise RuntimeError("hipMemcpyAsync failed")
+        copied[b] = copy_ev[b]
+        copied[b].record(copier)
+        compute.wait_event(copied[b])
+        evs = time_ev[s - args.warmup] if timed else None
         if timed:
-            evs[0].record()
-        P.pa_reshape_and_cache(kn_all[s], vn_all[s], db["slots"], k_pool, v_pool)
+            evs[0].record(compute)
+        check(L.pa_reshape_and_cache(kn_all[s].data_ptr(), vn_all[s].data_ptr(), db["slots"],
+                                     kp_ptr, vp_ptr, B, hkv, d, bs, nb, dt_code, cs),
+              "pa_reshape_and_cache")
         if timed:
-            evs[1].record()
-        P.pa_decode_partition(q_all[s], k_pool, v_pool, db["tables"], db["lens"], scale, out,
-                              max_seq_len=max_len, partition_tokens=ptok, variant=variant,
-                              workspace=ws)
+            evs[1].record(compute)
+        check(L.pa_decode_partition(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"], db["lens"],
+                                    c_scale, out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
+              "pa_decode_partition")
         if timed:
-            evs[2].record()
-        P.pa_decode_reduce(q_all[s], k_pool, db["tables"], db["lens"], out, max_seq_len=max_len,
-                           partition_tokens=ptok, variant=variant, workspace=ws)
+            evs[2].record(compute)
+        check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
+              "pa_decode_reduce")
         if timed:
-            evs[3].record()
+            evs[3].record(compute)
             ev.append(evs)
+        done[b] = done_ev[b]
+        done[b].record(compute)
 
     for s in range(args.warmup):
-        host_step(s, s % 2)
-        gpu_step(s, s % 2, False)
+        host_step(s, s % NBUF)
+        gpu_step(s, s % NBUF, False)
     torch.cuda.synchronize()
     log("warmup done")
     if P.pa_device_errors() != 0:
@@ -189,14 +279,16 @@ def main() -> int:
     step_bytes.clear()
     t0 = time.perf_counter()
     for s in range(args.warmup, nsteps):
-        host_step(s, s % 2)
-        gpu_step(s, s % 2, True)
+        h0 = time.perf_counter()
+        host_step(s, s % NBUF)
+        gpu_step(s, s % NBUF, True)
+        host_s[0] += time.perf_counter() - h0
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if P.pa_device_errors() != 0:
         raise RuntimeError("device index error during the timed steps")
 
-    log(f"timed {args.steps} steps in {t1 - t0:.3f} s")
+    log(f"timed {args.steps} steps in {t1 - t0:.3f} s; host enqueue {1e6 * host_s[0] / args.steps:.0f} us/step")
     wall = t1 - t0
     K = args.steps
     total_bytes = sum(step_bytes)
@@ -204,6 +296,9 @@ def main() -> int:
     part_ms = [a.elapsed_time(b) for _, a, b, _ in ev]
     red_ms = [a.elapsed_time(b) for _, _, a, b in ev]
     cache_ms = [a.elapsed_time(b) for a, b, _, _ in ev]
+    period_ms = [ev[k][0].elapsed_time(ev[k + 1][0]) for k in range(len(ev) - 1)]
+    gap_ms = [ev[k][3].elapsed_time(ev[k + 1][0]) for k in range(len(ev) - 1)]
+    log(f"GPU step period {1e3 * np.mean(period_ms):.1f} us, gap between steps {1e3 * np.mean(gap_ms):.1f} us")
     part_avg_s = float(np.mean(part_ms)) / 1e3
     bytes_per_launch = total_bytes / K
     achieved = bytes_per_launch / part_avg_s / 1e9
@@ -225,8 +320,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": B, "num_q_heads": hq, "num_kv_heads": hkv,
                    "head_dim": d, "block_size": bs, "partition_tokens": ptok,
-                   "context_tokens": f"U{{{w.lengths[1]}..{w.lengths[2]}}}+step",
-                   "kernel": vname, "parallelism": "single GPU"},
+                   "context_tokens": (f"U{{{w.lengths[1]}..{w.lengths[2]}}}+step"
+                                      if w.lengths[0] == "uniform" else f"{w.lengths}+step"),
+                   "kernel": vname, "block_order": args.block_order,
+                   "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(B * K / wall, 1),
         "kernels_us": {"partition": round(1e3 * float(np.mean(part_ms)), 2),
@@ -238,11 +335,97 @@ def main() -> int:
                      "kernel": "decode_partition_" + vname,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
     }
+    if args.copy_calibration_mib > 0:
+        result["copy_calibration"] = copy_calibration(P, torch, dev, args.copy_calibration_mib,
+                                                      hkv * bs * d * eb)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, kp_host, vp_host, storage_np(q_all[nsteps - 1]),
                                               ctx, order, nb, nsteps, scale, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def copy_calibration(P, torch, dev, mib: int, block_bytes: int) -> dict:
+    """pa_copy_blocks over a fresh pair of pools: n blocks copied to n other
+    blocks in each of the K and V pools, so that exactly 2 * n * block_bytes
+    bytes are read and as many written. Its FETCH_SIZE / WRITE_SIZE readings
+    calibrate the counters (KiB per dispatch) against a known byte count."""
+    n = max(1, mib * 2**20 // block_bytes)
+    kp = torch.zeros((2 * n, block_bytes // 2), dtype=torch.int16, device=dev)
+    vp = torch.zeros_like(kp)
+    pairs = torch.stack([torch.arange(n), torch.arange(n, 2 * n)], dim=1).to(
+        device=dev, dtype=torch.int64).contiguous()
+    for _ in range(3):
+        P.pa_copy_blocks(kp.view(2 * n, 1, 1, block_bytes // 2), vp.view(2 * n, 1, 1, block_bytes // 2),
+                         pairs)
+    torch.cuda.synchronize()
+    return {"pairs": n, "block_bytes": block_bytes, "read_bytes": 2 * n * block_bytes,
+            "write_bytes": 2 * n * block_bytes, "launches": 3}
+
+
+def _counter_rows(directory: str, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {directory}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarise_traffic(args) -> int:
+    """HBM bytes per partition-kernel launch from two rocprofv3 --pmc runs.
+
+    Each counter (KiB per dispatch) is scaled by copy-bytes / counter-reading
+    of the calibration copy kernel (pa_copy_blocks of a known size) in the
+    same run, then averaged over the partition kernel's dispatches."""
+    fetch_dir, write_dir = args.traffic_from
+    out = {"source_hash": kernel_source_hash(), "workload": args.workload}
+    per_launch = 0.0
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(directory, counter)
+        part = [v for k, v in rows if "decode_partition" in k]
+        cal = [v for k, v in rows if "copy_blocks_kernel" in k]
+        if not part or not cal:
+            raise RuntimeError(f"{counter}: need partition and copy dispatches in {directory}")
+        if args.steps and len(part) > args.steps:
+            part = part[-args.steps:]      # the timed steps; warm-up dispatches come first
+        variant = "mfma" if any("decode_partition_mfma" in k for k, _ in rows) else "valu"
+        cal_kib = float(np.median(cal))
+        out[counter] = {"partition_kib_mean": float(np.mean(part)), "dispatches": len(part),
+                        "copy_kib_median": cal_kib}
+        out["variant"] = variant
+    return _finish_traffic(args, out)
+
+
+def _finish_traffic(args, out) -> int:
+    cal = args.copy_calibration_mib
+    if cal <= 0:
+        raise SystemExit("--copy-calibration-mib must give the calibration size used in the runs")
+    w_ = __import__("workloads").get(args.workload)
+    block_bytes = w_.num_kv_heads * w_.block_size * w_.head_dim * w_.elem_bytes
+    n = max(1, cal * 2**20 // block_bytes)
+    known_kib = 2 * n * block_bytes / 1024.0
+    total = 0.0
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        c = out[counter]
+        c["scale"] = known_kib / c["copy_kib_median"]
+        c["partition_bytes"] = c["partition_kib_mean"] * c["scale"] * 1024.0
+        total += c["partition_bytes"]
+    out["bytes_per_launch"] = round(total)
+    out["calibration_bytes_each_way"] = int(2 * n * block_bytes)
+    text = json.dumps(out, indent=1)
+    print(text)
+    if args.traffic_out:
+        with open(args.traffic_out, "w") as fh:
+            fh.write(text + "\n")
     return 0
 
 

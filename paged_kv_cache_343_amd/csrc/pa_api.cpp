@@ -66,9 +66,11 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan) {
   if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
   plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant};
   if (!pa::decode_partition_supported(plan->key)) return PA_EUNSUPPORTED;
+  if (group * 2 > pa::kMlRecord) return PA_EUNSUPPORTED;
   const size_t rows = (size_t)s->num_seqs * s->num_q_heads * plan->max_parts;
+  const size_t recs = (size_t)s->num_seqs * s->num_kv_heads * plan->max_parts;
   if (plan->max_parts > 1) {
-    plan->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+    plan->ml_bytes = round_up(recs * pa::kMlRecord * sizeof(float), 256);
     plan->o_bytes = round_up(rows * (size_t)s->head_dim * sizeof(float), 256);
   }
   return PA_OK;

@@ -9,11 +9,12 @@
 // ("PagedAttention & vLLM", "Copy-on-write sharing"; n4n.ai "Prefix
 // sharing"); finished sequences give their blocks straight back (n4n.ai,
 // chat workload example).
+#include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <deque>
 #include <new>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "pa.h"
@@ -26,8 +27,11 @@ struct pa_bm {
   struct Seq {
     std::vector<int32_t> table;                // logical block -> physical id
     int32_t ntok = 0;
+    uint64_t stamp = 0;                        // call that last listed it
   };
   std::unordered_map<int32_t, Seq> seqs;
+  uint64_t epoch = 0;                          // append call counter
+  std::vector<Seq*> batch;                     // scratch of pa_bm_append_slots
 
   int32_t take() {
     const int32_t b = free_list.front();
@@ -95,15 +99,17 @@ pa_status_t pa_bm_append_slots(pa_bm_t* bm, const int32_t* seq_ids, int32_t n, i
     return PA_EINVAL;
   *num_cow = 0;
   // Validate the whole batch and count the blocks it needs before changing
-  // anything, so that a failure leaves the state untouched.
-  std::vector<pa_bm::Seq*> batch((size_t)n);
-  std::unordered_set<int32_t> listed;
-  listed.reserve((size_t)n * 2);
+  // anything, so that a failure leaves the state untouched. A sequence
+  // listed twice is caught by its stamp (set to this call's epoch).
+  std::vector<pa_bm::Seq*>& batch = bm->batch;
+  batch.resize((size_t)n);
+  const uint64_t epoch = ++bm->epoch;
   int64_t need = 0;
   for (int32_t k = 0; k < n; ++k) {
     auto it = bm->seqs.find(seq_ids[k]);
-    if (it == bm->seqs.end() || !listed.insert(seq_ids[k]).second) return PA_EINVAL;
+    if (it == bm->seqs.end() || it->second.stamp == epoch) return PA_EINVAL;
     if (it->second.ntok == INT32_MAX) return PA_EINVAL;
+    it->second.stamp = epoch;
     batch[k] = &it->second;
     need += bm->append_needs_block(it->second) ? 1 : 0;
   }
@@ -167,8 +173,9 @@ pa_status_t pa_bm_export(const pa_bm_t* bm, const int32_t* seq_ids, int32_t n,
     const pa_bm::Seq& s = bm->seqs.find(seq_ids[k])->second;
     if (tables) {
       int32_t* row = tables + (int64_t)k * max_blocks;
-      const int32_t len = (int32_t)s.table.size();
-      for (int32_t c = 0; c < max_blocks; ++c) row[c] = c < len ? s.table[c] : -1;
+      const size_t len = s.table.size();
+      if (len) std::memcpy(row, s.table.data(), len * sizeof(int32_t));
+      std::fill(row + len, row + max_blocks, -1);
     }
     if (lens) lens[k] = s.ntok;
   }

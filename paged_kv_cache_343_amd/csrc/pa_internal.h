@@ -6,6 +6,10 @@
 
 namespace pa {
 
+// Floats per (sequence, KV head, partition) record of partial softmax
+// statistics: one 128-byte line, room for (max, exp-sum) of 16 query heads.
+constexpr int kMlRecord = 32;
+
 // Everything one decode launch needs, passed by value as the kernel argument.
 struct DecodeArgs {
   const void* q;              // [B][Hq][D]
@@ -14,7 +18,8 @@ struct DecodeArgs {
   const int32_t* block_tables;  // [B][max_blocks]
   const int32_t* seq_lens;      // [B]
   void* out;                    // [B][Hq][D]
-  float* part_ml;               // [B][Hq][max_parts][2]: max score (log2 units), exp-sum
+  float* part_ml;               // [B][Hkv][max_parts][kMlRecord]: per query head of the
+                                //   group, max score (log2 units) then exp-sum; rest 0
   float* part_o;                // [B][Hq][max_parts][D]: normalised partial output
   float qscale;                 // softmax scale * log2(e)
   int32_t num_seqs;
@@ -71,6 +76,9 @@ hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream);
 hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);
 
 // Workgroup size (waves) of the partition kernels.
-constexpr int kDecodeWaves = 4;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;
 
 }  // namespace pa

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -98,6 +100,21 @@ struct Elem<uint16_t> {
   }
   __device__ static __forceinline__ void store(uint16_t* p, float x) { *p = to_bf16(x); }
 };
+
+// Four consecutive outputs (16-byte aligned for fp32, 8-byte for bf16).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float x0, float x1, float x2, float x3);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float x0, float x1, float x2,
+                                                 float x3) {
+  const uint32_t lo = (uint32_t)to_bf16(x0) | ((uint32_t)to_bf16(x1) << 16);
+  const uint32_t hi = (uint32_t)to_bf16(x2) | ((uint32_t)to_bf16(x3) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
 
 __device__ __forceinline__ uint4 ld16(const char* base, uint32_t byte_off) {
   return *reinterpret_cast<const uint4*>(base + byte_off);
@@ -201,31 +218,73 @@ __device__ void write_zero_rows(const DecodeArgs& a, int i, int g) {
 // final output (single-partition sequence) or the partition's partials.
 // Inputs per lane: m[h], l[h] of the lane's row stream (log2 units) and
 // acc[h][e] = unnormalised output for dims c*EPL + e, where c = lane % LPR.
+#ifndef PA_FINISH_PERMLANE
+#define PA_FINISH_PERMLANE 1
+#endif
+#ifndef PA_PART_STORE_NT
+#define PA_PART_STORE_NT 0
+#endif
+
+// Value held by lane (lane ^ OFF), for OFF in {16, 32}: the permlane swap
+// instructions exchange 16- or 32-lane halves between two registers on the
+// VALU, with no trip through LDS.
+template <int OFF>
+__device__ __forceinline__ float xor_lanes(float x) {
+  static_assert(OFF == 16 || OFF == 32, "row exchange");
+  const uint32_t u = __float_as_uint(x);
+  const int lane = threadIdx.x & 63;
+  if constexpr (OFF == 32) {
+    // first: lanes 32-63 take lanes 0-31 of the second operand;
+    // second: lanes 0-31 take lanes 32-63 of the first operand
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(lane < 32 ? r[1] : r[0]);
+  } else {
+    // same exchange between odd and even 16-lane rows
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  }
+}
+
+template <int OFF>
+__device__ __forceinline__ float row_partner(float x) {
+#if PA_FINISH_PERMLANE
+  if constexpr (OFF == 16 || OFF == 32) return xor_lanes<OFF>(x);
+#endif
+  return __shfl_xor(x, OFF);
+}
+
+// Merges the per-row softmax streams of every wave and writes either the
+// final output (single-partition sequence) or the partition's partials.
+// Inputs per lane: m[h], l[h] of the lane's row stream (log2 units) and
+// acc[h][e] = unnormalised output for dims c*EPL + e, where c = lane % LPR.
 template <typename T, int D, int G, int NW, int LPR, int EPL>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const PartitionWork& wk,
                                                  float (&m)[G], float (&l)[G],
                                                  float (&acc)[G][EPL]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane % LPR;
   // rows of one wave: butterfly over the lane bits above the row
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
+  auto merge_rows = [&](auto off_tag) {
+    constexpr int OFF = decltype(off_tag)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
+      const float mo = row_partner<OFF>(m[h]);
+      const float lo = row_partner<OFF>(l[h]);
       const float big = fmaxf(m[h], mo);
       const float f1 = merge_weight(m[h], big), f2 = merge_weight(mo, big);
       l[h] = f1 * l[h] + f2 * lo;
       m[h] = big;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float ao = __shfl_xor(acc[h][e], off);
+        const float ao = row_partner<OFF>(acc[h][e]);
         acc[h][e] = f1 * acc[h][e] + f2 * ao;
       }
     }
-  }
+  };
+  if constexpr (LPR <= 8) merge_rows(std::integral_constant<int, 8>{});
+  if constexpr (LPR <= 16) merge_rows(std::integral_constant<int, 16>{});
+  if constexpr (LPR <= 32) merge_rows(std::integral_constant<int, 32>{});
   __shared__ float s_m[NW][G], s_l[NW][G];
-  __shared__ float s_acc[NW][G][D];
+  __shared__ __align__(16) float s_acc[NW][G][D];
   if (lane < LPR) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -238,44 +297,97 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
     }
   }
   __syncthreads();
-  T* out = reinterpret_cast<T*>(a.out);
-  for (int t = threadIdx.x; t < G * D; t += NW * 64) {
-    const int h = t / D, d = t % D;
+  // Merge of the NW wave streams, 4 consecutive dims per thread: 16-byte
+  // stores of the partial output (8-byte for a bf16 final row).
+  constexpr int V4 = D / 4;
+  for (int t = threadIdx.x; t < G * V4; t += NW * 64) {
+    const int h = t / V4, d0 = (t % V4) * 4;
     float big = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
-    float lsum = 0.0f, o = 0.0f;
+    float lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const float f = merge_weight(s_m[k][h], big);
       lsum += f * s_l[k][h];
-      o += f * s_acc[k][h][d];
+      const float4 sa = *reinterpret_cast<const float4*>(&s_acc[k][h][d0]);
+      o[0] += f * sa.x;
+      o[1] += f * sa.y;
+      o[2] += f * sa.z;
+      o[3] += f * sa.w;
     }
-    const int hq = wk.g * G + h;
-    const int64_t row = (int64_t)wk.i * a.num_q_heads + hq;
-    const float val = lsum > 0.0f ? o / lsum : 0.0f;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    const int64_t row = (int64_t)wk.i * a.num_q_heads + wk.g * G + h;
     if (wk.nparts == 1) {
-      Elem<T>::store(out + row * D + d, val);
+      store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
+                o[3] * inv);
     } else {
-      const int64_t prow = row * a.max_parts + wk.j;
-      a.part_o[prow * D + d] = val;
-      if (d == 0) {
-        a.part_ml[prow * 2 + 0] = big;
-        a.part_ml[prow * 2 + 1] = lsum;
-      }
+      float4* dst = reinterpret_cast<float4*>(a.part_o + (row * a.max_parts + wk.j) * D + d0);
+#if PA_PART_STORE_NT
+      const f32x4_t val = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(dst));
+#else
+      *dst = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+#endif
     }
   }
+  // (max, exp-sum) of every head of the group: one full 128-byte record per
+  // workgroup, so the write never covers part of a cache line.
+  if (wk.nparts > 1 && threadIdx.x < kMlRecord / 4) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int f = threadIdx.x * 4 + e, h = f >> 1;
+      v[e] = 0.0f;
+      if (h < G) {
+        float big = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) lsum += merge_weight(s_m[k][h], big) * s_l[k][h];
+        v[e] = (f & 1) ? lsum : big;
+      }
+    }
+    const int64_t rec = (((int64_t)wk.i * a.num_kv_heads + wk.g) * a.max_parts + wk.j) * kMlRecord;
+    reinterpret_cast<float4*>(a.part_ml + rec)[threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
+
+
+// Order in which workgroup ids enumerate (KV head, sequence, partition),
+// fastest first: 0 = head, sequence, partition; 1 = sequence, head,
+// partition; 2 = head, partition, sequence; 3 = partition, head, sequence.
+#ifndef PA_GRID_ORDER
+#define PA_GRID_ORDER 3
+#endif
 
 // Decodes blockIdx.x into (KV head, sequence, partition); returns false if
 // the workgroup has nothing to do (after writing zeros for empty sequences).
 template <typename T, int D, int BS, int G, int NW>
 __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk) {
   int id = blockIdx.x;
+#if PA_GRID_ORDER == 1
+  wk.i = id % a.num_seqs;
+  id /= a.num_seqs;
+  wk.g = id % a.num_kv_heads;
+  wk.j = id / a.num_kv_heads;
+#elif PA_GRID_ORDER == 2
+  wk.g = id % a.num_kv_heads;
+  id /= a.num_kv_heads;
+  wk.j = id % a.max_parts;
+  wk.i = id / a.max_parts;
+#elif PA_GRID_ORDER == 3
+  wk.j = id % a.max_parts;
+  id /= a.max_parts;
+  wk.g = id % a.num_kv_heads;
+  wk.i = id / a.num_kv_heads;
+#else
   wk.g = id % a.num_kv_heads;
   id /= a.num_kv_heads;
   wk.i = id % a.num_seqs;
   wk.j = id / a.num_seqs;
+#endif
   wk.len = checked_len(a, wk.i);
   wk.nparts = (wk.len + a.part_tokens - 1) / a.part_tokens;
   if (wk.len == 0) {
@@ -396,15 +508,149 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_valu(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // MFMA partition kernel (bf16, D = 128, G in {1, 2, 4})
 // ---------------------------------------------------------------------------
-// Positions are taken 16 at a time ("chunk"; a 16-token block, or half of a
-// 32-token block). Lane l: R = l / 16 (row), c = l % 16.
+// Positions are taken 16 at a time ("chunk"; a 16-token block, or a 16-token
+// slice of a larger block). Lane l: R = l / 16 (row), c = l % 16.
 //   K load s (s = 0..3): token (l % 16), dims [32 s + 8 R, +8)  -> A operand
 //   q operand step s:    query row (l % 16) % G, same dims        -> B operand
 //   MFMA result reg r:   score of token 4 R + r for head (l % G)
 //   V load jj (0..3):    token 4 R + jj, dims [8 c, +8), coalesced 256 B rows
 // Row R is one softmax stream over tokens {4R .. 4R+3} of every chunk.
+//
+// Wave w of the workgroup takes chunks w, w + NW, w + 2 NW, ... of the
+// partition. The physical block ids of those chunks are read once, one per
+// lane, into a register window of 64 chunks (re-read only for partitions of
+// more than 64 * NW chunks), and broadcast per chunk with a lane read, so the
+// K/V loads never wait for a block-table load. K/V of the next chunk are
+// issued before the current chunk is computed (two register buffers); the
+// last chunk "prefetches" itself again, a cache hit that keeps the load
+// count per iteration constant.
+struct KVChunk {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+// Occupancy floor of the MFMA partition kernel (waves per SIMD; 0 = the
+// compiler's choice) and the cache-policy bits of its K/V loads.
+#ifndef PA_MFMA_WAVES_PER_EU
+#define PA_MFMA_WAVES_PER_EU 0
+#endif
+#if PA_MFMA_WAVES_PER_EU > 0
+#define PA_MFMA_BOUNDS(threads) __launch_bounds__(threads, PA_MFMA_WAVES_PER_EU)
+#else
+#define PA_MFMA_BOUNDS(threads) __launch_bounds__(threads)
+#endif
+#ifndef PA_KV_LOAD_AUX
+#define PA_KV_LOAD_AUX 0
+#endif
+
+// Buffer resource over `bytes` bytes at a wave-uniform address (gfx9
+// descriptor: raw 32-bit data format, no swizzle); loads past `bytes` return
+// zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, 0x00020000);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes at voff + soff of the buffer (soff wave-uniform).
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, PA_KV_LOAD_AUX);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// K and V rows of the 16-token chunk that starts at row `tok_in_blk` of
+// physical block `phys`. The chunk's base address is wave-uniform and goes
+// into the buffer descriptor (scalar registers); each lane only adds its own
+// fixed offset, so no per-lane 64-bit address is formed per chunk.
+template <int BS>
+__device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, const char* vbase,
+                                              int64_t blk_bytes, int phys, int tok_in_blk,
+                                              uint32_t k_off, uint32_t v_off) {
+  constexpr int ROW = 256;
+  const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, 16 * ROW);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, 16 * ROW);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c.k[s] = buf_ld16(kr, k_off, s * 64);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld16(vr, v_off, jj * ROW);
+}
+
+// Block-id window: lane k gets the physical block holding this wave's chunk
+// (first + k), for chunks inside the partition; other lanes get 0. Each id is
+// range-checked here, once.
+template <int BS, int NW>
+__device__ __forceinline__ int load_id_window(const DecodeArgs& a, const PartitionWork& wk, int w,
+                                              int first, int nmine) {
+  const int lane = threadIdx.x & 63;
+  const int k = first + lane;
+  int id = 0;
+  if (k < nmine) {
+    const int tok = wk.tok0 + (w + k * NW) * 16;
+    id = a.block_tables[(int64_t)wk.i * a.max_blocks + tok / BS];
+    if ((unsigned)id >= (unsigned)a.num_blocks) {
+      flag_error(kErrBlockId);
+      id = 0;
+    }
+  }
+  return id;
+}
+
+template <int G>
+__device__ __forceinline__ void mfma_chunk(const KVChunk& c, const bf16x8_t (&qop)[4],
+                                           float qscale, int tokc, int tok1, int R, float& m,
+                                           float& lsum, float (&acc)[G][8]) {
+  f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, c.k[s]), qop[s], sc,
+                                                 0, 0, 0);
+  const bool full = tokc + 16 <= tok1;
+  float sv[4];
+  bool ok[4];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = sc[r] * qscale;
+    ok[r] = full || (tokc + 4 * R + r < tok1);
+    bm = ok[r] ? fmaxf(bm, sv[r]) : bm;
+  }
+  const float mn = fmaxf(m, bm);
+  const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
+  m = mn;
+  float p[4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = ok[r] ? exp2_fast(sv[r] - mn) : 0.0f;
+    psum += p[r];
+  }
+  lsum = lsum * alpha + psum;
+  float al[G], ph[4][G];
+  quad_spread<G>(alpha, al);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) quad_spread<G>(p[r], ph[r]);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float vf[8];
+    Elem<uint16_t>::unpack(c.v[jj], vf);
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = ok[jj] ? vf[e] : 0.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[jj][h], vf[e], acc[h][e]);
+  }
+}
+
 template <int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
+__global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int ROW = D * 2;                      // bytes per token row
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
@@ -437,65 +683,28 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_mfma(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
 
   const int nch = (wk.tok1 - wk.tok0 + 15) / 16;
-  for (int cc = w; cc < nch; cc += NW) {
-    const int tokc = wk.tok0 + cc * 16;
-    const int lb = tokc / BS;
-    const int phys = checked_block(a, wk.i, lb);
-    const int64_t base = (int64_t)phys * blk_bytes + (int64_t)(tokc % BS) * ROW;
-    const char* kb = kbase + base;
-    const char* vb = vbase + base;
-    uint4 kr[4], vr[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kr[s] = ld16(kb, k_off + s * 64);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vr[jj] = ld16(vb, v_off + jj * ROW);
-
-    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[s],
-                                                   sc, 0, 0, 0);
-    const bool full = tokc + 16 <= wk.tok1;
-    float sv[4];
-    bool ok[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = sc[r] * a.qscale;
-      ok[r] = full || (tokc + 4 * R + r < wk.tok1);
-      bm = ok[r] ? fmaxf(bm, sv[r]) : bm;
-    }
-    const float mn = fmaxf(m, bm);
-    const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
-    m = mn;
-    float p[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = ok[r] ? exp2_fast(sv[r] - mn) : 0.0f;
-      psum += p[r];
-    }
-    lsum = lsum * alpha + psum;
-    float al[G], ph[4][G];
-    quad_spread<G>(alpha, al);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) quad_spread<G>(p[r], ph[r]);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float vf[8];
-      Elem<uint16_t>::unpack(vr[jj], vf);
-      if (!full) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = ok[jj] ? vf[e] : 0.0f;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[jj][h], vf[e], acc[h][e]);
+  const int nmine = nch > w ? (nch - w + NW - 1) / NW : 0;   // chunks of this wave
+  auto chunk_tok = [&](int t) { return wk.tok0 + (w + t * NW) * 16; };
+  // Windows of 64 chunks: one block-id load per window, then a two-buffer
+  // pipeline over the window's chunks (no load inside the loop depends on
+  // another load, so the compiler's wait counts stay partial).
+  for (int win = 0; win < nmine; win += 64) {
+    const int ids = load_id_window<BS, NW>(a, wk, w, win, nmine);
+    const int cnt = min(64, nmine - win);
+    auto issue = [&](KVChunk& buf, int t) {
+      const int phys = __builtin_amdgcn_readlane(ids, t);
+      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + t) % BS, k_off,
+                        v_off);
+    };
+    KVChunk b0, b1;
+    issue(b0, 0);
+    for (int t = 0;;) {
+      issue(b1, t + 1 < cnt ? t + 1 : t);
+      mfma_chunk<G>(b0, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
+      if (++t >= cnt) break;
+      issue(b0, t + 1 < cnt ? t + 1 : t);
+      mfma_chunk<G>(b1, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
+      if (++t >= cnt) break;
     }
   }
   float mh[G], lh[G];
@@ -517,12 +726,15 @@ __global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
   len = len < 0 ? 0 : min(len, a.len_cap);
   const int np = (len + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
+  const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t prow = ((int64_t)i * a.num_q_heads + hq) * a.max_parts;
-  const float* ml = a.part_ml + prow * 2;
+  // record of partition j: ml[j * kMlRecord] = (max, exp-sum) of this head
+  const float* ml = a.part_ml +
+                    ((int64_t)i * a.num_kv_heads + hq / G) * a.max_parts * kMlRecord + 2 * (hq % G);
   const float* po = a.part_o + prow * D;
   const int lane = threadIdx.x;
   float big = -INFINITY;
-  for (int j = lane; j < np; j += 64) big = fmaxf(big, ml[2 * j]);
+  for (int j = lane; j < np; j += 64) big = fmaxf(big, ml[(int64_t)j * kMlRecord]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
   float wsum = 0.0f;
@@ -530,7 +742,7 @@ __global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) o[k] = 0.0f;
   for (int j = 0; j < np; ++j) {
-    const float wj = ml[2 * j + 1] * merge_weight(ml[2 * j], big);
+    const float wj = ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
     wsum += wj;
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) o[k] = fmaf(wj, po[(int64_t)j * D + lane + 64 * k], o[k]);
