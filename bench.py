@@ -78,6 +78,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="override the workload's block size (tokens per block)")
     ap.add_argument("--block-order", default="shuffled", choices=["shuffled", "identity"],
                     help="free-list order: a seeded permutation (scattered blocks, the "
                          "default) or 0, 1, 2, ... (each sequence's blocks contiguous)")
@@ -115,6 +117,8 @@ def main() -> int:
         return 1
     variant = {"auto": P.PA_VARIANT_AUTO, "valu": P.PA_VARIANT_VALU, "mfma": P.PA_VARIANT_MFMA}[args.variant]
     B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    if args.block_size:
+        bs = args.block_size
     ptok = args.partition_tokens if args.partition_tokens is not None else w.partition_tokens
     nsteps = args.warmup + args.steps
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

@@ -47,7 +47,9 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan) {
   if (elem_bytes(s->dtype) == 0) return PA_EINVAL;
   if ((s->head_dim * elem_bytes(s->dtype)) % 16 != 0) return PA_EINVAL;
   if (s->head_dim != 64 && s->head_dim != 128) return PA_EUNSUPPORTED;
-  if (s->block_size != 16 && s->block_size != 32) return PA_EUNSUPPORTED;
+  if (s->block_size != 8 && s->block_size != 16 && s->block_size != 32 && s->block_size != 64 &&
+      s->block_size != 128)
+    return PA_EUNSUPPORTED;
   const int group = s->num_q_heads / s->num_kv_heads;
   int pt = s->partition_tokens;
   if (pt == 0) pt = kDefaultPartitionTokens;

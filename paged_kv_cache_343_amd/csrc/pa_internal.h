@@ -80,5 +80,7 @@ hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);
 #define PA_DECODE_WAVES 4
 #endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;
+// Waves per workgroup of the partition merge (one wave per query head).
+constexpr int kReduceWaves = 4;
 
 }  // namespace pa

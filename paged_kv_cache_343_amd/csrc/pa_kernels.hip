@@ -576,21 +576,49 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, con
   for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld16(vr, v_off, jj * ROW);
 }
 
-// Block-id window: lane k gets the physical block holding this wave's chunk
-// (first + k), for chunks inside the partition; other lanes get 0. Each id is
+// 16-token chunk that spans two 8-token blocks: lanes pick their block per
+// row, so the loads use per-lane 64-bit addresses instead of a descriptor.
+__device__ __forceinline__ void load_kv_chunk_bs8(KVChunk& c, const char* kbase, const char* vbase,
+                                                  int64_t blk_bytes, int phys0, int phys1) {
+  constexpr int ROW = 256;
+  const int lane = threadIdx.x & 63, R = lane >> 4, cc = lane & 15;
+  // K: token cc of the chunk; V: tokens 4R .. 4R + 3
+  const char* kb = kbase + (int64_t)(cc < 8 ? phys0 : phys1) * blk_bytes + (cc & 7) * ROW + R * 16;
+  const char* vb = vbase + (int64_t)(R < 2 ? phys0 : phys1) * blk_bytes + ((4 * R) & 7) * ROW +
+                   cc * 16;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c.k[s] = ld16(kb, s * 64);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) c.v[jj] = ld16(vb, jj * ROW);
+}
+
+__device__ __forceinline__ int checked_id(const DecodeArgs& a, int64_t row, int logical_block) {
+  int id = a.block_tables[row + logical_block];
+  if ((unsigned)id >= (unsigned)a.num_blocks) {
+    flag_error(kErrBlockId);
+    id = 0;
+  }
+  return id;
+}
+
+// Block-id window: lane k gets the physical block holding the start of this
+// wave's chunk (first + k), for chunks inside the partition; other lanes get
+// 0. With 8-token blocks a chunk covers two blocks; .y is the second one
+// (read only when the chunk has a valid position in it). Each id is
 // range-checked here, once.
 template <int BS, int NW>
-__device__ __forceinline__ int load_id_window(const DecodeArgs& a, const PartitionWork& wk, int w,
-                                              int first, int nmine) {
+__device__ __forceinline__ int2 load_id_window(const DecodeArgs& a, const PartitionWork& wk, int w,
+                                               int first, int nmine) {
   const int lane = threadIdx.x & 63;
   const int k = first + lane;
-  int id = 0;
+  int2 id = make_int2(0, 0);
   if (k < nmine) {
     const int tok = wk.tok0 + (w + k * NW) * 16;
-    id = a.block_tables[(int64_t)wk.i * a.max_blocks + tok / BS];
-    if ((unsigned)id >= (unsigned)a.num_blocks) {
-      flag_error(kErrBlockId);
-      id = 0;
+    const int64_t row = (int64_t)wk.i * a.max_blocks;
+    id.x = checked_id(a, row, tok / BS);
+    id.y = id.x;
+    if constexpr (BS == 8) {
+      if (tok + 8 < wk.tok1) id.y = checked_id(a, row, tok / 8 + 1);
     }
   }
   return id;
@@ -654,7 +682,7 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   constexpr int D = 128;
   constexpr int ROW = D * 2;                      // bytes per token row
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
-  static_assert(BS % 16 == 0, "block must hold whole 16-token chunks");
+  static_assert(BS == 8 || BS % 16 == 0, "block must hold whole 16-token chunks, or half of one");
 
   PartitionWork wk;
   if (!setup_partition<uint16_t, D, BS, G, NW>(a, wk)) return;
@@ -689,12 +717,16 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   // pipeline over the window's chunks (no load inside the loop depends on
   // another load, so the compiler's wait counts stay partial).
   for (int win = 0; win < nmine; win += 64) {
-    const int ids = load_id_window<BS, NW>(a, wk, w, win, nmine);
+    const int2 ids = load_id_window<BS, NW>(a, wk, w, win, nmine);
     const int cnt = min(64, nmine - win);
     auto issue = [&](KVChunk& buf, int t) {
-      const int phys = __builtin_amdgcn_readlane(ids, t);
-      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + t) % BS, k_off,
-                        v_off);
+      const int phys = __builtin_amdgcn_readlane(ids.x, t);
+      if constexpr (BS == 8) {
+        load_kv_chunk_bs8(buf, kbase, vbase, blk_bytes, phys, __builtin_amdgcn_readlane(ids.y, t));
+      } else {
+        load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + t) % BS, k_off,
+                          v_off);
+      }
     };
     KVChunk b0, b1;
     issue(b0, 0);
@@ -719,38 +751,59 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
 // One wave per (sequence, query head); only sequences with more than one
 // partition have anything to merge.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
-  const int hq = blockIdx.x % a.num_q_heads;
-  const int i = blockIdx.x / a.num_q_heads;
+__global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a) {
+  // one wave per (sequence, query head); kReduceWaves consecutive pairs per
+  // workgroup
+  const int pair = blockIdx.x * kReduceWaves + (threadIdx.x >> 6);
+  if (pair >= a.num_seqs * a.num_q_heads) return;
+  const int hq = pair % a.num_q_heads;
+  const int i = pair / a.num_q_heads;
   int len = a.seq_lens[i];
   len = len < 0 ? 0 : min(len, a.len_cap);
   const int np = (len + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int64_t prow = ((int64_t)i * a.num_q_heads + hq) * a.max_parts;
   // record of partition j: ml[j * kMlRecord] = (max, exp-sum) of this head
   const float* ml = a.part_ml +
                     ((int64_t)i * a.num_kv_heads + hq / G) * a.max_parts * kMlRecord + 2 * (hq % G);
-  const float* po = a.part_o + prow * D;
-  const int lane = threadIdx.x;
-  float big = -INFINITY;
-  for (int j = lane; j < np; j += 64) big = fmaxf(big, ml[(int64_t)j * kMlRecord]);
+  const float* po = a.part_o + ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
+  const int lane = threadIdx.x & 63;
+  // lane j holds partition j's statistics (partitions past 64 are folded in
+  // by the same lane, merged on the fly)
+  float mj = -INFINITY, lj = 0.0f;
+  for (int j = lane; j < np; j += 64) {
+    const float m2 = ml[(int64_t)j * kMlRecord], l2 = ml[(int64_t)j * kMlRecord + 1];
+    const float big = fmaxf(mj, m2);
+    lj = lj * merge_weight(mj, big) + l2 * merge_weight(m2, big);
+    mj = big;
+  }
+  float big = mj;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
-  float wsum = 0.0f;
-  float o[D / 64];
+  float wsum = lj * merge_weight(mj, big);
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) o[k] = 0.0f;
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  // out = sum_j w_j o_j / sum_j w_j, w_j = l_j 2^(m_j - M); D / 64 dims per lane
+  constexpr int DPL = D / 64;
+  float o[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) o[k] = 0.0f;
+#pragma unroll 4
   for (int j = 0; j < np; ++j) {
     const float wj = ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
-    wsum += wj;
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) o[k] = fmaf(wj, po[(int64_t)j * D + lane + 64 * k], o[k]);
+    const float* src = po + (int64_t)j * D + lane * DPL;
+    if constexpr (DPL == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      o[0] = fmaf(wj, v.x, o[0]);
+      o[1] = fmaf(wj, v.y, o[1]);
+    } else {
+      o[0] = fmaf(wj, src[0], o[0]);
+    }
   }
-  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)i * a.num_q_heads + hq) * D;
+  T* out = reinterpret_cast<T*>(a.out) + ((int64_t)i * a.num_q_heads + hq) * D + lane * DPL;
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) Elem<T>::store(out + lane + 64 * k, o[k] * inv);
+  for (int k = 0; k < DPL; ++k) Elem<T>::store(out + k, o[k] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -839,8 +892,14 @@ static PartitionKernel pick_partition(const DecodeKey& k) {
   }
   if (k.variant == 2) {
     if (k.dtype != 1 || k.head_dim != 128) return nullptr;
-    if (k.block_size == 16) return pick_mfma<16>(k.group);
-    if (k.block_size == 32) return pick_mfma<32>(k.group);
+    switch (k.block_size) {
+      case 8: return pick_mfma<8>(k.group);
+      case 16: return pick_mfma<16>(k.group);
+      case 32: return pick_mfma<32>(k.group);
+      case 64: return pick_mfma<64>(k.group);
+      case 128: return pick_mfma<128>(k.group);
+      default: return nullptr;
+    }
   }
   return nullptr;
 }
@@ -861,16 +920,17 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
 hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
                                 hipStream_t stream) {
   if (args.max_parts <= 1) return hipSuccess;
-  const int64_t groups = (int64_t)args.num_seqs * args.num_q_heads;
-  if (groups <= 0) return hipSuccess;
-  if (groups > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t pairs = (int64_t)args.num_seqs * args.num_q_heads;
+  if (pairs <= 0) return hipSuccess;
+  if (pairs > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t groups = (pairs + kReduceWaves - 1) / kReduceWaves;
   PartitionKernel kern = nullptr;
   if (dtype == 0 && head_dim == 64) kern = decode_reduce<float, 64>;
   if (dtype == 0 && head_dim == 128) kern = decode_reduce<float, 128>;
   if (dtype == 1 && head_dim == 64) kern = decode_reduce<uint16_t, 64>;
   if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
   if (!kern) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(64), 0, stream, args);
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kReduceWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -54,7 +54,8 @@ def test_workspace_bytes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(num_q_heads=30), 1), (dict(head_dim=80), 2), (dict(block_size=8), 2),
+    (dict(num_q_heads=30), 1), (dict(head_dim=80), 2), (dict(block_size=24), 2),
+    (dict(block_size=8, variant=1), 2),
     (dict(dtype=5), 1), (dict(num_q_heads=24), 2), (dict(variant=2, dtype=P.PA_F32), 2),
     (dict(partition_tokens=40), 1), (dict(num_blocks=0), 1),
 ])

@@ -40,6 +40,11 @@ SHAPES = [
     ("bf16", 8, 8, 128, 16, VALU),
     ("bf16", 8, 4, 128, 16, MFMA),
     ("bf16", 32, 8, 128, 32, MFMA),
+    ("bf16", 32, 8, 128, 8, MFMA),
+    ("bf16", 32, 8, 128, 64, MFMA),
+    ("bf16", 32, 8, 128, 128, MFMA),
+    ("bf16", 8, 8, 128, 8, MFMA),
+    ("bf16", 16, 8, 128, 128, MFMA),
     ("bf16", 16, 8, 128, 32, VALU),
     ("bf16", 16, 2, 64, 16, VALU),
     ("bf16", 4, 4, 64, 32, VALU),
@@ -72,6 +77,21 @@ def test_partition_lengths(dev, ptok, variant):
     ref = c.oracle_all()
     out = c.decode(variant=variant, partition_tokens=ptok)
     check_close(_f64(out, "bf16"), ref, "bf16", f"partition {ptok}")
+    assert P.pa_device_errors() == 0
+
+
+@pytest.mark.parametrize("bs", [8, 64, 128])
+@pytest.mark.parametrize("ptok", [-1, 128, 512])
+def test_block_sizes_with_partitions(dev, bs, ptok):
+    """Block sizes other than 16/32 on the matrix-core kernel, including
+    8-token blocks (a 16-token chunk spans two blocks) and blocks longer than
+    a partition of 128 tokens' worth of chunks."""
+    if ptok > 0 and ptok % bs:
+        pytest.skip("partition must be a multiple of the block size")
+    w = _custom("bsizes", 104, 32, 8, 128, bs, "bf16")
+    c = build(w, dev, lens=[1, 7, 8, 9, 130, 511, 777, 1600])
+    out = c.decode(variant=MFMA, partition_tokens=ptok)
+    check_close(_f64(out, "bf16"), c.oracle_all(), "bf16", f"bs {bs} ptok {ptok}")
     assert P.pa_device_errors() == 0
 
 
