@@ -183,6 +183,7 @@ def main() -> int:
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     step_bytes = []
     host_s = [0.0]  # host time per timed step, waits excluded
+    bm_s = [0.0]    # block manager (append + export) time
     ev = []  # per step: (reshape start, partition start, partition end, reduce end)
 
     # Host side of a step through the raw C ABI (block manager: append one
@@ -201,6 +202,7 @@ def main() -> int:
             copied[b].synchronize()          # the staging buffer's last copy has landed
             host_s[0] -= time.perf_counter() - w0
         sp = stage_ptr[b]
+        t_bm = time.perf_counter()
         st = Lh.pa_bm_append_slots(bm._h, ids_ptr, B, sp["slots"], pairs_ptr, ctypes.byref(ncow))
         if st != 0:
             raise P.PaError(st, "pa_bm_append_slots")
@@ -209,6 +211,7 @@ def main() -> int:
         st = Lh.pa_bm_export(bm._h, ids_ptr, B, maxb, sp["tables"], sp["lens"])
         if st != 0:
             raise P.PaError(st, "pa_bm_export")
+        bm_s[0] += time.perf_counter() - t_bm
         step_bytes.append(int(lens_np[b].sum(dtype=np.int64)) * 2 * hkv * d * eb)
 
     # Raw C-ABI calls with pointers resolved once: the step's host cost stays
@@ -281,6 +284,7 @@ def main() -> int:
     if P.pa_device_errors() != 0:
         raise RuntimeError("device index error during warmup")
     step_bytes.clear()
+    bm_s[0] = 0.0
     t0 = time.perf_counter()
     for s in range(args.warmup, nsteps):
         h0 = time.perf_counter()
@@ -339,6 +343,24 @@ def main() -> int:
                      "kernel": "decode_partition_" + vname,
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
     }
+    avg_len = total_bytes / K / (2 * hkv * d * eb) / B
+    parts = float(np.mean([-(-int(x) // ptok) for x in stage[0]["lens"].numpy()])) if ptok > 0 else 1.0
+    red_bytes = B * hq * (parts * (d * 4) + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
+    cache_bytes = 2 * B * 2 * hkv * d * eb
+    result["rows"] = {
+        "a1_block_manager_host_us": round(1e6 * bm_s[0] / K, 1),
+        "a2_reshape_and_cache": {"us": round(1e3 * float(np.mean(cache_ms)), 2),
+                                 "bytes_moved": cache_bytes,
+                                 "GBps": round(cache_bytes / (float(np.mean(cache_ms)) / 1e3) / 1e9, 1)},
+        "a3_decode_partition": {"us": round(1e3 * float(np.mean(part_ms)), 2),
+                                "GBps": round(achieved, 1), "mean_len": round(avg_len, 1)},
+        "a4_decode_reduce": {"us": round(1e3 * float(np.mean(red_ms)), 2), "bytes_moved": int(red_bytes),
+                             "GBps": round(red_bytes / (float(np.mean(red_ms)) / 1e3) / 1e9, 1)},
+        "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
+        "a6_fork_cow_host_us": fork_cow_host_us(P),
+    }
+    peak = stream_read_peak(torch, dev)
+    result["practical_peak"] = dict(peak, partition_frac=round(achieved / peak["GBps"], 4))
     if args.copy_calibration_mib > 0:
         result["copy_calibration"] = copy_calibration(P, torch, dev, args.copy_calibration_mib,
                                                       hkv * bs * d * eb)
@@ -348,6 +370,82 @@ def main() -> int:
                                               ctx, order, nb, nsteps, scale, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def stream_read_peak(torch, dev) -> dict:
+    """Practical HBM read ceiling: the streaming-read probe (libpa_probe.so)
+    over a 4 GiB buffer, best of three grid sizes, 10 timed launches each."""
+    path = os.path.join(ROOT, "paged_kv_cache_343_amd", "libpa_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.pa_probe_stream_read.restype = ctypes.c_int
+    lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    best = 0.0
+    for grid in (1024, 2048, 4096):
+        for _ in range(2):
+            if lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, sink.data_ptr(), s):
+                raise RuntimeError("probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, sink.data_ptr(), s)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9)
+    del buf
+    return {"GBps": round(best, 1), "bytes": nbytes, "kernel": "pa_probe_stream_read"}
+
+
+def copy_blocks_rate(P, torch, dev) -> dict:
+    """pa_copy_blocks on the shared-prefix workload's copy-on-write set (64
+    prompt groups x 3 diverging samples = 192 blocks of 32 tokens, 8 KV
+    heads, D 128, bf16: 64 KiB per block per pool) and on 4096 blocks, timed
+    with HIP events on a pool pair of its own."""
+    hkv, bs, d = 8, 32, 128
+    nb = 8192
+    kp = torch.zeros((nb, hkv, bs, d), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    block_bytes = hkv * bs * d * 2
+    out = {}
+    for npairs in (192, 4096):
+        perm = np.random.default_rng(7).permutation(nb)
+        pairs = torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).astype(np.int64)).to(dev)
+        for _ in range(3):
+            P.pa_copy_blocks(kp, vp, pairs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            P.pa_copy_blocks(kp, vp, pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 20 / 1e3
+        moved = 2 * 2 * npairs * block_bytes        # K and V, read and written
+        out[f"{npairs}_pairs"] = {"us": round(t * 1e6, 2), "bytes_moved": moved,
+                                  "GBps": round(moved / t / 1e9, 1)}
+    return out
+
+
+def fork_cow_host_us(P) -> float:
+    """Host time of the shared-prefix workload's sharing decisions: 64 prompt
+    groups of 1040 tokens at block size 32, three forks each, then the first
+    private token of all 256 samples (192 copy-on-write pairs)."""
+    groups, samples, bs, prefix = 64, 4, 32, 1040
+    nb = groups * (prefix // bs + 1) + groups * samples * 2 + 64
+    bm = P.BlockManager(nb, bs)
+    t0 = time.perf_counter()
+    for gi in range(groups):
+        bm.add_seq(gi * samples, prefix)
+        for k in range(1, samples):
+            bm.fork(gi * samples, gi * samples + k)
+    _, pairs = bm.append_slots(np.arange(groups * samples, dtype=np.int32))
+    el = time.perf_counter() - t0
+    if pairs.shape[0] != groups * (samples - 1):
+        raise RuntimeError("unexpected copy-on-write count")
+    return round(el * 1e6, 1)
 
 
 def copy_calibration(P, torch, dev, mib: int, block_bytes: int) -> dict:

@@ -31,6 +31,15 @@ def test_library_exports_every_declared_symbol():
     assert _declared() <= exported
 
 
+def test_probe_library_exports_its_header():
+    text = open(os.path.join(ROOT, "include", "pa_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    lib = os.path.join(os.path.dirname(P.LIB_PATH), "libpa_probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True).stdout
+    assert declared and declared <= set(re.findall(r" T (pa_[a-z0-9_]+)", out))
+
+
 def _shape(**kw):
     base = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                 num_blocks=100, max_blocks_per_seq=8, max_seq_len=128, partition_tokens=0,
