@@ -358,6 +358,7 @@ def main() -> int:
                              "GBps": round(red_bytes / (float(np.mean(red_ms)) / 1e3) / 1e9, 1)},
         "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
         "a6_fork_cow_host_us": fork_cow_host_us(P),
+        "n3_swap_blocks": swap_rate(P, torch, dev),
     }
     peak = stream_read_peak(torch, dev)
     result["practical_peak"] = dict(peak, partition_frac=round(achieved / peak["GBps"], 4))
@@ -427,6 +428,36 @@ def copy_blocks_rate(P, torch, dev) -> dict:
         out[f"{npairs}_pairs"] = {"us": round(t * 1e6, 2), "bytes_moved": moved,
                                   "GBps": round(moved / t / 1e9, 1)}
     return out
+
+
+def swap_rate(P, torch, dev) -> dict:
+    """pa_swap_blocks between a device pool pair and a pinned host pool pair:
+    1024 blocks of the headline shape (8 KV heads x 16 tokens x D 128, bf16:
+    32 KiB per block per pool), out and back in, timed with HIP events."""
+    nb, n = 4096, 1024
+    shape = (nb, 8, 16, 128)
+    kp = torch.randn(shape, device=dev).to(torch.bfloat16)
+    vp = torch.randn(shape, device=dev).to(torch.bfloat16)
+    hk = torch.empty((n,) + shape[1:], dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    perm = np.random.default_rng(11).permutation(nb)[:n]
+    out_pairs = torch.from_numpy(np.stack([perm, np.arange(n)], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), perm], 1).astype(np.int64)).to(dev)
+    res = {}
+    for name, args in (("device_to_host", (kp, vp, hk, hv, out_pairs)),
+                       ("host_to_device", (hk, hv, kp, vp, in_pairs))):
+        for _ in range(2):
+            P.pa_swap_blocks(*args)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            P.pa_swap_blocks(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 5 / 1e3
+        moved = 2 * n * kp[0].numel() * 2
+        res[name] = {"us": round(t * 1e6, 1), "bytes": moved, "GBps": round(moved / t / 1e9, 1)}
+    return res
 
 
 def fork_cow_host_us(P) -> float:

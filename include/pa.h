@@ -61,7 +61,7 @@ typedef enum {
 #define PA_DEVERR_BLOCK_ID 0x1u   /* block table entry outside [0, num_blocks) */
 #define PA_DEVERR_SEQ_LEN 0x2u    /* seq_len < 0, > max_seq_len, or > table   */
 #define PA_DEVERR_SLOT 0x4u       /* slot >= num_blocks * block_size          */
-#define PA_DEVERR_COPY_PAIR 0x8u  /* copy pair id outside [0, num_blocks)     */
+#define PA_DEVERR_COPY_PAIR 0x8u  /* copy/swap pair id outside its pool         */
 
 /* Decode kernel variants (pa_decode_shape_t.variant). */
 #define PA_VARIANT_AUTO 0   /* library's choice for the shape                     */
@@ -75,7 +75,8 @@ typedef struct {
   int32_t num_q_heads;        /* Hq                                            */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0, group G = Hq / Hkv         */
   int32_t head_dim;           /* D: 64 or 128                                  */
-  int32_t block_size;         /* tokens per block: 16 or 32                    */
+  int32_t block_size;         /* tokens per block: 8, 16, 32, 64 or 128 with
+                                 PA_VARIANT_MFMA; 16 or 32 with PA_VARIANT_VALU */
   int32_t num_blocks;         /* physical blocks in each pool                  */
   int32_t max_blocks_per_seq; /* row stride (entries) of block_tables          */
   int32_t max_seq_len;        /* host bound on every seq_lens[i]; sizes the
@@ -171,6 +172,28 @@ pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* sl
 pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,
                            int64_t block_bytes, int32_t num_blocks, void* stream);
 
+/*
+ * pa_swap_blocks — move whole blocks between two pool pairs: a device pool
+ * and a swap pool in pinned host memory, either way.
+ *
+ * [N4N] "Why it matters for KV cache" (swapping and preemption: blocks are
+ * evicted to CPU memory when GPU memory runs short and fetched back when the
+ * request resumes). For each pair n, with (src, dst) = (pairs[2n],
+ * pairs[2n+1]):
+ *     dst_k[dst] = src_k[src],  dst_v[dst] = src_v[src]   (bitwise)
+ * One kernel moves every pair: host memory is read or written by the GPU
+ * over the host link, so host pools must be pinned, device-mapped memory
+ * (hipHostMalloc, or a pinned torch tensor). Destinations must be distinct.
+ *
+ *   src_k,src_v   [dev or pinned host] src_num_blocks blocks of block_bytes
+ *   dst_k,dst_v   [dev or pinned host] dst_num_blocks blocks of block_bytes
+ *   pairs         [dev] int64 [num_pairs][2]; ids out of range are skipped
+ *                 and flagged (PA_DEVERR_COPY_PAIR)
+ */
+pa_status_t pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                           const int64_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                           int32_t src_num_blocks, int32_t dst_num_blocks, void* stream);
+
 /* Waits for `stream`, then returns the current device's error word in
  * *flags (PA_DEVERR_* bits, 0 = clean) and clears it. Returns PA_EDEVICE if
  * any bit was set, PA_EHIP if a HIP call failed. */
@@ -193,7 +216,7 @@ const char* pa_status_str(pa_status_t status);
  * shared block).
  *
  * Readings: a fork shares every parent block including a partial last
- * block; within one batch, writers are served in order, so the last writer
+ * block; freeing a swapped-out sequence returns its swap blocks; within one batch, writers are served in order, so the last writer
  * into a shared block keeps the original; freed blocks rejoin the back of
  * the free list in table order; the free list hands out blocks front first.
  * ------------------------------------------------------------------------ */
@@ -230,6 +253,35 @@ pa_status_t pa_bm_free_seq(pa_bm_t* bm, int32_t seq_id);
  * longer than max_blocks. Either output may be NULL. */
 pa_status_t pa_bm_export(const pa_bm_t* bm, const int32_t* seq_ids, int32_t n,
                          int32_t max_blocks, int32_t* tables, int32_t* lens);
+
+/* Swap space for preemption ([N4N] "Why it matters for KV cache", swapping
+ * and preemption; [ZQ] summary, "easy preemption"): `num_cpu_blocks` host
+ * blocks with their own free list (0, 1, 2, ... handed out front first).
+ * PA_EINVAL while a sequence is swapped out. */
+pa_status_t pa_bm_set_swap_space(pa_bm_t* bm, int32_t num_cpu_blocks);
+
+/* Moves every block of `seq_id` to swap space, in table order: pairs [host]
+ * int64[2 * max_pairs] receives (device block, swap block) for pa_swap_blocks
+ * (device pools -> host pools); *num_pairs their count. A device block still
+ * shared by other sequences stays with them (count - 1); the others return
+ * to the back of the free list. A swapped-out sequence cannot be appended
+ * to, forked or exported. PA_ENOBLOCKS (swap space short) leaves state
+ * unchanged. */
+pa_status_t pa_bm_swap_out(pa_bm_t* bm, int32_t seq_id, int64_t* pairs, int32_t max_pairs,
+                           int32_t* num_pairs);
+
+/* Brings a swapped-out sequence back: each swap block, in table order, gets
+ * a fresh device block from the free list; pairs receives (swap block,
+ * device block) for pa_swap_blocks (host pools -> device pools); swap blocks
+ * rejoin the back of the swap free list. PA_ENOBLOCKS leaves state
+ * unchanged. */
+pa_status_t pa_bm_swap_in(pa_bm_t* bm, int32_t seq_id, int64_t* pairs, int32_t max_pairs,
+                          int32_t* num_pairs);
+
+/* Free swap-space blocks; 1 if `seq_id` is swapped out, 0 if resident, -1 if
+ * unknown. */
+int32_t pa_bm_num_free_swap(const pa_bm_t* bm);
+int32_t pa_bm_is_swapped(const pa_bm_t* bm, int32_t seq_id);
 
 int32_t pa_bm_num_free(const pa_bm_t* bm);
 /* Reference count of `block`, or -1 if out of range. */

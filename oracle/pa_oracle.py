@@ -18,7 +18,9 @@ converted exactly from their fp32 or bf16 bits):
   then exact softmax attention over those rows;
 * the same attention split into fixed-length context partitions and combined
   by the log-sum-exp identity;
-* the slot write of new K/V rows and the whole-block copy, bit for bit.
+* the slot write of new K/V rows and the whole-block copy, bit for bit;
+* swapping: a second (host) pool with its own free list, a sequence's blocks
+  moved out to it and back, and the block moves between the two pools.
 
 Sources (page title, then the section used):
   [Vij]  "PagedAttention Explained: KV Blocks, Allocation, and Sharing"
@@ -42,7 +44,11 @@ design notes of the repository):
     copies it first; writers are served in call order, so the last writer
     keeps the original block;
   * freed blocks return to the back of the free list, in table order;
-  * a slot < 0 means "no write" (padding).
+  * a slot < 0 means "no write" (padding);
+  * swap space hands out its blocks front first (0, 1, 2, ...); swapping a
+    sequence out moves its table entries in order, a device block still
+    shared by other sequences stays with them, the others and returned swap
+    blocks rejoin the back of their free lists.
 
 Every function here is pinned by tests against the pages' worked numbers,
 closed forms, invariants, a library routine or brute force; none is
@@ -60,7 +66,7 @@ __all__ = [
     "OracleNoBlocks", "OracleRefcountError", "OracleBlockManager",
     "as_f64", "positions_to_rows", "kv_head_of",
     "decode", "decode_one", "partition_partials", "combine_partials",
-    "decode_partitioned", "reshape_and_cache", "copy_blocks",
+    "decode_partitioned", "reshape_and_cache", "copy_blocks", "swap_blocks",
 ]
 
 
@@ -137,6 +143,8 @@ class OracleBlockManager:
         self.ref = [0] * self.num_blocks
         self.tables: dict[int, list[int]] = {}
         self.ntok: dict[int, int] = {}
+        self.swap_free: deque = deque()
+        self.swapped: set = set()
 
     # -- helpers ----------------------------------------------------------
     def _take(self) -> int:
@@ -183,6 +191,8 @@ class OracleBlockManager:
 
     def append_slots(self, seqs):
         """append_slot for each listed sequence in order; all or nothing."""
+        if any(s in self.swapped for s in seqs):
+            raise ValueError("a swapped-out sequence cannot be appended to")
         need = sum(1 for s in seqs if self._append_needs_block(s)) if len(set(seqs)) == len(seqs) else None
         if need is None:
             raise ValueError("a sequence may appear once per batch")
@@ -215,6 +225,8 @@ class OracleBlockManager:
         included) and the parent's token count."""
         if child in self.tables:
             raise ValueError(f"sequence {child} exists")
+        if parent in self.swapped:
+            raise ValueError("a swapped-out sequence cannot be forked")
         self.tables[child] = list(self.tables[parent])
         self.ntok[child] = self.ntok[parent]
         for b in self.tables[child]:
@@ -222,8 +234,15 @@ class OracleBlockManager:
 
     def free_seq(self, seq: int) -> None:
         """Drop a sequence; blocks whose count reaches zero rejoin the back
-        of the free list in table order."""
+        of the free list in table order. A swapped-out sequence returns its
+        swap blocks instead."""
         t = self.tables[seq]
+        if seq in self.swapped:
+            self.swap_free.extend(t)
+            self.swapped.discard(seq)
+            del self.tables[seq]
+            del self.ntok[seq]
+            return
         for b in t:
             if self.ref[b] <= 0:
                 raise OracleRefcountError(f"block {b}")
@@ -234,6 +253,53 @@ class OracleBlockManager:
         del self.tables[seq]
         del self.ntok[seq]
 
+    # -- swapping ([N4N] "Why it matters for KV cache": under memory
+    # pressure blocks are evicted to CPU memory and fetched back when the
+    # request resumes; [ZQ] summary: easy preemption) ---------------------
+    def set_swap_space(self, num_cpu_blocks: int) -> None:
+        if self.swapped:
+            raise ValueError("swap space in use")
+        self.swap_free = deque(range(int(num_cpu_blocks)))
+
+    def swap_out(self, seq: int):
+        """Every table entry, in order, moves to the next free swap block;
+        returns the (device block, swap block) moves. The device block is
+        released once (it stays on the device while other sequences share
+        it)."""
+        if seq in self.swapped:
+            raise ValueError("already swapped out")
+        t = self.tables[seq]
+        if len(t) > len(self.swap_free):
+            raise OracleNoBlocks(f"need {len(t)} swap blocks, free {len(self.swap_free)}")
+        moves = []
+        for k, b in enumerate(t):
+            c = self.swap_free.popleft()
+            moves.append((b, c))
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+            t[k] = c
+        self.swapped.add(seq)
+        return moves
+
+    def swap_in(self, seq: int):
+        """Every swap block, in table order, gets a fresh device block from
+        the front of the free list; returns the (swap block, device block)
+        moves; the swap blocks rejoin the back of the swap free list."""
+        if seq not in self.swapped:
+            raise ValueError("not swapped out")
+        t = self.tables[seq]
+        if len(t) > len(self.free):
+            raise OracleNoBlocks(f"need {len(t)}, free {len(self.free)}")
+        moves = []
+        for k, c in enumerate(t):
+            d = self._take()
+            moves.append((c, d))
+            self.swap_free.append(c)
+            t[k] = d
+        self.swapped.discard(seq)
+        return moves
+
     def export(self, seqs, max_blocks: int):
         """Block tables padded with -1 (the [N4N] BlockTable's "unallocated"
         marker) and token counts, for the listed sequences."""
@@ -241,6 +307,8 @@ class OracleBlockManager:
         lens = np.zeros(len(seqs), dtype=np.int32)
         for r, s in enumerate(seqs):
             t = self.tables[s]
+            if s in self.swapped:
+                raise ValueError("a swapped-out sequence has no device table")
             if len(t) > max_blocks:
                 raise ValueError("table longer than max_blocks")
             tab[r, :len(t)] = t
@@ -398,3 +466,12 @@ def copy_blocks(k_pool, v_pool, pairs):
     for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
         k_pool[dst] = k_pool[src]
         v_pool[dst] = v_pool[src]
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """For each (src, dst): block dst of the destination pools becomes a bit
+    copy of block src of the source pools (device pools to swap space or
+    back; [N4N] "Why it matters for KV cache", swapping and preemption)."""
+    for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]

@@ -7,7 +7,8 @@ not been built, importing the binding's functions raises.
 
 Calls mirror the C ABI in include/pa.h:
     pa_decode, pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes,
-    pa_reshape_and_cache, pa_copy_blocks, pa_device_errors, BlockManager (pa_bm_*).
+    pa_reshape_and_cache, pa_copy_blocks, pa_swap_blocks, pa_device_errors,
+    BlockManager (pa_bm_*).
 """
 from __future__ import annotations
 
@@ -17,16 +18,19 @@ import os
 import numpy as np
 
 __all__ = [
-    "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16",
+    "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16", "PA_DEVERR_BLOCK_ID", "PA_DEVERR_SEQ_LEN",
+    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_device_errors", "BlockManager",
-    "EXPORTED_SYMBOLS",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
+    "BlockManager", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_BF16 = 0, 1
+# device error word bits (include/pa.h PA_DEVERR_*)
+PA_DEVERR_BLOCK_ID, PA_DEVERR_SEQ_LEN, PA_DEVERR_SLOT, PA_DEVERR_COPY_PAIR = 0x1, 0x2, 0x4, 0x8
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
            4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
@@ -34,9 +38,12 @@ _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
 # Every function include/pa.h declares.
 EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_device_errors", "pa_status_str",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
+    "pa_status_str",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
+    "pa_bm_set_swap_space", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_num_free_swap",
+    "pa_bm_is_swapped",
 )
 
 
@@ -64,6 +71,7 @@ _SIGS = {
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _vp]),
+    "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp]),
     "pa_device_errors": (_i32, [ctypes.POINTER(ctypes.c_uint32), _vp]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
     "pa_bm_create": (_i32, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
@@ -76,6 +84,11 @@ _SIGS = {
     "pa_bm_num_free": (_i32, [_vp]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_num_tokens": (_i32, [_vp, _i32]),
+    "pa_bm_set_swap_space": (_i32, [_vp, _i32]),
+    "pa_bm_swap_out": (_i32, [_vp, _i32, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_swap_in": (_i32, [_vp, _i32, _vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_num_free_swap": (_i32, [_vp]),
+    "pa_bm_is_swapped": (_i32, [_vp, _i32]),
 }
 
 _lib = None
@@ -243,6 +256,29 @@ def pa_copy_blocks(k_pool, v_pool, pairs, stream=None):
     _check(st, "pa_copy_blocks")
 
 
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None):
+    """Move whole blocks (src, dst) = pairs[n] from (src_k, src_v) to (dst_k,
+    dst_v); one side is normally a pinned host pool. pairs int64 [N,2] on the
+    device; block shapes must match."""
+    torch = _torch()
+    dev = pairs.device
+    for name, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v)):
+        _need(t, name, dim=4)
+        if t.device.type == "cpu" and not t.is_pinned():
+            raise ValueError(f"{name} is host memory that is not pinned")
+    _need(pairs, "pairs", dtype=torch.int64)
+    if pairs.device.type != "cuda":
+        raise ValueError("pairs must be device memory")
+    if (tuple(src_k.shape[1:]) != tuple(dst_k.shape[1:]) or src_k.shape != src_v.shape or
+            dst_k.shape != dst_v.shape or src_k.dtype != dst_k.dtype):
+        raise ValueError("block shape or dtype mismatch")
+    block_bytes = src_k[0].numel() * src_k.element_size()
+    st = lib().pa_swap_blocks(src_k.data_ptr(), src_v.data_ptr(), dst_k.data_ptr(),
+                              dst_v.data_ptr(), pairs.data_ptr(), pairs.numel() // 2, block_bytes,
+                              src_k.shape[0], dst_k.shape[0], _stream_ptr(stream, dev))
+    _check(st, "pa_swap_blocks")
+
+
 def pa_device_errors(stream=None, device=None) -> int:
     """Synchronise the stream and return (and clear) the device error word."""
     torch = _torch()
@@ -323,6 +359,33 @@ class BlockManager:
                                   lens.ctypes.data)
         _check(st, "pa_bm_export")
         return tab, lens
+
+    def set_swap_space(self, num_cpu_blocks: int) -> None:
+        _check(self._l.pa_bm_set_swap_space(self._h, num_cpu_blocks), "pa_bm_set_swap_space")
+
+    def _swap(self, fn, seq_id: int):
+        cap = 1 << 16
+        pairs = np.empty(2 * cap, dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(getattr(self._l, fn)(self._h, seq_id, pairs.ctypes.data, cap, ctypes.byref(n)), fn)
+        return pairs[: 2 * n.value].reshape(-1, 2)
+
+    def swap_out(self, seq_id: int):
+        """(device block, swap block) pairs, int64 [k, 2]."""
+        return self._swap("pa_bm_swap_out", seq_id)
+
+    def swap_in(self, seq_id: int):
+        """(swap block, device block) pairs, int64 [k, 2]."""
+        return self._swap("pa_bm_swap_in", seq_id)
+
+    def num_free_swap(self) -> int:
+        return int(self._l.pa_bm_num_free_swap(self._h))
+
+    def is_swapped(self, seq_id: int) -> bool:
+        v = int(self._l.pa_bm_is_swapped(self._h, seq_id))
+        if v < 0:
+            raise KeyError(seq_id)
+        return bool(v)
 
     def num_free(self) -> int:
         return int(self._l.pa_bm_num_free(self._h))

@@ -217,21 +217,59 @@ pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* sl
   return from_hip(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
 }
 
-pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,
-                           int64_t block_bytes, int32_t num_blocks, void* stream) {
-  if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 16 != 0 || num_blocks <= 0)
+static pa_status_t copy_impl(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int64_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                             int32_t src_blocks, int32_t dst_blocks, void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 16 != 0 || src_blocks <= 0 ||
+      dst_blocks <= 0)
     return PA_EINVAL;
   if (num_pairs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !pairs || !aligned16(k_pool) || !aligned16(v_pool))
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs || !aligned16(src_k) || !aligned16(src_v) ||
+      !aligned16(dst_k) || !aligned16(dst_v))
     return PA_EINVAL;
   pa::CopyArgs a{};
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
+  a.src_k = src_k;
+  a.src_v = src_v;
+  a.dst_k = dst_k;
+  a.dst_v = dst_v;
   a.pairs = pairs;
   a.block_chunks = block_bytes / 16;
   a.num_pairs = num_pairs;
-  a.num_blocks = num_blocks;
+  a.src_blocks = src_blocks;
+  a.dst_blocks = dst_blocks;
   return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,
+                           int64_t block_bytes, int32_t num_blocks, void* stream) {
+  return copy_impl(k_pool, v_pool, k_pool, v_pool, pairs, num_pairs, block_bytes, num_blocks,
+                   num_blocks, stream);
+}
+
+// A pool the swap kernel may touch: device memory, or pinned host memory
+// mapped into the device's address space at the same address. Pageable host
+// memory (unknown to HIP) is refused before any launch.
+static bool device_reachable(const void* p) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error of the failed query
+    return false;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) return true;
+  if (attr.type == hipMemoryTypeHost) return attr.devicePointer == p;
+  return false;
+}
+
+pa_status_t pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                           const int64_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                           int32_t src_num_blocks, int32_t dst_num_blocks, void* stream) {
+  if (num_pairs > 0) {
+    for (const void* p : {src_k, src_v, static_cast<const void*>(dst_k),
+                          static_cast<const void*>(dst_v), static_cast<const void*>(pairs)})
+      if (p && !device_reachable(p)) return PA_EINVAL;
+  }
+  return copy_impl(src_k, src_v, dst_k, dst_v, pairs, num_pairs, block_bytes, src_num_blocks,
+                   dst_num_blocks, stream);
 }
 
 pa_status_t pa_device_errors(uint32_t* flags, void* stream) {

@@ -28,7 +28,10 @@ struct pa_bm {
     std::vector<int32_t> table;                // logical block -> physical id
     int32_t ntok = 0;
     uint64_t stamp = 0;                        // call that last listed it
+    bool swapped = false;                      // table names swap-space blocks
   };
+  int32_t num_cpu_blocks = 0;                  // swap space (host) blocks
+  std::deque<int32_t> cpu_free;
   std::unordered_map<int32_t, Seq> seqs;
   uint64_t epoch = 0;                          // append call counter
   std::vector<Seq*> batch;                     // scratch of pa_bm_append_slots
@@ -108,7 +111,7 @@ pa_status_t pa_bm_append_slots(pa_bm_t* bm, const int32_t* seq_ids, int32_t n, i
   for (int32_t k = 0; k < n; ++k) {
     auto it = bm->seqs.find(seq_ids[k]);
     if (it == bm->seqs.end() || it->second.stamp == epoch) return PA_EINVAL;
-    if (it->second.ntok == INT32_MAX) return PA_EINVAL;
+    if (it->second.ntok == INT32_MAX || it->second.swapped) return PA_EINVAL;
     it->second.stamp = epoch;
     batch[k] = &it->second;
     need += bm->append_needs_block(it->second) ? 1 : 0;
@@ -141,7 +144,7 @@ pa_status_t pa_bm_append_slots(pa_bm_t* bm, const int32_t* seq_ids, int32_t n, i
 pa_status_t pa_bm_fork(pa_bm_t* bm, int32_t parent_id, int32_t child_id) {
   if (!bm) return PA_EINVAL;
   auto it = bm->seqs.find(parent_id);
-  if (it == bm->seqs.end() || bm->seqs.count(child_id)) return PA_EINVAL;
+  if (it == bm->seqs.end() || bm->seqs.count(child_id) || it->second.swapped) return PA_EINVAL;
   pa_bm::Seq child = it->second;
   for (int32_t b : child.table) bm->ref[b] += 1;
   bm->seqs.emplace(child_id, std::move(child));
@@ -152,6 +155,11 @@ pa_status_t pa_bm_free_seq(pa_bm_t* bm, int32_t seq_id) {
   if (!bm) return PA_EINVAL;
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_EINVAL;
+  if (it->second.swapped) {
+    for (int32_t c : it->second.table) bm->cpu_free.push_back(c);
+    bm->seqs.erase(it);
+    return PA_OK;
+  }
   for (int32_t b : it->second.table)
     if (bm->ref[b] <= 0) return PA_EREFCOUNT;
   for (int32_t b : it->second.table) {
@@ -166,7 +174,7 @@ pa_status_t pa_bm_export(const pa_bm_t* bm, const int32_t* seq_ids, int32_t n,
   if (!bm || n < 0 || max_blocks < 0 || (n > 0 && !seq_ids)) return PA_EINVAL;
   for (int32_t k = 0; k < n; ++k) {
     auto it = bm->seqs.find(seq_ids[k]);
-    if (it == bm->seqs.end()) return PA_EINVAL;
+    if (it == bm->seqs.end() || it->second.swapped) return PA_EINVAL;
     if ((int64_t)it->second.table.size() > max_blocks) return PA_EINVAL;
   }
   for (int32_t k = 0; k < n; ++k) {
@@ -180,6 +188,77 @@ pa_status_t pa_bm_export(const pa_bm_t* bm, const int32_t* seq_ids, int32_t n,
     if (lens) lens[k] = s.ntok;
   }
   return PA_OK;
+}
+
+// Swapping ([N4N] "Why it matters for KV cache": blocks evicted to CPU memory
+// under pressure and fetched back when the request resumes; [ZQ] summary:
+// easy preemption). Swap space is a second pool of host blocks with its own
+// free list, handed out front first; a swapped-out sequence's table names
+// swap-space blocks until it is swapped back in.
+pa_status_t pa_bm_set_swap_space(pa_bm_t* bm, int32_t num_cpu_blocks) {
+  if (!bm || num_cpu_blocks < 0) return PA_EINVAL;
+  for (const auto& kv : bm->seqs)
+    if (kv.second.swapped) return PA_EINVAL;    // swap space in use
+  bm->num_cpu_blocks = num_cpu_blocks;
+  bm->cpu_free.clear();
+  for (int32_t c = 0; c < num_cpu_blocks; ++c) bm->cpu_free.push_back(c);
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swap_out(pa_bm_t* bm, int32_t seq_id, int64_t* pairs, int32_t max_pairs,
+                           int32_t* num_pairs) {
+  if (!bm || !num_pairs) return PA_EINVAL;
+  *num_pairs = 0;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end() || it->second.swapped) return PA_EINVAL;
+  pa_bm::Seq& s = it->second;
+  const int32_t n = (int32_t)s.table.size();
+  if (n > max_pairs || (n > 0 && !pairs)) return PA_EINVAL;
+  if (n > (int32_t)bm->cpu_free.size()) return PA_ENOBLOCKS;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t b = s.table[k];
+    const int32_t c = bm->cpu_free.front();
+    bm->cpu_free.pop_front();
+    pairs[2 * k] = b;
+    pairs[2 * k + 1] = c;
+    // a block still shared by other sequences stays on the device for them
+    if (--bm->ref[b] == 0) bm->free_list.push_back(b);
+    s.table[k] = c;
+  }
+  s.swapped = true;
+  *num_pairs = n;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swap_in(pa_bm_t* bm, int32_t seq_id, int64_t* pairs, int32_t max_pairs,
+                          int32_t* num_pairs) {
+  if (!bm || !num_pairs) return PA_EINVAL;
+  *num_pairs = 0;
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end() || !it->second.swapped) return PA_EINVAL;
+  pa_bm::Seq& s = it->second;
+  const int32_t n = (int32_t)s.table.size();
+  if (n > max_pairs || (n > 0 && !pairs)) return PA_EINVAL;
+  if (n > (int32_t)bm->free_list.size()) return PA_ENOBLOCKS;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t c = s.table[k];
+    const int32_t d = bm->take();
+    pairs[2 * k] = c;
+    pairs[2 * k + 1] = d;
+    bm->cpu_free.push_back(c);
+    s.table[k] = d;
+  }
+  s.swapped = false;
+  *num_pairs = n;
+  return PA_OK;
+}
+
+int32_t pa_bm_num_free_swap(const pa_bm_t* bm) { return bm ? (int32_t)bm->cpu_free.size() : -1; }
+
+int32_t pa_bm_is_swapped(const pa_bm_t* bm, int32_t seq_id) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq_id);
+  return it == bm->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
 }
 
 int32_t pa_bm_num_free(const pa_bm_t* bm) { return bm ? (int32_t)bm->free_list.size() : -1; }

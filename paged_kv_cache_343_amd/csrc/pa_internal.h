@@ -46,13 +46,18 @@ struct CacheArgs {
   int32_t block_size;
 };
 
+// Whole-block copies from (src_k, src_v) to (dst_k, dst_v): the same pools
+// for copy-on-write, a device pool and a pinned host pool for swapping.
 struct CopyArgs {
-  void* k_pool;
-  void* v_pool;
-  const int64_t* pairs;         // [N][2]
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int64_t* pairs;         // [N][2] (src block, dst block)
   int64_t block_chunks;         // 16-byte chunks per block
   int32_t num_pairs;
-  int32_t num_blocks;
+  int32_t src_blocks;           // blocks in the source pools
+  int32_t dst_blocks;           // blocks in the destination pools
 };
 
 // Kernel selection key for pa_decode_partition.

@@ -173,3 +173,81 @@ def test_random_churn_matches_oracle():
             assert pairs.tolist() == [list(c) for _, c in ores if c is not None]
     maxb = max(len(ob.table(s)) for s in live) if live else 1
     _same_state(bm, ob, live, maxb)
+
+
+def _same_swap_state(bm, ob, seqs):
+    assert bm.num_free() == ob.num_free() and bm.num_free_swap() == len(ob.swap_free)
+    for b in range(ob.num_blocks):
+        assert bm.refcount(b) == ob.refcount(b)
+    for s in seqs:
+        assert bm.is_swapped(s) == (s in ob.swapped)
+
+
+def test_swap_out_in_bit_exact():
+    """Forked and private sequences swapped out and back in between decode
+    steps: every move pair, table, refcount and free count as the mirror."""
+    bs = 16
+    rng = np.random.default_rng(21)
+    nb, ncpu = 400, 120
+    order = W.free_order(nb, rng)
+    bm, ob = P.BlockManager(nb, bs, order), O.OracleBlockManager(nb, bs, order)
+    bm.set_swap_space(ncpu); ob.set_swap_space(ncpu)
+    lens = rng.integers(1, 200, 10)
+    for m in (bm, ob):
+        for i, L in enumerate(lens):
+            m.add_seq(i, int(L))
+        m.fork(0, 10)          # seq 10 shares seq 0's blocks
+        m.fork(3, 11)
+    live = list(range(12))
+    for step in range(30):
+        out = [s for s in live if rng.random() < 0.5]
+        res = [s for s in live if s not in out]
+        if step % 3 == 0 and res:
+            s = int(rng.choice(res))
+            p1, p2 = bm.swap_out(s), np.array(ob.swap_out(s), dtype=np.int64).reshape(-1, 2)
+            assert np.array_equal(p1, p2)
+        swapped = [s for s in live if s in ob.swapped]
+        if step % 3 == 1 and swapped:
+            s = int(rng.choice(swapped))
+            p1, p2 = bm.swap_in(s), np.array(ob.swap_in(s), dtype=np.int64).reshape(-1, 2)
+            assert np.array_equal(p1, p2)
+        batch = [s for s in live if s not in ob.swapped and rng.random() < 0.7]
+        slots, pairs = bm.append_slots(batch)
+        ores = ob.append_slots(batch)
+        assert slots.tolist() == [x for x, _ in ores]
+        assert pairs.tolist() == [list(c) for _, c in ores if c is not None]
+        _same_swap_state(bm, ob, live)
+    resident = [s for s in live if s not in ob.swapped]
+    maxb = max(len(ob.table(s)) for s in resident)
+    t1, l1 = bm.export(resident, maxb)
+    t2, l2 = ob.export(resident, maxb)
+    assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+    for s in live:
+        bm.free_seq(s); ob.free_seq(s)
+    assert bm.num_free() == nb and bm.num_free_swap() == ncpu
+    _same_swap_state(bm, ob, [])
+
+
+def test_swap_errors_leave_state_unchanged():
+    bm = P.BlockManager(20, 16)
+    bm.add_seq(0, 100)                          # 7 blocks
+    bm.set_swap_space(5)
+    with pytest.raises(P.PaError) as e:
+        bm.swap_out(0)                          # 7 > 5 swap blocks
+    assert e.value.name == "PA_ENOBLOCKS"
+    assert not bm.is_swapped(0) and bm.num_free_swap() == 5 and bm.num_free() == 13
+    bm.set_swap_space(8)
+    moves = bm.swap_out(0)
+    assert moves.shape == (7, 2) and bm.is_swapped(0) and bm.num_free() == 20
+    for call in (lambda: bm.append_slots([0]), lambda: bm.export([0], 8), lambda: bm.fork(0, 1),
+                 lambda: bm.swap_out(0), lambda: bm.set_swap_space(10)):
+        with pytest.raises(P.PaError):
+            call()
+    bm.add_seq(2, 16 * 15)                      # leaves 5 device blocks: too few to swap in
+    with pytest.raises(P.PaError) as e:
+        bm.swap_in(0)
+    assert e.value.name == "PA_ENOBLOCKS" and bm.is_swapped(0)
+    bm.free_seq(2)
+    back = bm.swap_in(0)
+    assert back[:, 0].tolist() == moves[:, 1].tolist() and not bm.is_swapped(0)
+    assert bm.num_tokens(0) == 100 and bm.num_free_swap() == 8

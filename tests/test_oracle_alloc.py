@@ -147,3 +147,68 @@ def test_random_churn_invariants():
             bm.free_seq(s)
         _invariants(bm) if step % 100 == 0 else None
     _invariants(bm)
+
+
+# -- swapping ([N4N] "Why it matters for KV cache": blocks evicted to CPU
+# memory and fetched back when the request resumes) --------------------------
+
+def _check_swap_invariants(ob, ncpu):
+    held = {}
+    for s, t in ob.tables.items():
+        if s in ob.swapped:
+            continue
+        for b in t:
+            held[b] = held.get(b, 0) + 1
+    assert all(ob.ref[b] == held.get(b, 0) for b in range(ob.num_blocks))
+    assert sorted(list(ob.free) + list(held)) == list(range(ob.num_blocks))
+    on_host = [c for s in ob.swapped for c in ob.tables[s]]
+    assert sorted(list(ob.swap_free) + on_host) == list(range(ncpu))
+
+
+def test_oracle_swap_invariants_random_ops():
+    rng = np.random.default_rng(31)
+    ob = O.OracleBlockManager(300, 16, rng.permutation(300))
+    ncpu = 150
+    ob.set_swap_space(ncpu)
+    for i in range(8):
+        ob.add_seq(i, int(rng.integers(1, 150)))
+    ob.fork(1, 8); ob.fork(1, 9)
+    live = list(range(10))
+    for _ in range(200):
+        s = int(rng.choice(live))
+        op = rng.integers(0, 3)
+        try:
+            if op == 0:
+                ob.swap_out(s)
+            elif op == 1:
+                ob.swap_in(s)
+            elif s not in ob.swapped:
+                ob.append_slots([s])
+        except (ValueError, O.OracleNoBlocks):
+            pass
+        _check_swap_invariants(ob, ncpu)
+
+
+def test_oracle_swap_round_trip_keeps_attention_bitwise():
+    """A sequence swapped out, its device blocks reused (poisoned), then
+    swapped back into different blocks decodes to the same bits."""
+    rng = np.random.default_rng(32)
+    bs, nb, hkv, d = 16, 40, 2, 8
+    ob = O.OracleBlockManager(nb, bs, rng.permutation(nb))
+    ob.set_swap_space(12)
+    ob.add_seq(0, 90); ob.add_seq(1, 30)
+    kp = rng.standard_normal((nb, hkv, bs, d)); vp = rng.standard_normal((nb, hkv, bs, d))
+    hk = np.zeros((12, hkv, bs, d)); hv = np.zeros((12, hkv, bs, d))
+    q = rng.standard_normal((2, 4, d))
+    tab, lens = ob.export([0, 1], 8)
+    before = O.decode(q, kp, vp, tab, lens, 0.3)
+    old_blocks = list(tab[0][tab[0] >= 0])
+    O.swap_blocks(kp, vp, hk, hv, ob.swap_out(0))
+    kp[old_blocks] = np.nan; vp[old_blocks] = np.nan      # freed blocks reused
+    ob.add_seq(2, 40)                                      # takes some of them
+    moves = ob.swap_in(0)
+    O.swap_blocks(hk, hv, kp, vp, moves)
+    tab2, lens2 = ob.export([0, 1], 8)
+    after = O.decode(q, kp, vp, tab2, lens2, 0.3)
+    assert not np.array_equal(tab2[0], tab[0])             # new physical blocks
+    assert np.array_equal(before, after)
