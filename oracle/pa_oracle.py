@@ -18,6 +18,9 @@ converted exactly from their fp32 or bf16 bits):
   then exact softmax attention over those rows;
 * the same attention split into fixed-length context partitions and combined
   by the log-sum-exp identity;
+* attention of several new query tokens per sequence (a prefill chunk or
+  speculative tokens) over the same paged cache, each token attending to
+  every position up to and including its own;
 * the slot write of new K/V rows and the whole-block copy, bit for bit;
 * swapping: a second (host) pool with its own free list, a sequence's blocks
   moved out to it and back, and the block moves between the two pools.
@@ -67,6 +70,7 @@ __all__ = [
     "as_f64", "positions_to_rows", "kv_head_of",
     "decode", "decode_one", "partition_partials", "combine_partials",
     "decode_partitioned", "reshape_and_cache", "copy_blocks", "swap_blocks",
+    "multi_query",
 ]
 
 
@@ -437,6 +441,45 @@ def decode_partitioned(q, k_pool, v_pool, block_tables, seq_lens, scale,
                                        int(seq_lens[i]), scale,
                                        kv_head_of(h, hq, hkv), bs, partition_tokens)
             out[i, h] = combine_partials(parts, d)
+    return out
+
+
+def multi_query(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale):
+    """Attention of several query tokens per sequence over its paged cache,
+    float64, causal inside the chunk.
+
+    Sequence i's query tokens are rows query_start[i] .. query_start[i+1]-1
+    of q [T, Hq, D]; they are its last Tq_i = query_start[i+1] -
+    query_start[i] positions, already written to the cache, so seq_lens[i]
+    counts them. Token t (0 <= t < Tq_i) sits at position L_i - Tq_i + t and
+    attends to positions 0 .. L_i - Tq_i + t through the block table. Output
+    [T, Hq, D].
+
+    [ZQ] comparison table: paged attention is ordinary FlashAttention with a
+    block-table dereference ("Real kernels fuse this with FlashAttention
+    tiling", pseudo-code comment); the multi-token form is the reading taken
+    for a prefill chunk or speculative tokens: standard causal attention
+    whose key/value rows come through the table. With one query token per
+    sequence it is exactly `decode`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    bs = k_pool.shape[2]
+    out = np.zeros((T, hq, d), dtype=np.float64)
+    starts = [int(x) for x in query_start]
+    for i in range(len(starts) - 1):
+        t0, t1 = starts[i], starts[i + 1]
+        L = int(seq_lens[i])
+        tq = t1 - t0
+        if tq > L:
+            raise ValueError("more query tokens than cached positions")
+        for t in range(tq):
+            n_att = L - tq + t + 1            # positions 0 .. L - tq + t
+            for h in range(hq):
+                g = kv_head_of(h, hq, hkv)
+                out[t0 + t, h] = decode_one(q[t0 + t, h], k_pool, v_pool, block_tables[i],
+                                            n_att, scale, g, bs)
     return out
 
 
