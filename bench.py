@@ -358,6 +358,7 @@ def main() -> int:
                              "GBps": round(red_bytes / (float(np.mean(red_ms)) / 1e3) / 1e9, 1)},
         "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
         "a6_fork_cow_host_us": fork_cow_host_us(P),
+        "n2_multi_query": multi_query_rate(P, torch, dev, W),
         "n3_swap_blocks": swap_rate(P, torch, dev),
     }
     peak = stream_read_peak(torch, dev)
@@ -457,6 +458,58 @@ def swap_rate(P, torch, dev) -> dict:
         t = e0.elapsed_time(e1) / 5 / 1e3
         moved = 2 * n * kp[0].numel() * 2
         res[name] = {"us": round(t * 1e6, 1), "bytes": moved, "GBps": round(moved / t / 1e9, 1)}
+    return res
+
+
+def multi_query_rate(P, torch, dev, W) -> dict:
+    """pa_multi_query on the headline head shape (32 query / 8 KV heads, D 128,
+    bf16, block size 16, scattered blocks): a 512-token prefill chunk at the
+    end of 4096-token contexts for 16 sequences, and 4 speculative tokens for
+    each of the 256 headline sequences (lengths U{512..4096}). Matrix-core
+    bound: flops = 4 * D * Hq * (positions each query token attends)."""
+    hq, hkv, d, bs = 32, 8, 128, 16
+    res = {}
+    rng = np.random.default_rng(17)
+    cases = {"prefill_chunk_512_of_4096_x16": (np.full(16, 4096), np.full(16, 512)),
+             "speculative_4_x256": (rng.integers(512, 4097, 256), np.full(256, 4))}
+    for name, (lens, tqs) in cases.items():
+        B = len(lens)
+        nblk = [-(-int(L) // bs) for L in lens]
+        nb = int(sum(nblk) * 1.1) + 1
+        order = rng.permutation(nb)
+        maxb = max(nblk)
+        tab = np.full((B, maxb), -1, dtype=np.int32)
+        p0 = 0
+        for i, n in enumerate(nblk):
+            tab[i, :n] = order[p0:p0 + n]
+            p0 += n
+        kp = W.normal_device((nb, hkv, bs, d), 901, "bf16", dev)
+        vp = W.normal_device((nb, hkv, bs, d), 902, "bf16", dev)
+        qs = np.concatenate([[0], np.cumsum(tqs)]).astype(np.int32)
+        T = int(qs[-1])
+        q = W.normal_device((T, hq, d), 903, "bf16", dev)
+        out = torch.empty_like(q)
+        args = (q, kp, vp, torch.from_numpy(tab).to(dev),
+                torch.from_numpy(lens.astype(np.int32)).to(dev), torch.from_numpy(qs).to(dev),
+                1.0 / math.sqrt(d), out)
+        kw = dict(max_seq_len=int(lens.max()), max_query_len=int(tqs.max()))
+        for _ in range(2):
+            P.pa_multi_query(*args, **kw)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            P.pa_multi_query(*args, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 10 / 1e3
+        attended = sum(int(tq) * (int(L) - int(tq)) + int(tq) * (int(tq) + 1) // 2
+                       for L, tq in zip(lens, tqs))
+        flops = 4 * d * hq * attended
+        kv = int(lens.sum()) * 2 * hkv * d * 2
+        res[name] = {"us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+                     "mfma_bf16_frac": round(flops / t / 2.5e15, 4),
+                     "kv_GBps": round(kv / t / 1e9, 1), "query_tokens": T}
+        del kp, vp
     return res
 
 

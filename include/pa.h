@@ -62,6 +62,7 @@ typedef enum {
 #define PA_DEVERR_SEQ_LEN 0x2u    /* seq_len < 0, > max_seq_len, or > table   */
 #define PA_DEVERR_SLOT 0x4u       /* slot >= num_blocks * block_size          */
 #define PA_DEVERR_COPY_PAIR 0x8u  /* copy/swap pair id outside its pool         */
+#define PA_DEVERR_QUERY 0x10u     /* multi-query: bad query range or length    */
 
 /* Decode kernel variants (pa_decode_shape_t.variant). */
 #define PA_VARIANT_AUTO 0   /* library's choice for the shape                     */
@@ -136,6 +137,51 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
 pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out,
                              const pa_decode_shape_t* shape, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Shape of one pa_multi_query call. */
+typedef struct {
+  int32_t num_seqs;           /* B                                             */
+  int32_t num_q_heads;        /* Hq                                            */
+  int32_t num_kv_heads;       /* Hkv; G = Hq / Hkv in {1, 2, 4, 8, 16}          */
+  int32_t head_dim;           /* D: 128                                        */
+  int32_t block_size;         /* 16, 32, 64 or 128                             */
+  int32_t num_blocks;         /* physical blocks in each pool                  */
+  int32_t max_blocks_per_seq; /* row stride (entries) of block_tables          */
+  int32_t max_seq_len;        /* host bound on every seq_lens[i]               */
+  int32_t max_query_len;      /* host bound on query tokens per sequence;
+                                 sizes the grid                                */
+  int32_t num_tokens;         /* T = query_start[B], rows of q and out         */
+  int32_t dtype;              /* PA_BF16                                       */
+} pa_multi_query_shape_t;
+
+/*
+ * pa_multi_query — attention of several new query tokens per sequence (a
+ * prefill chunk, or speculative tokens to verify) over the paged cache.
+ *
+ * [ZQ] comparison table: the paged kernel is FlashAttention with a
+ * block-table dereference (pseudo-code: "Real kernels fuse this with
+ * FlashAttention tiling"). Sequence i's query tokens are rows
+ * query_start[i] .. query_start[i+1]-1 of q; they are its last Tq_i
+ * positions and are already in the cache (pa_reshape_and_cache first), so
+ * seq_lens[i] counts them. Token t sits at position p = seq_lens[i] - Tq_i
+ * + t and, for every query head h (KV head h / G), attends causally to
+ * positions 0 .. p:
+ *     out[row][h] = sum_{p' <= p} softmax_p'(scale * q[row][h] . K[p']) V[p']
+ * With one token per sequence this is pa_decode. Both products run on the
+ * matrix cores; a sequence whose query range is invalid (Tq_i < 0,
+ * Tq_i > seq_lens[i], > max_query_len, or past num_tokens) is skipped and
+ * flagged (PA_DEVERR_QUERY).
+ *
+ *   q, out        [dev] [num_tokens][Hq][D] bf16
+ *   k_pool,v_pool [dev] [num_blocks][Hkv][bs][D] bf16
+ *   block_tables  [dev] int32 [B][max_blocks_per_seq]
+ *   seq_lens      [dev] int32 [B]
+ *   query_start   [dev] int32 [B + 1], non-decreasing, query_start[0] = 0
+ */
+pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* query_start, float scale, void* out,
+                           const pa_multi_query_shape_t* shape, void* stream);
 
 /*
  * pa_reshape_and_cache — write new tokens' K and V rows into their slots.

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16", "PA_DEVERR_BLOCK_ID", "PA_DEVERR_SEQ_LEN",
-    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR",
+    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "MultiQueryShape", "pa_multi_query",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
@@ -31,6 +31,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16 = 0, 1
 # device error word bits (include/pa.h PA_DEVERR_*)
 PA_DEVERR_BLOCK_ID, PA_DEVERR_SEQ_LEN, PA_DEVERR_SLOT, PA_DEVERR_COPY_PAIR = 0x1, 0x2, 0x4, 0x8
+PA_DEVERR_QUERY = 0x10
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
            4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
@@ -39,7 +40,7 @@ _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
 EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
-    "pa_status_str",
+    "pa_status_str", "pa_multi_query",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
     "pa_bm_set_swap_space", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_num_free_swap",
@@ -60,6 +61,12 @@ class DecodeShape(ctypes.Structure):
         "max_blocks_per_seq", "max_seq_len", "partition_tokens", "dtype", "variant")]
 
 
+class MultiQueryShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
+        "max_blocks_per_seq", "max_seq_len", "max_query_len", "num_tokens", "dtype")]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(DecodeShape)]),
@@ -72,6 +79,8 @@ _SIGS = {
                                     _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _vp]),
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp]),
+    "pa_multi_query": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                              ctypes.POINTER(MultiQueryShape), _vp]),
     "pa_device_errors": (_i32, [ctypes.POINTER(ctypes.c_uint32), _vp]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
     "pa_bm_create": (_i32, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
@@ -219,6 +228,36 @@ def pa_decode_reduce(q, k_pool, block_tables, seq_lens, out, *, max_seq_len, par
     st = lib().pa_decode_reduce(seq_lens.data_ptr(), out.data_ptr(), ctypes.byref(shape),
                                 workspace.data_ptr(), ws_bytes, _stream_ptr(stream, out.device))
     _check(st, "pa_decode_reduce")
+    return out
+
+
+def pa_multi_query(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out, *,
+                   max_seq_len, max_query_len, stream=None):
+    """Attention of several query tokens per sequence (include/pa.h
+    pa_multi_query). q, out [T, Hq, D] bf16; query_start int32 [B+1]."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", dtype=torch.bfloat16, dim=3)
+    _need(k_pool, "k_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(v_pool, "v_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(query_start, "query_start", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    T, hq, d = q.shape
+    nb, hkv, bs, d2 = k_pool.shape
+    B = seq_lens.shape[0]
+    if d2 != d or tuple(out.shape) != tuple(q.shape) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("shape mismatch")
+    if block_tables.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("batch mismatch")
+    shape = MultiQueryShape(B, hq, hkv, d, bs, nb, block_tables.shape[1], int(max_seq_len),
+                            int(max_query_len), T, PA_BF16)
+    st = lib().pa_multi_query(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                              block_tables.data_ptr(), seq_lens.data_ptr(), query_start.data_ptr(),
+                              ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
+                              _stream_ptr(stream, dev))
+    _check(st, "pa_multi_query")
     return out
 
 

@@ -190,6 +190,47 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
                                            static_cast<hipStream_t>(stream)));
 }
 
+pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* query_start, float scale, void* out,
+                           const pa_multi_query_shape_t* s, void* stream) {
+  if (!s) return PA_EINVAL;
+  if (s->num_seqs < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_blocks <= 0 ||
+      s->max_blocks_per_seq <= 0 || s->max_seq_len < 0 || s->max_query_len < 0 ||
+      s->num_tokens < 0 || s->block_size <= 0 || s->head_dim <= 0)
+    return PA_EINVAL;
+  if (s->num_q_heads % s->num_kv_heads != 0 || elem_bytes(s->dtype) == 0) return PA_EINVAL;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  if (!pa::multi_query_supported(s->dtype, s->head_dim, s->block_size, group))
+    return PA_EUNSUPPORTED;
+  if (!std::isfinite(scale)) return PA_EINVAL;
+  if (s->num_seqs == 0 || s->num_tokens == 0 || s->max_query_len == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start || !out)
+    return PA_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_EINVAL;
+  pa::MqArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start = query_start;
+  a.out = out;
+  a.qscale = scale * 1.4426950408889634f;
+  a.num_seqs = s->num_seqs;
+  a.num_q_heads = s->num_q_heads;
+  a.num_kv_heads = s->num_kv_heads;
+  a.num_blocks = s->num_blocks;
+  a.max_blocks = s->max_blocks_per_seq;
+  const int64_t table_cap = (int64_t)s->max_blocks_per_seq * s->block_size;
+  a.len_cap = (int)(table_cap < s->max_seq_len ? table_cap : s->max_seq_len);
+  a.max_query_len = s->max_query_len;
+  a.num_tokens = s->num_tokens;
+  return from_hip(pa::launch_multi_query(s->block_size, group, a,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
                                  void* k_pool, void* v_pool, int32_t num_tokens,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -60,6 +60,26 @@ struct CopyArgs {
   int32_t dst_blocks;           // blocks in the destination pools
 };
 
+// Multi-token query launch (prefill chunk / speculative tokens).
+struct MqArgs {
+  const void* q;                // [T][Hq][D]
+  const void* k_pool;           // [NB][Hkv][bs][D]
+  const void* v_pool;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* seq_lens;      // [B], query tokens included
+  const int32_t* query_start;   // [B + 1]
+  void* out;                    // [T][Hq][D]
+  float qscale;                 // softmax scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t max_blocks;
+  int32_t len_cap;              // min(max_seq_len, max_blocks * bs)
+  int32_t max_query_len;
+  int32_t num_tokens;           // T
+};
+
 // Kernel selection key for pa_decode_partition.
 struct DecodeKey {
   int dtype;       // 0 f32, 1 bf16
@@ -76,6 +96,8 @@ bool decode_partition_supported(const DecodeKey& key);
 hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
                                 hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream);
+bool multi_query_supported(int dtype, int head_dim, int block_size, int group);
+hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream);
 // Synchronises `stream`, returns the device error word and clears it.
 hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);

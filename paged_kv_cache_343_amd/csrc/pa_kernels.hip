@@ -55,6 +55,7 @@ constexpr uint32_t kErrBlockId = 0x1u;
 constexpr uint32_t kErrSeqLen = 0x2u;
 constexpr uint32_t kErrSlot = 0x4u;
 constexpr uint32_t kErrCopyPair = 0x8u;
+constexpr uint32_t kErrQuery = 0x10u;
 
 __device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_word, bit); }
 
@@ -592,9 +593,10 @@ __device__ __forceinline__ void load_kv_chunk_bs8(KVChunk& c, const char* kbase,
   for (int jj = 0; jj < 4; ++jj) c.v[jj] = ld16(vb, jj * ROW);
 }
 
-__device__ __forceinline__ int checked_id(const DecodeArgs& a, int64_t row, int logical_block) {
-  int id = a.block_tables[row + logical_block];
-  if ((unsigned)id >= (unsigned)a.num_blocks) {
+__device__ __forceinline__ int checked_id(const int32_t* tables, int32_t num_blocks, int64_t row,
+                                          int logical_block) {
+  int id = tables[row + logical_block];
+  if ((unsigned)id >= (unsigned)num_blocks) {
     flag_error(kErrBlockId);
     id = 0;
   }
@@ -615,10 +617,10 @@ __device__ __forceinline__ int2 load_id_window(const DecodeArgs& a, const Partit
   if (k < nmine) {
     const int tok = wk.tok0 + (w + k * NW) * 16;
     const int64_t row = (int64_t)wk.i * a.max_blocks;
-    id.x = checked_id(a, row, tok / BS);
+    id.x = checked_id(a.block_tables, a.num_blocks, row, tok / BS);
     id.y = id.x;
     if constexpr (BS == 8) {
-      if (tok + 8 < wk.tok1) id.y = checked_id(a, row, tok / 8 + 1);
+      if (tok + 8 < wk.tok1) id.y = checked_id(a.block_tables, a.num_blocks, row, tok / 8 + 1);
     }
   }
   return id;
@@ -856,12 +858,205 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   for (; k < a.block_chunks; k += step) d[k] = s[k];
 }
 
+
+// ---------------------------------------------------------------------------
+// Multi-token queries (prefill chunk / speculative tokens) on matrix cores
+// ---------------------------------------------------------------------------
+// Unit of work: one wave per (sequence, KV head, tile of 16 query rows); a
+// query row is a (query token, head of the group) pair, row = token * G + h,
+// so a tile holds 16 / G consecutive tokens. Positions are walked 16 at a
+// time (a "chunk"), up to the tile's last token, through the block table.
+// Lane l: R = l / 16, c = l % 16.
+//   S^T = K Q^T (v_mfma_f32_16x16x32_bf16): A = K rows of the chunk (lane:
+//     token c, dims 8R + 32s ..), B = the tile's query rows (lane: row c,
+//     same dims); lane gets S[row c][tokens 4R .. 4R+3].
+//   causal mask per row, online softmax per row (row c's 16 scores sit in
+//     lanes c, c+16, c+32, c+48: reduced with 16/32-lane swaps).
+//   O += P V (v_mfma_f32_16x16x16_bf16, 8 tiles of 16 dims): A = P exactly
+//     as the softmax leaves it (lane: row c, tokens 4R ..; split into two
+//     bf16 terms, so two products per tile), B = V[tokens
+//     4R .. 4R+3][dim 16t + c], read from the chunk's V rows staged in LDS
+//     (row-major, 272-byte rows so the four 16-lane groups hit different
+//     banks); lane gets O[rows 4R .. 4R+3][dim 16t + c].
+// Each wave owns its LDS buffers and its unit, so waves never wait for one
+// another; K/V of chunk c+1 are issued before chunk c is computed.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMqWaves = 4;
+constexpr int kMqLdsRow = 136;   // bf16 elements per staged V row (128 + 8 pad)
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return to_bf16(f); }
+
+template <int BS, int G>
+__global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
+  constexpr int D = 128, ROW = 256;
+  constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
+  static_assert(BS % 16 == 0 && 16 % G == 0, "whole chunks per block, whole tokens per tile");
+  __shared__ __align__(16) uint16_t s_v[kMqWaves][2][16][kMqLdsRow];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = lane >> 4, c = lane & 15;
+  const int i = blockIdx.z, g = blockIdx.y;
+  const int tile = blockIdx.x * kMqWaves + w;
+
+  // validate the sequence's length and query range (device-resident)
+  const int L = a.seq_lens[i];
+  const int q0 = a.query_start[i], q1 = a.query_start[i + 1];
+  const int tq = q1 - q0;
+  if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
+      tq > a.max_query_len) {
+    if (lane == 0 && g == 0 && blockIdx.x == 0) flag_error(kErrQuery);
+    return;
+  }
+  const int rows = tq * G;
+  if (tile * 16 >= rows) return;
+  const int row0 = tile * 16;
+  const int t_last = min(tq - 1, (row0 + 15) / G);
+  const int npos = L - tq + t_last + 1;          // positions the tile's last token sees
+  const int nch = (npos + 15) / 16;
+
+  // this lane's query row (column of S^T): token tc, head hc
+  const int rc = row0 + c;
+  const bool row_ok = rc < rows;
+  const int tc = rc / G, hc = rc % G;
+  const int pos_c = L - tq + tc;                 // last position row c attends to
+  bf16x8_t qop[4];
+  {
+    const int trow = row_ok ? tc : 0;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)(q0 + trow) * a.num_q_heads + g * G + hc) * D + 8 * R) * 2;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      uint4 v = row_ok ? ld16(qp, s2 * 64) : make_uint4(0, 0, 0, 0);
+      qop[s2] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  const int64_t blk_bytes = kHeadBytes * a.num_kv_heads;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + g * kHeadBytes;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * kHeadBytes;
+  const uint32_t k_off = (uint32_t)(c * ROW + R * 16);
+  const uint32_t v_off = (uint32_t)(4 * R * ROW + c * 16);
+  const int64_t trow_base = (int64_t)i * a.max_blocks;
+
+  float m = -INFINITY, lsum = 0.0f;             // softmax state of row c
+  f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int win = 0; win < nch; win += 64) {
+    const int cnt = min(64, nch - win);
+    int ids = 0;
+    if (lane < cnt) ids = checked_id(a.block_tables, a.num_blocks, trow_base, ((win + lane) * 16) / BS);
+    auto issue = [&](KVChunk& buf, int t) {
+      const int phys = __builtin_amdgcn_readlane(ids, t);
+      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, ((win + t) * 16) % BS, k_off, v_off);
+    };
+    KVChunk b0, b1;
+    auto step = [&](KVChunk& cur, int t) {
+      const int chunk = win + t;
+      const int tok0 = chunk * 16;
+      // stage V rows of this chunk (tokens 4R + jj, dims 8c ..) in LDS; rows
+      // past the tile's last position are zeros, so that slack slots (which
+      // may hold anything, NaN included) never meet the zero weights
+      uint16_t(*sv)[kMqLdsRow] = s_v[w][chunk & 1];
+      const bool tail = tok0 + 16 > npos;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        uint4 v = cur.v[jj];
+        if (tail && tok0 + 4 * R + jj >= npos) v = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&sv[4 * R + jj][8 * c]) = v;
+      }
+      // S^T for the chunk
+      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s2]),
+                                                     qop[s2], sc, 0, 0, 0);
+      float sv4[4];
+      bool ok[4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv4[r] = sc[r] * a.qscale;
+        ok[r] = row_ok && (tok0 + 4 * R + r <= pos_c);
+        bm = ok[r] ? fmaxf(bm, sv4[r]) : bm;
+      }
+      bm = fmaxf(bm, xor_lanes<16>(bm));
+      bm = fmaxf(bm, xor_lanes<32>(bm));
+      const float mn = fmaxf(m, bm);
+      const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
+      m = mn;
+      float p[4], ps = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = ok[r] ? exp2_fast(sv4[r] - mn) : 0.0f;
+        ps += p[r];
+      }
+      ps += xor_lanes<16>(ps);
+      ps += xor_lanes<32>(ps);
+      lsum = lsum * alpha + ps;
+      // rescale output rows 4R + r by their rows' alpha (held by lane 4R + r)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * R + r);
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) acc[t2][r] *= ar;
+      }
+      // P enters the matrix cores as two bf16 terms, p = hi + lo (lo = the
+      // bf16 rounding of p - hi), so the weights keep ~16 significant bits
+      // instead of bf16's 8
+      s16x4_t p_hi, p_lo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint16_t hb = bf16_bits(p[r]);
+        p_hi[r] = (short)hb;
+        p_lo[r] = (short)bf16_bits(p[r] - __uint_as_float((uint32_t)hb << 16));
+      }
+      __builtin_amdgcn_wave_barrier();   // LDS rows above are complete (in-order per wave)
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) {
+        s16x4_t vb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vb[j] = (short)sv[4 * R + j][16 * t2 + c];
+        acc[t2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, vb, acc[t2], 0, 0, 0);
+        acc[t2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, vb, acc[t2], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+    issue(b0, 0);
+    for (int t = 0;;) {
+      issue(b1, t + 1 < cnt ? t + 1 : t);
+      step(b0, t);
+      if (++t >= cnt) break;
+      issue(b0, t + 1 < cnt ? t + 1 : t);
+      step(b1, t);
+      if (++t >= cnt) break;
+    }
+  }
+  // out[row] = O[row] / l[row]; lane holds rows 4R + r, dims 16 t + c
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float lr = __shfl(lsum, 4 * R + r);
+    const int row = row0 + 4 * R + r;
+    if (row >= rows) continue;
+    const int t = row / G, h = row % G;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                    ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + c;
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+#pragma unroll
+    for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[t2][r] * inv);
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 using PartitionKernel = void (*)(DecodeArgs);
+using PartitionKernelMq = void (*)(MqArgs);
 
 template <typename T, int D, int BS>
 static PartitionKernel pick_valu(int group) {
@@ -960,6 +1155,44 @@ hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream) {
   if (gy > 1024) gy = 1024;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)args.num_pairs, (unsigned)gy, 2),
                      dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+bool multi_query_supported(int dtype, int head_dim, int block_size, int group) {
+  return dtype == 1 && head_dim == 128 && (block_size == 16 || block_size == 32 ||
+                                           block_size == 64 || block_size == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+template <int BS>
+static PartitionKernelMq pick_mq(int group) {
+  switch (group) {
+    case 1: return multi_query_mfma<BS, 1>;
+    case 2: return multi_query_mfma<BS, 2>;
+    case 4: return multi_query_mfma<BS, 4>;
+    case 8: return multi_query_mfma<BS, 8>;
+    case 16: return multi_query_mfma<BS, 16>;
+    default: return nullptr;
+  }
+}
+
+hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream) {
+  PartitionKernelMq kern = nullptr;
+  switch (block_size) {
+    case 16: kern = pick_mq<16>(group); break;
+    case 32: kern = pick_mq<32>(group); break;
+    case 64: kern = pick_mq<64>(group); break;
+    case 128: kern = pick_mq<128>(group); break;
+    default: break;
+  }
+  if (!kern) return hipErrorInvalidValue;
+  const int64_t tiles = ((int64_t)args.max_query_len * group + 15) / 16;
+  const int64_t gx = (tiles + kMqWaves - 1) / kMqWaves;
+  if (gx <= 0 || args.num_seqs <= 0) return hipSuccess;
+  if (gx > 0x7fffffff || args.num_kv_heads > 65535 || args.num_seqs > 65535)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)args.num_kv_heads, (unsigned)args.num_seqs),
+                     dim3(kMqWaves * 64), 0, stream, args);
   return hipGetLastError();
 }
 
