@@ -23,7 +23,10 @@ converted exactly from their fp32 or bf16 bits):
   every position up to and including its own;
 * the slot write of new K/V rows and the whole-block copy, bit for bit;
 * swapping: a second (host) pool with its own free list, a sequence's blocks
-  moved out to it and back, and the block moves between the two pools.
+  moved out to it and back, and the block moves between the two pools;
+* an 8-bit KV pool: the OCP FP8 E4M3 code of every value, the slot write that
+  scales and rounds new rows into codes, and the dequantized pools that the
+  ordinary decode then reads.
 
 Sources (page title, then the section used):
   [Vij]  "PagedAttention Explained: KV Blocks, Allocation, and Sharing"
@@ -70,7 +73,8 @@ __all__ = [
     "as_f64", "positions_to_rows", "kv_head_of",
     "decode", "decode_one", "partition_partials", "combine_partials",
     "decode_partitioned", "reshape_and_cache", "copy_blocks", "swap_blocks",
-    "multi_query",
+    "multi_query", "E4M3_MAX", "e4m3_value", "e4m3_values", "e4m3_encode",
+    "reshape_and_cache_e4m3", "dequantize_e4m3",
 ]
 
 
@@ -518,3 +522,79 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
     for src, dst in np.asarray(pairs).reshape(-1, 2).tolist():
         dst_k[dst] = src_k[src]
         dst_v[dst] = src_v[src]
+
+
+# --------------------------------------------------------------------------
+# 8-bit KV pool (FP8 E4M3, OCP definition)
+# --------------------------------------------------------------------------
+# [ZQ] summary: paged attention composes with KV quantization; the pages give
+# no scheme. Reading taken: OCP FP8 E4M3 ("fn": no infinities, S.1111.111 is
+# NaN, largest finite 448), one scale per pool (K and V), a value x stored as
+# the code nearest to x / scale (ties to the even code), saturating to +-448;
+# the code's value times the scale is what attention reads.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 code: sign, 4-bit exponent (bias 7), 3-bit
+    mantissa; exponent 0 holds the subnormals m * 2^-9; S.1111.111 is NaN."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_values(codes) -> np.ndarray:
+    """Float64 values of an array of codes (uint8)."""
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest FP8 E4M3 code to each float32 value of x (ties to the code with
+    an even mantissa), saturating at +-448; NaN gives 0x7F with the input's
+    sign. Written as a search over the 127 non-negative finite codes."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    mags = np.array([e4m3_value(c) for c in range(0x7F)])        # codes 0x00..0x7E, ascending
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)  # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    code = np.where(np.isnan(x), np.where(np.signbit(x), 0xFF, 0x7F), code).astype(np.uint8)
+    return code
+
+
+def quantize_e4m3(x, scale: float) -> np.ndarray:
+    """Codes of x / scale: x (float32 values, e.g. from bf16) times the
+    float32 reciprocal of the float32 scale, the product rounded to float32,
+    then e4m3_encode."""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = (np.asarray(x, dtype=np.float32) * inv).astype(np.float32)
+    return e4m3_encode(y)
+
+
+def reshape_and_cache_e4m3(k_new, v_new, slot_mapping, k_codes, v_codes, k_scale, v_scale):
+    """The slot write into 8-bit pools: token t's K and V rows (float32
+    values) are quantized with their pool's scale and stored at slot
+    slot_mapping[t] = block * bs + offset; slot < 0 writes nothing."""
+    bs = k_codes.shape[2]
+    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
+        if slot < 0:
+            continue
+        b, o = slot // bs, slot % bs
+        k_codes[b, :, o, :] = quantize_e4m3(k_new[t], k_scale)
+        v_codes[b, :, o, :] = quantize_e4m3(v_new[t], v_scale)
+
+
+def dequantize_e4m3(codes, scale: float) -> np.ndarray:
+    """What attention reads from an 8-bit pool: code value times the scale
+    (float64; the scale is taken as its float32 value)."""
+    return e4m3_values(codes) * float(np.float32(scale))
