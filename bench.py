@@ -80,6 +80,9 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--block-size", type=int, default=None,
                     help="override the workload's block size (tokens per block)")
+    ap.add_argument("--kv-dtype", default="native", choices=["native", "e4m3"],
+                    help="KV pool storage: the workload's dtype, or FP8 E4M3 codes with one "
+                         "scale per pool (q and out stay bf16)")
     ap.add_argument("--block-order", default="shuffled", choices=["shuffled", "identity"],
                     help="free-list order: a seeded permutation (scattered blocks, the "
                          "default) or 0, 1, 2, ... (each sequence's blocks contiguous)")
@@ -123,6 +126,12 @@ def main() -> int:
     nsteps = args.warmup + args.steps
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     eb = 2 if w.dtype == "bf16" else 4
+    fp8 = args.kv_dtype == "e4m3"
+    if fp8 and (w.dtype != "bf16" or d != 128):
+        print("8-bit pools need a bf16 workload with head dim 128", file=sys.stderr)
+        return 1
+    pool_eb = 1 if fp8 else eb          # bytes per stored K/V element
+    k_scale = v_scale = 0.05            # 8-bit pools: scale per pool
 
     # ---- inputs (seeded, synthetic) ------------------------------------
     rng = np.random.default_rng(w.seed)
@@ -135,8 +144,13 @@ def main() -> int:
         order = np.arange(nb, dtype=np.int32)
     maxb = int(-(-int(final.max()) // bs))
     max_len = int(final.max())
-    k_pool = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 1, w.dtype, dev)
-    v_pool = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 2, w.dtype, dev)
+    if fp8:
+        k_pool = W.random_e4m3_codes_device((nb, hkv, bs, d), w.seed * 1000 + 1, dev)
+        v_pool = W.random_e4m3_codes_device((nb, hkv, bs, d), w.seed * 1000 + 2, dev)
+        args.no_cpu_baseline = True      # the CPU baseline leg times the native pools
+    else:
+        k_pool = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 1, w.dtype, dev)
+        v_pool = W.normal_device((nb, hkv, bs, d), w.seed * 1000 + 2, w.dtype, dev)
     q_all = W.normal_device((nsteps, B, hq, d), w.seed * 1000 + 3, w.dtype, dev)
     kn_all = W.normal_device((nsteps, B, hkv, d), w.seed * 1000 + 4, w.dtype, dev)
     vn_all = W.normal_device((nsteps, B, hkv, d), w.seed * 1000 + 5, w.dtype, dev)
@@ -212,12 +226,13 @@ def main() -> int:
         if st != 0:
             raise P.PaError(st, "pa_bm_export")
         bm_s[0] += time.perf_counter() - t_bm
-        step_bytes.append(int(lens_np[b].sum(dtype=np.int64)) * 2 * hkv * d * eb)
+        step_bytes.append(int(lens_np[b].sum(dtype=np.int64)) * 2 * hkv * d * pool_eb)
 
     # Raw C-ABI calls with pointers resolved once: the step's host cost stays
     # far below its GPU time, so the GPU never waits for the host.
     L = P.lib()
     c_scale = ctypes.c_float(scale)
+    c_kscale, c_vscale = ctypes.c_float(k_scale), ctypes.c_float(v_scale)
     shape_ref = ctypes.byref(shape)
     ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     kp_ptr, vp_ptr, out_ptr = k_pool.data_ptr(), v_pool.data_ptr(), out.data_ptr()
@@ -258,14 +273,25 @@ def main() -> int:
         evs = time_ev[s - args.warmup] if timed else None
         if timed:
             evs[0].record(compute)
-        check(L.pa_reshape_and_cache(kn_all[s].data_ptr(), vn_all[s].data_ptr(), db["slots"],
-                                     kp_ptr, vp_ptr, B, hkv, d, bs, nb, dt_code, cs),
-              "pa_reshape_and_cache")
+        if fp8:
+            check(L.pa_reshape_and_cache_e4m3(kn_all[s].data_ptr(), vn_all[s].data_ptr(),
+                                              db["slots"], kp_ptr, vp_ptr, B, hkv, d, bs, nb,
+                                              c_kscale, c_vscale, cs), "pa_reshape_and_cache_e4m3")
+        else:
+            check(L.pa_reshape_and_cache(kn_all[s].data_ptr(), vn_all[s].data_ptr(), db["slots"],
+                                         kp_ptr, vp_ptr, B, hkv, d, bs, nb, dt_code, cs),
+                  "pa_reshape_and_cache")
         if timed:
             evs[1].record(compute)
-        check(L.pa_decode_partition(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"], db["lens"],
-                                    c_scale, out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
-              "pa_decode_partition")
+        if fp8:
+            check(L.pa_decode_partition_e4m3(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
+                                             db["lens"], c_scale, c_kscale, c_vscale, out_ptr,
+                                             shape_ref, ws_ptr, ws_bytes, cs),
+                  "pa_decode_partition_e4m3")
+        else:
+            check(L.pa_decode_partition(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
+                                        db["lens"], c_scale, out_ptr, shape_ref, ws_ptr, ws_bytes,
+                                        cs), "pa_decode_partition")
         if timed:
             evs[2].record(compute)
         check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
@@ -324,13 +350,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": w.dtype if not fp8 else "bf16 q/out, e4m3 K/V",
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": B, "num_q_heads": hq, "num_kv_heads": hkv,
                    "head_dim": d, "block_size": bs, "partition_tokens": ptok,
                    "context_tokens": (f"U{{{w.lengths[1]}..{w.lengths[2]}}}+step"
                                       if w.lengths[0] == "uniform" else f"{w.lengths}+step"),
                    "kernel": vname, "block_order": args.block_order,
+                   "kv_storage": "e4m3" if fp8 else w.dtype,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(B * K / wall, 1),
@@ -339,14 +366,14 @@ def main() -> int:
                        "reshape_and_cache": round(1e3 * float(np.mean(cache_ms)), 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(vname),
-                     "kernel": "decode_partition_" + vname,
+                     "traffic": None if fp8 else recorded_traffic(vname),
+                     "kernel": "decode_partition_" + vname + ("_e4m3" if fp8 else ""),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
     }
-    avg_len = total_bytes / K / (2 * hkv * d * eb) / B
+    avg_len = total_bytes / K / (2 * hkv * d * pool_eb) / B
     parts = float(np.mean([-(-int(x) // ptok) for x in stage[0]["lens"].numpy()])) if ptok > 0 else 1.0
     red_bytes = B * hq * (parts * (d * 4) + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
-    cache_bytes = 2 * B * 2 * hkv * d * eb
+    cache_bytes = B * 2 * hkv * d * (eb + pool_eb)
     result["rows"] = {
         "a1_block_manager_host_us": round(1e6 * bm_s[0] / K, 1),
         "a2_reshape_and_cache": {"us": round(1e3 * float(np.mean(cache_ms)), 2),

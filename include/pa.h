@@ -131,6 +131,31 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
                                 float scale, void* out, const pa_decode_shape_t* shape,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * 8-bit KV pools (FP8 E4M3). [ZQ] summary: paged attention composes with KV
+ * quantization; the pages give no scheme, so this one is a reading: OCP FP8
+ * E4M3 codes ("fn": no infinities, S.1111.111 = NaN, largest finite 448),
+ * one positive float32 scale per pool; attention reads code value * scale.
+ * Pools are [num_blocks][Hkv][bs][D] bytes; q and out stay bf16.
+ *
+ * pa_decode_e4m3 — pa_decode over 8-bit pools: s_p = scale * k_scale *
+ * dot(q, code_K) and out = v_scale * sum_p softmax(s)_p code_V. shape->dtype
+ * must be PA_BF16 (q, out), head_dim 128, group 1, 2 or 4, block size 16,
+ * 32, 64 or 128; the matrix-core kernel runs whatever shape->variant says
+ * (PA_VARIANT_VALU gives PA_EUNSUPPORTED). Workspace as pa_decode; the
+ * second half is pa_decode_reduce unchanged.
+ */
+pa_status_t pa_decode_e4m3(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                           float k_scale, float v_scale, void* out,
+                           const pa_decode_shape_t* shape, void* workspace,
+                           size_t workspace_bytes, void* stream);
+pa_status_t pa_decode_partition_e4m3(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_tables, const int32_t* seq_lens,
+                                     float scale, float k_scale, float v_scale, void* out,
+                                     const pa_decode_shape_t* shape, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Second half of pa_decode: for every sequence with more than one partition,
  * out[i][h] = sum_j w_j o_j / sum_j w_j with w_j = l_j * exp(m_j - max_j m_j),
  * read from the workspace pa_decode_partition filled. */
@@ -201,6 +226,21 @@ pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* sl
                                  void* k_pool, void* v_pool, int32_t num_tokens,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                  int32_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * pa_reshape_and_cache_e4m3 — the slot write into 8-bit pools. For t with
+ * slot_mapping[t] >= 0 and every head h and dim d:
+ *     k_pool[slot / bs][h][slot % bs][d] = E4M3(k[t][h][d] * (1 / k_scale))
+ * (and v with v_scale), where 1 / k_scale and the product are rounded to
+ * float32 and E4M3 picks the nearest code (ties to the even mantissa),
+ * saturating at +-448, NaN to 0x7F. k, v [dev] bf16 [num_tokens][Hkv][D];
+ * head_dim a multiple of 16; scales finite and positive.
+ */
+pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
+                                      void* k_pool, void* v_pool, int32_t num_tokens,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, float k_scale, float v_scale,
+                                      void* stream);
 
 /*
  * pa_copy_blocks — copy-on-write duplication of whole physical blocks.

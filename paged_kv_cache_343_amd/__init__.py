@@ -20,6 +20,7 @@ import numpy as np
 __all__ = [
     "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16", "PA_DEVERR_BLOCK_ID", "PA_DEVERR_SEQ_LEN",
     "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "MultiQueryShape", "pa_multi_query",
+    "pa_decode_e4m3", "pa_reshape_and_cache_e4m3",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
@@ -40,7 +41,8 @@ _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
 EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
-    "pa_status_str", "pa_multi_query",
+    "pa_status_str", "pa_multi_query", "pa_decode_e4m3", "pa_decode_partition_e4m3",
+    "pa_reshape_and_cache_e4m3",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
     "pa_bm_set_swap_space", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_num_free_swap",
@@ -81,6 +83,13 @@ _SIGS = {
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp]),
     "pa_multi_query": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                               ctypes.POINTER(MultiQueryShape), _vp]),
+    "pa_decode_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
+                              ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+    "pa_decode_partition_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp,
+                                        _sz, _vp]),
+    "pa_reshape_and_cache_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.c_float, ctypes.c_float, _vp]),
     "pa_device_errors": (_i32, [ctypes.POINTER(ctypes.c_uint32), _vp]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
     "pa_bm_create": (_i32, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
@@ -229,6 +238,53 @@ def pa_decode_reduce(q, k_pool, block_tables, seq_lens, out, *, max_seq_len, par
                                 workspace.data_ptr(), ws_bytes, _stream_ptr(stream, out.device))
     _check(st, "pa_decode_reduce")
     return out
+
+
+def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_scale, out, *,
+                   max_seq_len, partition_tokens=0, workspace=None, stream=None):
+    """pa_decode over 8-bit pools (include/pa.h pa_decode_e4m3): q, out bf16
+    [B,Hq,D]; pools uint8 [NB,Hkv,bs,D] of FP8 E4M3 codes."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", dtype=torch.bfloat16, dim=3)
+    _need(k_pool, "k_pool", dtype=torch.uint8, dim=4, device=dev)
+    _need(v_pool, "v_pool", dtype=torch.uint8, dim=4, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, PA_VARIANT_MFMA)
+    need = pa_decode_workspace_bytes(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib().pa_decode_e4m3(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                              block_tables.data_ptr(), seq_lens.data_ptr(), ctypes.c_float(scale),
+                              ctypes.c_float(k_scale), ctypes.c_float(v_scale), out.data_ptr(),
+                              ctypes.byref(shape), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    _check(st, "pa_decode_e4m3")
+    return out
+
+
+def pa_reshape_and_cache_e4m3(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale, stream=None):
+    """Quantized slot write: k/v bf16 [T,Hkv,D] into uint8 pools of FP8 E4M3 codes."""
+    torch = _torch()
+    dev = k_pool.device
+    _need(k, "k", dtype=torch.bfloat16, dim=3, device=dev)
+    _need(v, "v", dtype=torch.bfloat16, dim=3, device=dev)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, dim=1, device=dev)
+    _need(k_pool, "k_pool", dtype=torch.uint8, dim=4)
+    _need(v_pool, "v_pool", dtype=torch.uint8, device=dev)
+    nb, hkv, bs, d = k_pool.shape
+    T = k.shape[0]
+    if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d) or slot_mapping.shape[0] != T:
+        raise ValueError("shape mismatch")
+    st = lib().pa_reshape_and_cache_e4m3(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                         k_pool.data_ptr(), v_pool.data_ptr(), T, hkv, d, bs, nb,
+                                         ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                                         _stream_ptr(stream, dev))
+    _check(st, "pa_reshape_and_cache_e4m3")
 
 
 def pa_multi_query(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out, *,

@@ -37,7 +37,7 @@ int auto_variant(const pa_decode_shape_t& s, int group) {
   return PA_VARIANT_VALU;
 }
 
-pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan) {
+pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = false) {
   if (!s) return PA_EINVAL;
   if (s->num_seqs < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_blocks <= 0 ||
       s->max_blocks_per_seq <= 0 || s->max_seq_len < 0 || s->block_size <= 0 ||
@@ -66,7 +66,7 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan) {
   plan->group = group;
   int variant = s->variant == PA_VARIANT_AUTO ? auto_variant(*s, group) : s->variant;
   if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
-  plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant};
+  plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant, kv_fp8};
   if (!pa::decode_partition_supported(plan->key)) return PA_EUNSUPPORTED;
   if (group * 2 > pa::kMlRecord) return PA_EUNSUPPORTED;
   const size_t rows = (size_t)s->num_seqs * s->num_q_heads * plan->max_parts;
@@ -101,6 +101,7 @@ pa_status_t fill_args(const void* q, const void* k_pool, const void* v_pool,
   a->part_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes)
                        : nullptr;
   a->qscale = scale * 1.4426950408889634f;  // log2(e): scores kept in log2 units
+  a->out_scale = 1.0f;
   a->num_seqs = s->num_seqs;
   a->num_q_heads = s->num_q_heads;
   a->num_kv_heads = s->num_kv_heads;
@@ -129,14 +130,30 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
                                const int32_t* block_tables, const int32_t* seq_lens, float scale,
                                void* out, const pa_decode_shape_t* shape, void* workspace,
                                size_t workspace_bytes, void* stream, bool do_partition,
-                               bool do_reduce) {
+                               bool do_reduce, const float* fp8_scales = nullptr) {
   Plan plan;
-  pa_status_t st = make_plan(shape, &plan);
+  if (fp8_scales && shape &&
+      (shape->dtype != PA_BF16 || shape->variant == PA_VARIANT_VALU))
+    return PA_EUNSUPPORTED;
+  pa_decode_shape_t s8{};
+  if (fp8_scales) {           // the 8-bit kernel is a matrix-core variant
+    s8 = *shape;
+    s8.variant = PA_VARIANT_MFMA;
+    shape = &s8;
+  }
+  pa_status_t st = make_plan(shape, &plan, fp8_scales != nullptr);
   if (st != PA_OK) return st;
   pa::DecodeArgs a{};
   st = fill_args(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, plan, workspace,
                  workspace_bytes, &a);
   if (st != PA_OK) return st;
+  if (fp8_scales) {
+    if (!std::isfinite(fp8_scales[0]) || !std::isfinite(fp8_scales[1]) || fp8_scales[0] <= 0.0f ||
+        fp8_scales[1] <= 0.0f)
+      return PA_EINVAL;
+    a.qscale *= fp8_scales[0];
+    a.out_scale = fp8_scales[1];
+  }
   if (shape->num_seqs == 0) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_partition) {
@@ -161,6 +178,26 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
                                 void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
                      workspace_bytes, stream, true, false);
+}
+
+pa_status_t pa_decode_e4m3(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                           float k_scale, float v_scale, void* out,
+                           const pa_decode_shape_t* shape, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const float sc[2] = {k_scale, v_scale};
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, true, sc);
+}
+
+pa_status_t pa_decode_partition_e4m3(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_tables, const int32_t* seq_lens,
+                                     float scale, float k_scale, float v_scale, void* out,
+                                     const pa_decode_shape_t* shape, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const float sc[2] = {k_scale, v_scale};
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, false, sc);
 }
 
 pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode_shape_t* shape,
@@ -279,6 +316,36 @@ static pa_status_t copy_impl(const void* src_k, const void* src_v, void* dst_k, 
   a.src_blocks = src_blocks;
   a.dst_blocks = dst_blocks;
   return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
+                                      void* k_pool, void* v_pool, int32_t num_tokens,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, float k_scale, float v_scale,
+                                      void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 16 != 0 ||
+      block_size <= 0 || num_blocks <= 0)
+    return PA_EINVAL;
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.0f || v_scale <= 0.0f)
+    return PA_EINVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PA_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PA_EINVAL;
+  pa::CacheArgs8 a{};
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_slots = (int64_t)num_blocks * block_size;
+  a.k_inv = 1.0f / k_scale;
+  a.v_inv = 1.0f / v_scale;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.row_groups = head_dim / 8;
+  a.block_size = block_size;
+  return from_hip(pa::launch_reshape_and_cache_e4m3(a, static_cast<hipStream_t>(stream)));
 }
 
 pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,

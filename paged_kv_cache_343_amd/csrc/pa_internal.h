@@ -21,7 +21,8 @@ struct DecodeArgs {
   float* part_ml;               // [B][Hkv][max_parts][kMlRecord]: per query head of the
                                 //   group, max score (log2 units) then exp-sum; rest 0
   float* part_o;                // [B][Hq][max_parts][D]: normalised partial output
-  float qscale;                 // softmax scale * log2(e)
+  float qscale;                 // softmax scale * log2(e) (* k_scale for 8-bit pools)
+  float out_scale;              // v_scale for 8-bit pools
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -43,6 +44,22 @@ struct CacheArgs {
   int32_t num_tokens;
   int32_t num_kv_heads;
   int32_t row_chunks;           // 16-byte chunks per (token, head) row = D * elem / 16
+  int32_t block_size;
+};
+
+// Slot write into FP8 E4M3 pools from bf16 rows.
+struct CacheArgs8 {
+  const void* k;                // [T][Hkv][D] bf16
+  const void* v;
+  const int64_t* slots;         // [T]
+  void* k_pool;                 // [NB][Hkv][bs][D] codes
+  void* v_pool;
+  int64_t num_slots;            // num_blocks * block_size
+  float k_inv;                  // float32 1 / k_scale
+  float v_inv;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t row_groups;           // 8-element groups per row = D / 8
   int32_t block_size;
 };
 
@@ -87,6 +104,7 @@ struct DecodeKey {
   int block_size;  // 16, 32
   int group;       // 1, 2, 4, 8
   int variant;     // 1 VALU, 2 MFMA
+  bool kv_fp8;     // pools hold FP8 E4M3 codes (q, out bf16)
 };
 
 // Returns hipErrorInvalidValue (and launches nothing) if `key` has no kernel.
@@ -96,6 +114,7 @@ bool decode_partition_supported(const DecodeKey& key);
 hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
                                 hipStream_t stream);
 hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream);
+hipError_t launch_reshape_and_cache_e4m3(const CacheArgs8& args, hipStream_t stream);
 bool multi_query_supported(int dtype, int head_dim, int block_size, int group);
 hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream);

@@ -261,7 +261,7 @@ __device__ __forceinline__ float row_partner(float x) {
 template <typename T, int D, int G, int NW, int LPR, int EPL>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const PartitionWork& wk,
                                                  float (&m)[G], float (&l)[G],
-                                                 float (&acc)[G][EPL]) {
+                                                 float (&acc)[G][EPL], float out_scale = 1.0f) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane % LPR;
   // rows of one wave: butterfly over the lane bits above the row
   auto merge_rows = [&](auto off_tag) {
@@ -317,7 +317,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
       o[2] += f * sa.z;
       o[3] += f * sa.w;
     }
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    const float inv = lsum > 0.0f ? out_scale / lsum : 0.0f;
     const int64_t row = (int64_t)wk.i * a.num_q_heads + wk.g * G + h;
     if (wk.nparts == 1) {
       store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
@@ -525,9 +525,50 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_valu(DecodeArgs a) {
 // issued before the current chunk is computed (two register buffers); the
 // last chunk "prefetches" itself again, a cache hit that keeps the load
 // count per iteration constant.
-struct KVChunk {
+// One 16-token chunk of K and V rows in registers, with the operand views
+// the matrix-core kernel needs: kop(s) = the bf16x8 A operand of q.K step s,
+// vrow(jj, f) = the 8 V values of the lane's jj-th row as floats.
+struct KVChunk {                       // bf16 pools
   uint4 k[4];
   uint4 v[4];
+  __device__ __forceinline__ bf16x8_t kop(int s) const { return __builtin_bit_cast(bf16x8_t, k[s]); }
+  __device__ __forceinline__ void vrow(int jj, float (&f)[8]) const {
+    Elem<uint16_t>::unpack(v[jj], f);
+  }
+};
+
+// Two FP8 E4M3 codes (bytes 0-1, or 2-3 with HI) of a word as a bf16 pair.
+// The hardware conversion is exact (an E4M3 value has 4 significant bits),
+// so is dropping the float's low half.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f[1]) & 0xffff0000u) | (__float_as_uint(f[0]) >> 16);
+}
+
+template <bool HI>
+__device__ __forceinline__ void e4m3x2_to_f32(uint32_t w, float& a, float& b) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  a = f[0];
+  b = f[1];
+}
+
+struct KVChunk8 {                      // FP8 E4M3 pools: 128-byte rows
+  uint4 k[2];                          // dims 16R + 64 h .. +16 for h = 0, 1
+  uint2 v[4];                          // dims 8c .. 8c + 7 of rows 4R + jj
+  __device__ __forceinline__ bf16x8_t kop(int s) const {
+    const uint4& w = k[s >> 1];
+    const uint32_t lo = (s & 1) ? w.z : w.x, hi = (s & 1) ? w.w : w.y;
+    const uint4 r = make_uint4(e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
+                               e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi));
+    return __builtin_bit_cast(bf16x8_t, r);
+  }
+  __device__ __forceinline__ void vrow(int jj, float (&f)[8]) const {
+    e4m3x2_to_f32<false>(v[jj].x, f[0], f[1]);
+    e4m3x2_to_f32<true>(v[jj].x, f[2], f[3]);
+    e4m3x2_to_f32<false>(v[jj].y, f[4], f[5]);
+    e4m3x2_to_f32<true>(v[jj].y, f[6], f[7]);
+  }
 };
 
 // Occupancy floor of the MFMA partition kernel (waves per SIMD; 0 = the
@@ -557,6 +598,29 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, PA_KV_LOAD_AUX);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, PA_KV_LOAD_AUX);
+  return make_uint2(v.x, v.y);
+}
+
+// FP8 pools: K rows as two 16-byte loads per lane (dims 16R + 64h), V rows
+// as four 8-byte loads (dims 8c of rows 4R + jj); 2 KiB per chunk and pool.
+template <int BS>
+__device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, const char* vbase,
+                                              int64_t blk_bytes, int phys, int tok_in_blk,
+                                              uint32_t k_off, uint32_t v_off) {
+  constexpr int ROW = 128;
+  const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, 16 * ROW);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, 16 * ROW);
+  c.k[0] = buf_ld16(kr, k_off, 0);
+  c.k[1] = buf_ld16(kr, k_off, 64);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld8(vr, v_off, jj * ROW);
 }
 
 // K and V rows of the 16-token chunk that starts at row `tok_in_blk` of
@@ -626,15 +690,14 @@ __device__ __forceinline__ int2 load_id_window(const DecodeArgs& a, const Partit
   return id;
 }
 
-template <int G>
-__device__ __forceinline__ void mfma_chunk(const KVChunk& c, const bf16x8_t (&qop)[4],
+template <int G, typename CH>
+__device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4],
                                            float qscale, int tokc, int tok1, int R, float& m,
                                            float& lsum, float (&acc)[G][8]) {
   f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, c.k[s]), qop[s], sc,
-                                                 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.kop(s), qop[s], sc, 0, 0, 0);
   const bool full = tokc + 16 <= tok1;
   float sv[4];
   bool ok[4];
@@ -667,7 +730,7 @@ __device__ __forceinline__ void mfma_chunk(const KVChunk& c, const bf16x8_t (&qo
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float vf[8];
-    Elem<uint16_t>::unpack(c.v[jj], vf);
+    c.vrow(jj, vf);
     if (!full) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) vf[e] = ok[jj] ? vf[e] : 0.0f;
@@ -679,12 +742,16 @@ __device__ __forceinline__ void mfma_chunk(const KVChunk& c, const bf16x8_t (&qo
   }
 }
 
-template <int BS, int G, int NW>
+// F8: the pools hold FP8 E4M3 codes (q and out stay bf16); scores use
+// qscale = scale * log2(e) * k_scale and outputs are multiplied by v_scale.
+template <int BS, int G, int NW, bool F8>
 __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   constexpr int D = 128;
-  constexpr int ROW = D * 2;                      // bytes per token row
+  constexpr int ROW = F8 ? D : D * 2;             // bytes per token row
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS == 8 || BS % 16 == 0, "block must hold whole 16-token chunks, or half of one");
+  static_assert(!F8 || BS != 8, "8-bit pools take blocks of 16 tokens or more");
+  using Chunk = typename std::conditional<F8, KVChunk8, KVChunk>::type;
 
   PartitionWork wk;
   if (!setup_partition<uint16_t, D, BS, G, NW>(a, wk)) return;
@@ -700,10 +767,16 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
     const char* qp = reinterpret_cast<const char*>(a.q) +
                      (((int64_t)wk.i * a.num_q_heads + wk.g * G + (lane % G)) * D + 8 * R) * 2;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8_t, ld16(qp, s * 64));
+    for (int s = 0; s < 4; ++s) {
+      // q.K step s covers dims 8R + 32s (bf16 pools) or 16R + 64(s/2) +
+      // 8(s%2) (8-bit pools: the dims of a lane's two 16-byte K loads)
+      const uint32_t off = F8 ? (uint32_t)(16 * R + 64 * (s >> 1) + 8 * (s & 1)) * 2 - 16 * R
+                              : (uint32_t)s * 64;
+      qop[s] = __builtin_bit_cast(bf16x8_t, ld16(qp, off));
+    }
   }
-  const uint32_t k_off = (uint32_t)(c * ROW + R * 16);       // + s * 64
-  const uint32_t v_off = (uint32_t)(4 * R * ROW + c * 16);   // + jj * ROW
+  const uint32_t k_off = (uint32_t)(c * ROW + R * 16);       // + s * 64 (bf16), + h * 64 (8-bit)
+  const uint32_t v_off = (uint32_t)(4 * R * ROW + c * (F8 ? 8 : 16));   // + jj * ROW
 
   float m = -INFINITY, lsum = 0.0f;  // stream of row R, head lane % G
   float acc[G][8];
@@ -721,7 +794,7 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   for (int win = 0; win < nmine; win += 64) {
     const int2 ids = load_id_window<BS, NW>(a, wk, w, win, nmine);
     const int cnt = min(64, nmine - win);
-    auto issue = [&](KVChunk& buf, int t) {
+    auto issue = [&](Chunk& buf, int t) {
       const int phys = __builtin_amdgcn_readlane(ids.x, t);
       if constexpr (BS == 8) {
         load_kv_chunk_bs8(buf, kbase, vbase, blk_bytes, phys, __builtin_amdgcn_readlane(ids.y, t));
@@ -730,7 +803,7 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
                           v_off);
       }
     };
-    KVChunk b0, b1;
+    Chunk b0, b1;
     issue(b0, 0);
     for (int t = 0;;) {
       issue(b1, t + 1 < cnt ? t + 1 : t);
@@ -744,7 +817,7 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   float mh[G], lh[G];
   quad_spread<G>(m, mh);
   quad_spread<G>(lsum, lh);
-  finish_partition<uint16_t, D, G, NW, 16, 8>(a, wk, mh, lh, acc);
+  finish_partition<uint16_t, D, G, NW, 16, 8>(a, wk, mh, lh, acc, F8 ? a.out_scale : 1.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -831,6 +904,53 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
   const int64_t src = idx;  // [T][Hkv][row_chunks] is exactly the thread order
   reinterpret_cast<uint4*>(a.k_pool)[dst] = reinterpret_cast<const uint4*>(a.k)[src];
   reinterpret_cast<uint4*>(a.v_pool)[dst] = reinterpret_cast<const uint4*>(a.v)[src];
+}
+
+// FP8 E4M3 code of y: nearest code, ties to the even mantissa, saturating at
+// +-448, NaN to 0x7F (with y's sign). Normal range: the float's mantissa is
+// rounded to 3 bits on its bit pattern (carry into the exponent included)
+// and the exponent rebased from 127 to 7; below 2^-6 the code is the
+// subnormal count round(|y| * 2^9).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a != a) return 0x7fu | sign;
+  if (a >= 448.0f) return 0x7eu | sign;
+  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f) | sign;
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
+  return ((r >> 20) - (120u << 3)) | sign;
+}
+
+// One thread per 8 elements of a (token, head) row, K and V together: 16
+// bytes of bf16 in, 8 bytes of codes out. x * inv is rounded to float32
+// before the code is chosen.
+__global__ __launch_bounds__(256) void reshape_and_cache_e4m3_kernel(CacheArgs8 a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_token = (int64_t)a.num_kv_heads * a.row_groups;
+  if (idx >= per_token * a.num_tokens) return;
+  const int64_t t = idx / per_token;
+  const int64_t rem = idx - t * per_token;
+  const int h = (int)(rem / a.row_groups);
+  const int c = (int)(rem - (int64_t)h * a.row_groups);
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    if (rem == 0) flag_error(kErrSlot);
+    return;
+  }
+  const int64_t b = slot / a.block_size, o = slot - b * a.block_size;
+  const int64_t dst = ((b * a.num_kv_heads + h) * a.block_size + o) * a.row_groups + c;
+  for (int pool = 0; pool < 2; ++pool) {
+    const uint4 x = reinterpret_cast<const uint4*>(pool ? a.v : a.k)[idx];
+    const float inv = pool ? a.v_inv : a.k_inv;
+    float f[8];
+    Elem<uint16_t>::unpack(x, f);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_code(f[e] * inv) << (8 * (e & 3));
+    reinterpret_cast<uint2*>(pool ? a.v_pool : a.k_pool)[dst] = make_uint2(w[0], w[1]);
+  }
 }
 
 // grid.x = pair, grid.z = pool (0 K, 1 V); grid.y strides over the block.
@@ -1078,30 +1198,40 @@ static PartitionKernel pick_valu_t(int d, int bs, int group) {
   return nullptr;
 }
 
-template <int BS>
+template <int BS, bool F8>
 static PartitionKernel pick_mfma(int group) {
   switch (group) {
-    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves>;
-    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves>;
-    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves>;
+    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves, F8>;
+    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves, F8>;
+    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves, F8>;
     default: return nullptr;
   }
 }
 
 static PartitionKernel pick_partition(const DecodeKey& k) {
   if (k.variant == 1) {
+    if (k.kv_fp8) return nullptr;
     if (k.dtype == 0) return pick_valu_t<float>(k.head_dim, k.block_size, k.group);
     if (k.dtype == 1) return pick_valu_t<uint16_t>(k.head_dim, k.block_size, k.group);
     return nullptr;
   }
   if (k.variant == 2) {
     if (k.dtype != 1 || k.head_dim != 128) return nullptr;
+    if (k.kv_fp8) {
+      switch (k.block_size) {
+        case 16: return pick_mfma<16, true>(k.group);
+        case 32: return pick_mfma<32, true>(k.group);
+        case 64: return pick_mfma<64, true>(k.group);
+        case 128: return pick_mfma<128, true>(k.group);
+        default: return nullptr;
+      }
+    }
     switch (k.block_size) {
-      case 8: return pick_mfma<8>(k.group);
-      case 16: return pick_mfma<16>(k.group);
-      case 32: return pick_mfma<32>(k.group);
-      case 64: return pick_mfma<64>(k.group);
-      case 128: return pick_mfma<128>(k.group);
+      case 8: return pick_mfma<8, false>(k.group);
+      case 16: return pick_mfma<16, false>(k.group);
+      case 32: return pick_mfma<32, false>(k.group);
+      case 64: return pick_mfma<64, false>(k.group);
+      case 128: return pick_mfma<128, false>(k.group);
       default: return nullptr;
     }
   }
@@ -1144,6 +1274,16 @@ hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream) {
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_e4m3(const CacheArgs8& args, hipStream_t stream) {
+  const int64_t total = (int64_t)args.num_tokens * args.num_kv_heads * args.row_groups;
+  if (total <= 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reshape_and_cache_e4m3_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     args);
   return hipGetLastError();
 }
 

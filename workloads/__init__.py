@@ -39,7 +39,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "draw_lengths", "pool_blocks",
-    "free_order", "normal_f32", "to_bf16_bits", "normal_values",
+    "free_order", "normal_f32", "to_bf16_bits", "normal_values", "random_e4m3_codes",
 ]
 
 
@@ -151,6 +151,26 @@ def normal_values(shape, rng: np.random.Generator, dtype: str) -> np.ndarray:
     """N(0,1) draws in the storage type: float32 array, or uint16 bf16 bits."""
     x = normal_f32(shape, rng)
     return x if dtype == "f32" else to_bf16_bits(x)
+
+
+def random_e4m3_codes(shape, rng: np.random.Generator) -> np.ndarray:
+    """Random FP8 E4M3 bytes for an 8-bit pool: a random sign bit over the
+    low 80 code points of each sign (the codes of magnitude below 4), drawn
+    uniformly. Raw bytes; the format's arithmetic is not used here."""
+    low = rng.integers(0, 0x50, size=shape, dtype=np.uint8)
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    return (low | sign).astype(np.uint8)
+
+
+def random_e4m3_codes_device(shape, seed: int, device):
+    """random_e4m3_codes drawn on `device` by torch's seeded generator (uint8
+    tensor), for pools too large to draw on the host quickly."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    low = torch.randint(0, 0x50, tuple(shape), generator=g, device=device, dtype=torch.int32)
+    sign = torch.randint(0, 2, tuple(shape), generator=g, device=device, dtype=torch.int32)
+    return (low | (sign << 7)).to(torch.uint8)
 
 
 def normal_device(shape, seed: int, dtype: str, device):
