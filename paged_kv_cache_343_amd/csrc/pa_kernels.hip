@@ -825,6 +825,9 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // One wave per (sequence, query head); only sequences with more than one
 // partition have anything to merge.
+// Partitions merged with every load issued up front (the common case).
+constexpr int kReduceFast = 16;
+
 template <typename T, int D>
 __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a) {
   // one wave per (sequence, query head); kReduceWaves consecutive pairs per
@@ -843,36 +846,58 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
                     ((int64_t)i * a.num_kv_heads + hq / G) * a.max_parts * kMlRecord + 2 * (hq % G);
   const float* po = a.part_o + ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
   const int lane = threadIdx.x & 63;
-  // lane j holds partition j's statistics (partitions past 64 are folded in
-  // by the same lane, merged on the fly)
-  float mj = -INFINITY, lj = 0.0f;
-  for (int j = lane; j < np; j += 64) {
-    const float m2 = ml[(int64_t)j * kMlRecord], l2 = ml[(int64_t)j * kMlRecord + 1];
-    const float big = fmaxf(mj, m2);
-    lj = lj * merge_weight(mj, big) + l2 * merge_weight(m2, big);
-    mj = big;
-  }
-  float big = mj;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
-  float wsum = lj * merge_weight(mj, big);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
-  // out = sum_j w_j o_j / sum_j w_j, w_j = l_j 2^(m_j - M); D / 64 dims per lane
   constexpr int DPL = D / 64;
   float o[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.0f;
+  float wsum;
+  if (np <= kReduceFast) {
+    // every load up front: lane j's statistics, then each partition's slice
+    const float mj = lane < np ? ml[(int64_t)lane * kMlRecord] : -INFINITY;
+    const float lj = lane < np ? ml[(int64_t)lane * kMlRecord + 1] : 0.0f;
+    float v[kReduceFast][DPL];
+#pragma unroll
+    for (int j = 0; j < kReduceFast; ++j) {
+      // partitions past np read partition 0's slice (in bounds) and drop it
+      const float* src = po + (int64_t)(j < np ? j : 0) * D + lane * DPL;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) v[j][k] = j < np ? src[k] : 0.0f;
+    }
+    float big = mj;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
+    const float wj = lj * merge_weight(mj, big);
+    wsum = wj;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+#pragma unroll
+    for (int j = 0; j < kReduceFast; ++j) {
+      const float w = __shfl(wj, j);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] = fmaf(w, v[j][k], o[k]);
+    }
+  } else {
+    // lane j folds partitions j, j + 64, ... into one (max, exp-sum) pair
+    float mj = -INFINITY, lj = 0.0f;
+    for (int j = lane; j < np; j += 64) {
+      const float m2 = ml[(int64_t)j * kMlRecord], l2 = ml[(int64_t)j * kMlRecord + 1];
+      const float big = fmaxf(mj, m2);
+      lj = lj * merge_weight(mj, big) + l2 * merge_weight(m2, big);
+      mj = big;
+    }
+    float big = mj;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
+    wsum = lj * merge_weight(mj, big);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
 #pragma unroll 4
-  for (int j = 0; j < np; ++j) {
-    const float wj = ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
-    const float* src = po + (int64_t)j * D + lane * DPL;
-    if constexpr (DPL == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(src);
-      o[0] = fmaf(wj, v.x, o[0]);
-      o[1] = fmaf(wj, v.y, o[1]);
-    } else {
-      o[0] = fmaf(wj, src[0], o[0]);
+    for (int j = 0; j < np; ++j) {
+      const float wj =
+          ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
+      const float* src = po + (int64_t)j * D + lane * DPL;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[k] = fmaf(wj, src[k], o[k]);
     }
   }
   T* out = reinterpret_cast<T*>(a.out) + ((int64_t)i * a.num_q_heads + hq) * D + lane * DPL;
