@@ -115,9 +115,7 @@ def main() -> int:
     P.lib()  # fail loudly if libpa.so is missing
     dev = torch.device("cuda", 0)
     w = W.get(args.workload)
-    if "prefix" in w.lengths[0]:
-        print("bench.py times the plain decode workloads", file=sys.stderr)
-        return 1
+    prefix = w.lengths[0] == "prefix_suffix"
     variant = {"auto": P.PA_VARIANT_AUTO, "valu": P.PA_VARIANT_VALU, "mfma": P.PA_VARIANT_MFMA}[args.variant]
     B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     if args.block_size:
@@ -135,10 +133,25 @@ def main() -> int:
 
     # ---- inputs (seeded, synthetic) ------------------------------------
     rng = np.random.default_rng(w.seed)
-    ctx = W.draw_lengths(w, rng)                       # tokens cached before the first step
+    if prefix:
+        # prompt groups: one parent holds the shared prompt, the other samples
+        # fork it, then every sample appends its private suffix (the first
+        # write into a shared partial block copies it) before timing starts
+        suffix = W.draw_lengths(w, rng)
+        ngroups, nsamp = w.extra["groups"], w.extra["samples"]
+        plen = w.lengths[1]
+        n_long = w.extra.get("long_seqs", 0)
+        ctx = np.concatenate([plen + suffix[:ngroups * nsamp],
+                              np.full(n_long, w.extra.get("long_len", 0))]).astype(np.int64)
+        args.no_cpu_baseline = True      # the CPU baseline leg times the headline workload
+        unique_prompt = ngroups * -(-plen // bs)
+        occupied = unique_prompt + int(sum(-(-int(L) // bs) - plen // bs for L in ctx[:ngroups * nsamp] + 1))
+        occupied += int(sum(-(-int(L) // bs) for L in ctx[ngroups * nsamp:] + 1))
+    else:
+        ctx = W.draw_lengths(w, rng)                   # tokens cached before the first step
+        occupied = int(sum(-(-int(L) // bs) for L in ctx + 1))
     final = ctx + nsteps
-    occupied = int(sum(-(-int(L) // bs) for L in ctx + 1))
-    nb = max(W.pool_blocks(w, occupied), int(sum(-(-int(L) // bs) for L in final)))
+    nb = max(W.pool_blocks(w, occupied), occupied + B * (-(-nsteps // bs) + 1))
     order = W.free_order(nb, rng)
     if args.block_order == "identity":
         order = np.arange(nb, dtype=np.int32)
@@ -162,8 +175,32 @@ def main() -> int:
     log(f"inputs ready: {B} sequences, {nb} blocks, {k_pool.numel() * eb * 2 / 1e9:.2f} GB of KV pool")
 
     bm = P.BlockManager(nb, bs, order)
-    for i, L in enumerate(ctx):
-        bm.add_seq(i, int(L))
+    cow_setup = 0
+    if prefix:
+        for gi in range(ngroups):
+            bm.add_seq(gi * nsamp, plen)
+            for k in range(1, nsamp):
+                bm.fork(gi * nsamp, gi * nsamp + k)
+        for k in range(n_long):
+            bm.add_seq(ngroups * nsamp + k, int(ctx[ngroups * nsamp + k]))
+        kz = torch.zeros((B, hkv, d), dtype=tdt, device=dev)
+        for step in range(int(suffix[:ngroups * nsamp].max())):
+            batch = np.array([sq for sq in range(ngroups * nsamp) if suffix[sq] > step], dtype=np.int32)
+            slots, pairs = bm.append_slots(batch)
+            if pairs.shape[0]:
+                cow_setup += pairs.shape[0]
+                P.pa_copy_blocks(k_pool, v_pool, torch.from_numpy(pairs).to(dev))
+            sl = torch.from_numpy(slots).to(dev)
+            n = len(batch)
+            if fp8:
+                P.pa_reshape_and_cache_e4m3(kz[:n], kz[:n], sl, k_pool, v_pool, k_scale, v_scale)
+            else:
+                P.pa_reshape_and_cache(kz[:n], kz[:n], sl, k_pool, v_pool)
+        torch.cuda.synchronize()
+        log(f"shared prompts forked, suffixes written ({cow_setup} copy-on-write blocks)")
+    else:
+        for i, L in enumerate(ctx):
+            bm.add_seq(i, int(L))
     seq_ids = np.arange(B, dtype=np.int32)
     # Per step the host produces slots (int64 [B]), lengths (int32 [B]) and
     # block tables (int32 [B, maxb]); they travel in one packed pinned buffer
@@ -197,6 +234,7 @@ def main() -> int:
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     step_bytes = []
     host_s = [0.0]  # host time per timed step, waits excluded
+    step_lens = []  # shared-prefix workloads: lengths per step, for the unique bytes
     bm_s = [0.0]    # block manager (append + export) time
     ev = []  # per step: (reshape start, partition start, partition end, reduce end)
 
@@ -227,6 +265,8 @@ def main() -> int:
             raise P.PaError(st, "pa_bm_export")
         bm_s[0] += time.perf_counter() - t_bm
         step_bytes.append(int(lens_np[b].sum(dtype=np.int64)) * 2 * hkv * d * pool_eb)
+        if prefix:
+            step_lens.append(lens_np[b].copy())
 
     # Raw C-ABI calls with pointers resolved once: the step's host cost stays
     # far below its GPU time, so the GPU never waits for the host.
@@ -310,6 +350,7 @@ def main() -> int:
     if P.pa_device_errors() != 0:
         raise RuntimeError("device index error during warmup")
     step_bytes.clear()
+    step_lens.clear()
     bm_s[0] = 0.0
     t0 = time.perf_counter()
     for s in range(args.warmup, nsteps):
@@ -410,6 +451,25 @@ def main() -> int:
     }
     peak = stream_read_peak(torch, dev)
     result["practical_peak"] = dict(peak, partition_frac=round(achieved / peak["GBps"], 4))
+    if prefix:
+        # bytes of distinct cached rows read per step: a shared prompt block is
+        # read once per step however many sequences point at it
+        tab_last = stage[(nsteps - 1) % NBUF]["tables"].numpy()
+        uniq = []
+        for lens_s in step_lens:
+            rows = np.zeros(nb, dtype=np.int64)
+            nblk = -(-lens_s.astype(np.int64) // bs)
+            for i in range(B):
+                k = np.arange(nblk[i])
+                np.maximum.at(rows, tab_last[i, :nblk[i]], np.minimum(bs, lens_s[i] - k * bs))
+            uniq.append(int(rows.sum()) * 2 * hkv * d * pool_eb)
+        ub = float(np.mean(uniq))
+        result["shared_prefix"] = {
+            "logical_bytes_per_step": int(total_bytes / K), "unique_bytes_per_step": int(ub),
+            "unique_GBps": round(ub / (wall / K) / 1e9, 1),
+            "pct_of_hbm_peak_unique": round(100.0 * ub / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
+            "partition_unique_GBps": round(ub / part_avg_s / 1e9, 1),
+            "copy_on_write_blocks_at_setup": cow_setup}
     if args.copy_calibration_mib > 0:
         result["copy_calibration"] = copy_calibration(P, torch, dev, args.copy_calibration_mib,
                                                       hkv * bs * d * eb)

@@ -358,9 +358,11 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
 
 // Order in which workgroup ids enumerate (KV head, sequence, partition),
 // fastest first: 0 = head, sequence, partition; 1 = sequence, head,
-// partition; 2 = head, partition, sequence; 3 = partition, head, sequence.
+// partition; 2 = head, partition, sequence; 3 = partition, head, sequence;
+// 4 = order 3 cut into one contiguous eighth per XCD; 6 (the default) =
+// XCD-balanced rounds, see below (order 3 when Hkv is not a multiple of 8).
 #ifndef PA_GRID_ORDER
-#define PA_GRID_ORDER 3
+#define PA_GRID_ORDER 6
 #endif
 
 // Decodes blockIdx.x into (KV head, sequence, partition); returns false if
@@ -378,11 +380,26 @@ __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWo
   id /= a.num_kv_heads;
   wk.j = id % a.max_parts;
   wk.i = id / a.max_parts;
-#elif PA_GRID_ORDER == 3
-  wk.j = id % a.max_parts;
-  id /= a.max_parts;
-  wk.g = id % a.num_kv_heads;
-  wk.i = id / a.num_kv_heads;
+#elif PA_GRID_ORDER == 6
+  if (a.num_kv_heads % 8 == 0) {
+    // Workgroup ids are dealt to the 8 XCDs round-robin (XCD x = id % 8).
+    // Round r = id / 8 names (sequence i, block of 8 KV heads, partition j),
+    // partition fastest, and XCD x takes KV head g = 8 * block + (x - j) mod
+    // 8 of it: each round hands every XCD a unit of the same (i, j), so the
+    // XCDs get equal work whatever the lengths, and a given (g, j) always
+    // lands on XCD (g + j) mod 8, so sequences sharing prompt blocks meet
+    // in one L2.
+    const int x = id & 7, r = id >> 3;
+    wk.j = r % a.max_parts;
+    const int rest = r / a.max_parts, nb8 = a.num_kv_heads >> 3;
+    wk.g = (rest % nb8) * 8 + ((x - wk.j) & 7);
+    wk.i = rest / nb8;
+  } else {
+    wk.j = id % a.max_parts;
+    id /= a.max_parts;
+    wk.g = id % a.num_kv_heads;
+    wk.i = id / a.num_kv_heads;
+  }
 #else
   wk.g = id % a.num_kv_heads;
   id /= a.num_kv_heads;
@@ -1269,8 +1286,11 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    hipStream_t stream) {
   PartitionKernel kern = pick_partition(key);
   if (!kern) return hipErrorInvalidValue;
-  const int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
+  int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
   if (groups <= 0) return hipSuccess;
+#if PA_GRID_ORDER == 4
+  groups = (groups + 7) / 8 * 8;
+#endif
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kDecodeWaves * 64), 0, stream, args);
   return hipGetLastError();
