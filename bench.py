@@ -639,6 +639,9 @@ def fork_cow_host_us(P) -> float:
     return round(el * 1e6, 1)
 
 
+CALIBRATION_LAUNCHES = 3
+
+
 def copy_calibration(P, torch, dev, mib: int, block_bytes: int) -> dict:
     """pa_copy_blocks over a fresh pair of pools: n blocks copied to n other
     blocks in each of the K and V pools, so that exactly 2 * n * block_bytes
@@ -649,12 +652,12 @@ def copy_calibration(P, torch, dev, mib: int, block_bytes: int) -> dict:
     vp = torch.zeros_like(kp)
     pairs = torch.stack([torch.arange(n), torch.arange(n, 2 * n)], dim=1).to(
         device=dev, dtype=torch.int64).contiguous()
-    for _ in range(3):
+    for _ in range(CALIBRATION_LAUNCHES):
         P.pa_copy_blocks(kp.view(2 * n, 1, 1, block_bytes // 2), vp.view(2 * n, 1, 1, block_bytes // 2),
                          pairs)
     torch.cuda.synchronize()
     return {"pairs": n, "block_bytes": block_bytes, "read_bytes": 2 * n * block_bytes,
-            "write_bytes": 2 * n * block_bytes, "launches": 3}
+            "write_bytes": 2 * n * block_bytes, "launches": CALIBRATION_LAUNCHES}
 
 
 def _counter_rows(directory: str, counter: str):
@@ -691,7 +694,9 @@ def summarise_traffic(args) -> int:
         if args.steps and len(part) > args.steps:
             part = part[-args.steps:]      # the timed steps; warm-up dispatches come first
         variant = "mfma" if any("decode_partition_mfma" in k for k, _ in rows) else "valu"
-        cal_kib = float(np.median(cal))
+        # the calibration copies are the run's last copy dispatches (the
+        # copy-on-write and swap measurements use the same kernel earlier)
+        cal_kib = float(np.median(cal[-CALIBRATION_LAUNCHES:]))
         out[counter] = {"partition_kib_mean": float(np.mean(part)), "dispatches": len(part),
                         "copy_kib_median": cal_kib}
         out["variant"] = variant
