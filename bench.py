@@ -433,7 +433,7 @@ def main() -> int:
     }
     avg_len = total_bytes / K / (2 * hkv * d * pool_eb) / B
     parts = float(np.mean([-(-int(x) // ptok) for x in stage[0]["lens"].numpy()])) if ptok > 0 else 1.0
-    red_bytes = B * hq * (parts * (d * 4) + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
+    red_bytes = B * hq * (parts * d * eb + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
     cache_bytes = B * 2 * hkv * d * (eb + pool_eb)
     result["rows"] = {
         "a1_block_manager_host_us": round(1e6 * bm_s[0] / K, 1),

@@ -89,8 +89,9 @@ typedef struct {
   int32_t variant;            /* PA_VARIANT_*                                  */
 } pa_decode_shape_t;
 
-/* Bytes of scratch workspace pa_decode needs for `shape` (partial softmax
- * statistics and partial outputs, fp32). 0 if the shape is invalid. */
+/* Bytes of scratch workspace pa_decode needs for `shape`: the partial softmax
+ * statistics (fp32) and the normalised partial outputs (in `dtype`; they are
+ * merged in fp32). 0 if the shape is invalid. */
 size_t pa_decode_workspace_bytes(const pa_decode_shape_t* shape);
 
 /*

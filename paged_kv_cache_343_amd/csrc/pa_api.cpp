@@ -73,7 +73,7 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   const size_t recs = (size_t)s->num_seqs * s->num_kv_heads * plan->max_parts;
   if (plan->max_parts > 1) {
     plan->ml_bytes = round_up(recs * pa::kMlRecord * sizeof(float), 256);
-    plan->o_bytes = round_up(rows * (size_t)s->head_dim * sizeof(float), 256);
+    plan->o_bytes = round_up(rows * (size_t)s->head_dim * elem_bytes(s->dtype), 256);
   }
   return PA_OK;
 }
@@ -98,7 +98,7 @@ pa_status_t fill_args(const void* q, const void* k_pool, const void* v_pool,
   a->seq_lens = seq_lens;
   a->out = out;
   a->part_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  a->part_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes)
+  a->part_o = need > 0 ? static_cast<void*>(static_cast<char*>(workspace) + plan.ml_bytes)
                        : nullptr;
   a->qscale = scale * 1.4426950408889634f;  // log2(e): scores kept in log2 units
   a->out_scale = 1.0f;
@@ -213,7 +213,7 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
   a.seq_lens = seq_lens;
   a.out = out;
   a.part_ml = static_cast<float*>(workspace);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ml_bytes);
+  a.part_o = static_cast<void*>(static_cast<char*>(workspace) + plan.ml_bytes);
   a.num_seqs = shape->num_seqs;
   a.num_q_heads = shape->num_q_heads;
   a.num_kv_heads = shape->num_kv_heads;

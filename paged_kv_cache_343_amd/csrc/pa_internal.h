@@ -20,7 +20,8 @@ struct DecodeArgs {
   void* out;                    // [B][Hq][D]
   float* part_ml;               // [B][Hkv][max_parts][kMlRecord]: per query head of the
                                 //   group, max score (log2 units) then exp-sum; rest 0
-  float* part_o;                // [B][Hq][max_parts][D]: normalised partial output
+  void* part_o;                 // [B][Hq][max_parts][D]: normalised partial output, in the
+                                //   output dtype
   float qscale;                 // softmax scale * log2(e) (* k_scale for 8-bit pools)
   float out_scale;              // v_scale for 8-bit pools
   int32_t num_seqs;

@@ -117,6 +117,29 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float x0, float x1
   *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
+// N consecutive elements (N = 1 or 2, aligned to N elements) as floats.
+template <typename T, int N>
+__device__ __forceinline__ void load_elems(const T* p, float (&f)[N]) {
+  static_assert(N == 1 || N == 2, "one or two elements");
+  if constexpr (std::is_same<T, float>::value) {
+    if constexpr (N == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      f[0] = v.x;
+      f[1] = v.y;
+    } else {
+      f[0] = *p;
+    }
+  } else {
+    if constexpr (N == 2) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+      f[0] = lo_bf16(v);
+      f[1] = hi_bf16(v);
+    } else {
+      f[0] = __uint_as_float((uint32_t)*p << 16);
+    }
+  }
+}
+
 __device__ __forceinline__ uint4 ld16(const char* base, uint32_t byte_off) {
   return *reinterpret_cast<const uint4*>(base + byte_off);
 }
@@ -222,9 +245,6 @@ __device__ void write_zero_rows(const DecodeArgs& a, int i, int g) {
 #ifndef PA_FINISH_PERMLANE
 #define PA_FINISH_PERMLANE 1
 #endif
-#ifndef PA_PART_STORE_NT
-#define PA_PART_STORE_NT 0
-#endif
 
 // Value held by lane (lane ^ OFF), for OFF in {16, 32}: the permlane swap
 // instructions exchange 16- or 32-lane halves between two registers on the
@@ -298,8 +318,8 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
     }
   }
   __syncthreads();
-  // Merge of the NW wave streams, 4 consecutive dims per thread: 16-byte
-  // stores of the partial output (8-byte for a bf16 final row).
+  // Merge of the NW wave streams, 4 consecutive dims per thread: one 16-byte
+  // (fp32) or 8-byte (bf16) store each.
   constexpr int V4 = D / 4;
   for (int t = threadIdx.x; t < G * V4; t += NW * 64) {
     const int h = t / V4, d0 = (t % V4) * 4;
@@ -323,13 +343,10 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
       store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
                 o[3] * inv);
     } else {
-      float4* dst = reinterpret_cast<float4*>(a.part_o + (row * a.max_parts + wk.j) * D + d0);
-#if PA_PART_STORE_NT
-      const f32x4_t val = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-      __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(dst));
-#else
-      *dst = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-#endif
+      // the partial output is stored in the output type; the merge of the
+      // partitions runs in fp32
+      store4<T>(reinterpret_cast<T*>(a.part_o) + (row * a.max_parts + wk.j) * D + d0, o[0] * inv,
+                o[1] * inv, o[2] * inv, o[3] * inv);
     }
   }
   // (max, exp-sum) of every head of the group: one full 128-byte record per
@@ -356,39 +373,21 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
 }
 
 
-// Order in which workgroup ids enumerate (KV head, sequence, partition),
-// fastest first: 0 = head, sequence, partition; 1 = sequence, head,
-// partition; 2 = head, partition, sequence; 3 = partition, head, sequence;
-// 4 = order 3 cut into one contiguous eighth per XCD; 6 (the default) =
-// XCD-balanced rounds, see below (order 3 when Hkv is not a multiple of 8).
-#ifndef PA_GRID_ORDER
-#define PA_GRID_ORDER 6
-#endif
-
-// Decodes blockIdx.x into (KV head, sequence, partition); returns false if
-// the workgroup has nothing to do (after writing zeros for empty sequences).
+// Work units are (sequence i, KV head g, partition j), one per workgroup.
+// Workgroup ids are dealt to the 8 XCDs round-robin (XCD x = id % 8). When
+// Hkv is a multiple of 8, round r = id / 8 names (sequence i, block of 8 KV
+// heads, partition j), partition fastest, and XCD x takes KV head
+// g = 8 * block + (x - j) mod 8: each round hands every XCD a unit of the
+// same (i, j), so the XCDs get equal work whatever the lengths, and a given
+// (g, j) always lands on XCD (g + j) mod 8, so sequences sharing prompt
+// blocks meet in one L2. Otherwise units are numbered partition fastest,
+// then head, then sequence.
+// Decodes blockIdx.x; returns false if the workgroup has nothing to do
+// (after writing zeros for an empty sequence).
 template <typename T, int D, int BS, int G, int NW>
 __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk) {
-  int id = blockIdx.x;
-#if PA_GRID_ORDER == 1
-  wk.i = id % a.num_seqs;
-  id /= a.num_seqs;
-  wk.g = id % a.num_kv_heads;
-  wk.j = id / a.num_kv_heads;
-#elif PA_GRID_ORDER == 2
-  wk.g = id % a.num_kv_heads;
-  id /= a.num_kv_heads;
-  wk.j = id % a.max_parts;
-  wk.i = id / a.max_parts;
-#elif PA_GRID_ORDER == 6
+  const int id = blockIdx.x;
   if (a.num_kv_heads % 8 == 0) {
-    // Workgroup ids are dealt to the 8 XCDs round-robin (XCD x = id % 8).
-    // Round r = id / 8 names (sequence i, block of 8 KV heads, partition j),
-    // partition fastest, and XCD x takes KV head g = 8 * block + (x - j) mod
-    // 8 of it: each round hands every XCD a unit of the same (i, j), so the
-    // XCDs get equal work whatever the lengths, and a given (g, j) always
-    // lands on XCD (g + j) mod 8, so sequences sharing prompt blocks meet
-    // in one L2.
     const int x = id & 7, r = id >> 3;
     wk.j = r % a.max_parts;
     const int rest = r / a.max_parts, nb8 = a.num_kv_heads >> 3;
@@ -396,16 +395,10 @@ __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWo
     wk.i = rest / nb8;
   } else {
     wk.j = id % a.max_parts;
-    id /= a.max_parts;
-    wk.g = id % a.num_kv_heads;
-    wk.i = id / a.num_kv_heads;
+    const int rest = id / a.max_parts;
+    wk.g = rest % a.num_kv_heads;
+    wk.i = rest / a.num_kv_heads;
   }
-#else
-  wk.g = id % a.num_kv_heads;
-  id /= a.num_kv_heads;
-  wk.i = id % a.num_seqs;
-  wk.j = id / a.num_seqs;
-#endif
   wk.len = checked_len(a, wk.i);
   wk.nparts = (wk.len + a.part_tokens - 1) / a.part_tokens;
   if (wk.len == 0) {
@@ -601,10 +594,18 @@ struct KVChunk8 {                      // FP8 E4M3 pools: 128-byte rows
 #ifndef PA_KV_LOAD_AUX
 #define PA_KV_LOAD_AUX 0
 #endif
+// depth of the K/V register pipeline of the matrix-core partition kernel
+#ifndef PA_PIPE_BF16
+#define PA_PIPE_BF16 2
+#endif
+#ifndef PA_PIPE_F8
+#define PA_PIPE_F8 2
+#endif
 
 // Buffer resource over `bytes` bytes at a wave-uniform address (gfx9
 // descriptor: raw 32-bit data format, no swizzle); loads past `bytes` return
-// zeros instead of touching memory.
+// zeros instead of touching memory (so a descriptor of 0 bytes makes a load
+// that only keeps the wait counts regular).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, 0x00020000);
 }
@@ -629,11 +630,11 @@ __device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff
 template <int BS>
 __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, const char* vbase,
                                               int64_t blk_bytes, int phys, int tok_in_blk,
-                                              uint32_t k_off, uint32_t v_off) {
+                                              uint32_t k_off, uint32_t v_off, bool live) {
   constexpr int ROW = 128;
   const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, 16 * ROW);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, 16 * ROW);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live ? 16 * ROW : 0);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live ? 16 * ROW : 0);
   c.k[0] = buf_ld16(kr, k_off, 0);
   c.k[1] = buf_ld16(kr, k_off, 64);
 #pragma unroll
@@ -647,11 +648,11 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, co
 template <int BS>
 __device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, const char* vbase,
                                               int64_t blk_bytes, int phys, int tok_in_blk,
-                                              uint32_t k_off, uint32_t v_off) {
+                                              uint32_t k_off, uint32_t v_off, bool live) {
   constexpr int ROW = 256;
   const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, 16 * ROW);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, 16 * ROW);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live ? 16 * ROW : 0);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live ? 16 * ROW : 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) c.k[s] = buf_ld16(kr, k_off, s * 64);
 #pragma unroll
@@ -759,19 +760,20 @@ __device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4]
   }
 }
 
+// One work unit (sequence, KV head, partition) of the matrix-core kernel.
 // F8: the pools hold FP8 E4M3 codes (q and out stay bf16); scores use
 // qscale = scale * log2(e) * k_scale and outputs are multiplied by v_scale.
 template <int BS, int G, int NW, bool F8>
-__global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
+__device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWork& wk) {
   constexpr int D = 128;
   constexpr int ROW = F8 ? D : D * 2;             // bytes per token row
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS == 8 || BS % 16 == 0, "block must hold whole 16-token chunks, or half of one");
   static_assert(!F8 || BS != 8, "8-bit pools take blocks of 16 tokens or more");
   using Chunk = typename std::conditional<F8, KVChunk8, KVChunk>::type;
+  // register buffers in the K/V pipeline (an 8-bit chunk takes half the registers)
+  constexpr int NBUF = BS == 8 ? 2 : (F8 ? PA_PIPE_F8 : PA_PIPE_BF16);
 
-  PartitionWork wk;
-  if (!setup_partition<uint16_t, D, BS, G, NW>(a, wk)) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = lane >> 4, c = lane & 15;
@@ -805,36 +807,68 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
   const int nch = (wk.tok1 - wk.tok0 + 15) / 16;
   const int nmine = nch > w ? (nch - w + NW - 1) / NW : 0;   // chunks of this wave
   auto chunk_tok = [&](int t) { return wk.tok0 + (w + t * NW) * 16; };
-  // Windows of 64 chunks: one block-id load per window, then a two-buffer
-  // pipeline over the window's chunks (no load inside the loop depends on
-  // another load, so the compiler's wait counts stay partial).
+  // Windows of 64 chunks: one block-id load per window, then a pipeline of
+  // NBUF register buffers over the window's chunks: chunk t + NBUF - 1 is
+  // issued before chunk t is computed. No load inside the loop depends on
+  // another load, so the compiler's wait counts stay partial; issues past
+  // the window's last chunk use an empty descriptor (no memory access; with
+  // 8-token blocks, which use per-lane addresses, the last chunk again).
   for (int win = 0; win < nmine; win += 64) {
     const int2 ids = load_id_window<BS, NW>(a, wk, w, win, nmine);
     const int cnt = min(64, nmine - win);
     auto issue = [&](Chunk& buf, int t) {
-      const int phys = __builtin_amdgcn_readlane(ids.x, t);
+      const bool live = t < cnt;
+      const int tt = live ? t : cnt - 1;
+      const int phys = __builtin_amdgcn_readlane(ids.x, tt);
       if constexpr (BS == 8) {
-        load_kv_chunk_bs8(buf, kbase, vbase, blk_bytes, phys, __builtin_amdgcn_readlane(ids.y, t));
+        load_kv_chunk_bs8(buf, kbase, vbase, blk_bytes, phys, __builtin_amdgcn_readlane(ids.y, tt));
       } else {
-        load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + t) % BS, k_off,
-                          v_off);
+        load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + tt) % BS, k_off,
+                          v_off, live);
       }
+    };
+    // one stage: issue chunk t + NBUF - 1 into `nxt`, compute chunk t from
+    // `cur`; true once the window is done. (Written out per depth: a loop
+    // over a buffer array costs the compiler ~30 more registers.)
+    int t = 0;
+    auto stage = [&](Chunk& nxt, const Chunk& cur) {
+      issue(nxt, t + NBUF - 1);
+      mfma_chunk<G>(cur, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
+      return ++t >= cnt;
     };
     Chunk b0, b1;
     issue(b0, 0);
-    for (int t = 0;;) {
-      issue(b1, t + 1 < cnt ? t + 1 : t);
-      mfma_chunk<G>(b0, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
-      if (++t >= cnt) break;
-      issue(b0, t + 1 < cnt ? t + 1 : t);
-      mfma_chunk<G>(b1, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
-      if (++t >= cnt) break;
+    if constexpr (NBUF == 2) {
+      for (;;) {
+        if (stage(b1, b0) || stage(b0, b1)) break;
+      }
+    } else if constexpr (NBUF == 3) {
+      Chunk b2;
+      issue(b1, 1);
+      for (;;) {
+        if (stage(b2, b0) || stage(b0, b1) || stage(b1, b2)) break;
+      }
+    } else {
+      static_assert(NBUF == 4, "pipeline depth 2, 3 or 4");
+      Chunk b2, b3;
+      issue(b1, 1);
+      issue(b2, 2);
+      for (;;) {
+        if (stage(b3, b0) || stage(b0, b1) || stage(b1, b2) || stage(b2, b3)) break;
+      }
     }
   }
   float mh[G], lh[G];
   quad_spread<G>(m, mh);
   quad_spread<G>(lsum, lh);
   finish_partition<uint16_t, D, G, NW, 16, 8>(a, wk, mh, lh, acc, F8 ? a.out_scale : 1.0f);
+}
+
+template <int BS, int G, int NW, bool F8>
+__global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
+  PartitionWork wk;
+  if (!setup_partition<uint16_t, 128, BS, G, NW>(a, wk)) return;
+  mfma_unit<BS, G, NW, F8>(a, wk);
 }
 
 // ---------------------------------------------------------------------------
@@ -861,7 +895,7 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   // record of partition j: ml[j * kMlRecord] = (max, exp-sum) of this head
   const float* ml = a.part_ml +
                     ((int64_t)i * a.num_kv_heads + hq / G) * a.max_parts * kMlRecord + 2 * (hq % G);
-  const float* po = a.part_o + ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
+  const T* po = reinterpret_cast<const T*>(a.part_o) + ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
   const int lane = threadIdx.x & 63;
   constexpr int DPL = D / 64;
   float o[DPL];
@@ -876,9 +910,10 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
 #pragma unroll
     for (int j = 0; j < kReduceFast; ++j) {
       // partitions past np read partition 0's slice (in bounds) and drop it
-      const float* src = po + (int64_t)(j < np ? j : 0) * D + lane * DPL;
+      float f[DPL];
+      load_elems<T, DPL>(po + (int64_t)(j < np ? j : 0) * D + lane * DPL, f);
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) v[j][k] = j < np ? src[k] : 0.0f;
+      for (int k = 0; k < DPL; ++k) v[j][k] = j < np ? f[k] : 0.0f;
     }
     float big = mj;
 #pragma unroll
@@ -912,9 +947,10 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
     for (int j = 0; j < np; ++j) {
       const float wj =
           ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
-      const float* src = po + (int64_t)j * D + lane * DPL;
+      float f[DPL];
+      load_elems<T, DPL>(po + (int64_t)j * D + lane * DPL, f);
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] = fmaf(wj, src[k], o[k]);
+      for (int k = 0; k < DPL; ++k) o[k] = fmaf(wj, f[k], o[k]);
     }
   }
   T* out = reinterpret_cast<T*>(a.out) + ((int64_t)i * a.num_q_heads + hq) * D + lane * DPL;
@@ -1113,7 +1149,8 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
     if (lane < cnt) ids = checked_id(a.block_tables, a.num_blocks, trow_base, ((win + lane) * 16) / BS);
     auto issue = [&](KVChunk& buf, int t) {
       const int phys = __builtin_amdgcn_readlane(ids, t);
-      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, ((win + t) * 16) % BS, k_off, v_off);
+      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, ((win + t) * 16) % BS, k_off, v_off,
+                        true);
     };
     KVChunk b0, b1;
     auto step = [&](KVChunk& cur, int t) {
@@ -1286,11 +1323,8 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    hipStream_t stream) {
   PartitionKernel kern = pick_partition(key);
   if (!kern) return hipErrorInvalidValue;
-  int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
+  const int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
   if (groups <= 0) return hipSuccess;
-#if PA_GRID_ORDER == 4
-  groups = (groups + 7) / 8 * 8;
-#endif
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kDecodeWaves * 64), 0, stream, args);
   return hipGetLastError();

@@ -55,8 +55,10 @@ def test_workspace_bytes():
     parts = 8
     rows = 4 * 32 * parts          # (sequence, query head, partition) partial outputs
     recs = 4 * 8 * parts           # (sequence, KV head, partition) 128-byte statistics records
-    want = -(-recs * 128 // 256) * 256 + -(-rows * 128 * 4 // 256) * 256
-    assert P.pa_decode_workspace_bytes(s) == want
+    for dtype, eb in ((P.PA_BF16, 2), (P.PA_F32, 4)):   # partial outputs in the output dtype
+        s = _shape(max_seq_len=4096, max_blocks_per_seq=256, dtype=dtype)
+        want = -(-recs * 128 // 256) * 256 + -(-rows * 128 * eb // 256) * 256
+        assert P.pa_decode_workspace_bytes(s) == want
     assert P.pa_decode_workspace_bytes(_shape(num_q_heads=30)) == 0          # Hq % Hkv
     assert P.pa_decode_workspace_bytes(_shape(head_dim=96)) == 0
     assert P.pa_decode_workspace_bytes(_shape(partition_tokens=24)) == 0      # not a multiple of bs
