@@ -727,6 +727,17 @@ def _finish_traffic(args, out) -> int:
     return 0
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, kp_host, vp_host, q_host, ctx, order, nb, nsteps, scale, seconds, n_seq=32):
     """The float64 C oracle on the host cores, on a bounded sample: the first
     `n_seq` sequences of the workload at their last timed step (block tables
@@ -755,9 +766,20 @@ def cpu_baseline(w, kp_host, vp_host, q_host, ctx, order, nb, nsteps, scale, sec
         if el >= seconds or reps >= 1000:
             break
     kv_bytes = int(lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    # the same oracle on one thread, for a third of the time
+    reps1, t1 = 0, time.perf_counter()
+    while True:
+        R.decode(q_host[:n_seq], kp_host, vp_host, tables, lens, scale, w.dtype, num_threads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 3 or reps1 >= 1000:
+            break
     return {"value": round(n_seq * reps / el, 2), "unit": "seq-steps/s", "cores": threads,
             "kind": "oracle",
             "kv_gb_per_s": round(kv_bytes * reps / el / 1e9, 3),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(n_seq * reps1 / el1, 2), "unit": "seq-steps/s",
+                              "repetitions": reps1, "seconds": round(el1, 1)},
             "sample": (f"first {n_seq} of {len(ctx)} {w.name} sequences at the last timed step "
                        f"(sum of lengths {int(lens.sum())}), plain C float64 oracle, "
                        f"{reps} repetitions in {el:.1f} s")}

@@ -1249,6 +1249,279 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Multi-token queries, many rows per (sequence, KV head): one workgroup of 4
+// waves per tile of 128 query rows (32 rows = two 16-row tiles per wave).
+// Positions are walked 64 at a time (a "block"); each block's K rows and V
+// rows are read from the pool once per workgroup and staged in LDS:
+//   K as rows (272-byte stride: the 16 lanes of an operand read hit distinct
+//     banks); the A operand of S^T = K Q^T is a 16-byte LDS read;
+//   V transposed (V^T, dims as rows, 144-byte stride), with the 64
+//     positions of a block permuted inside each 32-position half so that the
+//     8 positions a lane contributes to one P.V step are contiguous: the B
+//     operand of O += P V is a 16-byte LDS read too.
+// Lane l: R = l / 16, c = l % 16. Per 16-row tile and 16-position slice the
+// S^T product leaves lane (R, c) the scores of row c at positions 4R .. 4R+3
+// of the slice; with the two slices of a 32-position step these are exactly
+// the lane's 8 k-slots (8R .. 8R+7) of the P.V step, so P goes from the
+// softmax to the matrix cores without leaving the lane (as two bf16 terms,
+// p = hi + lo, for ~16 significant bits). The next block's K/V loads are
+// issued before the current block is computed. Workgroup ids: every tile of
+// one (sequence, KV head) lands on the same XCD (XCD = id % 8), so the tiles
+// share that XCD's L2 copy of the context; heavier (later) tiles first.
+constexpr int kFaRows = 128;     // query rows per workgroup
+constexpr int kFaPos = 64;       // positions per block
+constexpr int kFaKRow = 136;     // bf16 elements per staged K row (128 + 8 pad)
+constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad)
+
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats as a bf16 pair (round to nearest even), low element first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const float2 v = make_float2(lo, hi);
+  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+  const f32x2v_t f = {v.x, v.y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
+}
+
+// Slot of position j (0..63) of a block in a staged V^T row: inside each
+// 32-position half, positions 16h + 4R + r go to 8R + 4h + r.
+__device__ __forceinline__ int fa_vt_slot(int j) {
+  const int half = j >> 5, h = (j >> 4) & 1, R = (j >> 2) & 3, r = j & 3;
+  return 32 * half + 8 * R + 4 * h + r;
+}
+
+template <int BS, int G>
+__global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
+  constexpr int D = 128, ROW = 256;
+  constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
+  static_assert(BS % 16 == 0 && kFaRows % (2 * 16) == 0 && 16 % G == 0,
+                "whole 4-position groups per block, whole tokens per 16-row tile");
+  __shared__ __align__(16) uint16_t s_k[kFaPos][kFaKRow];
+  __shared__ __align__(16) uint16_t s_vt[D][kFaVRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = lane >> 4, c = lane & 15;
+
+  // workgroup id -> (tile, KV head, sequence)
+  const int ntiles = (a.max_query_len * G + kFaRows - 1) / kFaRows;
+  const int id = blockIdx.x, x = id & 7, rr = id >> 3;
+  const int tile = ntiles - 1 - rr % ntiles;
+  const int pair = (rr / ntiles) * 8 + x;
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int g = pair % a.num_kv_heads, i = pair / a.num_kv_heads;
+
+  // validate the sequence's length and query range (device-resident)
+  const int L = a.seq_lens[i];
+  const int q0 = a.query_start[i], q1 = a.query_start[i + 1];
+  const int tq = q1 - q0;
+  if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
+      tq > a.max_query_len) {
+    if (tid == 0 && g == 0 && tile == ntiles - 1) flag_error(kErrQuery);
+    return;
+  }
+  const int rows = tq * G;
+  const int row0 = tile * kFaRows;
+  if (row0 >= rows) return;
+  const int t_last = min(tq - 1, (row0 + kFaRows - 1) / G);
+  const int npos = L - tq + t_last + 1;          // positions the tile's last token sees
+  const int nblk = (npos + kFaPos - 1) / kFaPos;
+
+  // this lane's query rows (columns of S^T), one per 16-row tile
+  const int roww = row0 + 32 * w;
+  bf16x8_t qop[2][4];
+  int pos_c[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int rc = roww + 16 * rt + c;
+    const bool ok = rc < rows;
+    const int tc = ok ? rc / G : 0, hc = rc % G;
+    pos_c[rt] = ok ? L - tq + tc : -1;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)(q0 + tc) * a.num_q_heads + g * G + hc) * D + 8 * R) * 2;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      qop[rt][s2] = __builtin_bit_cast(bf16x8_t, ok ? ld16(qp, s2 * 64) : make_uint4(0, 0, 0, 0));
+  }
+  // every row of this wave sees positions below vis_w (its first row's token)
+  const int vis_w = L - tq + min(roww, rows - 1) / G + 1;
+
+  // loaders: K thread = (token group tk, 16-byte dim chunk dk), V thread =
+  // (token group tv, dim chunk dv); each moves 4 consecutive positions
+  const int dk = tid & 15, tk = tid >> 4;
+  const int tv = tid & 15, dv = tid >> 4;
+  const int64_t blk_bytes = kHeadBytes * a.num_kv_heads;
+  const char* kbase = reinterpret_cast<const char*>(a.k_pool) + g * kHeadBytes;
+  const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * kHeadBytes;
+  const int64_t trow = (int64_t)i * a.max_blocks;
+  uint4 kreg[4], vreg[4];
+  auto fetch = [&](int blk) {
+    const int pk = blk * kFaPos + 4 * tk, pv = blk * kFaPos + 4 * tv;
+    const char* kp = nullptr;
+    const char* vp = nullptr;
+    if (pk < npos)
+      kp = kbase + (int64_t)checked_id(a.block_tables, a.num_blocks, trow, pk / BS) * blk_bytes +
+           (pk % BS) * ROW + 16 * dk;
+    if (pv < npos)
+      vp = vbase + (int64_t)checked_id(a.block_tables, a.num_blocks, trow, pv / BS) * blk_bytes +
+           (pv % BS) * ROW + 16 * dv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kreg[r] = pk + r < npos ? ld16(kp, r * ROW) : make_uint4(0, 0, 0, 0);
+      vreg[r] = pv + r < npos ? ld16(vp, r * ROW) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&s_k[4 * tk + r][8 * dk]) = kreg[r];
+    const int slot = fa_vt_slot(4 * tv);
+    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
+    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // dims 8 dv + 2e (low halves) and + 2e + 1 (high halves) of positions 0..3
+      const uint2 lo = make_uint2((v0[e] & 0xffffu) | (v1[e] << 16), (v2[e] & 0xffffu) | (v3[e] << 16));
+      const uint2 hi = make_uint2((v0[e] >> 16) | (v1[e] & 0xffff0000u),
+                                  (v2[e] >> 16) | (v3[e] & 0xffff0000u));
+      *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e][slot]) = lo;
+      *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e + 1][slot]) = hi;
+    }
+  };
+
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+  f32x4_t acc[2][8];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  fetch(0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    if (blk > 0) __syncthreads();          // every wave is done with the previous block
+    stage();
+    __syncthreads();
+    if (blk + 1 < nblk) fetch(blk + 1);
+    const int p0 = blk * kFaPos;
+
+    // S^T for the block: sc[rt][sl] = scores of row c (tile rt) at positions
+    // p0 + 16 sl + 4R + r
+    f32x4_t sc[2][4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      bf16x8_t kop[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        kop[s2] = __builtin_bit_cast(bf16x8_t,
+                                     *reinterpret_cast<const uint4*>(&s_k[16 * sl + c][8 * R + 32 * s2]));
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        sc[rt][sl] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          sc[rt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s2], qop[rt][s2], sc[rt][sl], 0, 0, 0);
+      }
+    }
+    const bool full = p0 + kFaPos <= vis_w;     // no position of the block is masked for this wave
+    uint4 phi[2][2], plo[2][2];                 // [rt][32-position step]
+    bool rescale = false;
+    float alpha[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float sv[16];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = sc[rt][sl][r] * a.qscale;
+          const bool ok = full || p0 + 16 * sl + 4 * R + r <= pos_c[rt];
+          sv[4 * sl + r] = ok ? v : -INFINITY;
+          bm = fmaxf(bm, sv[4 * sl + r]);
+        }
+      bm = fmaxf(bm, xor_lanes<16>(bm));
+      bm = fmaxf(bm, xor_lanes<32>(bm));
+      const float mn = fmaxf(m[rt], bm);
+      alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
+      rescale |= alpha[rt] != 1.0f;
+      m[rt] = mn;
+      float p[16], ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - mn);
+        ps += p[e];
+      }
+      lsum[rt] = lsum[rt] * alpha[rt] + ps;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        // k-slots 8R + 4h + r <- position 32 st + 16 h + 4R + r = p[4 (2 st + h) + r]
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = p[8 * st + e];
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+          lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
+                              f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+        }
+        phi[rt][st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+        plo[rt][st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+      }
+    }
+    // rescale output rows 4R + r of each tile by their rows' alpha (row c's
+    // alpha sits in lane c); skipped when no row's maximum moved
+    if (__ballot(rescale) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha[rt], 4 * R + r);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[rt][t][r] *= ar;
+        }
+    }
+    // O += P V over 8 tiles of 16 dims and two 32-position steps
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8_t vb = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, phi[rt][st]), vb, acc[rt][t], 0, 0, 0);
+          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, plo[rt][st]), vb, acc[rt][t], 0, 0, 0);
+        }
+      }
+  }
+  // out[row] = O[row] / l[row]; lane holds rows 4R + r of each tile, dims 16 t + c
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float l = lsum[rt];
+    l += xor_lanes<16>(l);
+    l += xor_lanes<32>(l);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lr = __shfl(l, 4 * R + r);
+      const int row = roww + 16 * rt + 4 * R + r;
+      if (row >= rows) continue;
+      const int t = row / G, h = row % G;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                      ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + c;
+      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[rt][t2][r] * inv);
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1395,7 +1668,38 @@ static PartitionKernelMq pick_mq(int group) {
   }
 }
 
+template <int BS>
+static PartitionKernelMq pick_fa(int group) {
+  switch (group) {
+    case 1: return multi_query_fa<BS, 1>;
+    case 2: return multi_query_fa<BS, 2>;
+    case 4: return multi_query_fa<BS, 4>;
+    case 8: return multi_query_fa<BS, 8>;
+    case 16: return multi_query_fa<BS, 16>;
+    default: return nullptr;
+  }
+}
+
 hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream) {
+  if ((int64_t)args.max_query_len * group >= kFaRows) {
+    // many rows per (sequence, KV head): workgroup tiles sharing staged K/V
+    PartitionKernelMq kern = nullptr;
+    switch (block_size) {
+      case 16: kern = pick_fa<16>(group); break;
+      case 32: kern = pick_fa<32>(group); break;
+      case 64: kern = pick_fa<64>(group); break;
+      case 128: kern = pick_fa<128>(group); break;
+      default: break;
+    }
+    if (!kern) return hipErrorInvalidValue;
+    const int64_t tiles = ((int64_t)args.max_query_len * group + kFaRows - 1) / kFaRows;
+    const int64_t pairs = (int64_t)args.num_seqs * args.num_kv_heads;
+    if (pairs <= 0) return hipSuccess;
+    const int64_t gx = 8 * tiles * ((pairs + 7) / 8);
+    if (gx > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), 0, stream, args);
+    return hipGetLastError();
+  }
   PartitionKernelMq kern = nullptr;
   switch (block_size) {
     case 16: kern = pick_mq<16>(group); break;

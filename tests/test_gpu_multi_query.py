@@ -19,7 +19,13 @@ def dev():
     return torch.device("cuda", 0)
 
 
-def _run(dev, hq, hkv, bs, lens, tqs, seed=301, poison_out=True):
+# Query rows per (sequence, KV head) from which the library switches to the
+# workgroup-tiled kernel (staged K/V shared by 128 rows); a larger
+# max_query_len than the chunks need forces that kernel on small cases.
+FA_ROWS = 128
+
+
+def _run(dev, hq, hkv, bs, lens, tqs, seed=301, poison_out=True, mql=None):
     w = W.Workload("mq", seed, 0, hq, hkv, 128, bs, "bf16", ("fixed", 0), ("factor", 1.3))
     c = build(w, dev, lens=lens, append=False)
     rng = np.random.default_rng(seed + 1)
@@ -30,7 +36,8 @@ def _run(dev, hq, hkv, bs, lens, tqs, seed=301, poison_out=True):
     out = torch.full((T, hq, 128), float("nan") if poison_out else 0.0, dtype=torch.bfloat16,
                      device=dev)
     P.pa_multi_query(q, c.k_pool, c.v_pool, c.tables, c.lens, torch.from_numpy(qs).to(dev),
-                     c.scale, out, max_seq_len=c.max_len, max_query_len=max(1, max(tqs)))
+                     c.scale, out, max_seq_len=c.max_len,
+                     max_query_len=mql if mql is not None else max(1, max(tqs)))
     torch.cuda.synchronize()
     ref = O.multi_query(O.as_f64(q_np, "bf16"), O.as_f64(c.ok_pool, "bf16"),
                         O.as_f64(c.ov_pool, "bf16"), c.otables, c.olens, qs, c.scale)
@@ -47,9 +54,23 @@ def test_mixed_chunks_all_outputs(dev, hq, hkv, bs):
     check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16", f"mq {hq}/{hkv} bs {bs}")
 
 
-def test_one_token_per_sequence_matches_decode(dev):
+@pytest.mark.parametrize("hq,hkv,bs", [(8, 8, 16), (32, 8, 64), (4, 4, 32)])
+def test_tiled_kernel_on_short_chunks(dev, hq, hkv, bs):
+    # the same kind of batch with max_query_len raised so that every case
+    # takes the workgroup-tiled kernel: tiles past a sequence's rows, rows
+    # past its tokens, single-token rows and whole-prefill rows
+    lens = [1, 5, 40, 300, 1100, 17, 64, 130]
+    tqs = [1, 5, 7, 33, 100, 1, 64, 129]
+    mql = max(max(tqs), -(-FA_ROWS // (hq // hkv)))
+    c, q, out, ref = _run(dev, hq, hkv, bs, lens, tqs, seed=305, mql=mql)
+    assert P.pa_device_errors() == 0
+    check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16", f"tiled {hq}/{hkv} bs {bs}")
+
+
+@pytest.mark.parametrize("mql", [None, 64])
+def test_one_token_per_sequence_matches_decode(dev, mql):
     lens = [1, 16, 17, 511, 1000, 2049]
-    c, q, out, ref = _run(dev, 32, 8, 16, lens, [1] * len(lens))
+    c, q, out, ref = _run(dev, 32, 8, 16, lens, [1] * len(lens), mql=mql)
     dec = torch.empty_like(out)
     P.pa_decode(q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale,
                 dec, max_seq_len=c.max_len)
@@ -84,7 +105,8 @@ def test_long_chunk_over_long_context(dev):
     check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16", "long chunk")
 
 
-def test_nan_in_slack_and_unused_blocks_does_not_leak(dev):
+@pytest.mark.parametrize("mql", [20, 64])        # the per-tile kernel, the tiled one
+def test_nan_in_slack_and_unused_blocks_does_not_leak(dev, mql):
     lens = [5, 37, 100]
     tqs = [5, 6, 20]
     w = W.Workload("mq", 321, 0, 32, 8, 128, 16, "bf16", ("fixed", 0), ("factor", 1.3))
@@ -106,7 +128,7 @@ def test_nan_in_slack_and_unused_blocks_does_not_leak(dev):
     out = torch.empty((int(qs[-1]), 32, 128), dtype=torch.bfloat16, device=dev)
     P.pa_multi_query(to_device(q_np, "bf16", dev), c.k_pool, c.v_pool, c.tables, c.lens,
                      torch.from_numpy(qs).to(dev), c.scale, out, max_seq_len=c.max_len,
-                     max_query_len=20)
+                     max_query_len=mql)
     ref = O.multi_query(O.as_f64(q_np, "bf16"), O.as_f64(kp, "bf16"), O.as_f64(vp, "bf16"),
                         c.otables, c.olens, qs, c.scale)
     got = O.as_f64(to_storage_np(out), "bf16")
