@@ -1274,6 +1274,11 @@ constexpr int kFaRows = 128;     // query rows per workgroup
 constexpr int kFaPos = 64;       // positions per block
 constexpr int kFaKRow = 136;     // bf16 elements per staged K row (128 + 8 pad)
 constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad)
+#ifndef PA_FA_BUFS
+#define PA_FA_BUFS 2
+#endif
+constexpr int kFaBufs = PA_FA_BUFS;   // LDS stages of K and V^T
+constexpr float kFaLazy = 8.0f;       // log2 headroom of the softmax reference maximum
 
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 
@@ -1298,8 +1303,8 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS % 16 == 0 && kFaRows % (2 * 16) == 0 && 16 % G == 0,
                 "whole 4-position groups per block, whole tokens per 16-row tile");
-  __shared__ __align__(16) uint16_t s_k[kFaPos][kFaKRow];
-  __shared__ __align__(16) uint16_t s_vt[D][kFaVRow];
+  __shared__ __align__(16) uint16_t s_kb[kFaBufs][kFaPos][kFaKRow];
+  __shared__ __align__(16) uint16_t s_vtb[kFaBufs][D][kFaVRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1348,6 +1353,22 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
   }
   // every row of this wave sees positions below vis_w (its first row's token)
   const int vis_w = L - tq + min(roww, rows - 1) / G + 1;
+  // a negative softmax scale is folded into the sign of q, so the scale
+  // applied to the scores is never negative
+  const float qs = fabsf(a.qscale);
+  if (a.qscale < 0.0f) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        uint4 u = __builtin_bit_cast(uint4, qop[rt][s2]);
+        u.x ^= 0x80008000u;
+        u.y ^= 0x80008000u;
+        u.z ^= 0x80008000u;
+        u.w ^= 0x80008000u;
+        qop[rt][s2] = __builtin_bit_cast(bf16x8_t, u);
+      }
+  }
 
   // loaders: K thread = (token group tk, 16-byte dim chunk dk), V thread =
   // (token group tv, dim chunk dv); each moves 4 consecutive positions
@@ -1358,23 +1379,41 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * kHeadBytes;
   const int64_t trow = (int64_t)i * a.max_blocks;
   uint4 kreg[4], vreg[4];
-  auto fetch = [&](int blk) {
+  // physical blocks of this thread's K and V positions in block `blk`, read
+  // one block ahead of the K/V loads that use them and range-checked only
+  // there (a check at the read would make the wave wait for every load
+  // issued before it)
+  auto block_ids = [&](int blk, int& idk, int& idv) {
     const int pk = blk * kFaPos + 4 * tk, pv = blk * kFaPos + 4 * tv;
-    const char* kp = nullptr;
-    const char* vp = nullptr;
-    if (pk < npos)
-      kp = kbase + (int64_t)checked_id(a.block_tables, a.num_blocks, trow, pk / BS) * blk_bytes +
-           (pk % BS) * ROW + 16 * dk;
-    if (pv < npos)
-      vp = vbase + (int64_t)checked_id(a.block_tables, a.num_blocks, trow, pv / BS) * blk_bytes +
-           (pv % BS) * ROW + 16 * dv;
+    idk = pk < npos ? a.block_tables[trow + pk / BS] : 0;
+    idv = pv < npos ? a.block_tables[trow + pv / BS] : 0;
+  };
+  auto fetch = [&](int blk, int idk, int idv) {
+    const int pk = blk * kFaPos + 4 * tk, pv = blk * kFaPos + 4 * tv;
+    if ((unsigned)idk >= (unsigned)a.num_blocks || (unsigned)idv >= (unsigned)a.num_blocks) {
+      flag_error(kErrBlockId);
+      idk = (unsigned)idk >= (unsigned)a.num_blocks ? 0 : idk;
+      idv = (unsigned)idv >= (unsigned)a.num_blocks ? 0 : idv;
+    }
+    const char* kp = kbase + (int64_t)idk * blk_bytes + (pk % BS) * ROW + 16 * dk;
+    const char* vp = vbase + (int64_t)idv * blk_bytes + (pv % BS) * ROW + 16 * dv;
+    if ((blk + 1) * kFaPos <= npos) {      // every position of the block is cached
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      kreg[r] = pk + r < npos ? ld16(kp, r * ROW) : make_uint4(0, 0, 0, 0);
-      vreg[r] = pv + r < npos ? ld16(vp, r * ROW) : make_uint4(0, 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        kreg[r] = ld16(kp, r * ROW);
+        vreg[r] = ld16(vp, r * ROW);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kreg[r] = pk + r < npos ? ld16(kp, r * ROW) : make_uint4(0, 0, 0, 0);
+        vreg[r] = pv + r < npos ? ld16(vp, r * ROW) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
+    uint16_t(*s_k)[kFaKRow] = s_kb[buf];
+    uint16_t(*s_vt)[kFaVRow] = s_vtb[buf];
 #pragma unroll
     for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&s_k[4 * tk + r][8 * dk]) = kreg[r];
     const int slot = fa_vt_slot(4 * tv);
@@ -1400,12 +1439,35 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  fetch(0);
+  int idk, idv;
+  block_ids(0, idk, idv);
+  fetch(0, idk, idv);
+  if (nblk > 1) block_ids(1, idk, idv);
+#if PA_FA_BUFS == 2
+  // two LDS buffers: block b + 1 is staged while others may still compute
+  // block b, so one barrier per block suffices
+  stage(0);
+  if (nblk > 1) {
+    fetch(1, idk, idv);
+    if (nblk > 2) block_ids(2, idk, idv);
+  }
+  __syncthreads();
+#endif
   for (int blk = 0; blk < nblk; ++blk) {
+#if PA_FA_BUFS == 2
+    const uint16_t(*s_k)[kFaKRow] = s_kb[blk & 1];
+    const uint16_t(*s_vt)[kFaVRow] = s_vtb[blk & 1];
+#else
     if (blk > 0) __syncthreads();          // every wave is done with the previous block
-    stage();
+    stage(0);
     __syncthreads();
-    if (blk + 1 < nblk) fetch(blk + 1);
+    if (blk + 1 < nblk) {
+      fetch(blk + 1, idk, idv);
+      if (blk + 2 < nblk) block_ids(blk + 2, idk, idv);
+    }
+    const uint16_t(*s_k)[kFaKRow] = s_kb[0];
+    const uint16_t(*s_vt)[kFaVRow] = s_vtb[0];
+#endif
     const int p0 = blk * kFaPos;
 
     // S^T for the block: sc[rt][sl] = scores of row c (tile rt) at positions
@@ -1432,29 +1494,46 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
     float alpha[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      float sv[16];
+      // scores stay unscaled until the exponent: qs >= 0 (a negative scale
+      // was folded into q's sign), so the row maximum scales with them
       float bm = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
+        for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = sc[rt][sl][r] * a.qscale;
-          const bool ok = full || p0 + 16 * sl + 4 * R + r <= pos_c[rt];
-          sv[4 * sl + r] = ok ? v : -INFINITY;
-          bm = fmaxf(bm, sv[4 * sl + r]);
-        }
+          for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sc[rt][sl][r]);
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            bm = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? fmaxf(bm, sc[rt][sl][r]) : bm;
+      }
       bm = fmaxf(bm, xor_lanes<16>(bm));
       bm = fmaxf(bm, xor_lanes<32>(bm));
-      const float mn = fmaxf(m[rt], bm);
+      // the reference maximum moves only when a score exceeds it by more
+      // than 2^8 (so p <= 256): rows rarely need rescaling after the first
+      // block
+      const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
+      const float mn = bms > m[rt] + kFaLazy ? bms : m[rt];
       alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
       rescale |= alpha[rt] != 1.0f;
       m[rt] = mn;
       float p[16], ps = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - mn);
-        ps += p[e];
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[4 * sl + r] = exp2_fast(fmaf(sc[rt][sl][r], qs, -mn));
+      if (!full) {
+        // masked positions (and every position while the row has none) get 0
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            p[4 * sl + r] = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? p[4 * sl + r] : 0.0f;
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ps += p[e];
       lsum[rt] = lsum[rt] * alpha[rt] + ps;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -1500,6 +1579,18 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
               __builtin_bit_cast(bf16x8_t, plo[rt][st]), vb, acc[rt][t], 0, 0, 0);
         }
       }
+#if PA_FA_BUFS == 2
+    if (blk + 1 < nblk) {
+      // every wave finished block b - 1 before the barrier that ended it, so
+      // its buffer ((b + 1) & 1) is free
+      stage((blk + 1) & 1);
+      if (blk + 2 < nblk) {
+        fetch(blk + 2, idk, idv);
+        if (blk + 3 < nblk) block_ids(blk + 3, idk, idv);
+      }
+    }
+    __syncthreads();
+#endif
   }
   // out[row] = O[row] / l[row]; lane holds rows 4R + r of each tile, dims 16 t + c
 #pragma unroll
