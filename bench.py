@@ -577,9 +577,12 @@ def multi_query_rate(P, torch, dev, W) -> dict:
     hq, hkv, d, bs = 32, 8, 128, 16
     res = {}
     rng = np.random.default_rng(17)
-    cases = {"prefill_chunk_512_of_4096_x16": (np.full(16, 4096), np.full(16, 512)),
-             "speculative_4_x256": (rng.integers(512, 4097, 256), np.full(256, 4))}
-    for name, (lens, tqs) in cases.items():
+    spec_lens = rng.integers(512, 4097, 256)
+    # (lengths, query tokens, split the context into 512-position partitions)
+    cases = {"prefill_chunk_512_of_4096_x16": (np.full(16, 4096), np.full(16, 512), False),
+             "speculative_4_x256": (spec_lens, np.full(256, 4), True),
+             "speculative_4_x256_unsplit": (spec_lens, np.full(256, 4), False)}
+    for name, (lens, tqs, split) in cases.items():
         B = len(lens)
         nblk = [-(-int(L) // bs) for L in lens]
         nb = int(sum(nblk) * 1.1) + 1
@@ -599,7 +602,12 @@ def multi_query_rate(P, torch, dev, W) -> dict:
         args = (q, kp, vp, torch.from_numpy(tab).to(dev),
                 torch.from_numpy(lens.astype(np.int32)).to(dev), torch.from_numpy(qs).to(dev),
                 1.0 / math.sqrt(d), out)
-        kw = dict(max_seq_len=int(lens.max()), max_query_len=int(tqs.max()))
+        kw = dict(max_seq_len=int(lens.max()), max_query_len=int(tqs.max()), split=split)
+        if split:
+            shape = P.MultiQueryShape(B, hq, hkv, d, bs, nb, maxb, int(lens.max()),
+                                      int(tqs.max()), T, P.PA_BF16)
+            kw["workspace"] = torch.empty(max(16, P.pa_multi_query_workspace_bytes(shape)),
+                                          dtype=torch.uint8, device=dev)
         for _ in range(2):
             P.pa_multi_query(*args, **kw)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

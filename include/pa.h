@@ -209,6 +209,36 @@ pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool
                            const int32_t* query_start, float scale, void* out,
                            const pa_multi_query_shape_t* shape, void* stream);
 
+/* Bytes of workspace pa_multi_query_split needs for `shape` with context
+ * partitions of `partition_tokens` positions (0 = 512): per query row
+ * (token, query head) and partition, the (max, exp-sum) pair in fp32 and
+ * the normalised partial output in bf16. 0 if nothing would be split or the
+ * arguments are invalid (partition_tokens must be a positive multiple of
+ * 16). */
+size_t pa_multi_query_workspace_bytes(const pa_multi_query_shape_t* shape,
+                                      int32_t partition_tokens);
+
+/*
+ * pa_multi_query_split — pa_multi_query with the context split into
+ * partitions of `partition_tokens` positions for chunks of few query rows
+ * (under 128 per KV head: speculative tokens), so that a sequence's context
+ * is walked by many workgroups at once; a second kernel merges the
+ * partitions' softmax statistics and outputs exactly (log-sum-exp) in fp32.
+ * Larger chunks already have enough rows in flight and run unsplit, as in
+ * pa_multi_query. Same result (to rounding) and arguments as
+ * pa_multi_query, plus:
+ *   partition_tokens  positions per partition, a positive multiple of 16,
+ *                     or 0 for 512
+ *   workspace         [dev] >= pa_multi_query_workspace_bytes(shape,
+ *                     partition_tokens) bytes, 16-byte aligned (PA_EWORKSPACE
+ *                     otherwise); caller-owned, overwritten
+ */
+pa_status_t pa_multi_query_split(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 const int32_t* query_start, float scale, void* out,
+                                 const pa_multi_query_shape_t* shape, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * pa_reshape_and_cache — write new tokens' K and V rows into their slots.
  *

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16", "PA_DEVERR_BLOCK_ID", "PA_DEVERR_SEQ_LEN",
-    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "MultiQueryShape", "pa_multi_query",
+    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_decode_e4m3", "pa_reshape_and_cache_e4m3",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
@@ -41,7 +41,8 @@ _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
 EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
-    "pa_status_str", "pa_multi_query", "pa_decode_e4m3", "pa_decode_partition_e4m3",
+    "pa_status_str", "pa_multi_query", "pa_multi_query_workspace_bytes",
+    "pa_multi_query_split", "pa_decode_e4m3", "pa_decode_partition_e4m3",
     "pa_reshape_and_cache_e4m3",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
@@ -83,6 +84,9 @@ _SIGS = {
     "pa_swap_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _vp]),
     "pa_multi_query": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                               ctypes.POINTER(MultiQueryShape), _vp]),
+    "pa_multi_query_workspace_bytes": (_sz, [ctypes.POINTER(MultiQueryShape), _i32]),
+    "pa_multi_query_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                    ctypes.POINTER(MultiQueryShape), _i32, _vp, _sz, _vp]),
     "pa_decode_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
                               ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
     "pa_decode_partition_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
@@ -287,10 +291,18 @@ def pa_reshape_and_cache_e4m3(k, v, slot_mapping, k_pool, v_pool, k_scale, v_sca
     _check(st, "pa_reshape_and_cache_e4m3")
 
 
+def pa_multi_query_workspace_bytes(shape: MultiQueryShape, partition_tokens: int = 0) -> int:
+    return int(lib().pa_multi_query_workspace_bytes(ctypes.byref(shape), int(partition_tokens)))
+
+
 def pa_multi_query(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out, *,
-                   max_seq_len, max_query_len, stream=None):
+                   max_seq_len, max_query_len, stream=None, split=False, partition_tokens=0,
+                   workspace=None):
     """Attention of several query tokens per sequence (include/pa.h
-    pa_multi_query). q, out [T, Hq, D] bf16; query_start int32 [B+1]."""
+    pa_multi_query; with split=True, pa_multi_query_split over context
+    partitions of partition_tokens positions, the workspace allocated here
+    unless a large enough uint8 device tensor is passed).
+    q, out [T, Hq, D] bf16; query_start int32 [B+1]."""
     torch = _torch()
     dev = q.device
     _need(q, "q", dtype=torch.bfloat16, dim=3)
@@ -309,11 +321,24 @@ def pa_multi_query(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale
         raise ValueError("batch mismatch")
     shape = MultiQueryShape(B, hq, hkv, d, bs, nb, block_tables.shape[1], int(max_seq_len),
                             int(max_query_len), T, PA_BF16)
-    st = lib().pa_multi_query(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                              block_tables.data_ptr(), seq_lens.data_ptr(), query_start.data_ptr(),
-                              ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
-                              _stream_ptr(stream, dev))
-    _check(st, "pa_multi_query")
+    if not split:
+        st = lib().pa_multi_query(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                  block_tables.data_ptr(), seq_lens.data_ptr(),
+                                  query_start.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
+                                  ctypes.byref(shape), _stream_ptr(stream, dev))
+        _check(st, "pa_multi_query")
+        return out
+    need = pa_multi_query_workspace_bytes(shape, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+    st = lib().pa_multi_query_split(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                    block_tables.data_ptr(), seq_lens.data_ptr(),
+                                    query_start.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
+                                    ctypes.byref(shape), int(partition_tokens),
+                                    workspace.data_ptr(), workspace.numel(),
+                                    _stream_ptr(stream, dev))
+    _check(st, "pa_multi_query_split")
     return out
 
 

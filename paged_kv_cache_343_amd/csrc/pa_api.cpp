@@ -26,6 +26,7 @@ struct Plan {
   int group = 0;
   size_t ml_bytes = 0;    // partial (max, sum) region
   size_t o_bytes = 0;     // partial output region
+  bool part_half = false; // partial outputs in bf16
   pa::DecodeKey key{};
 };
 
@@ -73,7 +74,8 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   const size_t recs = (size_t)s->num_seqs * s->num_kv_heads * plan->max_parts;
   if (plan->max_parts > 1) {
     plan->ml_bytes = round_up(recs * pa::kMlRecord * sizeof(float), 256);
-    plan->o_bytes = round_up(rows * (size_t)s->head_dim * elem_bytes(s->dtype), 256);
+    plan->part_half = s->dtype == PA_BF16 && pt >= pa::kHalfPartialMinTokens;
+    plan->o_bytes = round_up(rows * (size_t)s->head_dim * (plan->part_half ? 2 : 4), 256);
   }
   return PA_OK;
 }
@@ -102,6 +104,7 @@ pa_status_t fill_args(const void* q, const void* k_pool, const void* v_pool,
                        : nullptr;
   a->qscale = scale * 1.4426950408889634f;  // log2(e): scores kept in log2 units
   a->out_scale = 1.0f;
+  a->part_half = plan.part_half ? 1 : 0;
   a->num_seqs = s->num_seqs;
   a->num_q_heads = s->num_q_heads;
   a->num_kv_heads = s->num_kv_heads;
@@ -214,6 +217,7 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
   a.out = out;
   a.part_ml = static_cast<float*>(workspace);
   a.part_o = static_cast<void*>(static_cast<char*>(workspace) + plan.ml_bytes);
+  a.part_half = plan.part_half ? 1 : 0;
   a.num_seqs = shape->num_seqs;
   a.num_q_heads = shape->num_q_heads;
   a.num_kv_heads = shape->num_kv_heads;
@@ -227,19 +231,57 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
                                            static_cast<hipStream_t>(stream)));
 }
 
-pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool,
-                           const int32_t* block_tables, const int32_t* seq_lens,
-                           const int32_t* query_start, float scale, void* out,
-                           const pa_multi_query_shape_t* s, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates a multi-query shape (not its pointers).
+pa_status_t check_mq_shape(const pa_multi_query_shape_t* s) {
   if (!s) return PA_EINVAL;
   if (s->num_seqs < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->num_blocks <= 0 ||
       s->max_blocks_per_seq <= 0 || s->max_seq_len < 0 || s->max_query_len < 0 ||
       s->num_tokens < 0 || s->block_size <= 0 || s->head_dim <= 0)
     return PA_EINVAL;
   if (s->num_q_heads % s->num_kv_heads != 0 || elem_bytes(s->dtype) == 0) return PA_EINVAL;
-  const int group = s->num_q_heads / s->num_kv_heads;
-  if (!pa::multi_query_supported(s->dtype, s->head_dim, s->block_size, group))
+  if (!pa::multi_query_supported(s->dtype, s->head_dim, s->block_size,
+                                 s->num_q_heads / s->num_kv_heads))
     return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+struct MqSplit {
+  int part_tokens = 0;   // 0: no split
+  int max_parts = 1;
+  bool part_half = false;
+  size_t ml_bytes = 0, o_bytes = 0;
+};
+
+// Partition plan of pa_multi_query_split (partition_tokens 0 = the default).
+pa_status_t mq_split_plan(const pa_multi_query_shape_t* s, int32_t partition_tokens,
+                          MqSplit* sp) {
+  pa_status_t st = check_mq_shape(s);
+  if (st != PA_OK) return st;
+  const int pt = partition_tokens == 0 ? kDefaultPartitionTokens : partition_tokens;
+  if (pt <= 0 || pt % 16 != 0) return PA_EINVAL;
+  sp->part_tokens = pt;
+  sp->max_parts = s->max_seq_len == 0 ? 1 : (s->max_seq_len + pt - 1) / pt;
+  if (pa::multi_query_tiled(s->num_q_heads / s->num_kv_heads, s->max_query_len))
+    sp->max_parts = 1;   // the tiled kernel never splits
+  if (sp->max_parts > 1) {
+    const size_t rows = (size_t)s->num_tokens * s->num_q_heads * sp->max_parts;
+    sp->part_half = pt >= pa::kHalfPartialMinTokens;
+    sp->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
+    sp->o_bytes = round_up(rows * (size_t)s->head_dim * (sp->part_half ? 2 : 4), 256);
+  }
+  return PA_OK;
+}
+
+pa_status_t multi_query_impl(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             const int32_t* query_start, float scale, void* out,
+                             const pa_multi_query_shape_t* s, const MqSplit& sp,
+                             void* workspace, void* stream) {
+  const int group = s->num_q_heads / s->num_kv_heads;
   if (!std::isfinite(scale)) return PA_EINVAL;
   if (s->num_seqs == 0 || s->num_tokens == 0 || s->max_query_len == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !query_start || !out)
@@ -264,8 +306,53 @@ pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool
   a.len_cap = (int)(table_cap < s->max_seq_len ? table_cap : s->max_seq_len);
   a.max_query_len = s->max_query_len;
   a.num_tokens = s->num_tokens;
+  a.part_tokens = 0;
+  a.max_parts = 1;
+  if (sp.max_parts > 1) {
+    a.part_tokens = sp.part_tokens;
+    a.max_parts = sp.max_parts;
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = static_cast<char*>(workspace) + sp.ml_bytes;
+    a.part_half = sp.part_half ? 1 : 0;
+  }
   return from_hip(pa::launch_multi_query(s->block_size, group, a,
                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* query_start, float scale, void* out,
+                           const pa_multi_query_shape_t* s, void* stream) {
+  pa_status_t st = check_mq_shape(s);
+  if (st != PA_OK) return st;
+  return multi_query_impl(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out, s,
+                          MqSplit{}, nullptr, stream);
+}
+
+size_t pa_multi_query_workspace_bytes(const pa_multi_query_shape_t* shape,
+                                      int32_t partition_tokens) {
+  MqSplit sp;
+  if (mq_split_plan(shape, partition_tokens, &sp) != PA_OK) return 0;
+  return sp.ml_bytes + sp.o_bytes;
+}
+
+pa_status_t pa_multi_query_split(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 const int32_t* query_start, float scale, void* out,
+                                 const pa_multi_query_shape_t* shape, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  MqSplit sp;
+  pa_status_t st = mq_split_plan(shape, partition_tokens, &sp);
+  if (st != PA_OK) return st;
+  const size_t need = sp.ml_bytes + sp.o_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PA_EWORKSPACE;
+  return multi_query_impl(q, k_pool, v_pool, block_tables, seq_lens, query_start, scale, out,
+                          shape, sp, workspace, stream);
 }
 
 pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,

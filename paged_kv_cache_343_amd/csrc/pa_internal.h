@@ -20,10 +20,11 @@ struct DecodeArgs {
   void* out;                    // [B][Hq][D]
   float* part_ml;               // [B][Hkv][max_parts][kMlRecord]: per query head of the
                                 //   group, max score (log2 units) then exp-sum; rest 0
-  void* part_o;                 // [B][Hq][max_parts][D]: normalised partial output, in the
-                                //   output dtype
+  void* part_o;                 // [B][Hq][max_parts][D]: normalised partial output, bf16
+                                //   if part_half, else fp32
   float qscale;                 // softmax scale * log2(e) (* k_scale for 8-bit pools)
   float out_scale;              // v_scale for 8-bit pools
+  int32_t part_half;            // partial outputs stored as bf16
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -96,7 +97,19 @@ struct MqArgs {
   int32_t len_cap;              // min(max_seq_len, max_blocks * bs)
   int32_t max_query_len;
   int32_t num_tokens;           // T
+  int32_t part_tokens;          // context partition length (0: one partition)
+  int32_t max_parts;            // partitions of the longest context (1 if unsplit)
+  float* part_ml;               // [T][Hq][max_parts][2]: max score (log2 units), exp-sum
+  void* part_o;                 // [T][Hq][max_parts][D]: normalised partial output, bf16
+                                //   if part_half, else fp32
+  int32_t part_half;
 };
+
+// Partial outputs of split-context attention are kept in bf16 when the
+// partitions are at least this long (each is then an average over many
+// positions, far from the size of single values) and the output is bf16;
+// otherwise in fp32.
+constexpr int kHalfPartialMinTokens = 256;
 
 // Kernel selection key for pa_decode_partition.
 struct DecodeKey {
@@ -118,6 +131,9 @@ hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream);
 hipError_t launch_reshape_and_cache_e4m3(const CacheArgs8& args, hipStream_t stream);
 bool multi_query_supported(int dtype, int head_dim, int block_size, int group);
 hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream);
+// True if chunks of up to max_query_len tokens run on the workgroup-tiled
+// kernel (which never splits the context).
+bool multi_query_tiled(int group, int max_query_len);
 hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream);
 // Synchronises `stream`, returns the device error word and clears it.
 hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);

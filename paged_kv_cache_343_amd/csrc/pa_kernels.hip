@@ -343,10 +343,15 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
       store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
                 o[3] * inv);
     } else {
-      // the partial output is stored in the output type; the merge of the
-      // partitions runs in fp32
-      store4<T>(reinterpret_cast<T*>(a.part_o) + (row * a.max_parts + wk.j) * D + d0, o[0] * inv,
-                o[1] * inv, o[2] * inv, o[3] * inv);
+      // the partial output is stored in bf16 or fp32 (see part_half); the
+      // merge of the partitions runs in fp32
+      const int64_t po = (row * a.max_parts + wk.j) * D + d0;
+      if (a.part_half)
+        store4<uint16_t>(reinterpret_cast<uint16_t*>(a.part_o) + po, o[0] * inv, o[1] * inv,
+                         o[2] * inv, o[3] * inv);
+      else
+        store4<float>(reinterpret_cast<float*>(a.part_o) + po, o[0] * inv, o[1] * inv,
+                      o[2] * inv, o[3] * inv);
     }
   }
   // (max, exp-sum) of every head of the group: one full 128-byte record per
@@ -895,7 +900,13 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   // record of partition j: ml[j * kMlRecord] = (max, exp-sum) of this head
   const float* ml = a.part_ml +
                     ((int64_t)i * a.num_kv_heads + hq / G) * a.max_parts * kMlRecord + 2 * (hq % G);
-  const T* po = reinterpret_cast<const T*>(a.part_o) + ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
+  const int64_t po = ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
+  auto load_part = [&](int64_t off, float (&f)[D / 64]) {
+    if (a.part_half)
+      load_elems<uint16_t, D / 64>(reinterpret_cast<const uint16_t*>(a.part_o) + po + off, f);
+    else
+      load_elems<float, D / 64>(reinterpret_cast<const float*>(a.part_o) + po + off, f);
+  };
   const int lane = threadIdx.x & 63;
   constexpr int DPL = D / 64;
   float o[DPL];
@@ -911,7 +922,7 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
     for (int j = 0; j < kReduceFast; ++j) {
       // partitions past np read partition 0's slice (in bounds) and drop it
       float f[DPL];
-      load_elems<T, DPL>(po + (int64_t)(j < np ? j : 0) * D + lane * DPL, f);
+      load_part((int64_t)(j < np ? j : 0) * D + lane * DPL, f);
 #pragma unroll
       for (int k = 0; k < DPL; ++k) v[j][k] = j < np ? f[k] : 0.0f;
     }
@@ -948,7 +959,7 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
       const float wj =
           ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
       float f[DPL];
-      load_elems<T, DPL>(po + (int64_t)j * D + lane * DPL, f);
+      load_part((int64_t)j * D + lane * DPL, f);
 #pragma unroll
       for (int k = 0; k < DPL; ++k) o[k] = fmaf(wj, f[k], o[k]);
     }
@@ -1096,7 +1107,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = lane >> 4, c = lane & 15;
   const int i = blockIdx.z, g = blockIdx.y;
-  const int tile = blockIdx.x * kMqWaves + w;
+  // units (tile, context partition), partition fastest, one per wave
+  const int unit = blockIdx.x * kMqWaves + w;
+  const int part = unit % a.max_parts;
+  const int tile = unit / a.max_parts;
 
   // validate the sequence's length and query range (device-resident)
   const int L = a.seq_lens[i];
@@ -1112,7 +1126,13 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
   const int row0 = tile * 16;
   const int t_last = min(tq - 1, (row0 + 15) / G);
   const int npos = L - tq + t_last + 1;          // positions the tile's last token sees
-  const int nch = (npos + 15) / 16;
+  // this wave's context partition: positions [pos0, pos1)
+  const int nparts = a.part_tokens > 0 ? (npos + a.part_tokens - 1) / a.part_tokens : 1;
+  if (part >= nparts) return;
+  const int pos0 = a.part_tokens > 0 ? part * a.part_tokens : 0;
+  const int pos1 = a.part_tokens > 0 ? min(npos, pos0 + a.part_tokens) : npos;
+  const int ch0 = pos0 / 16;
+  const int nch = (pos1 + 15) / 16 - ch0;
 
   // this lane's query row (column of S^T): token tc, head hc
   const int rc = row0 + c;
@@ -1146,15 +1166,16 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
   for (int win = 0; win < nch; win += 64) {
     const int cnt = min(64, nch - win);
     int ids = 0;
-    if (lane < cnt) ids = checked_id(a.block_tables, a.num_blocks, trow_base, ((win + lane) * 16) / BS);
+    if (lane < cnt)
+      ids = checked_id(a.block_tables, a.num_blocks, trow_base, ((ch0 + win + lane) * 16) / BS);
     auto issue = [&](KVChunk& buf, int t) {
       const int phys = __builtin_amdgcn_readlane(ids, t);
-      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, ((win + t) * 16) % BS, k_off, v_off,
-                        true);
+      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, ((ch0 + win + t) * 16) % BS, k_off,
+                        v_off, true);
     };
     KVChunk b0, b1;
     auto step = [&](KVChunk& cur, int t) {
-      const int chunk = win + t;
+      const int chunk = ch0 + win + t;
       const int tok0 = chunk * 16;
       // stage V rows of this chunk (tokens 4R + jj, dims 8c ..) in LDS; rows
       // past the tile's last position are zeros, so that slack slots (which
@@ -1234,19 +1255,93 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
       if (++t >= cnt) break;
     }
   }
-  // out[row] = O[row] / l[row]; lane holds rows 4R + r, dims 16 t + c
+  // out[row] = O[row] / l[row]; lane holds rows 4R + r, dims 16 t + c. With
+  // several partitions: the normalised partial output (bf16) and the row's
+  // (max, exp-sum), merged by multi_query_reduce.
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float lr = __shfl(lsum, 4 * R + r);
+    const float mr = __shfl(m, 4 * R + r);
     const int row = row0 + 4 * R + r;
     if (row >= rows) continue;
     const int t = row / G, h = row % G;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
-                    ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + c;
+    const int64_t qrow = (int64_t)(q0 + t) * a.num_q_heads + g * G + h;
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+    if (nparts == 1 || a.part_half) {
+      uint16_t* dst = nparts == 1 ? reinterpret_cast<uint16_t*>(a.out) + qrow * D + c
+                                  : reinterpret_cast<uint16_t*>(a.part_o) +
+                                        (qrow * a.max_parts + part) * D + c;
 #pragma unroll
-    for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[t2][r] * inv);
+      for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[t2][r] * inv);
+    } else {
+      float* dst = reinterpret_cast<float*>(a.part_o) + (qrow * a.max_parts + part) * D + c;
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = acc[t2][r] * inv;
+    }
+    if (nparts > 1 && c == 0) {
+      float* ml = a.part_ml + (qrow * a.max_parts + part) * 2;
+      ml[0] = mr;
+      ml[1] = lr;
+    }
   }
+}
+
+// Merge of the context partitions of pa_multi_query's split form: one wave
+// per (sequence, query token, query head) row, kMqWaves rows per workgroup;
+// the partition count of a row is that of its 16-row tile, as in
+// multi_query_mfma.
+template <int G>
+__global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
+  constexpr int D = 128, DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.y;
+  const int lr = blockIdx.x * kMqWaves + (threadIdx.x >> 6);   // row within the sequence
+  const int L = a.seq_lens[i];
+  const int q0 = a.query_start[i], q1 = a.query_start[i + 1];
+  const int tq = q1 - q0;
+  if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
+      tq > a.max_query_len)
+    return;                                      // flagged by multi_query_mfma
+  if (lr >= tq * a.num_q_heads) return;
+  const int t = lr / a.num_q_heads, hq = lr % a.num_q_heads;
+  const int row0 = ((t * G + hq % G) / 16) * 16;  // first row of its tile
+  const int t_last = min(tq - 1, (row0 + 15) / G);
+  const int npos = L - tq + t_last + 1;
+  const int np = (npos + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+  const int64_t qrow = (int64_t)(q0 + t) * a.num_q_heads + hq;
+  const float* ml = a.part_ml + qrow * a.max_parts * 2;
+  const int64_t po = qrow * a.max_parts * D;
+  float mj = -INFINITY, lj = 0.0f;
+  for (int j = lane; j < np; j += 64) {
+    const float m2 = ml[2 * j], l2 = ml[2 * j + 1];
+    const float big = fmaxf(mj, m2);
+    lj = lj * merge_weight(mj, big) + l2 * merge_weight(m2, big);
+    mj = big;
+  }
+  float big = mj;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
+  float wsum = lj * merge_weight(mj, big);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  float o[DPL] = {0.0f, 0.0f};
+  for (int j = 0; j < np; ++j) {
+    const float wj = ml[2 * j + 1] * merge_weight(ml[2 * j], big);
+    float f[DPL];
+    if (a.part_half)
+      load_elems<uint16_t, DPL>(reinterpret_cast<const uint16_t*>(a.part_o) + po + (int64_t)j * D +
+                                    lane * DPL, f);
+    else
+      load_elems<float, DPL>(reinterpret_cast<const float*>(a.part_o) + po + (int64_t)j * D +
+                                 lane * DPL, f);
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = fmaf(wj, f[k], o[k]);
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + qrow * D + lane * DPL;
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) out[k] = bf16_bits(o[k] * inv);
 }
 
 
@@ -1759,6 +1854,8 @@ static PartitionKernelMq pick_mq(int group) {
   }
 }
 
+bool multi_query_tiled(int group, int max_query_len);
+
 template <int BS>
 static PartitionKernelMq pick_fa(int group) {
   switch (group) {
@@ -1772,7 +1869,7 @@ static PartitionKernelMq pick_fa(int group) {
 }
 
 hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream) {
-  if ((int64_t)args.max_query_len * group >= kFaRows) {
+  if (multi_query_tiled(group, args.max_query_len)) {
     // many rows per (sequence, KV head): workgroup tiles sharing staged K/V
     PartitionKernelMq kern = nullptr;
     switch (block_size) {
@@ -1800,14 +1897,35 @@ hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hip
     default: break;
   }
   if (!kern) return hipErrorInvalidValue;
+  if (args.max_parts < 1 || (args.max_parts > 1 && args.part_tokens <= 0))
+    return hipErrorInvalidValue;
   const int64_t tiles = ((int64_t)args.max_query_len * group + 15) / 16;
-  const int64_t gx = (tiles + kMqWaves - 1) / kMqWaves;
+  const int64_t gx = (tiles * args.max_parts + kMqWaves - 1) / kMqWaves;
   if (gx <= 0 || args.num_seqs <= 0) return hipSuccess;
   if (gx > 0x7fffffff || args.num_kv_heads > 65535 || args.num_seqs > 65535)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)args.num_kv_heads, (unsigned)args.num_seqs),
                      dim3(kMqWaves * 64), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || args.max_parts == 1) return e;
+  PartitionKernelMq red = nullptr;
+  switch (group) {
+    case 1: red = multi_query_reduce<1>; break;
+    case 2: red = multi_query_reduce<2>; break;
+    case 4: red = multi_query_reduce<4>; break;
+    case 8: red = multi_query_reduce<8>; break;
+    case 16: red = multi_query_reduce<16>; break;
+    default: return hipErrorInvalidValue;
+  }
+  const int64_t rx = ((int64_t)args.max_query_len * args.num_q_heads + kMqWaves - 1) / kMqWaves;
+  if (rx > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(red, dim3((unsigned)rx, (unsigned)args.num_seqs), dim3(kMqWaves * 64), 0,
+                     stream, args);
   return hipGetLastError();
+}
+
+bool multi_query_tiled(int group, int max_query_len) {
+  return (int64_t)max_query_len * group >= kFaRows;
 }
 
 hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream) {

@@ -55,10 +55,15 @@ def test_workspace_bytes():
     parts = 8
     rows = 4 * 32 * parts          # (sequence, query head, partition) partial outputs
     recs = 4 * 8 * parts           # (sequence, KV head, partition) 128-byte statistics records
-    for dtype, eb in ((P.PA_BF16, 2), (P.PA_F32, 4)):   # partial outputs in the output dtype
-        s = _shape(max_seq_len=4096, max_blocks_per_seq=256, dtype=dtype)
-        want = -(-recs * 128 // 256) * 256 + -(-rows * 128 * eb // 256) * 256
+    # partial outputs: bf16 for bf16 runs with partitions of >= 256 positions, else fp32
+    for dtype, pt, eb in ((P.PA_BF16, 0, 2), (P.PA_F32, 0, 4), (P.PA_BF16, 256, 2)):
+        s = _shape(max_seq_len=4096, max_blocks_per_seq=256, dtype=dtype, partition_tokens=pt)
+        n = 4096 // (pt or 512)
+        want = (-(-4 * 8 * n * 128 // 256) * 256 + -(-4 * 32 * n * 128 * eb // 256) * 256)
         assert P.pa_decode_workspace_bytes(s) == want
+    s = _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=128)
+    assert P.pa_decode_workspace_bytes(s) == (-(-4 * 8 * 32 * 128 // 256) * 256 +
+                                             -(-4 * 32 * 32 * 128 * 4 // 256) * 256)
     assert P.pa_decode_workspace_bytes(_shape(num_q_heads=30)) == 0          # Hq % Hkv
     assert P.pa_decode_workspace_bytes(_shape(head_dim=96)) == 0
     assert P.pa_decode_workspace_bytes(_shape(partition_tokens=24)) == 0      # not a multiple of bs
@@ -110,3 +115,25 @@ def test_status_strings():
     lib = P.lib()
     for code in range(8):
         assert lib.pa_status_str(code).decode().startswith("PA_")
+
+
+def test_multi_query_workspace_bytes():
+    def shape(**kw):
+        base = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                    num_blocks=100, max_blocks_per_seq=256, max_seq_len=4096, max_query_len=4,
+                    num_tokens=16, dtype=P.PA_BF16)
+        base.update(kw)
+        return P.MultiQueryShape(*[base[k] for k in (
+            "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
+            "max_blocks_per_seq", "max_seq_len", "max_query_len", "num_tokens", "dtype")])
+    rows = 16 * 32 * 8                 # (token, query head) rows x 8 partitions of 512
+    want = -(-rows * 2 * 4 // 256) * 256 + -(-rows * 128 * 2 // 256) * 256
+    assert P.pa_multi_query_workspace_bytes(shape()) == want
+    assert P.pa_multi_query_workspace_bytes(shape(), 512) == want
+    rows16 = 16 * 32 * 256             # 16-position partitions: fp32 partial outputs
+    assert P.pa_multi_query_workspace_bytes(shape(), 16) == (
+        -(-rows16 * 8 // 256) * 256 + -(-rows16 * 128 * 4 // 256) * 256)
+    assert P.pa_multi_query_workspace_bytes(shape(max_seq_len=512)) == 0    # one partition
+    assert P.pa_multi_query_workspace_bytes(shape(max_query_len=32)) == 0   # 128 rows: tiled
+    assert P.pa_multi_query_workspace_bytes(shape(), 24) == 0               # not a multiple of 16
+    assert P.pa_multi_query_workspace_bytes(shape(num_q_heads=30)) == 0     # Hq % Hkv

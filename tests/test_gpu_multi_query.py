@@ -25,7 +25,8 @@ def dev():
 FA_ROWS = 128
 
 
-def _run(dev, hq, hkv, bs, lens, tqs, seed=301, poison_out=True, mql=None):
+def _run(dev, hq, hkv, bs, lens, tqs, seed=301, poison_out=True, mql=None, split=False,
+         partition_tokens=0):
     w = W.Workload("mq", seed, 0, hq, hkv, 128, bs, "bf16", ("fixed", 0), ("factor", 1.3))
     c = build(w, dev, lens=lens, append=False)
     rng = np.random.default_rng(seed + 1)
@@ -37,7 +38,8 @@ def _run(dev, hq, hkv, bs, lens, tqs, seed=301, poison_out=True, mql=None):
                      device=dev)
     P.pa_multi_query(q, c.k_pool, c.v_pool, c.tables, c.lens, torch.from_numpy(qs).to(dev),
                      c.scale, out, max_seq_len=c.max_len,
-                     max_query_len=mql if mql is not None else max(1, max(tqs)))
+                     max_query_len=mql if mql is not None else max(1, max(tqs)),
+                     split=split, partition_tokens=partition_tokens)
     torch.cuda.synchronize()
     ref = O.multi_query(O.as_f64(q_np, "bf16"), O.as_f64(c.ok_pool, "bf16"),
                         O.as_f64(c.ov_pool, "bf16"), c.otables, c.olens, qs, c.scale)
@@ -105,8 +107,10 @@ def test_long_chunk_over_long_context(dev):
     check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16", "long chunk")
 
 
-@pytest.mark.parametrize("mql", [20, 64])        # the per-tile kernel, the tiled one
-def test_nan_in_slack_and_unused_blocks_does_not_leak(dev, mql):
+@pytest.mark.parametrize("mql,split", [(20, False), (64, False), (20, True)])
+def test_nan_in_slack_and_unused_blocks_does_not_leak(dev, mql, split):
+    # the per-tile kernel, the tiled one, the per-tile one over 16-position
+    # context partitions
     lens = [5, 37, 100]
     tqs = [5, 6, 20]
     w = W.Workload("mq", 321, 0, 32, 8, 128, 16, "bf16", ("fixed", 0), ("factor", 1.3))
@@ -128,9 +132,41 @@ def test_nan_in_slack_and_unused_blocks_does_not_leak(dev, mql):
     out = torch.empty((int(qs[-1]), 32, 128), dtype=torch.bfloat16, device=dev)
     P.pa_multi_query(to_device(q_np, "bf16", dev), c.k_pool, c.v_pool, c.tables, c.lens,
                      torch.from_numpy(qs).to(dev), c.scale, out, max_seq_len=c.max_len,
-                     max_query_len=mql)
+                     max_query_len=mql, split=split, partition_tokens=16)
     ref = O.multi_query(O.as_f64(q_np, "bf16"), O.as_f64(kp, "bf16"), O.as_f64(vp, "bf16"),
                         c.otables, c.olens, qs, c.scale)
     got = O.as_f64(to_storage_np(out), "bf16")
     assert np.isfinite(got).all()
     check_close(got, ref, "bf16", "nan poison")
+
+
+@pytest.mark.parametrize("partition_tokens", [16, 64, 0])
+@pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (16, 16, 32), (16, 1, 64)])
+def test_split_context_few_rows(dev, hq, hkv, bs, partition_tokens):
+    # speculative-sized chunks: the context is split into partitions merged
+    # by a second kernel (1 to 129 partitions per row here, single-partition
+    # rows written directly)
+    lens = [1, 5, 40, 300, 1100, 17, 64, 2049]
+    tqs = [1, 4, 7, 4, 8, 1, 3, 2]
+    c, q, out, ref = _run(dev, hq, hkv, bs, lens, tqs, seed=331, split=True,
+                          partition_tokens=partition_tokens)
+    assert P.pa_device_errors() == 0
+    check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16",
+                f"split {hq}/{hkv} bs {bs} pt {partition_tokens}")
+
+
+def test_split_context_skips_bad_ranges(dev):
+    # one query head per KV head, so 45 query rows stay on the split path
+    lens = [300, 40, 1000]
+    c, q, out, ref = _run(dev, 8, 8, 16, lens, [4, 4, 4], seed=341, split=True,
+                          partition_tokens=128)
+    check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16", "split 128")
+    # an invalid query range is flagged and its rows stay untouched
+    qs = torch.tensor([0, 4, 4 + 45, 4 + 45 + 4], dtype=torch.int32, device=dev)   # 45 > 40
+    out2 = torch.zeros((53, 8, 128), dtype=torch.bfloat16, device=dev)
+    q2 = torch.zeros((53, 8, 128), dtype=torch.bfloat16, device=dev)
+    P.pa_multi_query(q2, c.k_pool, c.v_pool, c.tables, c.lens, qs, c.scale, out2,
+                     max_seq_len=c.max_len, max_query_len=45, split=True, partition_tokens=64)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == P.PA_DEVERR_QUERY
+    assert torch.count_nonzero(out2[4:49]) == 0
