@@ -580,8 +580,8 @@ def multi_query_rate(P, torch, dev, W) -> dict:
     spec_lens = rng.integers(512, 4097, 256)
     # (lengths, query tokens, split the context into 512-position partitions)
     cases = {"prefill_chunk_512_of_4096_x16": (np.full(16, 4096), np.full(16, 512), False),
-             "speculative_4_x256": (spec_lens, np.full(256, 4), True),
-             "speculative_4_x256_unsplit": (spec_lens, np.full(256, 4), False)}
+             "speculative_4_x256": (spec_lens, np.full(256, 4), False),
+             "speculative_4_x256_split": (spec_lens, np.full(256, 4), True)}
     for name, (lens, tqs, split) in cases.items():
         B = len(lens)
         nblk = [-(-int(L) // bs) for L in lens]

@@ -210,7 +210,7 @@ pa_status_t pa_multi_query(const void* q, const void* k_pool, const void* v_pool
                            const pa_multi_query_shape_t* shape, void* stream);
 
 /* Bytes of workspace pa_multi_query_split needs for `shape` with context
- * partitions of `partition_tokens` positions (0 = 512): per query row
+ * partitions of `partition_tokens` positions (0 = 1024): per query row
  * (token, query head) and partition, the (max, exp-sum) pair in fp32 and
  * the normalised partial output in bf16. 0 if nothing would be split or the
  * arguments are invalid (partition_tokens must be a positive multiple of
@@ -228,7 +228,7 @@ size_t pa_multi_query_workspace_bytes(const pa_multi_query_shape_t* shape,
  * pa_multi_query. Same result (to rounding) and arguments as
  * pa_multi_query, plus:
  *   partition_tokens  positions per partition, a positive multiple of 16,
- *                     or 0 for 512
+ *                     or 0 for 1024
  *   workspace         [dev] >= pa_multi_query_workspace_bytes(shape,
  *                     partition_tokens) bytes, 16-byte aligned (PA_EWORKSPACE
  *                     otherwise); caller-owned, overwritten

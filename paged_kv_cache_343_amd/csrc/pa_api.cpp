@@ -13,6 +13,9 @@
 namespace {
 
 constexpr int kDefaultPartitionTokens = 512;
+// pa_multi_query_split: one wave walks a partition for a whole 16-row tile,
+// so partitions are longer than decode's (measured best on 4-token chunks)
+constexpr int kDefaultMqPartitionTokens = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -261,7 +264,7 @@ pa_status_t mq_split_plan(const pa_multi_query_shape_t* s, int32_t partition_tok
                           MqSplit* sp) {
   pa_status_t st = check_mq_shape(s);
   if (st != PA_OK) return st;
-  const int pt = partition_tokens == 0 ? kDefaultPartitionTokens : partition_tokens;
+  const int pt = partition_tokens == 0 ? kDefaultMqPartitionTokens : partition_tokens;
   if (pt <= 0 || pt % 16 != 0) return PA_EINVAL;
   sp->part_tokens = pt;
   sp->max_parts = s->max_seq_len == 0 ? 1 : (s->max_seq_len + pt - 1) / pt;

@@ -1081,27 +1081,49 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
 //     same dims); lane gets S[row c][tokens 4R .. 4R+3].
 //   causal mask per row, online softmax per row (row c's 16 scores sit in
 //     lanes c, c+16, c+32, c+48: reduced with 16/32-lane swaps).
-//   O += P V (v_mfma_f32_16x16x16_bf16, 8 tiles of 16 dims): A = P exactly
-//     as the softmax leaves it (lane: row c, tokens 4R ..; split into two
-//     bf16 terms, so two products per tile), B = V[tokens
-//     4R .. 4R+3][dim 16t + c], read from the chunk's V rows staged in LDS
-//     (row-major, 272-byte rows so the four 16-lane groups hit different
-//     banks); lane gets O[rows 4R .. 4R+3][dim 16t + c].
+//   O += P V (v_mfma_f32_16x16x32_bf16, 8 tiles of 16 dims) once per pair of
+//     chunks: A = P exactly as the softmax leaves it (lane: row c, positions
+//     4R .. 4R+3 of both chunks = its 8 k-slots; split into two bf16 terms,
+//     so two products per tile), B = V^T[dim 16t + c][the same 8 positions],
+//     one 16-byte read of the pair's V staged transposed in LDS (each lane
+//     writes its 4 positions x 8 dims as 8-byte column pieces); lane gets
+//     O[rows 4R .. 4R+3][dim 16t + c].
 // Each wave owns its LDS buffers and its unit, so waves never wait for one
 // another; K/V of chunk c+1 are issued before chunk c is computed.
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats as a bf16 pair (round to nearest even), low element first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+  const f32x2v_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
+}
+
+// p as two bf16 terms hi + lo (lo = the bf16 rounding of p - hi), 8 values
+// per operand: ~16 significant bits instead of bf16's 8.
+__device__ __forceinline__ void split_bf16x8(const float (&p)[8], uint4& hi, uint4& lo) {
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hb[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+    lb[e] = pack_bf16x2(p[2 * e] - __uint_as_float(hb[e] << 16),
+                        p[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+  }
+  hi = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+  lo = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+}
 
 constexpr int kMqWaves = 4;
-constexpr int kMqLdsRow = 136;   // bf16 elements per staged V row (128 + 8 pad)
+constexpr int kMqVtRow = 40;     // bf16 elements per staged V^T row (32 positions + 8 pad)
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return to_bf16(f); }
 
 template <int BS, int G>
-__global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
+__global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
   constexpr int D = 128, ROW = 256;
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS % 16 == 0 && 16 % G == 0, "whole chunks per block, whole tokens per tile");
-  __shared__ __align__(16) uint16_t s_v[kMqWaves][2][16][kMqLdsRow];
+  __shared__ __align__(16) uint16_t s_vt[kMqWaves][128][kMqVtRow];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1174,76 +1196,110 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_mfma(MqArgs a) {
                         v_off, true);
     };
     KVChunk b0, b1;
-    auto step = [&](KVChunk& cur, int t) {
-      const int chunk = ch0 + win + t;
-      const int tok0 = chunk * 16;
-      // stage V rows of this chunk (tokens 4R + jj, dims 8c ..) in LDS; rows
-      // past the tile's last position are zeros, so that slack slots (which
-      // may hold anything, NaN included) never meet the zero weights
-      uint16_t(*sv)[kMqLdsRow] = s_v[w][chunk & 1];
-      const bool tail = tok0 + 16 > npos;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        uint4 v = cur.v[jj];
-        if (tail && tok0 + 4 * R + jj >= npos) v = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sv[4 * R + jj][8 * c]) = v;
-      }
-      // S^T for the chunk
-      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s2]),
-                                                     qop[s2], sc, 0, 0, 0);
-      float sv4[4];
-      bool ok[4];
+    // chunks go in pairs (32 positions: one P.V step); the first chunk's
+    // scores wait in sc_a while the second is loaded
+    f32x4_t sc_a = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto pair_step = [&](const f32x4_t& s0, const f32x4_t& s1, int tok0, bool has_b) {
+      // lane's 8 scores of row c: positions tok0 + 16h + 4R + r = k-slot 4h + r
+      float sv[8];
       float bm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv4[r] = sc[r] * a.qscale;
-        ok[r] = row_ok && (tok0 + 4 * R + r <= pos_c);
-        bm = ok[r] ? fmaxf(bm, sv4[r]) : bm;
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = (h ? s1[r] : s0[r]) * a.qscale;
+          const bool ok = row_ok && (h == 0 || has_b) && (tok0 + 16 * h + 4 * R + r <= pos_c);
+          sv[4 * h + r] = ok ? v : -INFINITY;
+          bm = fmaxf(bm, sv[4 * h + r]);
+        }
       bm = fmaxf(bm, xor_lanes<16>(bm));
       bm = fmaxf(bm, xor_lanes<32>(bm));
       const float mn = fmaxf(m, bm);
       const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
       m = mn;
-      float p[4], ps = 0.0f;
+      float p[8], ps = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = ok[r] ? exp2_fast(sv4[r] - mn) : 0.0f;
-        ps += p[r];
+      for (int e = 0; e < 8; ++e) {
+        p[e] = sv[e] == -INFINITY ? 0.0f : exp2_fast(sv[e] - mn);
+        ps += p[e];
       }
       ps += xor_lanes<16>(ps);
       ps += xor_lanes<32>(ps);
       lsum = lsum * alpha + ps;
       // rescale output rows 4R + r by their rows' alpha (held by lane 4R + r)
+      if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * R + r);
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * R + r);
 #pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2) acc[t2][r] *= ar;
+          for (int t2 = 0; t2 < 8; ++t2) acc[t2][r] *= ar;
+        }
       }
-      // P enters the matrix cores as two bf16 terms, p = hi + lo (lo = the
-      // bf16 rounding of p - hi), so the weights keep ~16 significant bits
-      // instead of bf16's 8
-      s16x4_t p_hi, p_lo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint16_t hb = bf16_bits(p[r]);
-        p_hi[r] = (short)hb;
-        p_lo[r] = (short)bf16_bits(p[r] - __uint_as_float((uint32_t)hb << 16));
-      }
-      __builtin_amdgcn_wave_barrier();   // LDS rows above are complete (in-order per wave)
+      uint4 phi, plo;
+      split_bf16x8(p, phi, plo);
+      __builtin_amdgcn_wave_barrier();   // the staged V^T rows are complete (in-order per wave)
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) {
-        s16x4_t vb;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vb[j] = (short)sv[4 * R + j][16 * t2 + c];
-        acc[t2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, vb, acc[t2], 0, 0, 0);
-        acc[t2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, vb, acc[t2], 0, 0, 0);
+        const bf16x8_t vb = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[w][16 * t2 + c][8 * R]));
+        acc[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, phi), vb,
+                                                          acc[t2], 0, 0, 0);
+        acc[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, plo), vb,
+                                                          acc[t2], 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
+    };
+    // stage V of half h of the pair transposed: V^T row = dim, slot 8R + 4h + r
+    // holds position 16h + 4R + r; rows past the tile's last position are
+    // zeros, so that slack slots (which may hold anything, NaN included)
+    // never meet the zero weights
+    auto stage_vt = [&](const KVChunk& cur, int h, bool zero) {
+      uint32_t v[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint4 x = zero ? make_uint4(0, 0, 0, 0) : cur.v[r];
+        v[r][0] = x.x;
+        v[r][1] = x.y;
+        v[r][2] = x.z;
+        v[r][3] = x.w;
+      }
+      const int slot = 8 * R + 4 * h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 lo = make_uint2((v[0][e] & 0xffffu) | (v[1][e] << 16),
+                                    (v[2][e] & 0xffffu) | (v[3][e] << 16));
+        const uint2 hi = make_uint2((v[0][e] >> 16) | (v[1][e] & 0xffff0000u),
+                                    (v[2][e] >> 16) | (v[3][e] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&s_vt[w][8 * c + 2 * e][slot]) = lo;
+        *reinterpret_cast<uint2*>(&s_vt[w][8 * c + 2 * e + 1][slot]) = hi;
+      }
+    };
+    auto step = [&](KVChunk& cur, int t) {
+      const int chunk = ch0 + win + t;
+      const int tok0 = chunk * 16;
+      const int h = (win + t) & 1;
+      if (tok0 + 16 > npos) {
+        // zero the rows of this chunk past npos
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (tok0 + 4 * R + jj >= npos) cur.v[jj] = make_uint4(0, 0, 0, 0);
+      }
+      stage_vt(cur, h, false);
+      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[s2]),
+                                                     qop[s2], sc, 0, 0, 0);
+      if (h == 0) {
+        sc_a = sc;
+        if (t + 1 >= cnt) {
+          // a chunk without a partner: its second half is empty
+          stage_vt(cur, 1, true);
+          pair_step(sc_a, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, tok0, false);
+        }
+      } else {
+        pair_step(sc_a, sc, tok0 - 16, true);
+      }
     };
     issue(b0, 0);
     for (int t = 0;;) {
@@ -1375,15 +1431,6 @@ constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad
 constexpr int kFaBufs = PA_FA_BUFS;   // LDS stages of K and V^T
 constexpr float kFaLazy = 8.0f;       // log2 headroom of the softmax reference maximum
 
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-
-// Two floats as a bf16 pair (round to nearest even), low element first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const float2 v = make_float2(lo, hi);
-  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
-  const f32x2v_t f = {v.x, v.y};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
-}
 
 // Slot of position j (0..63) of a block in a staged V^T row: inside each
 // 32-position half, positions 16h + 4R + r go to 8R + 4h + r.

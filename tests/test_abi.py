@@ -128,12 +128,14 @@ def test_multi_query_workspace_bytes():
             "max_blocks_per_seq", "max_seq_len", "max_query_len", "num_tokens", "dtype")])
     rows = 16 * 32 * 8                 # (token, query head) rows x 8 partitions of 512
     want = -(-rows * 2 * 4 // 256) * 256 + -(-rows * 128 * 2 // 256) * 256
-    assert P.pa_multi_query_workspace_bytes(shape()) == want
     assert P.pa_multi_query_workspace_bytes(shape(), 512) == want
+    rows = 16 * 32 * 4                 # default: partitions of 1024
+    assert P.pa_multi_query_workspace_bytes(shape()) == (
+        -(-rows * 2 * 4 // 256) * 256 + -(-rows * 128 * 2 // 256) * 256)
     rows16 = 16 * 32 * 256             # 16-position partitions: fp32 partial outputs
     assert P.pa_multi_query_workspace_bytes(shape(), 16) == (
         -(-rows16 * 8 // 256) * 256 + -(-rows16 * 128 * 4 // 256) * 256)
-    assert P.pa_multi_query_workspace_bytes(shape(max_seq_len=512)) == 0    # one partition
+    assert P.pa_multi_query_workspace_bytes(shape(max_seq_len=1024)) == 0   # one partition
     assert P.pa_multi_query_workspace_bytes(shape(max_query_len=32)) == 0   # 128 rows: tiled
     assert P.pa_multi_query_workspace_bytes(shape(), 24) == 0               # not a multiple of 16
     assert P.pa_multi_query_workspace_bytes(shape(num_q_heads=30)) == 0     # Hq % Hkv
