@@ -67,8 +67,12 @@ typedef enum {
 /* Decode kernel variants (pa_decode_shape_t.variant). */
 #define PA_VARIANT_AUTO 0   /* library's choice for the shape                     */
 #define PA_VARIANT_VALU 1   /* q.K and P.V on the vector ALUs                     */
-#define PA_VARIANT_MFMA 2   /* q.K on matrix cores, P.V on the vector ALUs; bf16,
-                               head_dim 128, group size 1, 2 or 4 only            */
+#define PA_VARIANT_MFMA 2   /* matrix cores; bf16, head_dim 128. Group 1, 2, 4:
+                               q.K on matrix cores, P.V on the vector ALUs (the
+                               default there). Group 8, 16 (block size 16-128):
+                               the multi-token kernel with one token per
+                               sequence, both products on matrix cores (the
+                               default there, ~2.5x the vector kernel)        */
 
 /* Shape of one pa_decode call. */
 typedef struct {
@@ -82,9 +86,10 @@ typedef struct {
   int32_t max_blocks_per_seq; /* row stride (entries) of block_tables          */
   int32_t max_seq_len;        /* host bound on every seq_lens[i]; sizes the
                                  grid and the workspace                        */
-  int32_t partition_tokens;   /* context partition length: 0 = 512, -1 = one
-                                 partition per sequence, else a positive
-                                 multiple of block_size                        */
+  int32_t partition_tokens;   /* context partition length: 0 = automatic (512;
+                                 1024 when G is 8 or 16 on the matrix cores),
+                                 -1 = one partition per sequence, else a
+                                 positive multiple of block_size               */
   int32_t dtype;              /* pa_dtype_t                                    */
   int32_t variant;            /* PA_VARIANT_*                                  */
 } pa_decode_shape_t;

@@ -30,15 +30,25 @@ struct Plan {
   size_t ml_bytes = 0;    // partial (max, sum) region
   size_t o_bytes = 0;     // partial output region
   bool part_half = false; // partial outputs in bf16
+  bool mq_route = false;  // runs on the multi-token per-tile kernel
   pa::DecodeKey key{};
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int auto_variant(const pa_decode_shape_t& s, int group) {
-  if (s.dtype == PA_BF16 && s.head_dim == 128 && (group == 1 || group == 2 || group == 4))
+  if (s.dtype == PA_BF16 && s.head_dim == 128 &&
+      (group == 1 || group == 2 || group == 4 || group == 8 || group == 16))
     return PA_VARIANT_MFMA;
   return PA_VARIANT_VALU;
+}
+
+// Matrix-core decode with 8 or 16 query heads per KV head runs on the
+// multi-token per-tile kernel (one 16-row tile = the whole group, both
+// products on the matrix cores) in its one-token-per-sequence mode.
+bool decode_on_multi_query(const pa_decode_shape_t& s, int group, int variant, bool kv_fp8) {
+  return !kv_fp8 && variant == PA_VARIANT_MFMA && (group == 8 || group == 16) &&
+         pa::multi_query_supported(s.dtype, s.head_dim, s.block_size, group);
 }
 
 pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = false) {
@@ -55,8 +65,13 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
       s->block_size != 128)
     return PA_EUNSUPPORTED;
   const int group = s->num_q_heads / s->num_kv_heads;
+  int variant = s->variant == PA_VARIANT_AUTO ? auto_variant(*s, group) : s->variant;
+  if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
+  plan->mq_route = decode_on_multi_query(*s, group, variant, kv_fp8);
   int pt = s->partition_tokens;
-  if (pt == 0) pt = kDefaultPartitionTokens;
+  // the per-tile kernel walks a partition with one wave per whole group, so
+  // its partitions are longer (measured best at group 8)
+  if (pt == 0) pt = plan->mq_route ? kDefaultMqPartitionTokens : kDefaultPartitionTokens;
   if (pt == -1) {
     // one partition per sequence
     pt = s->max_seq_len > 0 ? (int)round_up((size_t)s->max_seq_len, (size_t)s->block_size)
@@ -68,10 +83,8 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   const int64_t table_cap = (int64_t)s->max_blocks_per_seq * s->block_size;
   plan->len_cap = (int)(table_cap < s->max_seq_len ? table_cap : s->max_seq_len);
   plan->group = group;
-  int variant = s->variant == PA_VARIANT_AUTO ? auto_variant(*s, group) : s->variant;
-  if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
   plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant, kv_fp8};
-  if (!pa::decode_partition_supported(plan->key)) return PA_EUNSUPPORTED;
+  if (!plan->mq_route && !pa::decode_partition_supported(plan->key)) return PA_EUNSUPPORTED;
   if (group * 2 > pa::kMlRecord) return PA_EUNSUPPORTED;
   const size_t rows = (size_t)s->num_seqs * s->num_q_heads * plan->max_parts;
   const size_t recs = (size_t)s->num_seqs * s->num_kv_heads * plan->max_parts;
@@ -162,6 +175,39 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
   }
   if (shape->num_seqs == 0) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.mq_route) {
+    // the same workspace regions: per (sequence, query head, partition) the
+    // (max, exp-sum) pair (within the statistics records' space) and the
+    // partial output in the decode layout
+    pa::MqArgs m{};
+    m.q = a.q;
+    m.k_pool = a.k_pool;
+    m.v_pool = a.v_pool;
+    m.block_tables = a.block_tables;
+    m.seq_lens = a.seq_lens;
+    m.out = a.out;
+    m.qscale = a.qscale;
+    m.num_seqs = a.num_seqs;
+    m.num_q_heads = a.num_q_heads;
+    m.num_kv_heads = a.num_kv_heads;
+    m.num_blocks = a.num_blocks;
+    m.max_blocks = a.max_blocks;
+    m.len_cap = a.len_cap;
+    m.max_query_len = 1;
+    m.num_tokens = a.num_seqs;
+    m.decode_mode = 1;
+    m.max_parts = plan.max_parts;
+    m.part_tokens = plan.max_parts > 1 ? plan.part_tokens : 0;
+    m.part_ml = a.part_ml;
+    m.part_o = a.part_o;
+    m.part_half = a.part_half;
+    if (do_partition) {
+      st = from_hip(pa::launch_multi_query_tiles(shape->block_size, plan.group, m, s));
+      if (st != PA_OK) return st;
+    }
+    if (do_reduce) st = from_hip(pa::launch_multi_query_reduce(plan.group, m, s));
+    return st;
+  }
   if (do_partition) {
     st = from_hip(pa::launch_decode_partition(plan.key, a, s));
     if (st != PA_OK) return st;

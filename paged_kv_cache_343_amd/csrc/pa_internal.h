@@ -103,6 +103,8 @@ struct MqArgs {
   void* part_o;                 // [T][Hq][max_parts][D]: normalised partial output, bf16
                                 //   if part_half, else fp32
   int32_t part_half;
+  int32_t decode_mode;          // one query token per sequence: token i of sequence i,
+                                //   query_start unused, pa_decode's length rules
 };
 
 // Partial outputs of split-context attention are kept in bf16 when the
@@ -131,6 +133,11 @@ hipError_t launch_reshape_and_cache(const CacheArgs& args, hipStream_t stream);
 hipError_t launch_reshape_and_cache_e4m3(const CacheArgs8& args, hipStream_t stream);
 bool multi_query_supported(int dtype, int head_dim, int block_size, int group);
 hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream);
+// The two halves of the per-tile path: 16-row tiles (and context partitions
+// when args.max_parts > 1), then the merge of the partitions.
+hipError_t launch_multi_query_tiles(int block_size, int group, const MqArgs& args,
+                                   hipStream_t stream);
+hipError_t launch_multi_query_reduce(int group, const MqArgs& args, hipStream_t stream);
 // True if chunks of up to max_query_len tokens run on the workgroup-tiled
 // kernel (which never splits the context).
 bool multi_query_tiled(int group, int max_query_len);

@@ -1135,13 +1135,38 @@ __global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
   const int tile = unit / a.max_parts;
 
   // validate the sequence's length and query range (device-resident)
-  const int L = a.seq_lens[i];
-  const int q0 = a.query_start[i], q1 = a.query_start[i + 1];
-  const int tq = q1 - q0;
-  if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
-      tq > a.max_query_len) {
-    if (lane == 0 && g == 0 && blockIdx.x == 0) flag_error(kErrQuery);
-    return;
+  int L = a.seq_lens[i];
+  int q0, tq;
+  if (a.decode_mode) {
+    // pa_decode: token i; a length outside [0, len_cap] is clamped and
+    // flagged, and an empty sequence gets zero rows
+    q0 = i;
+    tq = 1;
+    if (L < 0 || L > a.len_cap) {
+      if (lane == 0 && g == 0 && unit == 0) flag_error(kErrSeqLen);
+      L = L < 0 ? 0 : a.len_cap;
+    }
+    if (L == 0) {
+      if (unit == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * R + r < G) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                            ((int64_t)i * a.num_q_heads + g * G + 4 * R + r) * D + c;
+#pragma unroll
+            for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = 0;
+          }
+      return;
+    }
+  } else {
+    q0 = a.query_start[i];
+    const int q1 = a.query_start[i + 1];
+    tq = q1 - q0;
+    if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
+        tq > a.max_query_len) {
+      if (lane == 0 && g == 0 && blockIdx.x == 0) flag_error(kErrQuery);
+      return;
+    }
   }
   const int rows = tq * G;
   if (tile * 16 >= rows) return;
@@ -1352,12 +1377,21 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.y;
   const int lr = blockIdx.x * kMqWaves + (threadIdx.x >> 6);   // row within the sequence
-  const int L = a.seq_lens[i];
-  const int q0 = a.query_start[i], q1 = a.query_start[i + 1];
-  const int tq = q1 - q0;
-  if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
-      tq > a.max_query_len)
-    return;                                      // flagged by multi_query_mfma
+  int L = a.seq_lens[i];
+  int q0, tq;
+  if (a.decode_mode) {
+    q0 = i;
+    tq = 1;
+    L = L < 0 ? 0 : min(L, a.len_cap);           // as multi_query_mfma
+    if (L == 0) return;
+  } else {
+    q0 = a.query_start[i];
+    const int q1 = a.query_start[i + 1];
+    tq = q1 - q0;
+    if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
+        tq > a.max_query_len)
+      return;                                    // flagged by multi_query_mfma
+  }
   if (lr >= tq * a.num_q_heads) return;
   const int t = lr / a.num_q_heads, hq = lr % a.num_q_heads;
   const int row0 = ((t * G + hq % G) / 16) * 16;  // first row of its tile
@@ -1935,6 +1969,13 @@ hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hip
     hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), 0, stream, args);
     return hipGetLastError();
   }
+  hipError_t e = launch_multi_query_tiles(block_size, group, args, stream);
+  if (e != hipSuccess || args.max_parts == 1) return e;
+  return launch_multi_query_reduce(group, args, stream);
+}
+
+hipError_t launch_multi_query_tiles(int block_size, int group, const MqArgs& args,
+                                   hipStream_t stream) {
   PartitionKernelMq kern = nullptr;
   switch (block_size) {
     case 16: kern = pick_mq<16>(group); break;
@@ -1953,8 +1994,13 @@ hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hip
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)args.num_kv_heads, (unsigned)args.num_seqs),
                      dim3(kMqWaves * 64), 0, stream, args);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || args.max_parts == 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_multi_query_reduce(int group, const MqArgs& args, hipStream_t stream) {
+  if (args.max_parts <= 1) return hipSuccess;
+  if (args.num_seqs <= 0 || args.num_seqs > 65535) return args.num_seqs <= 0 ? hipSuccess
+                                                                              : hipErrorInvalidValue;
   PartitionKernelMq red = nullptr;
   switch (group) {
     case 1: red = multi_query_reduce<1>; break;

@@ -45,6 +45,10 @@ SHAPES = [
     ("bf16", 32, 8, 128, 128, MFMA),
     ("bf16", 8, 8, 128, 8, MFMA),
     ("bf16", 16, 8, 128, 128, MFMA),
+    ("bf16", 64, 8, 128, 16, MFMA),     # group 8 and 16: the multi-token per-tile kernel
+    ("bf16", 32, 4, 128, 64, MFMA),
+    ("bf16", 16, 1, 128, 32, MFMA),
+    ("bf16", 32, 2, 128, 128, MFMA),
     ("bf16", 16, 8, 128, 32, VALU),
     ("bf16", 16, 2, 64, 16, VALU),
     ("bf16", 4, 4, 64, 32, VALU),
@@ -221,8 +225,24 @@ def test_variants_agree(dev):
     check_close(a, b, "bf16", "VALU vs MFMA")
 
 
-def test_device_index_errors_are_flagged(dev):
-    w = _custom("errs", 108, 8, 8, 128, 16, "bf16")
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (16, 1)])
+@pytest.mark.parametrize("ptok", [-1, 16, 128, 512])
+def test_large_groups_partition_lengths(dev, hq, hkv, ptok):
+    # group 8 / 16 decode runs on the multi-token per-tile kernel with its
+    # context partitions (fp32 partials below 256 positions, bf16 above)
+    w = _custom("groups", 110, hq, hkv, 128, 16, "bf16")
+    c = build(w, dev, lens=[0, 1, 100, 511, 700, 2047, 2500], append=False)
+    out = c.decode(variant=MFMA, partition_tokens=ptok)
+    check_close(_f64(out, "bf16"), c.oracle_all(), "bf16", f"group {hq // hkv} ptok {ptok}")
+    assert P.pa_device_errors() == 0
+    # the automatic choice takes the same path
+    auto = c.decode(partition_tokens=ptok)
+    assert torch.equal(auto.view(torch.int16), out.view(torch.int16))
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (64, 8)])
+def test_device_index_errors_are_flagged(dev, hq, hkv):
+    w = _custom("errs", 108, hq, hkv, 128, 16, "bf16")
     c = build(w, dev, lens=[40, 70], append=False)
     assert P.pa_device_errors() == 0
     bad = c.tables.clone()
@@ -234,7 +254,7 @@ def test_device_index_errors_are_flagged(dev):
     lens[0] = c.max_len + 1                    # longer than the host bound
     P.pa_decode(c.q, c.k_pool, c.v_pool, c.tables, lens, c.scale, out, max_seq_len=c.max_len)
     assert P.pa_device_errors() & 0x2
-    k = torch.zeros(1, 8, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, hkv, 128, dtype=torch.bfloat16, device=dev)
     P.pa_reshape_and_cache(k, k, torch.tensor([c.nb * 16], dtype=torch.int64, device=dev),
                            c.k_pool, c.v_pool)
     assert P.pa_device_errors() & 0x4
