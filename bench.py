@@ -447,6 +447,7 @@ def main() -> int:
         "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
         "a6_fork_cow_host_us": fork_cow_host_us(P),
         "n2_multi_query": multi_query_rate(P, torch, dev, W),
+        "decode_group8": group8_decode_rate(P, torch, dev, W),
         "n3_swap_blocks": swap_rate(P, torch, dev),
     }
     peak = stream_read_peak(torch, dev)
@@ -565,6 +566,47 @@ def swap_rate(P, torch, dev) -> dict:
         t = e0.elapsed_time(e1) / 5 / 1e3
         moved = 2 * n * kp[0].numel() * 2
         res[name] = {"us": round(t * 1e6, 1), "bytes": moved, "GBps": round(moved / t / 1e9, 1)}
+    return res
+
+
+def group8_decode_rate(P, torch, dev, W) -> dict:
+    """pa_decode at 8 query heads per KV head (64 query / 8 KV heads, D 128,
+    bf16, block size 16, scattered blocks; 256 sequences of U{512..4096}):
+    the matrix-core default and the vector-ALU kernel."""
+    hq, hkv, d, bs = 64, 8, 128, 16
+    rng = np.random.default_rng(19)
+    lens = rng.integers(512, 4097, 256)
+    B = len(lens)
+    nblk = [-(-int(L) // bs) for L in lens]
+    nb = int(sum(nblk) * 1.1) + 1
+    order = rng.permutation(nb)
+    tab = np.full((B, max(nblk)), -1, dtype=np.int32)
+    p0 = 0
+    for i, n in enumerate(nblk):
+        tab[i, :n] = order[p0:p0 + n]
+        p0 += n
+    kp = W.normal_device((nb, hkv, bs, d), 911, "bf16", dev)
+    vp = W.normal_device((nb, hkv, bs, d), 912, "bf16", dev)
+    q = W.normal_device((B, hq, d), 913, "bf16", dev)
+    tabd, lensd = torch.from_numpy(tab).to(dev), torch.from_numpy(lens.astype(np.int32)).to(dev)
+    kv = int(lens.sum()) * 2 * hkv * d * 2
+    res = {}
+    for name, variant in (("matrix_cores", P.PA_VARIANT_AUTO), ("vector_alu", P.PA_VARIANT_VALU)):
+        out = torch.empty_like(q)
+        for _ in range(2):
+            P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out,
+                        max_seq_len=int(lens.max()), variant=variant)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out,
+                        max_seq_len=int(lens.max()), variant=variant)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 10 / 1e3
+        res[name] = {"us": round(t * 1e6, 1), "kv_GBps": round(kv / t / 1e9, 1),
+                     "seq_steps_per_s": round(B / t, 1)}
+    del kp, vp
     return res
 
 
