@@ -120,11 +120,14 @@ def main() -> int:
     B, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     if args.block_size:
         bs = args.block_size
-    ptok = args.partition_tokens if args.partition_tokens is not None else w.partition_tokens
+    fp8 = args.kv_dtype == "e4m3"
+    # 8-bit pools: partitions of the same bytes as the workload's bf16 ones
+    # (twice the positions; the library's automatic choice)
+    ptok = (args.partition_tokens if args.partition_tokens is not None
+            else (2 * w.partition_tokens if fp8 else w.partition_tokens))
     nsteps = args.warmup + args.steps
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     eb = 2 if w.dtype == "bf16" else 4
-    fp8 = args.kv_dtype == "e4m3"
     if fp8 and (w.dtype != "bf16" or d != 128):
         print("8-bit pools need a bf16 workload with head dim 128", file=sys.stderr)
         return 1

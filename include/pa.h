@@ -87,7 +87,8 @@ typedef struct {
   int32_t max_seq_len;        /* host bound on every seq_lens[i]; sizes the
                                  grid and the workspace                        */
   int32_t partition_tokens;   /* context partition length: 0 = automatic (512;
-                                 1024 when G is 8 or 16 on the matrix cores),
+                                 1024 for 8-bit pools and when G is 8 or 16 on
+                                 the matrix cores),
                                  -1 = one partition per sequence, else a
                                  positive multiple of block_size               */
   int32_t dtype;              /* pa_dtype_t                                    */

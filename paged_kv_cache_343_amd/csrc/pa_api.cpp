@@ -69,9 +69,11 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
   plan->mq_route = decode_on_multi_query(*s, group, variant, kv_fp8);
   int pt = s->partition_tokens;
-  // the per-tile kernel walks a partition with one wave per whole group, so
-  // its partitions are longer (measured best at group 8)
-  if (pt == 0) pt = plan->mq_route ? kDefaultMqPartitionTokens : kDefaultPartitionTokens;
+  // automatic length: 512 positions; 1024 on the per-tile kernel (one wave
+  // walks a partition for the whole group; measured best at group 8) and
+  // for 8-bit pools (the same bytes per workgroup as 512 bf16 positions)
+  if (pt == 0)
+    pt = plan->mq_route || kv_fp8 ? kDefaultMqPartitionTokens : kDefaultPartitionTokens;
   if (pt == -1) {
     // one partition per sequence
     pt = s->max_seq_len > 0 ? (int)round_up((size_t)s->max_seq_len, (size_t)s->block_size)
