@@ -468,7 +468,11 @@ def main() -> int:
                 np.maximum.at(rows, tab_last[i, :nblk[i]], np.minimum(bs, lens_s[i] - k * bs))
             uniq.append(int(rows.sum()) * 2 * hkv * d * pool_eb)
         ub = float(np.mean(uniq))
+        cascade = None if fp8 else shared_prefix_rate(P, torch, dev, w, q_all[nsteps - 1], k_pool, v_pool,
+                                     devbuf[(nsteps - 1) % NBUF], plen, bs, max_len, scale,
+                                     uniq[-1], int(step_lens[-1].sum()) * 2 * hkv * d * pool_eb)
         result["shared_prefix"] = {
+            "pa_decode_shared_prefix": cascade,
             "logical_bytes_per_step": int(total_bytes / K), "unique_bytes_per_step": int(ub),
             "unique_GBps": round(ub / (wall / K) / 1e9, 1),
             "pct_of_hbm_peak_unique": round(100.0 * ub / (wall / K) / 1e9 / HBM_PEAK_GBS, 2),
@@ -569,6 +573,50 @@ def swap_rate(P, torch, dev) -> dict:
         t = e0.elapsed_time(e1) / 5 / 1e3
         moved = 2 * n * kp[0].numel() * 2
         res[name] = {"us": round(t * 1e6, 1), "bytes": moved, "GBps": round(moved / t / 1e9, 1)}
+    return res
+
+
+def shared_prefix_rate(P, torch, dev, w, q, k_pool, v_pool, db, plen, bs, max_len, scale,
+                       unique_bytes, logical_bytes) -> dict:
+    """The last timed step of a shared-prefix workload decoded twice: with
+    pa_decode and with pa_decode_shared_prefix (the prompt groups passed as
+    groups; the blocks they share are the whole prompt blocks, the partial
+    one having been copied on write), both on the compute path alone."""
+    ngroups, nsamp = w.extra["groups"], w.extra["samples"]
+    B = q.shape[0]
+    shared = (plen // bs) * bs
+    gs = torch.arange(0, ngroups * nsamp + 1, nsamp, dtype=torch.int32, device=dev)
+    prefix = torch.zeros(B, dtype=torch.int32, device=dev)
+    prefix[:ngroups * nsamp] = shared
+    out = torch.empty_like(q)
+    tables, lens = db["tables"], db["lens"]
+    shape = P.DecodeShape(B, q.shape[1], k_pool.shape[1], q.shape[2], bs, k_pool.shape[0],
+                          tables.shape[1], max_len, 0, P.PA_BF16, P.PA_VARIANT_AUTO)
+    ws_c = torch.empty(P.pa_decode_shared_prefix_workspace_bytes(shape, nsamp, shared),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(16, P.pa_decode_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in (
+            ("pa_decode", lambda: P.pa_decode(q, k_pool, v_pool, tables, lens, scale, out,
+                                              max_seq_len=max_len, workspace=ws_d)),
+            ("pa_decode_shared_prefix", lambda: P.pa_decode_shared_prefix(
+                q, k_pool, v_pool, tables, lens, scale, out, group_start=gs, prefix_lens=prefix,
+                max_group_size=nsamp, max_prefix_len=shared, max_seq_len=max_len,
+                workspace=ws_c))):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 20 / 1e3
+        res[name] = {"us": round(t * 1e6, 1), "logical_GBps": round(logical_bytes / t / 1e9, 1),
+                     "unique_GBps": round(unique_bytes / t / 1e9, 1),
+                     "pct_of_hbm_peak_unique": round(100.0 * unique_bytes / t / 1e9 / HBM_PEAK_GBS, 2)}
+    if P.pa_device_errors() != 0:
+        raise RuntimeError("device error flags set by the shared-prefix decode")
     return res
 
 

@@ -63,6 +63,7 @@ typedef enum {
 #define PA_DEVERR_SLOT 0x4u       /* slot >= num_blocks * block_size          */
 #define PA_DEVERR_COPY_PAIR 0x8u  /* copy/swap pair id outside its pool         */
 #define PA_DEVERR_QUERY 0x10u     /* multi-query: bad query range or length    */
+#define PA_DEVERR_PREFIX 0x20u    /* shared-prefix decode: bad group or prefix  */
 
 /* Decode kernel variants (pa_decode_shape_t.variant). */
 #define PA_VARIANT_AUTO 0   /* library's choice for the shape                     */
@@ -137,6 +138,47 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 float scale, void* out, const pa_decode_shape_t* shape,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_shared_prefix — pa_decode for a batch whose sequences come in
+ * groups that share a prompt (samples forked from one parent: [FP]
+ * "Copy-on-write sharing", [N4N] fork_block_table): sequences
+ * group_start[k] .. group_start[k+1]-1 hold the same physical blocks in
+ * their first prefix_lens[i] / block_size table entries. Same result as
+ * pa_decode (to rounding), but each shared block is read once per group:
+ * one pass per (group, KV head) attends the group's query rows (sequences x
+ * heads of the group) to the prefix, one pass per (sequence, KV head) to
+ * the positions after it, and a third kernel merges both passes' softmax
+ * statistics and outputs (log-sum-exp, fp32).
+ *
+ *   shape          as pa_decode: bf16, head_dim 128, G in {1, 2, 4, 8, 16},
+ *                  block size 16-128; partition_tokens 0 = 256 positions
+ *                  (both passes split their range into partitions), -1 is
+ *                  not accepted; variant ignored
+ *   group_start    [dev] int32 [num_groups + 1], non-decreasing, last <= B;
+ *                  sequences outside every group need prefix_lens 0
+ *   prefix_lens    [dev] int32 [B]: shared positions of each sequence, a
+ *                  multiple of block_size, equal within a group, at most
+ *                  seq_lens[i] and max_prefix_len; 0 = none
+ *   max_group_size host bound on group sizes (sizes the grid)
+ *   max_prefix_len host bound on prefix_lens, a multiple of block_size
+ *   workspace      [dev] >= pa_decode_shared_prefix_workspace_bytes(shape,
+ *                  max_group_size, max_prefix_len) bytes
+ * A group whose members do not share the prefix (lengths differ, blocks
+ * differ, or a member holds fewer positions), or a prefix length that is
+ * not a multiple of block_size or exceeds max_prefix_len or its sequence,
+ * is flagged (PA_DEVERR_PREFIX); the affected outputs are then undefined,
+ * but every access stays inside the buffers.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(const pa_decode_shape_t* shape,
+                                               int32_t max_group_size, int32_t max_prefix_len);
+pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    float scale, void* out, const pa_decode_shape_t* shape,
+                                    int32_t num_groups, const int32_t* group_start,
+                                    const int32_t* prefix_lens, int32_t max_group_size,
+                                    int32_t max_prefix_len, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * 8-bit KV pools (FP8 E4M3). [ZQ] summary: paged attention composes with KV

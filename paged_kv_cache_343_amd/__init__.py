@@ -19,7 +19,8 @@ import numpy as np
 
 __all__ = [
     "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16", "PA_DEVERR_BLOCK_ID", "PA_DEVERR_SEQ_LEN",
-    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
+    "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "PA_DEVERR_PREFIX",
+    "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_decode_e4m3", "pa_reshape_and_cache_e4m3",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
@@ -33,6 +34,7 @@ PA_F32, PA_BF16 = 0, 1
 # device error word bits (include/pa.h PA_DEVERR_*)
 PA_DEVERR_BLOCK_ID, PA_DEVERR_SEQ_LEN, PA_DEVERR_SLOT, PA_DEVERR_COPY_PAIR = 0x1, 0x2, 0x4, 0x8
 PA_DEVERR_QUERY = 0x10
+PA_DEVERR_PREFIX = 0x20
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
            4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
@@ -42,7 +44,8 @@ EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
     "pa_status_str", "pa_multi_query", "pa_multi_query_workspace_bytes",
-    "pa_multi_query_split", "pa_decode_e4m3", "pa_decode_partition_e4m3",
+    "pa_multi_query_split", "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
+    "pa_decode_e4m3", "pa_decode_partition_e4m3",
     "pa_reshape_and_cache_e4m3",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
@@ -85,6 +88,10 @@ _SIGS = {
     "pa_multi_query": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                               ctypes.POINTER(MultiQueryShape), _vp]),
     "pa_multi_query_workspace_bytes": (_sz, [ctypes.POINTER(MultiQueryShape), _i32]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [ctypes.POINTER(DecodeShape), _i32, _i32]),
+    "pa_decode_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                       ctypes.POINTER(DecodeShape), _i32, _vp, _vp, _i32, _i32,
+                                       _vp, _sz, _vp]),
     "pa_multi_query_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                     ctypes.POINTER(MultiQueryShape), _i32, _vp, _sz, _vp]),
     "pa_decode_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
@@ -222,6 +229,49 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_
     return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                         max_seq_len=max_seq_len, partition_tokens=partition_tokens,
                         variant=variant, workspace=workspace, stream=stream)
+
+
+def pa_decode_shared_prefix_workspace_bytes(shape: DecodeShape, max_group_size: int,
+                                            max_prefix_len: int) -> int:
+    return int(lib().pa_decode_shared_prefix_workspace_bytes(
+        ctypes.byref(shape), int(max_group_size), int(max_prefix_len)))
+
+
+def pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
+                            group_start, prefix_lens, max_group_size, max_prefix_len,
+                            max_seq_len, partition_tokens=0, workspace=None, stream=None):
+    """pa_decode for groups of sequences sharing a prompt (include/pa.h
+    pa_decode_shared_prefix). group_start int32 [G+1] and prefix_lens int32
+    [B] on the device; the workspace is allocated here unless given."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", dtype=torch.bfloat16, dim=3)
+    _need(k_pool, "k_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(v_pool, "v_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(group_start, "group_start", dtype=torch.int32, dim=1, device=dev)
+    _need(prefix_lens, "prefix_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    B = q.shape[0]
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B or prefix_lens.shape[0] != B:
+        raise ValueError("batch mismatch")
+    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens,
+                          PA_VARIANT_AUTO)
+    need = pa_decode_shared_prefix_workspace_bytes(shape, max_group_size, max_prefix_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    st = lib().pa_decode_shared_prefix(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
+        group_start.shape[0] - 1, group_start.data_ptr(), prefix_lens.data_ptr(),
+        int(max_group_size), int(max_prefix_len), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    _check(st, "pa_decode_shared_prefix")
+    return out
 
 
 def pa_decode_partition(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,

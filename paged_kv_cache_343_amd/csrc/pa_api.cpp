@@ -16,6 +16,8 @@ constexpr int kDefaultPartitionTokens = 512;
 // pa_multi_query_split: one wave walks a partition for a whole 16-row tile,
 // so partitions are longer than decode's (measured best on 4-token chunks)
 constexpr int kDefaultMqPartitionTokens = 1024;
+// pa_decode_shared_prefix: a prefix is walked once per group
+constexpr int kDefaultPrefixPartitionTokens = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -92,8 +94,10 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   const size_t recs = (size_t)s->num_seqs * s->num_kv_heads * plan->max_parts;
   if (plan->max_parts > 1) {
     plan->ml_bytes = round_up(recs * pa::kMlRecord * sizeof(float), 256);
-    plan->part_half = s->dtype == PA_BF16 && pt >= pa::kHalfPartialMinTokens;
-    plan->o_bytes = round_up(rows * (size_t)s->head_dim * (plan->part_half ? 2 : 4), 256);
+    // bf16 partials only for full-length partitions of the decode kernels
+    // (the per-tile multi-token kernel keeps fp32)
+    plan->part_half = s->dtype == PA_BF16 && pt >= pa::kHalfPartialMinTokens && !plan->mq_route;
+    plan->o_bytes = round_up(rows * (size_t)s->head_dim * 4, 256);
   }
   return PA_OK;
 }
@@ -197,6 +201,7 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
     m.len_cap = a.len_cap;
     m.max_query_len = 1;
     m.num_tokens = a.num_seqs;
+    m.block_size = shape->block_size;
     m.decode_mode = 1;
     m.max_parts = plan.max_parts;
     m.part_tokens = plan.max_parts > 1 ? plan.part_tokens : 0;
@@ -282,6 +287,155 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
                                            static_cast<hipStream_t>(stream)));
 }
 
+// Shared-prefix decode plan: partitions of the prefix pass, then of the
+// per-sequence pass, in one partial array per (sequence, query head).
+struct PrefixPlan {
+  Plan base;              // the per-sequence walks (pa_decode's partitions)
+  int pref_tokens = 0;    // partition length of the prefix pass
+  int pref_parts = 0, suf_parts = 0;
+  size_t ml_bytes = 0, o_bytes = 0;
+};
+
+pa_status_t prefix_plan(const pa_decode_shape_t* s, int32_t max_group_size,
+                        int32_t max_prefix_len, PrefixPlan* pp) {
+  if (!s || max_group_size <= 0 || max_prefix_len < 0) return PA_EINVAL;
+  pa_decode_shape_t s2 = *s;
+  s2.variant = PA_VARIANT_MFMA;
+  if (s2.partition_tokens == -1) return PA_EINVAL;
+  pa_status_t st = make_plan(&s2, &pp->base);
+  if (st != PA_OK) return st;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  if (!pa::multi_query_supported(s->dtype, s->head_dim, s->block_size, group))
+    return PA_EUNSUPPORTED;
+  if (max_prefix_len % s->block_size != 0 || max_prefix_len > s->max_seq_len) return PA_EINVAL;
+  if ((int64_t)max_group_size * group > (1 << 24)) return PA_EINVAL;
+  // the walks after the prefix use pa_decode's partitions; the prefix pass
+  // (read once per group, so it needs shorter partitions to spread over the
+  // GPU) uses 256 positions unless partition_tokens is given
+  const int pt = pp->base.part_tokens;
+  pp->pref_tokens = s->partition_tokens == 0 ? kDefaultPrefixPartitionTokens : pt;
+  pp->pref_parts = (max_prefix_len + pp->pref_tokens - 1) / pp->pref_tokens;
+  pp->suf_parts = s->max_seq_len == 0 ? 1 : (s->max_seq_len + pt - 1) / pt;
+  const size_t slots = (size_t)(pp->pref_parts + pp->suf_parts);
+  // statistics in pa_decode's 128-byte records per (sequence, KV head, slot)
+  // (the group-8/16 path keeps a pair per query row in the same space)
+  pp->ml_bytes = round_up((size_t)s->num_seqs * s->num_kv_heads * slots * pa::kMlRecord *
+                              sizeof(float), 256);
+  pp->o_bytes = round_up((size_t)s->num_seqs * s->num_q_heads * slots * s->head_dim * 4, 256);
+  // the decode kernel's own partitions may keep bf16 partials (prefix pass: fp32)
+  pp->base.part_half = s->dtype == PA_BF16 && pt >= pa::kHalfPartialMinTokens &&
+                       group <= 4;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_shared_prefix_workspace_bytes(const pa_decode_shape_t* shape,
+                                               int32_t max_group_size, int32_t max_prefix_len) {
+  PrefixPlan pp;
+  if (prefix_plan(shape, max_group_size, max_prefix_len, &pp) != PA_OK) return 0;
+  return pp.ml_bytes + pp.o_bytes;
+}
+
+pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    float scale, void* out, const pa_decode_shape_t* shape,
+                                    int32_t num_groups, const int32_t* group_start,
+                                    const int32_t* prefix_lens, int32_t max_group_size,
+                                    int32_t max_prefix_len, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  PrefixPlan pp;
+  pa_status_t st = prefix_plan(shape, max_group_size, max_prefix_len, &pp);
+  if (st != PA_OK) return st;
+  if (num_groups < 0 || (num_groups > 0 && !group_start) || !prefix_lens) return PA_EINVAL;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_EINVAL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PA_EINVAL;
+  if (!std::isfinite(scale)) return PA_EINVAL;
+  const size_t need = pp.ml_bytes + pp.o_bytes;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PA_EWORKSPACE;
+  if (num_groups > 65535 || shape->num_seqs > 65535) return PA_EUNSUPPORTED;
+  const int group = shape->num_q_heads / shape->num_kv_heads;
+  pa::MqArgs m{};
+  m.q = q;
+  m.k_pool = k_pool;
+  m.v_pool = v_pool;
+  m.block_tables = block_tables;
+  m.seq_lens = seq_lens;
+  m.out = out;
+  m.qscale = scale * 1.4426950408889634f;
+  m.num_seqs = shape->num_seqs;
+  m.num_q_heads = shape->num_q_heads;
+  m.num_kv_heads = shape->num_kv_heads;
+  m.num_blocks = shape->num_blocks;
+  m.max_blocks = shape->max_blocks_per_seq;
+  m.len_cap = pp.base.len_cap;
+  m.num_tokens = shape->num_seqs;
+  m.block_size = shape->block_size;
+  m.part_tokens = pp.base.part_tokens;
+  m.prefix_part_tokens = pp.pref_tokens;
+  m.max_parts = pp.pref_parts + pp.suf_parts;
+  m.part_ml = static_cast<float*>(workspace);
+  m.part_o = static_cast<char*>(workspace) + pp.ml_bytes;
+  m.part_half = pp.base.part_half ? 1 : 0;
+  m.group_start = group_start;
+  m.prefix_lens = prefix_lens;
+  m.suffix_slot0 = pp.pref_parts;
+  m.max_prefix = max_prefix_len;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1. per group: the shared prefix, the group's sequences as query rows
+  m.slot_stride = pp.pref_parts + pp.suf_parts;
+  m.part_half = 0;
+  const bool decode_kernel = group <= 4;   // the walks on pa_decode's kernel
+  pa::MqArgs m2 = m;
+  m2.mode = 2;
+  m2.part_tokens = pp.pref_tokens;
+  m2.num_seqs = num_groups;       // the grid runs over groups
+  m2.max_query_len = max_group_size;
+  m2.max_parts = num_groups > 0 ? pp.pref_parts : 0;
+  m2.ml_records = decode_kernel ? 1 : 0;
+  if (!decode_kernel && m2.max_parts > 0) {
+    st = from_hip(pa::launch_multi_query_tiles(shape->block_size, group, m2, s));
+    if (st != PA_OK) return st;
+  }
+  if (decode_kernel) {
+    // 1 + 2. the prefix pass and the walks after the prefix (pa_decode's
+    //    kernel, per (sequence, KV head, partition)) in one launch; 3. the
+    //    decode reduce merges both passes' slots
+    pa::DecodeArgs a{};
+    st = fill_args(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, pp.base,
+                   workspace, workspace_bytes, &a);
+    if (st != PA_OK) return st;
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_o = static_cast<char*>(workspace) + pp.ml_bytes;
+    a.part_tokens = pp.base.part_tokens;
+    a.max_parts = pp.suf_parts;
+    a.part_half = pp.base.part_half ? 1 : 0;
+    a.pos_start = prefix_lens;
+    a.prefix_part_tokens = pp.pref_tokens;
+    a.slot0 = pp.pref_parts;
+    a.slot_stride = pp.pref_parts + pp.suf_parts;
+    a.max_prefix = max_prefix_len;
+    a.block_size = shape->block_size;
+    st = from_hip(pa::launch_shared_prefix_decode(shape->block_size, group, m2, a, s));
+    if (st != PA_OK) return st;
+    return from_hip(pa::launch_decode_reduce(shape->dtype, shape->head_dim, a, s));
+  }
+  // 2. per sequence: the positions after its prefix
+  pa::MqArgs m3 = m;
+  m3.mode = 3;
+  m3.max_query_len = 1;
+  m3.max_parts = pp.suf_parts;
+  st = from_hip(pa::launch_multi_query_tiles(shape->block_size, group, m3, s));
+  if (st != PA_OK) return st;
+  // 3. merge both passes' partials
+  m3.max_parts = m.slot_stride;
+  return from_hip(pa::launch_multi_query_reduce(group, m3, s));
+}
+
 }  // extern "C"
 
 namespace {
@@ -320,9 +474,9 @@ pa_status_t mq_split_plan(const pa_multi_query_shape_t* s, int32_t partition_tok
     sp->max_parts = 1;   // the tiled kernel never splits
   if (sp->max_parts > 1) {
     const size_t rows = (size_t)s->num_tokens * s->num_q_heads * sp->max_parts;
-    sp->part_half = pt >= pa::kHalfPartialMinTokens;
+    sp->part_half = false;
     sp->ml_bytes = round_up(rows * 2 * sizeof(float), 256);
-    sp->o_bytes = round_up(rows * (size_t)s->head_dim * (sp->part_half ? 2 : 4), 256);
+    sp->o_bytes = round_up(rows * (size_t)s->head_dim * 4, 256);
   }
   return PA_OK;
 }
@@ -357,6 +511,7 @@ pa_status_t multi_query_impl(const void* q, const void* k_pool, const void* v_po
   a.len_cap = (int)(table_cap < s->max_seq_len ? table_cap : s->max_seq_len);
   a.max_query_len = s->max_query_len;
   a.num_tokens = s->num_tokens;
+  a.block_size = s->block_size;
   a.part_tokens = 0;
   a.max_parts = 1;
   if (sp.max_parts > 1) {

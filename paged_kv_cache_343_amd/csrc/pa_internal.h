@@ -20,8 +20,8 @@ struct DecodeArgs {
   void* out;                    // [B][Hq][D]
   float* part_ml;               // [B][Hkv][max_parts][kMlRecord]: per query head of the
                                 //   group, max score (log2 units) then exp-sum; rest 0
-  void* part_o;                 // [B][Hq][max_parts][D]: normalised partial output, bf16
-                                //   if part_half, else fp32
+  void* part_o;                 // [B][Hq][max_parts][D] fp32 slots: normalised partial
+                                //   output (bf16 in a slot's first half, see part_half)
   float qscale;                 // softmax scale * log2(e) (* k_scale for 8-bit pools)
   float out_scale;              // v_scale for 8-bit pools
   int32_t part_half;            // partial outputs stored as bf16
@@ -33,7 +33,17 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t len_cap;              // min(max_seq_len, max_blocks * bs)
   int32_t part_tokens;          // partition length in positions (multiple of bs)
-  int32_t max_parts;            // ceil(max_seq_len / part_tokens)
+  int32_t max_parts;            // ceil(max_seq_len / part_tokens): partitions in the grid
+  // shared-prefix decode: the walk of sequence i starts at pos_start[i] (a
+  // multiple of block_size, at most max_prefix), its partitions fill partial
+  // slots slot0 .. and always leave partials; the reduce also merges the
+  // prefix pass's slots 0 .. ceil(pos_start[i] / part_tokens) - 1 (fp32)
+  const int32_t* pos_start;     // [B] or null
+  int32_t prefix_part_tokens;   // partition length of the prefix pass
+  int32_t slot0;
+  int32_t slot_stride;          // partial slots per row (0: max_parts)
+  int32_t max_prefix;
+  int32_t block_size;
 };
 
 struct CacheArgs {
@@ -105,12 +115,23 @@ struct MqArgs {
   int32_t part_half;
   int32_t decode_mode;          // one query token per sequence: token i of sequence i,
                                 //   query_start unused, pa_decode's length rules
+  // shared-prefix decode (mode 2: one pass per group over the shared prefix,
+  // mode 3: one pass per sequence over the rest); 0 otherwise
+  int32_t mode;
+  const int32_t* group_start;   // [num_groups + 1] (mode 2)
+  const int32_t* prefix_lens;   // [B] shared positions of each sequence (modes 2, 3)
+  int32_t suffix_slot0;         // first partial slot of the per-sequence pass
+  int32_t prefix_part_tokens;   // partition length of the prefix pass (mode 2)
+  int32_t max_prefix;           // host bound on prefix_lens (sizes the prefix slots)
+  int32_t block_size;
+  int32_t slot_stride;          // partial slots per row (0: max_parts)
+  int32_t ml_records;           // mode 2: (max, exp-sum) in pa_decode's 128-byte records
 };
 
-// Partial outputs of split-context attention are kept in bf16 when the
-// partitions are at least this long (each is then an average over many
-// positions, far from the size of single values) and the output is bf16;
-// otherwise in fp32.
+// The decode kernels keep the partial output of a partition in bf16 when it
+// covers at least this many positions and the output is bf16 (an average
+// over many positions stays far from the size of single values); shorter
+// partials, and those of the multi-token kernels, stay fp32.
 constexpr int kHalfPartialMinTokens = 256;
 
 // Kernel selection key for pa_decode_partition.
@@ -138,6 +159,11 @@ hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hip
 hipError_t launch_multi_query_tiles(int block_size, int group, const MqArgs& args,
                                    hipStream_t stream);
 hipError_t launch_multi_query_reduce(int group, const MqArgs& args, hipStream_t stream);
+// Shared-prefix decode's two passes in one launch: the prefix pass (pre,
+// mode 2, the per-tile kernel) and the per-sequence walks (walk, with
+// pos_start; group 1, 2 or 4); the decode reduce merges them afterwards.
+hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& pre,
+                                       const DecodeArgs& walk, hipStream_t stream);
 // True if chunks of up to max_query_len tokens run on the workgroup-tiled
 // kernel (which never splits the context).
 bool multi_query_tiled(int group, int max_query_len);

@@ -56,6 +56,7 @@ constexpr uint32_t kErrSeqLen = 0x2u;
 constexpr uint32_t kErrSlot = 0x4u;
 constexpr uint32_t kErrCopyPair = 0x8u;
 constexpr uint32_t kErrQuery = 0x10u;
+constexpr uint32_t kErrPrefix = 0x20u;
 
 __device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_word, bit); }
 
@@ -204,7 +205,21 @@ struct PartitionWork {
   int len;           // validated sequence length
   int nparts;        // partitions of this sequence
   int tok0, tok1;    // positions [tok0, tok1) of partition j
+  int slot;          // partial slot of partition j
+  bool direct;       // the partition is the whole walk: write out itself
 };
+
+// Start of sequence i's walk for shared-prefix decode (0 otherwise); an
+// invalid start is flagged and replaced by 0 (the reduce does the same).
+__device__ __forceinline__ int walk_start(const DecodeArgs& a, int i, int len, bool flag) {
+  if (!a.pos_start) return 0;
+  const int s = a.pos_start[i];
+  if (s < 0 || s > len || s > a.max_prefix || s % a.block_size != 0) {
+    if (flag) flag_error(kErrPrefix);
+    return 0;
+  }
+  return s;
+}
 
 // Sequence length checked against the host bound (len_cap = min(max_seq_len,
 // max_blocks * bs)); out-of-range values are clamped and flagged.
@@ -278,7 +293,7 @@ __device__ __forceinline__ float row_partner(float x) {
 // final output (single-partition sequence) or the partition's partials.
 // Inputs per lane: m[h], l[h] of the lane's row stream (log2 units) and
 // acc[h][e] = unnormalised output for dims c*EPL + e, where c = lane % LPR.
-template <typename T, int D, int G, int NW, int LPR, int EPL>
+template <typename T, int D, int G, int NW, int LPR, int EPL, bool PFX = false>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const PartitionWork& wk,
                                                  float (&m)[G], float (&l)[G],
                                                  float (&acc)[G][EPL], float out_scale = 1.0f) {
@@ -339,24 +354,26 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
     }
     const float inv = lsum > 0.0f ? out_scale / lsum : 0.0f;
     const int64_t row = (int64_t)wk.i * a.num_q_heads + wk.g * G + h;
-    if (wk.nparts == 1) {
+    if (wk.direct) {
       store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
                 o[3] * inv);
     } else {
-      // the partial output is stored in bf16 or fp32 (see part_half); the
-      // merge of the partitions runs in fp32
-      const int64_t po = (row * a.max_parts + wk.j) * D + d0;
-      if (a.part_half)
-        store4<uint16_t>(reinterpret_cast<uint16_t*>(a.part_o) + po, o[0] * inv, o[1] * inv,
+      // the partial output of a partition holding at least
+      // kHalfPartialMinTokens positions is stored in bf16 when part_half is
+      // set (in the first half of its fp32-sized slot), other partials in
+      // fp32; the merge of the partitions runs in fp32
+      float* slot = reinterpret_cast<float*>(a.part_o) +
+                    (row * (PFX ? a.slot_stride : a.max_parts) + wk.slot) * D;
+      if (a.part_half && wk.tok1 - wk.tok0 >= kHalfPartialMinTokens)
+        store4<uint16_t>(reinterpret_cast<uint16_t*>(slot) + d0, o[0] * inv, o[1] * inv,
                          o[2] * inv, o[3] * inv);
       else
-        store4<float>(reinterpret_cast<float*>(a.part_o) + po, o[0] * inv, o[1] * inv,
-                      o[2] * inv, o[3] * inv);
+        store4<float>(slot + d0, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     }
   }
   // (max, exp-sum) of every head of the group: one full 128-byte record per
   // workgroup, so the write never covers part of a cache line.
-  if (wk.nparts > 1 && threadIdx.x < kMlRecord / 4) {
+  if (!wk.direct && threadIdx.x < kMlRecord / 4) {
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -372,7 +389,8 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
         v[e] = (f & 1) ? lsum : big;
       }
     }
-    const int64_t rec = (((int64_t)wk.i * a.num_kv_heads + wk.g) * a.max_parts + wk.j) * kMlRecord;
+    const int64_t rec = (((int64_t)wk.i * a.num_kv_heads + wk.g) *
+                             (PFX ? a.slot_stride : a.max_parts) + wk.slot) * kMlRecord;
     reinterpret_cast<float4*>(a.part_ml + rec)[threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
@@ -387,11 +405,11 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
 // (g, j) always lands on XCD (g + j) mod 8, so sequences sharing prompt
 // blocks meet in one L2. Otherwise units are numbered partition fastest,
 // then head, then sequence.
-// Decodes blockIdx.x; returns false if the workgroup has nothing to do
+// Decodes workgroup id `id`; returns false if the workgroup has nothing to do
 // (after writing zeros for an empty sequence).
-template <typename T, int D, int BS, int G, int NW>
-__device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk) {
-  const int id = blockIdx.x;
+template <typename T, int D, int BS, int G, int NW, bool PFX = false>
+__device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk,
+                                                int id) {
   if (a.num_kv_heads % 8 == 0) {
     const int x = id & 7, r = id >> 3;
     wk.j = r % a.max_parts;
@@ -405,14 +423,19 @@ __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWo
     wk.i = rest / a.num_kv_heads;
   }
   wk.len = checked_len(a, wk.i);
-  wk.nparts = (wk.len + a.part_tokens - 1) / a.part_tokens;
   if (wk.len == 0) {
     if (wk.j == 0) write_zero_rows<T, D, G, NW>(a, wk.i, wk.g);
     return false;
   }
+  // PFX: shared-prefix decode's per-sequence walk (starts after the prefix,
+  // always leaves partials, in slots from slot0)
+  const int start = PFX ? walk_start(a, wk.i, wk.len, threadIdx.x == 0) : 0;
+  wk.nparts = (wk.len - start + a.part_tokens - 1) / a.part_tokens;
   if (wk.j >= wk.nparts) return false;
-  wk.tok0 = wk.j * a.part_tokens;
+  wk.tok0 = start + wk.j * a.part_tokens;
   wk.tok1 = min(wk.len, wk.tok0 + a.part_tokens);
+  wk.slot = PFX ? a.slot0 + wk.j : wk.j;
+  wk.direct = !PFX && wk.nparts == 1;
   return true;
 }
 
@@ -430,7 +453,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_valu(DecodeArgs a) {
   constexpr int64_t kHeadBytes = (int64_t)BS * D * S;
 
   PartitionWork wk;
-  if (!setup_partition<T, D, BS, G, NW>(a, wk)) return;
+  if (!setup_partition<T, D, BS, G, NW>(a, wk, blockIdx.x)) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR, c = lane % LPR;
@@ -768,7 +791,7 @@ __device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4]
 // One work unit (sequence, KV head, partition) of the matrix-core kernel.
 // F8: the pools hold FP8 E4M3 codes (q and out stay bf16); scores use
 // qscale = scale * log2(e) * k_scale and outputs are multiplied by v_scale.
-template <int BS, int G, int NW, bool F8>
+template <int BS, int G, int NW, bool F8, bool PFX>
 __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWork& wk) {
   constexpr int D = 128;
   constexpr int ROW = F8 ? D : D * 2;             // bytes per token row
@@ -866,14 +889,15 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
   float mh[G], lh[G];
   quad_spread<G>(m, mh);
   quad_spread<G>(lsum, lh);
-  finish_partition<uint16_t, D, G, NW, 16, 8>(a, wk, mh, lh, acc, F8 ? a.out_scale : 1.0f);
+  finish_partition<uint16_t, D, G, NW, 16, 8, PFX>(a, wk, mh, lh, acc, F8 ? a.out_scale : 1.0f);
 }
 
-template <int BS, int G, int NW, bool F8>
-__global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
+template <int BS, int G, int NW, bool F8, bool PFX = false>
+__global__ PA_MFMA_BOUNDS(NW * 64) __attribute__((amdgpu_waves_per_eu(PFX ? 3 : 1)))
+void decode_partition_mfma(DecodeArgs a) {
   PartitionWork wk;
-  if (!setup_partition<uint16_t, 128, BS, G, NW>(a, wk)) return;
-  mfma_unit<BS, G, NW, F8>(a, wk);
+  if (!setup_partition<uint16_t, 128, BS, G, NW, PFX>(a, wk, blockIdx.x)) return;
+  mfma_unit<BS, G, NW, F8, PFX>(a, wk);
 }
 
 // ---------------------------------------------------------------------------
@@ -884,7 +908,7 @@ __global__ PA_MFMA_BOUNDS(NW * 64) void decode_partition_mfma(DecodeArgs a) {
 // Partitions merged with every load issued up front (the common case).
 constexpr int kReduceFast = 16;
 
-template <typename T, int D>
+template <typename T, int D, bool PFX = false>
 __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a) {
   // one wave per (sequence, query head); kReduceWaves consecutive pairs per
   // workgroup
@@ -894,20 +918,43 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   const int i = pair / a.num_q_heads;
   int len = a.seq_lens[i];
   len = len < 0 ? 0 : min(len, a.len_cap);
-  const int np = (len + a.part_tokens - 1) / a.part_tokens;
-  if (np <= 1) return;
+  if (len == 0) return;
+  // partials k = 0 .. np - 1 of the row: with shared-prefix decode first the
+  // prefix pass's np_pref slots (fp32), then the walk's own partitions
+  const int pt = a.part_tokens;
+  const int start = PFX ? walk_start(a, i, len, false) : 0;
+  const int np_pref = PFX ? (start + a.prefix_part_tokens - 1) / a.prefix_part_tokens : 0;
+  const int np = np_pref + (len - start + pt - 1) / pt;
+  if (!PFX && np <= 1) return;                   // written by the partition kernel
   const int G = a.num_q_heads / a.num_kv_heads;
-  // record of partition j: ml[j * kMlRecord] = (max, exp-sum) of this head
+  const int64_t stride = PFX ? a.slot_stride : a.max_parts;
+  auto slot_of = [&](int k) { return PFX && k >= np_pref ? a.slot0 + (k - np_pref) : k; };
+  // record of slot s: ml[s * kMlRecord] = (max, exp-sum) of this head
   const float* ml = a.part_ml +
-                    ((int64_t)i * a.num_kv_heads + hq / G) * a.max_parts * kMlRecord + 2 * (hq % G);
-  const int64_t po = ((int64_t)i * a.num_q_heads + hq) * a.max_parts * D;
-  auto load_part = [&](int64_t off, float (&f)[D / 64]) {
-    if (a.part_half)
-      load_elems<uint16_t, D / 64>(reinterpret_cast<const uint16_t*>(a.part_o) + po + off, f);
-    else
-      load_elems<float, D / 64>(reinterpret_cast<const float*>(a.part_o) + po + off, f);
-  };
+                    ((int64_t)i * a.num_kv_heads + hq / G) * stride * kMlRecord + 2 * (hq % G);
   const int lane = threadIdx.x & 63;
+  // partial k (see finish_partition for its storage type)
+  const float* po = reinterpret_cast<const float*>(a.part_o) +
+                    ((int64_t)i * a.num_q_heads + hq) * stride * D;
+  // (branch-free, so that the loads of a batch can all be issued first: one
+  // 8-byte load at the lane's bf16 or fp32 position, decoded by a select;
+  // the bf16 case reads 4 bytes past its pair, still inside the slot)
+  auto load_part = [&](int k, float (&f)[D / 64]) {
+    const float* slot = po + (int64_t)slot_of(k) * D;
+    const int t0 = start + (k - np_pref) * pt;
+    const bool half = (!PFX || k >= np_pref) && a.part_half &&
+                      min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+    if constexpr (D / 64 == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(slot) +
+                                                      (half ? 4 : 8) * lane);
+      f[0] = half ? lo_bf16(w.x) : __uint_as_float(w.x);
+      f[1] = half ? hi_bf16(w.x) : __uint_as_float(w.y);
+    } else if (half) {
+      load_elems<uint16_t, D / 64>(reinterpret_cast<const uint16_t*>(slot) + lane * (D / 64), f);
+    } else {
+      load_elems<float, D / 64>(slot + lane * (D / 64), f);
+    }
+  };
   constexpr int DPL = D / 64;
   float o[DPL];
 #pragma unroll
@@ -915,14 +962,14 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   float wsum;
   if (np <= kReduceFast) {
     // every load up front: lane j's statistics, then each partition's slice
-    const float mj = lane < np ? ml[(int64_t)lane * kMlRecord] : -INFINITY;
-    const float lj = lane < np ? ml[(int64_t)lane * kMlRecord + 1] : 0.0f;
+    const float mj = lane < np ? ml[(int64_t)slot_of(lane) * kMlRecord] : -INFINITY;
+    const float lj = lane < np ? ml[(int64_t)slot_of(lane) * kMlRecord + 1] : 0.0f;
     float v[kReduceFast][DPL];
 #pragma unroll
     for (int j = 0; j < kReduceFast; ++j) {
       // partitions past np read partition 0's slice (in bounds) and drop it
       float f[DPL];
-      load_part((int64_t)(j < np ? j : 0) * D + lane * DPL, f);
+      load_part(j < np ? j : 0, f);
 #pragma unroll
       for (int k = 0; k < DPL; ++k) v[j][k] = j < np ? f[k] : 0.0f;
     }
@@ -942,8 +989,9 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   } else {
     // lane j folds partitions j, j + 64, ... into one (max, exp-sum) pair
     float mj = -INFINITY, lj = 0.0f;
-    for (int j = lane; j < np; j += 64) {
-      const float m2 = ml[(int64_t)j * kMlRecord], l2 = ml[(int64_t)j * kMlRecord + 1];
+    for (int k = lane; k < np; k += 64) {
+      const int64_t j = slot_of(k);
+      const float m2 = ml[j * kMlRecord], l2 = ml[j * kMlRecord + 1];
       const float big = fmaxf(mj, m2);
       lj = lj * merge_weight(mj, big) + l2 * merge_weight(m2, big);
       mj = big;
@@ -954,14 +1002,62 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
     wsum = lj * merge_weight(mj, big);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
-#pragma unroll 4
-    for (int j = 0; j < np; ++j) {
-      const float wj =
-          ml[(int64_t)j * kMlRecord + 1] * merge_weight(ml[(int64_t)j * kMlRecord], big);
-      float f[DPL];
-      load_part((int64_t)j * D + lane * DPL, f);
+    if constexpr (D == 128) {
+      // the four 16-lane rows take every fourth partition, 8 dims per lane
+      // (dims 8c .. 8c + 7), four partitions' loads in flight at a time; the
+      // rows' sums are then combined with 16/32-lane swaps
+      const int R = lane >> 4, c = lane & 15;
+      float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k0 = R; k0 < np; k0 += 16) {
+        float wv[4], v[4][8];
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] = fmaf(wj, f[k], o[k]);
+        for (int u = 0; u < 4; ++u) {
+          const int k = k0 + 4 * u < np ? k0 + 4 * u : R;   // past np: reread R, drop it
+          const int64_t j = slot_of(k);
+          wv[u] = k0 + 4 * u < np ? ml[j * kMlRecord + 1] * merge_weight(ml[j * kMlRecord], big)
+                                  : 0.0f;
+          const float* sl = po + j * D;
+          const int t0 = start + (k - np_pref) * pt;
+          const bool half = (!PFX || k >= np_pref) && a.part_half &&
+                            min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+          // 16 bytes at the lane's bf16 position, or 32 at its fp32 one
+          const uint4 w0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(sl) +
+                                                          (half ? 16 : 32) * c);
+          const uint4 w1 = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(sl) +
+                                                          (half ? 16 : 32) * c + 16);
+          if (half) {
+            Elem<uint16_t>::unpack(w0, v[u]);
+          } else {
+            Elem<float>::unpack(w0, v[u]);
+            Elem<float>::unpack(w1, v[u] + 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc8[e] = fmaf(wv[u], v[u][e], acc8[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc8[e] += xor_lanes<16>(acc8[e]);
+        acc8[e] += xor_lanes<32>(acc8[e]);
+      }
+      // lane (R, c) keeps dims 8c + 2R, 8c + 2R + 1 of the sum, which the
+      // store below expects as dims 2 * lane', 2 * lane' + 1 of lane'
+      // = 4c + R
+      const float d0 = acc8[2 * R], d1 = acc8[2 * R + 1];
+      const int src = ((lane & 3) << 4) | (lane >> 2);    // lane (R', c') with 4c' + R' = lane
+      o[0] = __shfl(d0, src);
+      o[1] = __shfl(d1, src);
+    } else {
+      for (int k = 0; k < np; ++k) {
+        const int64_t j = slot_of(k);
+        const float wj = ml[j * kMlRecord + 1] * merge_weight(ml[j * kMlRecord], big);
+        float f[DPL];
+        load_part(k, f);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = fmaf(wj, f[e], o[e]);
+      }
     }
   }
   T* out = reinterpret_cast<T*>(a.out) + ((int64_t)i * a.num_q_heads + hq) * D + lane * DPL;
@@ -1118,28 +1214,34 @@ constexpr int kMqVtRow = 40;     // bf16 elements per staged V^T row (32 positio
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return to_bf16(f); }
 
+// The per-tile kernel's work for workgroup (bx, by = KV head, bz = sequence
+// or group), staging V^T in s_vt.
 template <int BS, int G>
-__global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
+__device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz,
+                                         uint16_t (*s_vt)[128][kMqVtRow]) {
   constexpr int D = 128, ROW = 256;
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS % 16 == 0 && 16 % G == 0, "whole chunks per block, whole tokens per tile");
-  __shared__ __align__(16) uint16_t s_vt[kMqWaves][128][kMqVtRow];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = lane >> 4, c = lane & 15;
-  const int i = blockIdx.z, g = blockIdx.y;
+  const int i = bz, g = by;
   // units (tile, context partition), partition fastest, one per wave
-  const int unit = blockIdx.x * kMqWaves + w;
+  const int unit = bx * kMqWaves + w;
   const int part = unit % a.max_parts;
   const int tile = unit / a.max_parts;
 
-  // validate the sequence's length and query range (device-resident)
-  int L = a.seq_lens[i];
-  int q0, tq;
-  if (a.decode_mode) {
+  // validate the sequence's length and query range (device-resident). The
+  // walk covers positions [wstart, npos) of the sequence (the tile's last
+  // row sees npos - 1); row c sees positions up to pos_c (below).
+  int L, q0, tq, wstart = 0;
+  int64_t trow_base = (int64_t)i * a.max_blocks;
+  const int mode = a.mode ? a.mode : (a.decode_mode ? 1 : 0);
+  if (mode == 1 || mode == 3) {
     // pa_decode: token i; a length outside [0, len_cap] is clamped and
     // flagged, and an empty sequence gets zero rows
+    L = a.seq_lens[i];
     q0 = i;
     tq = 1;
     if (L < 0 || L > a.len_cap) {
@@ -1158,13 +1260,53 @@ __global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
           }
       return;
     }
+    if (mode == 3) {
+      // the positions after the shared prefix
+      wstart = a.prefix_lens[i];
+      if (wstart < 0 || wstart > L || wstart > a.max_prefix || wstart % BS != 0) {
+        if (lane == 0 && g == 0 && unit == 0) flag_error(kErrPrefix);
+        wstart = 0;
+      }
+      if (wstart == L) return;
+    }
+  } else if (mode == 2) {
+    // one group: its sequences are the query tokens, the first one's table
+    // and prefix length serve all of them, every row sees the whole prefix
+    q0 = a.group_start[i];
+    tq = a.group_start[i + 1] - q0;
+    if (q0 < 0 || tq < 0 || q0 + tq > a.num_tokens || tq > a.max_query_len) {
+      if (lane == 0 && g == 0 && unit == 0) flag_error(kErrPrefix);
+      return;
+    }
+    if (tq == 0) return;
+    L = a.prefix_lens[q0];
+    if (L < 0 || L > a.len_cap || L > a.max_prefix || L % BS != 0) {
+      if (lane == 0 && g == 0 && unit == 0) flag_error(kErrPrefix);
+      return;
+    }
+    if (L == 0) return;
+    trow_base = (int64_t)q0 * a.max_blocks;
+    if (g == 0 && unit == 0) {
+      // every member must share the prefix: same length, same blocks, and
+      // at least that many cached positions
+      bool bad = false;
+      const int nb = L / BS;
+      for (int k = lane; k < (tq - 1) * nb; k += 64) {
+        const int sm = q0 + 1 + k / nb, blk = k % nb;
+        bad |= a.block_tables[(int64_t)sm * a.max_blocks + blk] != a.block_tables[trow_base + blk];
+      }
+      for (int sm = q0 + lane; sm < q0 + tq; sm += 64)
+        bad |= a.prefix_lens[sm] != L || a.seq_lens[sm] < L;
+      if (__ballot(bad) != 0 && lane == 0) flag_error(kErrPrefix);
+    }
   } else {
+    L = a.seq_lens[i];
     q0 = a.query_start[i];
     const int q1 = a.query_start[i + 1];
     tq = q1 - q0;
     if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
         tq > a.max_query_len) {
-      if (lane == 0 && g == 0 && blockIdx.x == 0) flag_error(kErrQuery);
+      if (lane == 0 && g == 0 && bx == 0) flag_error(kErrQuery);
       return;
     }
   }
@@ -1172,20 +1314,26 @@ __global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
   if (tile * 16 >= rows) return;
   const int row0 = tile * 16;
   const int t_last = min(tq - 1, (row0 + 15) / G);
-  const int npos = L - tq + t_last + 1;          // positions the tile's last token sees
+  const bool causal = mode <= 1;
+  const int npos = causal ? L - tq + t_last + 1 : L;
   // this wave's context partition: positions [pos0, pos1)
-  const int nparts = a.part_tokens > 0 ? (npos + a.part_tokens - 1) / a.part_tokens : 1;
+  const int nparts =
+      a.part_tokens > 0 ? (npos - wstart + a.part_tokens - 1) / a.part_tokens : 1;
   if (part >= nparts) return;
-  const int pos0 = a.part_tokens > 0 ? part * a.part_tokens : 0;
+  const int pos0 = wstart + (a.part_tokens > 0 ? part * a.part_tokens : 0);
   const int pos1 = a.part_tokens > 0 ? min(npos, pos0 + a.part_tokens) : npos;
   const int ch0 = pos0 / 16;
   const int nch = (pos1 + 15) / 16 - ch0;
+  // the shared-prefix passes always leave partials (merged with the other
+  // pass); the per-sequence pass after the prefix pass's slots
+  const bool direct = causal && nparts == 1;
+  const int slot = (mode == 3 ? a.suffix_slot0 : 0) + part;
 
   // this lane's query row (column of S^T): token tc, head hc
   const int rc = row0 + c;
   const bool row_ok = rc < rows;
   const int tc = rc / G, hc = rc % G;
-  const int pos_c = L - tq + tc;                 // last position row c attends to
+  const int pos_c = causal ? L - tq + tc : L - 1;   // last position row c attends to
   bf16x8_t qop[4];
   {
     const int trow = row_ok ? tc : 0;
@@ -1203,7 +1351,6 @@ __global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * kHeadBytes;
   const uint32_t k_off = (uint32_t)(c * ROW + R * 16);
   const uint32_t v_off = (uint32_t)(4 * R * ROW + c * 16);
-  const int64_t trow_base = (int64_t)i * a.max_blocks;
 
   float m = -INFINITY, lsum = 0.0f;             // softmax state of row c
   f32x4_t acc[8];
@@ -1348,23 +1495,62 @@ __global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
     const int t = row / G, h = row % G;
     const int64_t qrow = (int64_t)(q0 + t) * a.num_q_heads + g * G + h;
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-    if (nparts == 1 || a.part_half) {
-      uint16_t* dst = nparts == 1 ? reinterpret_cast<uint16_t*>(a.out) + qrow * D + c
-                                  : reinterpret_cast<uint16_t*>(a.part_o) +
-                                        (qrow * a.max_parts + part) * D + c;
+    const int64_t pslot = qrow * (a.slot_stride ? a.slot_stride : a.max_parts) + slot;
+    if (direct || a.part_half) {
+      uint16_t* dst = direct ? reinterpret_cast<uint16_t*>(a.out) + qrow * D + c
+                             : reinterpret_cast<uint16_t*>(a.part_o) + pslot * D + c;
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[t2][r] * inv);
     } else {
-      float* dst = reinterpret_cast<float*>(a.part_o) + (qrow * a.max_parts + part) * D + c;
+      float* dst = reinterpret_cast<float*>(a.part_o) + pslot * D + c;
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = acc[t2][r] * inv;
     }
-    if (nparts > 1 && c == 0) {
-      float* ml = a.part_ml + (qrow * a.max_parts + part) * 2;
+    if (!direct && c == 0) {
+      // per row, or pa_decode's records: (sequence, KV head, slot), the
+      // group's heads side by side
+      float* ml = a.ml_records
+                      ? a.part_ml + (((int64_t)(q0 + t) * a.num_kv_heads + g) *
+                                         (a.slot_stride ? a.slot_stride : a.max_parts) + slot) *
+                                        kMlRecord + 2 * h
+                      : a.part_ml + pslot * 2;
       ml[0] = mr;
       ml[1] = lr;
     }
   }
+}
+
+template <int BS, int G>
+__global__ __launch_bounds__(kMqWaves * 64, 3) void multi_query_mfma(MqArgs a) {
+  __shared__ __align__(16) uint16_t s_vt[kMqWaves][128][kMqVtRow];
+  mq_tiles<BS, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, s_vt);
+}
+
+// Shared-prefix decode, both passes in one launch so that they run side by
+// side: workgroups 0 .. n_prefix - 1 are the prefix pass (the per-tile kernel
+// over (tile/partition group, KV head, group)), the rest the per-sequence
+// walks (pa_decode's matrix-core kernel after the prefix).
+struct CascadeArgs {
+  MqArgs pre;
+  DecodeArgs walk;
+  int32_t n_prefix;      // workgroups of the prefix pass
+  int32_t pre_gx;        // its grid: pre_gx x num_kv_heads x num_groups
+};
+
+template <int BS, int G>
+__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void shared_prefix_decode(CascadeArgs ca) {
+  __shared__ __align__(16) uint16_t s_vt[kMqWaves][128][kMqVtRow];
+  const int id = blockIdx.x;
+  if (id < ca.n_prefix) {
+    const int bx = id % ca.pre_gx, r = id / ca.pre_gx;
+    mq_tiles<BS, G>(ca.pre, bx, r % ca.pre.num_kv_heads, r / ca.pre.num_kv_heads, s_vt);
+    return;
+  }
+  PartitionWork wk;
+  if (!setup_partition<uint16_t, 128, BS, G, kDecodeWaves, true>(ca.walk, wk, id - ca.n_prefix))
+    return;
+  mfma_unit<BS, G, kDecodeWaves, false, true>(ca.walk, wk);
 }
 
 // Merge of the context partitions of pa_multi_query's split form: one wave
@@ -1379,11 +1565,17 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
   const int lr = blockIdx.x * kMqWaves + (threadIdx.x >> 6);   // row within the sequence
   int L = a.seq_lens[i];
   int q0, tq;
-  if (a.decode_mode) {
+  int np_pref = 0, start = 0;    // shared-prefix decode: the prefix pass's slots
+  if (a.decode_mode || a.mode == 3) {
     q0 = i;
     tq = 1;
     L = L < 0 ? 0 : min(L, a.len_cap);           // as multi_query_mfma
     if (L == 0) return;
+    if (a.mode == 3) {
+      start = a.prefix_lens[i];
+      if (start < 0 || start > L || start > a.max_prefix || start % a.block_size != 0) start = 0;
+      np_pref = (start + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
+    }
   } else {
     q0 = a.query_start[i];
     const int q1 = a.query_start[i + 1];
@@ -1397,13 +1589,19 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
   const int row0 = ((t * G + hq % G) / 16) * 16;  // first row of its tile
   const int t_last = min(tq - 1, (row0 + 15) / G);
   const int npos = L - tq + t_last + 1;
-  const int np = (npos + a.part_tokens - 1) / a.part_tokens;
-  if (np <= 1) return;
+  // partial k of the row sits in slot k, or for shared-prefix decode the
+  // prefix pass's np_pref slots come first, then the per-sequence pass's
+  const int np = a.mode == 3 ? np_pref + (L - start + a.part_tokens - 1) / a.part_tokens
+                             : (npos + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1 && a.mode != 3) return;
+  auto slot = [&](int k) { return a.mode == 3 && k >= np_pref ? a.suffix_slot0 + k - np_pref : k; };
   const int64_t qrow = (int64_t)(q0 + t) * a.num_q_heads + hq;
-  const float* ml = a.part_ml + qrow * a.max_parts * 2;
-  const int64_t po = qrow * a.max_parts * D;
+  const int64_t stride = a.slot_stride ? a.slot_stride : a.max_parts;
+  const float* ml = a.part_ml + qrow * stride * 2;
+  const int64_t po = qrow * stride * D;
   float mj = -INFINITY, lj = 0.0f;
-  for (int j = lane; j < np; j += 64) {
+  for (int k = lane; k < np; k += 64) {
+    const int j = slot(k);
     const float m2 = ml[2 * j], l2 = ml[2 * j + 1];
     const float big = fmaxf(mj, m2);
     lj = lj * merge_weight(mj, big) + l2 * merge_weight(m2, big);
@@ -1416,7 +1614,8 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
   float o[DPL] = {0.0f, 0.0f};
-  for (int j = 0; j < np; ++j) {
+  for (int k = 0; k < np; ++k) {
+    const int j = slot(k);
     const float wj = ml[2 * j + 1] * merge_weight(ml[2 * j], big);
     float f[DPL];
     if (a.part_half)
@@ -1859,9 +2058,32 @@ static PartitionKernel pick_partition(const DecodeKey& k) {
 
 bool decode_partition_supported(const DecodeKey& key) { return pick_partition(key) != nullptr; }
 
+template <int BS>
+static PartitionKernel pick_mfma_prefix(int group) {
+  switch (group) {
+    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves, false, true>;
+    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves, false, true>;
+    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves, false, true>;
+    default: return nullptr;
+  }
+}
+
 hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    hipStream_t stream) {
   PartitionKernel kern = pick_partition(key);
+  if (args.pos_start) {
+    // shared-prefix decode's per-sequence walk: bf16 matrix-core kernel only
+    kern = nullptr;
+    if (key.dtype == 1 && key.head_dim == 128 && key.variant == 2 && !key.kv_fp8) {
+      switch (key.block_size) {
+        case 16: kern = pick_mfma_prefix<16>(key.group); break;
+        case 32: kern = pick_mfma_prefix<32>(key.group); break;
+        case 64: kern = pick_mfma_prefix<64>(key.group); break;
+        case 128: kern = pick_mfma_prefix<128>(key.group); break;
+        default: break;
+      }
+    }
+  }
   if (!kern) return hipErrorInvalidValue;
   const int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
   if (groups <= 0) return hipSuccess;
@@ -1872,7 +2094,7 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
 
 hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
                                 hipStream_t stream) {
-  if (args.max_parts <= 1) return hipSuccess;
+  if (args.max_parts <= 1 && !args.pos_start) return hipSuccess;
   const int64_t pairs = (int64_t)args.num_seqs * args.num_q_heads;
   if (pairs <= 0) return hipSuccess;
   if (pairs > 0x7fffffff) return hipErrorInvalidValue;
@@ -1882,6 +2104,7 @@ hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
   if (dtype == 0 && head_dim == 128) kern = decode_reduce<float, 128>;
   if (dtype == 1 && head_dim == 64) kern = decode_reduce<uint16_t, 64>;
   if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
+  if (args.pos_start) kern = dtype == 1 && head_dim == 128 ? decode_reduce<uint16_t, 128, true> : nullptr;
   if (!kern) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kReduceWaves * 64), 0, stream, args);
   return hipGetLastError();
@@ -1998,7 +2221,8 @@ hipError_t launch_multi_query_tiles(int block_size, int group, const MqArgs& arg
 }
 
 hipError_t launch_multi_query_reduce(int group, const MqArgs& args, hipStream_t stream) {
-  if (args.max_parts <= 1) return hipSuccess;
+  // (shared-prefix decode always merges: its passes only leave partials)
+  if (args.max_parts <= 1 && args.mode != 3) return hipSuccess;
   if (args.num_seqs <= 0 || args.num_seqs > 65535) return args.num_seqs <= 0 ? hipSuccess
                                                                               : hipErrorInvalidValue;
   PartitionKernelMq red = nullptr;
@@ -2014,6 +2238,43 @@ hipError_t launch_multi_query_reduce(int group, const MqArgs& args, hipStream_t 
   if (rx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(red, dim3((unsigned)rx, (unsigned)args.num_seqs), dim3(kMqWaves * 64), 0,
                      stream, args);
+  return hipGetLastError();
+}
+
+template <int BS>
+static void (*pick_cascade(int group))(CascadeArgs) {
+  switch (group) {
+    case 1: return shared_prefix_decode<BS, 1>;
+    case 2: return shared_prefix_decode<BS, 2>;
+    case 4: return shared_prefix_decode<BS, 4>;
+    default: return nullptr;
+  }
+}
+
+hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& pre,
+                                       const DecodeArgs& walk, hipStream_t stream) {
+  void (*kern)(CascadeArgs) = nullptr;
+  switch (block_size) {
+    case 16: kern = pick_cascade<16>(group); break;
+    case 32: kern = pick_cascade<32>(group); break;
+    case 64: kern = pick_cascade<64>(group); break;
+    case 128: kern = pick_cascade<128>(group); break;
+    default: break;
+  }
+  if (!kern || !walk.pos_start || pre.mode != 2) return hipErrorInvalidValue;
+  CascadeArgs ca{};
+  ca.pre = pre;
+  ca.walk = walk;
+  const int64_t tiles = ((int64_t)pre.max_query_len * group + 15) / 16;
+  const int64_t pre_gx = pre.max_parts > 0 ? (tiles * pre.max_parts + kMqWaves - 1) / kMqWaves : 0;
+  const int64_t n_prefix = pre_gx * pre.num_kv_heads * pre.num_seqs;
+  const int64_t n_walk = (int64_t)walk.num_kv_heads * walk.num_seqs * walk.max_parts;
+  if (n_prefix + n_walk <= 0) return hipSuccess;
+  if (n_prefix + n_walk > 0x7fffffff) return hipErrorInvalidValue;
+  ca.n_prefix = (int32_t)n_prefix;
+  ca.pre_gx = (int32_t)(pre_gx > 0 ? pre_gx : 1);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(n_prefix + n_walk)), dim3(kMqWaves * 64), 0, stream,
+                     ca);
   return hipGetLastError();
 }
 

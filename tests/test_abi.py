@@ -55,15 +55,12 @@ def test_workspace_bytes():
     parts = 8
     rows = 4 * 32 * parts          # (sequence, query head, partition) partial outputs
     recs = 4 * 8 * parts           # (sequence, KV head, partition) 128-byte statistics records
-    # partial outputs: bf16 for bf16 runs with partitions of >= 256 positions, else fp32
-    for dtype, pt, eb in ((P.PA_BF16, 0, 2), (P.PA_F32, 0, 4), (P.PA_BF16, 256, 2)):
+    # partial outputs in fp32-sized slots (a full-length bf16 partial uses half of one)
+    for dtype, pt in ((P.PA_BF16, 0), (P.PA_F32, 0), (P.PA_BF16, 256), (P.PA_BF16, 128)):
         s = _shape(max_seq_len=4096, max_blocks_per_seq=256, dtype=dtype, partition_tokens=pt)
         n = 4096 // (pt or 512)
-        want = (-(-4 * 8 * n * 128 // 256) * 256 + -(-4 * 32 * n * 128 * eb // 256) * 256)
+        want = (-(-4 * 8 * n * 128 // 256) * 256 + -(-4 * 32 * n * 128 * 4 // 256) * 256)
         assert P.pa_decode_workspace_bytes(s) == want
-    s = _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=128)
-    assert P.pa_decode_workspace_bytes(s) == (-(-4 * 8 * 32 * 128 // 256) * 256 +
-                                             -(-4 * 32 * 32 * 128 * 4 // 256) * 256)
     assert P.pa_decode_workspace_bytes(_shape(num_q_heads=30)) == 0          # Hq % Hkv
     assert P.pa_decode_workspace_bytes(_shape(head_dim=96)) == 0
     assert P.pa_decode_workspace_bytes(_shape(partition_tokens=24)) == 0      # not a multiple of bs
@@ -126,16 +123,25 @@ def test_multi_query_workspace_bytes():
         return P.MultiQueryShape(*[base[k] for k in (
             "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
             "max_blocks_per_seq", "max_seq_len", "max_query_len", "num_tokens", "dtype")])
-    rows = 16 * 32 * 8                 # (token, query head) rows x 8 partitions of 512
-    want = -(-rows * 2 * 4 // 256) * 256 + -(-rows * 128 * 2 // 256) * 256
-    assert P.pa_multi_query_workspace_bytes(shape(), 512) == want
-    rows = 16 * 32 * 4                 # default: partitions of 1024
-    assert P.pa_multi_query_workspace_bytes(shape()) == (
-        -(-rows * 2 * 4 // 256) * 256 + -(-rows * 128 * 2 // 256) * 256)
-    rows16 = 16 * 32 * 256             # 16-position partitions: fp32 partial outputs
-    assert P.pa_multi_query_workspace_bytes(shape(), 16) == (
-        -(-rows16 * 8 // 256) * 256 + -(-rows16 * 128 * 4 // 256) * 256)
+    def want(parts):                   # (token, query head) rows x partitions; fp32 partials
+        rows = 16 * 32 * parts
+        return -(-rows * 2 * 4 // 256) * 256 + -(-rows * 128 * 4 // 256) * 256
+    assert P.pa_multi_query_workspace_bytes(shape(), 512) == want(8)
+    assert P.pa_multi_query_workspace_bytes(shape()) == want(4)      # default: 1024 positions
+    assert P.pa_multi_query_workspace_bytes(shape(), 16) == want(256)
     assert P.pa_multi_query_workspace_bytes(shape(max_seq_len=1024)) == 0   # one partition
     assert P.pa_multi_query_workspace_bytes(shape(max_query_len=32)) == 0   # 128 rows: tiled
     assert P.pa_multi_query_workspace_bytes(shape(), 24) == 0               # not a multiple of 16
     assert P.pa_multi_query_workspace_bytes(shape(num_q_heads=30)) == 0     # Hq % Hkv
+
+
+def test_shared_prefix_workspace_bytes():
+    s = _shape(max_seq_len=4096, max_blocks_per_seq=256)
+    slots = 1024 // 256 + 4096 // 512              # prefix pass (256) + walks (512) partitions
+    # 128-byte statistics records per (sequence, KV head, slot); fp32 partial outputs
+    want = -(-4 * 8 * slots * 128 // 256) * 256 + -(-4 * 32 * slots * 128 * 4 // 256) * 256
+    assert P.pa_decode_shared_prefix_workspace_bytes(s, 4, 1024) == want
+    assert P.pa_decode_shared_prefix_workspace_bytes(s, 4, 1000) == 0     # not whole blocks
+    assert P.pa_decode_shared_prefix_workspace_bytes(s, 0, 1024) == 0     # no group size
+    assert P.pa_decode_shared_prefix_workspace_bytes(
+        _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=-1), 4, 1024) == 0
