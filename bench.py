@@ -232,8 +232,10 @@ def main() -> int:
     torch.cuda.synchronize(dev)      # inputs drawn on the null stream are ready
     copied = [None] * NBUF    # H2D copy of staging buffer b done
     done = [None] * NBUF      # kernels reading device buffer b done
+    # forked samples share their prompt blocks: say so to the library
     shape = P.DecodeShape(B, hq, hkv, d, bs, nb, maxb, max_len, ptok,
-                          P.PA_BF16 if w.dtype == "bf16" else P.PA_F32, variant)
+                          P.PA_BF16 if w.dtype == "bf16" else P.PA_F32,
+                          variant | (P.PA_DECODE_SHARED_KV if prefix else 0))
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     step_bytes = []
     host_s = [0.0]  # host time per timed step, waits excluded
@@ -578,10 +580,11 @@ def swap_rate(P, torch, dev) -> dict:
 
 def shared_prefix_rate(P, torch, dev, w, q, k_pool, v_pool, db, plen, bs, max_len, scale,
                        unique_bytes, logical_bytes) -> dict:
-    """The last timed step of a shared-prefix workload decoded twice: with
-    pa_decode and with pa_decode_shared_prefix (the prompt groups passed as
-    groups; the blocks they share are the whole prompt blocks, the partial
-    one having been copied on write), both on the compute path alone."""
+    """The last timed step of a shared-prefix workload decoded three ways:
+    pa_decode with and without the shared-blocks hint, and
+    pa_decode_shared_prefix (the prompt groups passed as groups; the blocks
+    they share are the whole prompt blocks, the partial one having been
+    copied on write), all on the compute path alone."""
     ngroups, nsamp = w.extra["groups"], w.extra["samples"]
     B = q.shape[0]
     shared = (plen // bs) * bs
@@ -598,7 +601,10 @@ def shared_prefix_rate(P, torch, dev, w, q, k_pool, v_pool, db, plen, bs, max_le
     res = {}
     for name, fn in (
             ("pa_decode", lambda: P.pa_decode(q, k_pool, v_pool, tables, lens, scale, out,
-                                              max_seq_len=max_len, workspace=ws_d)),
+                                              max_seq_len=max_len, workspace=ws_d,
+                                              variant=P.PA_DECODE_SHARED_KV)),
+            ("pa_decode_no_hint", lambda: P.pa_decode(q, k_pool, v_pool, tables, lens, scale,
+                                                      out, max_seq_len=max_len, workspace=ws_d)),
             ("pa_decode_shared_prefix", lambda: P.pa_decode_shared_prefix(
                 q, k_pool, v_pool, tables, lens, scale, out, group_start=gs, prefix_lens=prefix,
                 max_group_size=nsamp, max_prefix_len=shared, max_seq_len=max_len,

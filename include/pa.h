@@ -74,6 +74,14 @@ typedef enum {
                                the multi-token kernel with one token per
                                sequence, both products on matrix cores (the
                                default there, ~2.5x the vector kernel)        */
+/* Hint OR-ed into pa_decode_shape_t.variant: sequences of the batch share
+ * physical blocks (samples forked from one prompt, [FP] "Copy-on-write
+ * sharing"). The group 1, 2, 4 matrix-core kernel then loads K/V with the
+ * plain cache policy, so that a shared block read by one sequence is still
+ * in L2 for the next; without it K/V loads stream (non-temporal), which is
+ * faster when every block belongs to one sequence. Results are identical
+ * either way. */
+#define PA_DECODE_SHARED_KV 0x100
 
 /* Shape of one pa_decode call. */
 typedef struct {
@@ -93,7 +101,7 @@ typedef struct {
                                  -1 = one partition per sequence, else a
                                  positive multiple of block_size               */
   int32_t dtype;              /* pa_dtype_t                                    */
-  int32_t variant;            /* PA_VARIANT_*                                  */
+  int32_t variant;            /* PA_VARIANT_*, optionally | PA_DECODE_SHARED_KV */
 } pa_decode_shape_t;
 
 /* Bytes of scratch workspace pa_decode needs for `shape`: the partial softmax
@@ -191,7 +199,8 @@ pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const voi
  * dot(q, code_K) and out = v_scale * sum_p softmax(s)_p code_V. shape->dtype
  * must be PA_BF16 (q, out), head_dim 128, group 1, 2 or 4, block size 16,
  * 32, 64 or 128; the matrix-core kernel runs whatever shape->variant says
- * (PA_VARIANT_VALU gives PA_EUNSUPPORTED). Workspace as pa_decode; the
+ * (PA_VARIANT_VALU gives PA_EUNSUPPORTED; PA_DECODE_SHARED_KV applies as in
+ * pa_decode). Workspace as pa_decode; the
  * second half is pa_decode_reduce unchanged.
  */
 pa_status_t pa_decode_e4m3(const void* q, const void* k_pool, const void* v_pool,

@@ -22,7 +22,7 @@ __all__ = [
     "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "PA_DEVERR_PREFIX",
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_decode_e4m3", "pa_reshape_and_cache_e4m3",
-    "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "DecodeShape",
+    "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "PA_DECODE_SHARED_KV", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
     "BlockManager", "EXPORTED_SYMBOLS",
@@ -36,6 +36,8 @@ PA_DEVERR_BLOCK_ID, PA_DEVERR_SEQ_LEN, PA_DEVERR_SLOT, PA_DEVERR_COPY_PAIR = 0x1
 PA_DEVERR_QUERY = 0x10
 PA_DEVERR_PREFIX = 0x20
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
+# hint OR-ed into `variant`: the batch's sequences share blocks (pa.h)
+PA_DECODE_SHARED_KV = 0x100
 _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
            4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
 
@@ -295,9 +297,11 @@ def pa_decode_reduce(q, k_pool, block_tables, seq_lens, out, *, max_seq_len, par
 
 
 def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_scale, out, *,
-                   max_seq_len, partition_tokens=0, workspace=None, stream=None):
+                   max_seq_len, partition_tokens=0, variant=PA_VARIANT_MFMA, workspace=None,
+                   stream=None):
     """pa_decode over 8-bit pools (include/pa.h pa_decode_e4m3): q, out bf16
-    [B,Hq,D]; pools uint8 [NB,Hkv,bs,D] of FP8 E4M3 codes."""
+    [B,Hq,D]; pools uint8 [NB,Hkv,bs,D] of FP8 E4M3 codes. `variant` may carry
+    PA_DECODE_SHARED_KV (the kernel is always the matrix-core one)."""
     torch = _torch()
     dev = q.device
     _need(q, "q", dtype=torch.bfloat16, dim=3)
@@ -308,7 +312,7 @@ def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_
     _need(out, "out", dtype=q.dtype, device=dev)
     if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != tuple(q.shape):
         raise ValueError("shape mismatch")
-    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, PA_VARIANT_MFMA)
+    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, variant)
     need = pa_decode_workspace_bytes(shape)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

@@ -38,6 +38,9 @@ struct Plan {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// pa_decode_shape_t.variant: kernel choice in the low byte, hint flags above.
+constexpr int kVariantMask = 0xff;
+
 int auto_variant(const pa_decode_shape_t& s, int group) {
   if (s.dtype == PA_BF16 && s.head_dim == 128 &&
       (group == 1 || group == 2 || group == 4 || group == 8 || group == 16))
@@ -67,7 +70,9 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
       s->block_size != 128)
     return PA_EUNSUPPORTED;
   const int group = s->num_q_heads / s->num_kv_heads;
-  int variant = s->variant == PA_VARIANT_AUTO ? auto_variant(*s, group) : s->variant;
+  if (s->variant & ~(kVariantMask | PA_DECODE_SHARED_KV)) return PA_EINVAL;
+  const int base = s->variant & kVariantMask;
+  int variant = base == PA_VARIANT_AUTO ? auto_variant(*s, group) : base;
   if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
   plan->mq_route = decode_on_multi_query(*s, group, variant, kv_fp8);
   int pt = s->partition_tokens;
@@ -87,7 +92,8 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   const int64_t table_cap = (int64_t)s->max_blocks_per_seq * s->block_size;
   plan->len_cap = (int)(table_cap < s->max_seq_len ? table_cap : s->max_seq_len);
   plan->group = group;
-  plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant, kv_fp8};
+  plan->key = pa::DecodeKey{s->dtype, s->head_dim, s->block_size, group, variant, kv_fp8,
+                            (s->variant & PA_DECODE_SHARED_KV) != 0};
   if (!plan->mq_route && !pa::decode_partition_supported(plan->key)) return PA_EUNSUPPORTED;
   if (group * 2 > pa::kMlRecord) return PA_EUNSUPPORTED;
   const size_t rows = (size_t)s->num_seqs * s->num_q_heads * plan->max_parts;
@@ -158,12 +164,12 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
                                bool do_reduce, const float* fp8_scales = nullptr) {
   Plan plan;
   if (fp8_scales && shape &&
-      (shape->dtype != PA_BF16 || shape->variant == PA_VARIANT_VALU))
+      (shape->dtype != PA_BF16 || (shape->variant & kVariantMask) == PA_VARIANT_VALU))
     return PA_EUNSUPPORTED;
   pa_decode_shape_t s8{};
   if (fp8_scales) {           // the 8-bit kernel is a matrix-core variant
     s8 = *shape;
-    s8.variant = PA_VARIANT_MFMA;
+    s8.variant = PA_VARIANT_MFMA | (shape->variant & ~kVariantMask);
     shape = &s8;
   }
   pa_status_t st = make_plan(shape, &plan, fp8_scales != nullptr);

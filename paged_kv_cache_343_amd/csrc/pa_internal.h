@@ -142,6 +142,8 @@ struct DecodeKey {
   int group;       // 1, 2, 4, 8
   int variant;     // 1 VALU, 2 MFMA
   bool kv_fp8;     // pools hold FP8 E4M3 codes (q, out bf16)
+  bool cached_kv;  // blocks shared between sequences: plain (not streaming)
+                   //   K/V loads in the matrix-core kernel
 };
 
 // Returns hipErrorInvalidValue (and launches nothing) if `key` has no kernel.

@@ -619,9 +619,14 @@ struct KVChunk8 {                      // FP8 E4M3 pools: 128-byte rows
 #else
 #define PA_MFMA_BOUNDS(threads) __launch_bounds__(threads)
 #endif
-#ifndef PA_KV_LOAD_AUX
-#define PA_KV_LOAD_AUX 0
-#endif
+// Cache policies of the K/V loads (the buffer instructions' cache-policy
+// operand). Streaming (nt, non-temporal) is the default: each K/V line is
+// read once, and on the Llama-3-8B-shaped decode it takes about 4% off the
+// partition kernel. When sequences of one batch share blocks (forked samples,
+// a common prompt), a sequence reads lines that its neighbours in the grid
+// just brought into L2; the plain policy keeps them there.
+constexpr int kKvStream = 2;
+constexpr int kKvCached = 0;
 // depth of the K/V register pipeline of the matrix-core partition kernel
 #ifndef PA_PIPE_BF16
 #define PA_PIPE_BF16 2
@@ -640,22 +645,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16 bytes at voff + soff of the buffer (soff wave-uniform).
+// 16 bytes at voff + soff of the buffer (soff wave-uniform), cache policy POL.
+template <int POL>
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, PA_KV_LOAD_AUX);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+template <int POL>
 __device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, PA_KV_LOAD_AUX);
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL);
   return make_uint2(v.x, v.y);
 }
 
 // FP8 pools: K rows as two 16-byte loads per lane (dims 16R + 64h), V rows
 // as four 8-byte loads (dims 8c of rows 4R + jj); 2 KiB per chunk and pool.
-template <int BS>
+template <int BS, int POL = kKvStream>
 __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, const char* vbase,
                                               int64_t blk_bytes, int phys, int tok_in_blk,
                                               uint32_t k_off, uint32_t v_off, bool live) {
@@ -663,17 +670,17 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, co
   const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live ? 16 * ROW : 0);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live ? 16 * ROW : 0);
-  c.k[0] = buf_ld16(kr, k_off, 0);
-  c.k[1] = buf_ld16(kr, k_off, 64);
+  c.k[0] = buf_ld16<POL>(kr, k_off, 0);
+  c.k[1] = buf_ld16<POL>(kr, k_off, 64);
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld8(vr, v_off, jj * ROW);
+  for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld8<POL>(vr, v_off, jj * ROW);
 }
 
 // K and V rows of the 16-token chunk that starts at row `tok_in_blk` of
 // physical block `phys`. The chunk's base address is wave-uniform and goes
 // into the buffer descriptor (scalar registers); each lane only adds its own
 // fixed offset, so no per-lane 64-bit address is formed per chunk.
-template <int BS>
+template <int BS, int POL = kKvStream>
 __device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, const char* vbase,
                                               int64_t blk_bytes, int phys, int tok_in_blk,
                                               uint32_t k_off, uint32_t v_off, bool live) {
@@ -682,9 +689,9 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, con
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live ? 16 * ROW : 0);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live ? 16 * ROW : 0);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) c.k[s] = buf_ld16(kr, k_off, s * 64);
+  for (int s = 0; s < 4; ++s) c.k[s] = buf_ld16<POL>(kr, k_off, s * 64);
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld16(vr, v_off, jj * ROW);
+  for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld16<POL>(vr, v_off, jj * ROW);
 }
 
 // 16-token chunk that spans two 8-token blocks: lanes pick their block per
@@ -791,7 +798,7 @@ __device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4]
 // One work unit (sequence, KV head, partition) of the matrix-core kernel.
 // F8: the pools hold FP8 E4M3 codes (q and out stay bf16); scores use
 // qscale = scale * log2(e) * k_scale and outputs are multiplied by v_scale.
-template <int BS, int G, int NW, bool F8, bool PFX>
+template <int BS, int G, int NW, bool F8, bool PFX, int POL = kKvStream>
 __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWork& wk) {
   constexpr int D = 128;
   constexpr int ROW = F8 ? D : D * 2;             // bytes per token row
@@ -851,8 +858,8 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
       if constexpr (BS == 8) {
         load_kv_chunk_bs8(buf, kbase, vbase, blk_bytes, phys, __builtin_amdgcn_readlane(ids.y, tt));
       } else {
-        load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + tt) % BS, k_off,
-                          v_off, live);
+        load_kv_chunk<BS, POL>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + tt) % BS,
+                               k_off, v_off, live);
       }
     };
     // one stage: issue chunk t + NBUF - 1 into `nxt`, compute chunk t from
@@ -892,12 +899,12 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
   finish_partition<uint16_t, D, G, NW, 16, 8, PFX>(a, wk, mh, lh, acc, F8 ? a.out_scale : 1.0f);
 }
 
-template <int BS, int G, int NW, bool F8, bool PFX = false>
+template <int BS, int G, int NW, bool F8, bool PFX = false, int POL = kKvStream>
 __global__ PA_MFMA_BOUNDS(NW * 64) __attribute__((amdgpu_waves_per_eu(PFX ? 3 : 1)))
 void decode_partition_mfma(DecodeArgs a) {
   PartitionWork wk;
   if (!setup_partition<uint16_t, 128, BS, G, NW, PFX>(a, wk, blockIdx.x)) return;
-  mfma_unit<BS, G, NW, F8, PFX>(a, wk);
+  mfma_unit<BS, G, NW, F8, PFX, POL>(a, wk);
 }
 
 // ---------------------------------------------------------------------------
@@ -1064,6 +1071,93 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
 #pragma unroll
   for (int k = 0; k < DPL; ++k) Elem<T>::store(out + k, o[k] * inv);
+}
+
+// The reduce for bf16 output, head dim 128 and 4 query heads per KV head:
+// one wave per (sequence, KV head). Lane l serves head l / 16 of the group
+// and dims 8 (l % 16) .. + 7, so the group's statistics record is read once
+// and a partial slice is one 16-byte (bf16) or 32-byte (fp32) read per lane.
+// Lane c of a row holds the statistics of partition c of each batch of 16.
+__global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs a) {
+  constexpr int D = 128, G = 4, R = kReduceFast;
+  static_assert(R == 16, "one partition per lane of a 16-lane row");
+  const int unit = blockIdx.x * kReduceWaves + (threadIdx.x >> 6);
+  if (unit >= a.num_seqs * a.num_kv_heads) return;
+  const int g = unit % a.num_kv_heads, i = unit / a.num_kv_heads;
+  int len = a.seq_lens[i];
+  len = len < 0 ? 0 : min(len, a.len_cap);
+  const int pt = a.part_tokens;
+  const int np = (len + pt - 1) / pt;
+  if (np <= 1) return;                           // written by the partition kernel
+  const int lane = threadIdx.x & 63, h = lane >> 4, c = lane & 15;
+  const float* rec = a.part_ml + ((int64_t)i * a.num_kv_heads + g) * a.max_parts * kMlRecord + 2 * h;
+  const int64_t row = (int64_t)i * a.num_q_heads + g * G + h;
+  const char* po = reinterpret_cast<const char*>(a.part_o) + row * a.max_parts * D * 4;
+  float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  // batch of partitions j0 .. j0 + 15 with weights wj (lane c: partition j0 + c)
+  auto accumulate = [&](int j0, float wj) {
+    float v[R][8];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      // past np: partition j0's slice again (in bounds), weight 0
+      const int j = j0 + u < np ? j0 + u : j0;
+      const int t0 = j * pt;
+      const bool half = a.part_half && min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+      const char* sl = po + (int64_t)j * D * 4 + (half ? 16 : 32) * c;
+      const uint4 w0 = *reinterpret_cast<const uint4*>(sl);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(sl + 16);
+      float f[8];
+      Elem<uint16_t>::unpack(w0, f);
+      v[u][0] = half ? f[0] : __uint_as_float(w0.x);
+      v[u][1] = half ? f[1] : __uint_as_float(w0.y);
+      v[u][2] = half ? f[2] : __uint_as_float(w0.z);
+      v[u][3] = half ? f[3] : __uint_as_float(w0.w);
+      v[u][4] = half ? f[4] : __uint_as_float(w1.x);
+      v[u][5] = half ? f[5] : __uint_as_float(w1.y);
+      v[u][6] = half ? f[6] : __uint_as_float(w1.z);
+      v[u][7] = half ? f[7] : __uint_as_float(w1.w);
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const float w = __shfl(wj, (lane & 48) | u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, v[u][e], o[e]);
+    }
+  };
+  auto row_max = [](float x) {
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+  };
+  float wsum;
+  if (np <= R) {
+    // every read up front
+    const float mj = c < np ? rec[(int64_t)c * kMlRecord] : -INFINITY;
+    const float lj = c < np ? rec[(int64_t)c * kMlRecord + 1] : 0.0f;
+    const float wj = lj * merge_weight(mj, row_max(mj));
+    accumulate(0, wj);
+    wsum = wj;
+  } else {
+    float big = -INFINITY;
+    for (int j0 = 0; j0 < np; j0 += R)
+      if (j0 + c < np) big = fmaxf(big, rec[(int64_t)(j0 + c) * kMlRecord]);
+    big = row_max(big);
+    wsum = 0.0f;
+    for (int j0 = 0; j0 < np; j0 += R) {
+      const int j = j0 + c;
+      const float wj =
+          j < np ? rec[(int64_t)j * kMlRecord + 1] * merge_weight(rec[(int64_t)j * kMlRecord], big)
+                 : 0.0f;
+      accumulate(j0, wj);
+      wsum += wj;
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D + 8 * c;
+  store4<uint16_t>(out, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  store4<uint16_t>(out + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -2016,14 +2110,20 @@ static PartitionKernel pick_valu_t(int d, int bs, int group) {
   return nullptr;
 }
 
-template <int BS, bool F8>
-static PartitionKernel pick_mfma(int group) {
+template <int BS, bool F8, int POL>
+static PartitionKernel pick_mfma_pol(int group) {
   switch (group) {
-    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves, F8>;
-    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves, F8>;
-    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves, F8>;
+    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves, F8, false, POL>;
+    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves, F8, false, POL>;
+    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves, F8, false, POL>;
     default: return nullptr;
   }
+}
+
+template <int BS, bool F8>
+static PartitionKernel pick_mfma(const DecodeKey& k) {
+  return k.cached_kv ? pick_mfma_pol<BS, F8, kKvCached>(k.group)
+                     : pick_mfma_pol<BS, F8, kKvStream>(k.group);
 }
 
 static PartitionKernel pick_partition(const DecodeKey& k) {
@@ -2037,19 +2137,19 @@ static PartitionKernel pick_partition(const DecodeKey& k) {
     if (k.dtype != 1 || k.head_dim != 128) return nullptr;
     if (k.kv_fp8) {
       switch (k.block_size) {
-        case 16: return pick_mfma<16, true>(k.group);
-        case 32: return pick_mfma<32, true>(k.group);
-        case 64: return pick_mfma<64, true>(k.group);
-        case 128: return pick_mfma<128, true>(k.group);
+        case 16: return pick_mfma<16, true>(k);
+        case 32: return pick_mfma<32, true>(k);
+        case 64: return pick_mfma<64, true>(k);
+        case 128: return pick_mfma<128, true>(k);
         default: return nullptr;
       }
     }
     switch (k.block_size) {
-      case 8: return pick_mfma<8, false>(k.group);
-      case 16: return pick_mfma<16, false>(k.group);
-      case 32: return pick_mfma<32, false>(k.group);
-      case 64: return pick_mfma<64, false>(k.group);
-      case 128: return pick_mfma<128, false>(k.group);
+      case 8: return pick_mfma<8, false>(k);
+      case 16: return pick_mfma<16, false>(k);
+      case 32: return pick_mfma<32, false>(k);
+      case 64: return pick_mfma<64, false>(k);
+      case 128: return pick_mfma<128, false>(k);
       default: return nullptr;
     }
   }
@@ -2106,6 +2206,13 @@ hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
   if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
   if (args.pos_start) kern = dtype == 1 && head_dim == 128 ? decode_reduce<uint16_t, 128, true> : nullptr;
   if (!kern) return hipErrorInvalidValue;
+  if (!args.pos_start && dtype == 1 && head_dim == 128 && args.num_q_heads == 4 * args.num_kv_heads) {
+    // one wave per (sequence, KV head)
+    const int64_t units = (int64_t)args.num_seqs * args.num_kv_heads;
+    hipLaunchKernelGGL(decode_reduce_g4, dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
+                       dim3(kReduceWaves * 64), 0, stream, args);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kReduceWaves * 64), 0, stream, args);
   return hipGetLastError();
 }

@@ -64,6 +64,13 @@ def test_workspace_bytes():
     assert P.pa_decode_workspace_bytes(_shape(num_q_heads=30)) == 0          # Hq % Hkv
     assert P.pa_decode_workspace_bytes(_shape(head_dim=96)) == 0
     assert P.pa_decode_workspace_bytes(_shape(partition_tokens=24)) == 0      # not a multiple of bs
+    # the shared-blocks hint changes the loads' cache policy, not the plan
+    big = dict(max_seq_len=4096, max_blocks_per_seq=256)
+    for v in (P.PA_VARIANT_AUTO, P.PA_VARIANT_MFMA, P.PA_VARIANT_VALU):
+        assert (P.pa_decode_workspace_bytes(_shape(variant=v | P.PA_DECODE_SHARED_KV, **big)) ==
+                P.pa_decode_workspace_bytes(_shape(variant=v, **big)) > 0)
+    assert P.pa_decode_workspace_bytes(_shape(variant=0x200, **big)) == 0     # unknown flag
+    assert P.pa_decode_workspace_bytes(_shape(variant=3, **big)) == 0         # unknown kernel
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -75,6 +75,24 @@ def test_decode_over_code_pools(dev, hq, hkv, bs, ptok):
     assert np.array_equal(got[0], np.zeros_like(got[0]))
 
 
+def test_shared_kv_hint_same_bits(dev):
+    """The shared-blocks hint only changes the loads' cache policy."""
+    c, kc, vc = _code_case(dev, 32, 8, 16, [0, 17, 513, 1025, 2100])
+    kc_t, vc_t = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    outs = []
+    for variant in (P.PA_VARIANT_AUTO, P.PA_DECODE_SHARED_KV):
+        out = torch.full_like(c.q, float("nan"))
+        P.pa_decode_e4m3(c.q, kc_t, vc_t, c.tables, c.lens, c.scale, 0.37, 0.11, out,
+                         max_seq_len=c.max_len, variant=variant)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = O.decode(O.as_f64(c.oq, "bf16"), O.dequantize_e4m3(kc, 0.37), O.dequantize_e4m3(vc, 0.11),
+                   c.otables, c.olens, c.scale)
+    check_close(O.as_f64(to_storage_np(outs[1]), "bf16"), ref, "bf16", "e4m3 hint")
+
+
 def test_nan_codes_outside_sequences_do_not_leak(dev):
     lens = [5, 16, 17, 600, 1300]
     c, kc, vc = _code_case(dev, 32, 8, 16, lens, seed=421)

@@ -146,3 +146,30 @@ def test_shared_prefix_workloads(dev, name):
     ref = c.oracle_rows(pairs)
     got = O.as_f64(to_storage_np(out), "bf16")
     check_close(np.stack([got[i, h] for i, h in pairs]), ref, "bf16", f"{name} sampled")
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (16, 8, 32), (8, 8, 64), (32, 8, 128),
+                                       (64, 8, 16)])
+def test_shared_kv_hint_same_bits(dev, hq, hkv, bs):
+    """pa_decode with PA_DECODE_SHARED_KV (plain rather than streaming K/V
+    loads) on a batch with shared blocks: the same bits as without the hint,
+    and the oracle's values."""
+    c = _groups_case(131 + bs, hq, hkv, bs, [(4, 1024 // bs, [16, 40, 255, 1]),
+                                             (3, 3, [0, 17, 600]), (1, 0, [900])])
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q = to_device(c["q"], "bf16", dev)
+    kp, vp = to_device(c["kp"], "bf16", dev), to_device(c["vp"], "bf16", dev)
+    outs = []
+    for variant in (P.PA_VARIANT_AUTO, P.PA_VARIANT_AUTO | P.PA_DECODE_SHARED_KV,
+                    P.PA_VARIANT_MFMA | P.PA_DECODE_SHARED_KV):
+        out = torch.full_like(q, float("nan"))
+        P.pa_decode(q, kp, vp, t(c["tab"]), t(c["lens"]), scale_for(c["d"]), out,
+                    max_seq_len=int(c["lens"].max()), variant=variant)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+    ref = O.decode(O.as_f64(c["q"], "bf16"), O.as_f64(c["kp"], "bf16"),
+                   O.as_f64(c["vp"], "bf16"), c["tab"], c["lens"], scale_for(c["d"]))
+    check_close(O.as_f64(to_storage_np(outs[1]), "bf16"), ref, "bf16", f"hint {hq}/{hkv} bs {bs}")
