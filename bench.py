@@ -86,6 +86,8 @@ def main() -> int:
     ap.add_argument("--block-order", default="shuffled", choices=["shuffled", "identity"],
                     help="free-list order: a seeded permutation (scattered blocks, the "
                          "default) or 0, 1, 2, ... (each sequence's blocks contiguous)")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="launch pa_decode's full grid instead of a host work plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -211,13 +213,30 @@ def main() -> int:
     # the host run up to NBUF - 1 steps ahead, so host jitter never leaves the
     # GPU waiting, and the copy of step s+1 overlaps the kernels of step s.
     NBUF = 4
+    # forked samples share their prompt blocks: say so to the library
+    shape = P.DecodeShape(B, hq, hkv, d, bs, nb, maxb, max_len, ptok,
+                          P.PA_BF16 if w.dtype == "bf16" else P.PA_F32,
+                          variant | (P.PA_DECODE_SHARED_KV if prefix else 0))
+    # Work plan (pa_decode_plan): the host lists the step's (sequence,
+    # partition) units from the lengths it just exported, into the same
+    # staging buffer; the partition kernel's grid then holds only those.
+    plan_cap = 0
+    if not args.no_plan and not fp8:
+        try:
+            P.pa_decode_plan(shape, np.minimum(ctx + 1, max_len).astype(np.int32))
+            plan_cap = P.pa_decode_plan_capacity(shape)
+        except P.PaError:
+            plan_cap = 0                 # a shape on the per-tile kernel: full grid
     n_slots, n_lens, n_tab = 8 * B, 4 * B, 4 * B * maxb
-    pack_bytes = n_slots + n_lens + n_tab
+    plan_off = -(-(n_slots + n_lens + n_tab) // 16) * 16
+    base_bytes = n_slots + n_lens + n_tab
+    pack_bytes = plan_off + 16 * plan_cap
 
     def views(buf):
         return dict(slots=buf[:n_slots].view(torch.int64),
                     lens=buf[n_slots:n_slots + n_lens].view(torch.int32),
-                    tables=buf[n_slots + n_lens:].view(torch.int32).view(B, maxb))
+                    tables=buf[n_slots + n_lens:base_bytes].view(torch.int32).view(B, maxb),
+                    plan=buf[plan_off:pack_bytes].view(torch.int32))
 
     stage_raw = [torch.empty(pack_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(NBUF)]
     dev_raw = [torch.empty(pack_bytes, dtype=torch.uint8, device=dev) for _ in range(NBUF)]
@@ -232,15 +251,15 @@ def main() -> int:
     torch.cuda.synchronize(dev)      # inputs drawn on the null stream are ready
     copied = [None] * NBUF    # H2D copy of staging buffer b done
     done = [None] * NBUF      # kernels reading device buffer b done
-    # forked samples share their prompt blocks: say so to the library
-    shape = P.DecodeShape(B, hq, hkv, d, bs, nb, maxb, max_len, ptok,
-                          P.PA_BF16 if w.dtype == "bf16" else P.PA_F32,
-                          variant | (P.PA_DECODE_SHARED_KV if prefix else 0))
+    n_units = [0] * NBUF      # work-plan units in staging / device buffer b
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     step_bytes = []
     host_s = [0.0]  # host time per timed step, waits excluded
     step_lens = []  # shared-prefix workloads: lengths per step, for the unique bytes
     bm_s = [0.0]    # block manager (append + export) time
+    plan_s = [0.0]  # work plan time
+    nunits_c = ctypes.c_int32(0)
+    shape_ref = ctypes.byref(shape)
     ev = []  # per step: (reshape start, partition start, partition end, reduce end)
 
     # Host side of a step through the raw C ABI (block manager: append one
@@ -269,6 +288,14 @@ def main() -> int:
         if st != 0:
             raise P.PaError(st, "pa_bm_export")
         bm_s[0] += time.perf_counter() - t_bm
+        if plan_cap:
+            t_pl = time.perf_counter()
+            st = Lh.pa_decode_plan(shape_ref, sp["lens"], sp["plan"], plan_cap,
+                                   ctypes.byref(nunits_c))
+            if st != 0:
+                raise P.PaError(st, "pa_decode_plan")
+            n_units[b] = nunits_c.value
+            plan_s[0] += time.perf_counter() - t_pl
         step_bytes.append(int(lens_np[b].sum(dtype=np.int64)) * 2 * hkv * d * pool_eb)
         if prefix:
             step_lens.append(lens_np[b].copy())
@@ -278,7 +305,6 @@ def main() -> int:
     L = P.lib()
     c_scale = ctypes.c_float(scale)
     c_kscale, c_vscale = ctypes.c_float(k_scale), ctypes.c_float(v_scale)
-    shape_ref = ctypes.byref(shape)
     ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
     kp_ptr, vp_ptr, out_ptr = k_pool.data_ptr(), v_pool.data_ptr(), out.data_ptr()
     dt_code = P.PA_BF16 if w.dtype == "bf16" else P.PA_F32
@@ -314,7 +340,8 @@ def main() -> int:
             # (a GPU-side wait would make the runtime run the copy
             # synchronously), normally long since complete
             done[b].synchronize()
-        if hip.hipMemcpyAsync(dev_base[b], stage_base[b], pack_bytes, HIP_H2D, copier_handle):
+        nbytes = plan_off + 16 * n_units[b] if plan_cap else base_bytes
+        if hip.hipMemcpyAsync(dev_base[b], stage_base[b], nbytes, HIP_H2D, copier_handle):
             raise RuntimeError("hipMemcpyAsync failed")
         copied[b] = copy_ev[b]
         copied[b].record(copier)
@@ -335,6 +362,11 @@ def main() -> int:
                                              db["lens"], c_scale, c_kscale, c_vscale, out_ptr,
                                              shape_ref, ws_ptr, ws_bytes, cs),
                   "pa_decode_partition_e4m3")
+        elif plan_cap:
+            check(L.pa_decode_partition_planned(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
+                                                db["lens"], c_scale, out_ptr, shape_ref, db["plan"],
+                                                n_units[b], ws_ptr, ws_bytes, cs),
+                  "pa_decode_partition_planned")
         else:
             check(L.pa_decode_partition(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
                                         db["lens"], c_scale, out_ptr, shape_ref, ws_ptr, ws_bytes,
@@ -357,6 +389,7 @@ def main() -> int:
     step_bytes.clear()
     step_lens.clear()
     bm_s[0] = 0.0
+    plan_s[0] = 0.0
     t0 = time.perf_counter()
     for s in range(args.warmup, nsteps):
         h0 = time.perf_counter()
@@ -423,6 +456,7 @@ def main() -> int:
                    "context_tokens": (f"U{{{w.lengths[1]}..{w.lengths[2]}}}+step"
                                       if w.lengths[0] == "uniform" else f"{w.lengths}+step"),
                    "kernel": vname, "block_order": args.block_order,
+                   "work_plan": bool(plan_cap),
                    "kv_storage": "e4m3" if fp8 else w.dtype,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
@@ -442,6 +476,7 @@ def main() -> int:
     cache_bytes = B * 2 * hkv * d * (eb + pool_eb)
     result["rows"] = {
         "a1_block_manager_host_us": round(1e6 * bm_s[0] / K, 1),
+        "work_plan_host_us": round(1e6 * plan_s[0] / K, 1),
         "a2_reshape_and_cache": {"us": round(1e3 * float(np.mean(cache_ms)), 2),
                                  "bytes_moved": cache_bytes,
                                  "GBps": round(cache_bytes / (float(np.mean(cache_ms)) / 1e3) / 1e9, 1)},

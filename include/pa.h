@@ -64,6 +64,7 @@ typedef enum {
 #define PA_DEVERR_COPY_PAIR 0x8u  /* copy/swap pair id outside its pool         */
 #define PA_DEVERR_QUERY 0x10u     /* multi-query: bad query range or length    */
 #define PA_DEVERR_PREFIX 0x20u    /* shared-prefix decode: bad group or prefix  */
+#define PA_DEVERR_PLAN 0x40u      /* work plan entry: bad sequence, length or partition */
 
 /* Decode kernel variants (pa_decode_shape_t.variant). */
 #define PA_VARIANT_AUTO 0   /* library's choice for the shape                     */
@@ -146,6 +147,57 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 float scale, void* out, const pa_decode_shape_t* shape,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Work plans: pa_decode with a grid built on the host from the lengths.
+ *
+ * Same operation as pa_decode (same definition and citations). pa_decode's
+ * grid covers every (sequence, partition) pair up to max_seq_len, and the
+ * pairs past a sequence's own length exit at once. When the caller knows
+ * the lengths on the host (its block manager produced them), pa_decode_plan
+ * lists only the pairs that hold positions: every full partition first, in
+ * (sequence, partition) order, then each sequence's last, shorter partition,
+ * longest first (an empty sequence gets one unit that writes its zeros).
+ * The planned calls launch one workgroup per (unit, KV head) in that order.
+ * Each unit computes exactly what it computes in pa_decode, so the outputs
+ * are bit-identical to pa_decode's.
+ *
+ *   pa_decode_plan_capacity: units a plan for `shape` can hold at most
+ *     (num_seqs x partitions of max_seq_len); 0 if the shape is invalid.
+ *   pa_decode_plan: seq_lens [host] int32 [B], the same values the device
+ *     copy will hold; work_plan [host] int32 [capacity][4] receives one
+ *     entry (sequence, partition, that sequence's length, 0) per unit;
+ *     *num_units [host] receives their count.
+ *     PA_EINVAL if a length is negative or above min(max_seq_len,
+ *     max_blocks_per_seq * block_size), or capacity is too small.
+ *     PA_EUNSUPPORTED for shapes that run on the multi-token per-tile kernel
+ *     (8 or 16 query heads per KV head with PA_VARIANT_MFMA/AUTO).
+ *   pa_decode_planned / pa_decode_partition_planned: pa_decode /
+ *     pa_decode_partition with work_plan [dev] (16-byte aligned, the
+ *     pa_decode_plan output copied to the device) and its num_units. The
+ *     partition kernel takes each unit's length from its entry (seq_lens
+ *     serves the merge and the unplanned path). An entry whose sequence is
+ *     outside [0, B), whose length is negative or above the bound above, or
+ *     whose partition holds no position is skipped and raises
+ *     PA_DEVERR_PLAN. A plan built from other lengths than seq_lens leaves
+ *     outputs undefined (a partition missing from it is never computed,
+ *     and nothing is read outside the buffers). pa_decode_reduce
+ *     completes a pa_decode_partition_planned call as it does an unplanned
+ *     one.
+ */
+int64_t pa_decode_plan_capacity(const pa_decode_shape_t* shape);
+pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_lens,
+                           int32_t* work_plan, int64_t capacity, int32_t* num_units);
+pa_status_t pa_decode_planned(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              void* out, const pa_decode_shape_t* shape, const int32_t* work_plan,
+                              int32_t num_units, void* workspace, size_t workspace_bytes,
+                              void* stream);
+pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, const int32_t* seq_lens,
+                                        float scale, void* out, const pa_decode_shape_t* shape,
+                                        const int32_t* work_plan, int32_t num_units,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_decode_shared_prefix — pa_decode for a batch whose sequences come in

@@ -7,6 +7,7 @@ not been built, importing the binding's functions raises.
 
 Calls mirror the C ABI in include/pa.h:
     pa_decode, pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes,
+    pa_decode_plan_capacity, pa_decode_plan, pa_decode_planned, pa_decode_partition_planned,
     pa_reshape_and_cache, pa_copy_blocks, pa_swap_blocks, pa_device_errors,
     BlockManager (pa_bm_*).
 """
@@ -21,7 +22,8 @@ __all__ = [
     "LIB_PATH", "PaError", "lib", "PA_F32", "PA_BF16", "PA_DEVERR_BLOCK_ID", "PA_DEVERR_SEQ_LEN",
     "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "PA_DEVERR_PREFIX",
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
-    "pa_decode_e4m3", "pa_reshape_and_cache_e4m3",
+    "pa_decode_e4m3", "pa_reshape_and_cache_e4m3", "PA_DEVERR_PLAN",
+    "pa_decode_plan_capacity", "pa_decode_plan", "pa_decode_planned", "pa_decode_partition_planned",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "PA_DECODE_SHARED_KV", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
@@ -35,6 +37,7 @@ PA_F32, PA_BF16 = 0, 1
 PA_DEVERR_BLOCK_ID, PA_DEVERR_SEQ_LEN, PA_DEVERR_SLOT, PA_DEVERR_COPY_PAIR = 0x1, 0x2, 0x4, 0x8
 PA_DEVERR_QUERY = 0x10
 PA_DEVERR_PREFIX = 0x20
+PA_DEVERR_PLAN = 0x40
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 # hint OR-ed into `variant`: the batch's sequences share blocks (pa.h)
 PA_DECODE_SHARED_KV = 0x100
@@ -49,6 +52,8 @@ EXPORTED_SYMBOLS = (
     "pa_multi_query_split", "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
     "pa_decode_e4m3", "pa_decode_partition_e4m3",
     "pa_reshape_and_cache_e4m3",
+    "pa_decode_plan_capacity", "pa_decode_plan", "pa_decode_planned",
+    "pa_decode_partition_planned",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
     "pa_bm_set_swap_space", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_num_free_swap",
@@ -83,6 +88,14 @@ _SIGS = {
     "pa_decode_partition": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                    ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+    "pa_decode_plan_capacity": (_i64, [ctypes.POINTER(DecodeShape)]),
+    "pa_decode_plan": (_i32, [ctypes.POINTER(DecodeShape), _vp, _vp, _i64,
+                              ctypes.POINTER(_i32)]),
+    "pa_decode_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                 ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz, _vp]),
+    "pa_decode_partition_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                           ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz,
+                                           _vp]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _vp]),
@@ -194,9 +207,28 @@ def pa_decode_workspace_bytes(shape: DecodeShape) -> int:
     return int(lib().pa_decode_workspace_bytes(ctypes.byref(shape)))
 
 
+def pa_decode_plan_capacity(shape: DecodeShape) -> int:
+    return int(lib().pa_decode_plan_capacity(ctypes.byref(shape)))
+
+
+def pa_decode_plan(shape: DecodeShape, seq_lens_host) -> np.ndarray:
+    """Host work plan of a decode call (include/pa.h pa_decode_plan):
+    int32 [num_units, 4] entries (sequence, partition, length, 0), built
+    from the host lengths (int32 array-like [B])."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    if lens.shape != (shape.num_seqs,):
+        raise ValueError("seq_lens must hold num_seqs lengths")
+    cap = pa_decode_plan_capacity(shape)
+    plan = np.zeros((max(cap, 1), 4), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data, plan.ctypes.data, cap,
+                                ctypes.byref(n)), "pa_decode_plan")
+    return plan[:n.value].copy()
+
+
 def _decode_call(fn_name, q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
                  max_seq_len, partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None,
-                 stream=None):
+                 stream=None, work_plan=None):
     torch = _torch()
     dev = q.device
     _need(q, "q", dim=3)
@@ -215,12 +247,38 @@ def _decode_call(fn_name, q, k_pool, v_pool, block_tables, seq_lens, scale, out,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
+    plan_args = ()
+    if work_plan is not None:
+        _need(work_plan, "work_plan", dtype=torch.int32, dim=2, device=dev)
+        if work_plan.shape[1] != 4:
+            raise ValueError("work_plan must be [num_units, 4]")
+        plan_args = (work_plan.data_ptr(), int(work_plan.shape[0]))
     st = getattr(lib(), fn_name)(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
         seq_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
-        workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
+        *plan_args, workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev))
     _check(st, fn_name)
     return out
+
+
+def pa_decode_planned(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, work_plan,
+                      max_seq_len, partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None,
+                      stream=None):
+    """pa_decode over a host-built work plan (include/pa.h
+    pa_decode_planned); work_plan: the pa_decode_plan output as a device
+    int32 tensor [num_units, 4]."""
+    return _decode_call("pa_decode_planned", q, k_pool, v_pool, block_tables, seq_lens, scale,
+                        out, max_seq_len=max_seq_len, partition_tokens=partition_tokens,
+                        variant=variant, workspace=workspace, stream=stream, work_plan=work_plan)
+
+
+def pa_decode_partition_planned(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
+                                work_plan, max_seq_len, partition_tokens=0,
+                                variant=PA_VARIANT_AUTO, workspace, stream=None):
+    """First half of pa_decode_planned; pa_decode_reduce completes it."""
+    return _decode_call("pa_decode_partition_planned", q, k_pool, v_pool, block_tables, seq_lens,
+                        scale, out, max_seq_len=max_seq_len, partition_tokens=partition_tokens,
+                        variant=variant, workspace=workspace, stream=stream, work_plan=work_plan)
 
 
 def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,

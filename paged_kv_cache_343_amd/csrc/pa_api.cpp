@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -161,7 +162,8 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
                                const int32_t* block_tables, const int32_t* seq_lens, float scale,
                                void* out, const pa_decode_shape_t* shape, void* workspace,
                                size_t workspace_bytes, void* stream, bool do_partition,
-                               bool do_reduce, const float* fp8_scales = nullptr) {
+                               bool do_reduce, const float* fp8_scales = nullptr,
+                               const int32_t* work_plan = nullptr, int32_t num_units = -1) {
   Plan plan;
   if (fp8_scales && shape &&
       (shape->dtype != PA_BF16 || (shape->variant & kVariantMask) == PA_VARIANT_VALU))
@@ -184,6 +186,16 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
       return PA_EINVAL;
     a.qscale *= fp8_scales[0];
     a.out_scale = fp8_scales[1];
+  }
+  if (num_units >= 0) {
+    // a work plan from pa_decode_plan (the per-tile route has its own grid)
+    if (plan.mq_route) return PA_EUNSUPPORTED;
+    if ((int64_t)num_units > (int64_t)shape->num_seqs * plan.max_parts) return PA_EINVAL;
+    if (num_units > 0 && (!work_plan || !aligned16(work_plan)))
+      return PA_EINVAL;
+    a.plan = work_plan;
+    a.num_units = num_units;
+    if (num_units == 0) do_partition = false;   // nothing to compute or zero
   }
   if (shape->num_seqs == 0) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -243,6 +255,86 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
                                 void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
                      workspace_bytes, stream, true, false);
+}
+
+int64_t pa_decode_plan_capacity(const pa_decode_shape_t* shape) {
+  Plan plan;
+  if (make_plan(shape, &plan) != PA_OK) return 0;
+  return (int64_t)shape->num_seqs * plan.max_parts;
+}
+
+pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_lens,
+                           int32_t* work_plan, int64_t capacity, int32_t* num_units) {
+  Plan plan;
+  pa_status_t st = make_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  if (plan.mq_route) return PA_EUNSUPPORTED;
+  if (!num_units || (shape->num_seqs > 0 && (!seq_lens || !work_plan))) return PA_EINVAL;
+  const int pt = plan.part_tokens;
+  // Units with a full partition come first, in (sequence, partition) order;
+  // then each sequence's last, shorter partition (and the zero-output unit
+  // of an empty sequence), longest first, so that the grid ends on the
+  // shortest work.
+  int64_t n = 0;
+  for (int32_t i = 0; i < shape->num_seqs; ++i) {
+    const int32_t len = seq_lens[i];
+    if (len < 0 || len > plan.len_cap) return PA_EINVAL;
+    const int full = len / pt;
+    if (n + full > capacity) return PA_EINVAL;
+    for (int j = 0; j < full; ++j) {
+      int32_t* e = work_plan + 4 * n++;
+      e[0] = i;
+      e[1] = j;
+      e[2] = len;
+      e[3] = 0;
+    }
+  }
+  // tail units: bucketed by length, longest first, sequence order inside a bucket
+  std::vector<int32_t> count(pt + 1, 0), start(pt + 2, 0);
+  int64_t tails = 0;
+  for (int32_t i = 0; i < shape->num_seqs; ++i) {
+    const int32_t len = seq_lens[i];
+    if (len == 0 || len % pt != 0) {
+      ++count[len % pt];
+      ++tails;
+    }
+  }
+  if (n + tails > capacity) return PA_EINVAL;
+  for (int c = pt; c >= 0; --c) start[c] = (c == pt ? 0 : start[c + 1] + count[c + 1]);
+  for (int32_t i = 0; i < shape->num_seqs; ++i) {
+    const int32_t len = seq_lens[i];
+    if (len == 0 || len % pt != 0) {
+      int32_t* e = work_plan + 4 * (n + start[len % pt]++);
+      e[0] = i;
+      e[1] = len / pt;
+      e[2] = len;
+      e[3] = 0;
+    }
+  }
+  n += tails;
+  if (n > INT32_MAX) return PA_EINVAL;
+  *num_units = (int32_t)n;
+  return PA_OK;
+}
+
+pa_status_t pa_decode_planned(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              void* out, const pa_decode_shape_t* shape, const int32_t* work_plan,
+                              int32_t num_units, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (num_units < 0) return PA_EINVAL;
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, true, nullptr, work_plan, num_units);
+}
+
+pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, const int32_t* seq_lens,
+                                        float scale, void* out, const pa_decode_shape_t* shape,
+                                        const int32_t* work_plan, int32_t num_units,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_units < 0) return PA_EINVAL;
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, false, nullptr, work_plan, num_units);
 }
 
 pa_status_t pa_decode_e4m3(const void* q, const void* k_pool, const void* v_pool,

@@ -44,6 +44,10 @@ struct DecodeArgs {
   int32_t slot_stride;          // partial slots per row (0: max_parts)
   int32_t max_prefix;
   int32_t block_size;
+  // host-built work plan (pa_decode_plan): the grid covers num_units
+  // (sequence, partition) pairs x Hkv instead of B x max_parts x Hkv
+  const int32_t* plan;          // [num_units][4] (sequence, partition, length, 0) or null
+  int32_t num_units;
 };
 
 struct CacheArgs {

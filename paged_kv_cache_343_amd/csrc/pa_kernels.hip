@@ -57,6 +57,7 @@ constexpr uint32_t kErrSlot = 0x4u;
 constexpr uint32_t kErrCopyPair = 0x8u;
 constexpr uint32_t kErrQuery = 0x10u;
 constexpr uint32_t kErrPrefix = 0x20u;
+constexpr uint32_t kErrPlan = 0x40u;
 
 __device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_word, bit); }
 
@@ -407,10 +408,36 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
 // then head, then sequence.
 // Decodes workgroup id `id`; returns false if the workgroup has nothing to do
 // (after writing zeros for an empty sequence).
+// With a work plan (a.plan), unit u = (sequence, partition, length) comes
+// from a.plan[u] instead: rounds name (unit, block of 8 KV heads), head block
+// fastest, the same XCD deal inside a round; without Hkv % 8 == 0, KV head
+// fastest, then unit. The grid then holds only units with work, in the
+// plan's order.
 template <typename T, int D, int BS, int G, int NW, bool PFX = false>
 __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk,
                                                 int id) {
-  if (a.num_kv_heads % 8 == 0) {
+  if (!PFX && a.plan) {
+    // entry (sequence, partition, sequence length, 0): the length comes with
+    // the unit, so no dependent load of seq_lens precedes the table window
+    int4 e;
+    if (a.num_kv_heads % 8 == 0) {
+      const int x = id & 7, r = id >> 3, nb8 = a.num_kv_heads >> 3;
+      e = reinterpret_cast<const int4*>(a.plan)[r / nb8];
+      wk.g = (r % nb8) * 8 + ((x - e.y) & 7);
+    } else {
+      e = reinterpret_cast<const int4*>(a.plan)[id / a.num_kv_heads];
+      wk.g = id % a.num_kv_heads;
+    }
+    wk.i = e.x;
+    wk.j = e.y;
+    wk.len = e.z;
+    const int np = (wk.len + a.part_tokens - 1) / a.part_tokens;
+    if ((unsigned)wk.i >= (unsigned)a.num_seqs || (unsigned)wk.len > (unsigned)a.len_cap ||
+        wk.j < 0 || wk.j >= (np > 1 ? np : 1)) {
+      if (threadIdx.x == 0) flag_error(kErrPlan);
+      return false;
+    }
+  } else if (a.num_kv_heads % 8 == 0) {
     const int x = id & 7, r = id >> 3;
     wk.j = r % a.max_parts;
     const int rest = r / a.max_parts, nb8 = a.num_kv_heads >> 3;
@@ -422,7 +449,7 @@ __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWo
     wk.g = rest % a.num_kv_heads;
     wk.i = rest / a.num_kv_heads;
   }
-  wk.len = checked_len(a, wk.i);
+  if (PFX || !a.plan) wk.len = checked_len(a, wk.i);
   if (wk.len == 0) {
     if (wk.j == 0) write_zero_rows<T, D, G, NW>(a, wk.i, wk.g);
     return false;
@@ -2185,7 +2212,9 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
     }
   }
   if (!kern) return hipErrorInvalidValue;
-  const int64_t groups = (int64_t)args.num_kv_heads * args.num_seqs * args.max_parts;
+  const int64_t groups = (int64_t)args.num_kv_heads *
+                        (args.plan ? (int64_t)args.num_units
+                                   : (int64_t)args.num_seqs * args.max_parts);
   if (groups <= 0) return hipSuccess;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kDecodeWaves * 64), 0, stream, args);
