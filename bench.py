@@ -88,6 +88,8 @@ def main() -> int:
                          "default) or 0, 1, 2, ... (each sequence's blocks contiguous)")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch pa_decode's full grid instead of a host work plan")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="record the partition kernel's timing events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -394,7 +396,7 @@ def main() -> int:
     for s in range(args.warmup, nsteps):
         h0 = time.perf_counter()
         host_step(s, s % NBUF)
-        gpu_step(s, s % NBUF, True)
+        gpu_step(s, s % NBUF, (s - args.warmup) % args.event_every == 0)
         host_s[0] += time.perf_counter() - h0
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -430,7 +432,8 @@ def main() -> int:
         torch.cuda.synchronize()
         cache_ms.append(e[0].elapsed_time(e[1]))
         red_ms.append(e[1].elapsed_time(e[2]))
-    period_ms = [ev[k][0].elapsed_time(ev[k + 1][0]) for k in range(len(ev) - 1)]
+    period_ms = [ev[k][0].elapsed_time(ev[k + 1][0]) / args.event_every
+                 for k in range(len(ev) - 1)]
     log(f"GPU step period {1e3 * np.mean(period_ms):.1f} us")
     part_avg_s = float(np.mean(part_ms)) / 1e3
     bytes_per_launch = total_bytes / K
@@ -814,8 +817,10 @@ def _counter_rows(directory: str, counter: str):
         with open(f, newline="") as fh:
             for r in csv.DictReader(fh):
                 if r.get("Counter_Name") == counter:
-                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
-    return rows
+                    rows.append((int(r.get("Dispatch_Id") or len(rows)), r["Kernel_Name"],
+                                 float(r["Counter_Value"])))
+    rows.sort(key=lambda x: x[0])                 # dispatch order
+    return [(k, v) for _, k, v in rows]
 
 
 def summarise_traffic(args) -> int:
@@ -829,13 +834,16 @@ def summarise_traffic(args) -> int:
     per_launch = 0.0
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(directory, counter)
-        part = [v for k, v in rows if "decode_partition" in k]
+        # the step loop's partition kernel is the run's first decode_partition
+        # dispatch; later side measurements launch other instances
+        main = next((k for k, _ in rows if "decode_partition" in k), None)
+        part = [v for k, v in rows if k == main]
         cal = [v for k, v in rows if "copy_blocks_kernel" in k]
         if not part or not cal:
             raise RuntimeError(f"{counter}: need partition and copy dispatches in {directory}")
-        if args.steps and len(part) > args.steps:
-            part = part[-args.steps:]      # the timed steps; warm-up dispatches come first
-        variant = "mfma" if any("decode_partition_mfma" in k for k, _ in rows) else "valu"
+        # warm-up dispatches first, then the timed steps
+        part = part[args.warmup:args.warmup + args.steps] if args.steps else part
+        variant = "mfma" if "decode_partition_mfma" in main else "valu"
         # the calibration copies are the run's last copy dispatches (the
         # copy-on-write and swap measurements use the same kernel earlier)
         cal_kib = float(np.median(cal[-CALIBRATION_LAUNCHES:]))

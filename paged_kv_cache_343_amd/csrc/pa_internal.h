@@ -182,6 +182,14 @@ hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);
 #define PA_DECODE_WAVES 4
 #endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;
+// Waves per workgroup of the matrix-core decode kernel with 1, 2 or 4 query
+// heads per KV head (its shared-prefix walk keeps kDecodeWaves): two waves
+// make twice the workgroups, each walking 16 of a 512-position partition's
+// 32 chunks, which evens out the end of the grid.
+#ifndef PA_MFMA_DECODE_WAVES
+#define PA_MFMA_DECODE_WAVES 2
+#endif
+constexpr int kMfmaDecodeWaves = PA_MFMA_DECODE_WAVES;
 // Waves per workgroup of the partition merge (one wave per query head).
 constexpr int kReduceWaves = 4;
 

@@ -12,11 +12,11 @@
 // PagedAttention works"), so each block is one contiguous bs x D tile per
 // head and is read with full 16-byte, fully used loads.
 //
-// Work decomposition (one workgroup = 4 wave64s per (sequence, KV head,
-// context partition)):
-//   * a partition covers part_tokens consecutive positions; its blocks are
-//     dealt round-robin to the 4 waves; all G query heads of the KV head
-//     share every K/V load;
+// Work decomposition (one workgroup per (sequence, KV head, context
+// partition): 2 wave64s in the matrix-core kernel, 4 in the others):
+//   * a partition covers part_tokens consecutive positions; its 16-position
+//     chunks are dealt round-robin to the waves; all G query heads of the KV
+//     head share every K/V load;
 //   * inside a wave, lanes are split into "rows"; each row is an independent
 //     online-softmax stream over a fixed subset of the positions, so no
 //     cross-row communication happens in the main loop;
@@ -2140,9 +2140,9 @@ static PartitionKernel pick_valu_t(int d, int bs, int group) {
 template <int BS, bool F8, int POL>
 static PartitionKernel pick_mfma_pol(int group) {
   switch (group) {
-    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves, F8, false, POL>;
-    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves, F8, false, POL>;
-    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves, F8, false, POL>;
+    case 1: return decode_partition_mfma<BS, 1, kMfmaDecodeWaves, F8, false, POL>;
+    case 2: return decode_partition_mfma<BS, 2, kMfmaDecodeWaves, F8, false, POL>;
+    case 4: return decode_partition_mfma<BS, 4, kMfmaDecodeWaves, F8, false, POL>;
     default: return nullptr;
   }
 }
@@ -2217,7 +2217,8 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    : (int64_t)args.num_seqs * args.max_parts);
   if (groups <= 0) return hipSuccess;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kDecodeWaves * 64), 0, stream, args);
+  const int waves = key.variant == 2 && !args.pos_start ? kMfmaDecodeWaves : kDecodeWaves;
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(waves * 64), 0, stream, args);
   return hipGetLastError();
 }
 
