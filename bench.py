@@ -86,6 +86,9 @@ def main() -> int:
     ap.add_argument("--block-order", default="shuffled", choices=["shuffled", "identity"],
                     help="free-list order: a seeded permutation (scattered blocks, the "
                          "default) or 0, 1, 2, ... (each sequence's blocks contiguous)")
+    ap.add_argument("--upload-tables", action="store_true",
+                    help="upload whole block tables and lengths every step instead of keeping "
+                         "them on the device (pa_append_tokens)")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch pa_decode's full grid instead of a host work plan")
     ap.add_argument("--event-every", type=int, default=5,
@@ -209,12 +212,22 @@ def main() -> int:
         for i, L in enumerate(ctx):
             bm.add_seq(i, int(L))
     seq_ids = np.arange(B, dtype=np.int32)
-    # Per step the host produces slots (int64 [B]), lengths (int32 [B]) and
-    # block tables (int32 [B, maxb]); they travel in one packed pinned buffer
-    # and one H2D copy on a side stream. NBUF staging/device buffer pairs let
-    # the host run up to NBUF - 1 steps ahead, so host jitter never leaves the
-    # GPU waiting, and the copy of step s+1 overlaps the kernels of step s.
+    # Per step the host produces slots (int64 [B]) and the work plan; they
+    # travel in one packed pinned buffer and one H2D copy on a side stream.
+    # Block tables and lengths stay on the device: pa_append_tokens applies
+    # each step's append to them (the host block manager still decides every
+    # slot and block; the device copies are checked against it at the end).
+    # With --upload-tables the host exports tables (int32 [B, maxb]) and
+    # lengths (int32 [B]) into the same buffer every step instead. NBUF
+    # staging/device buffer pairs let the host run up to NBUF - 1 steps
+    # ahead, so host jitter never leaves the GPU waiting, and the copy of
+    # step s+1 overlaps the kernels of step s.
     NBUF = 4
+    upload = args.upload_tables
+    tab0, len0 = bm.export(list(range(B)), maxb)
+    lens_host = len0.astype(np.int32).copy()        # the host's lengths, kept by the loop
+    tables_dev = torch.from_numpy(tab0).to(dev)
+    lens_dev = torch.from_numpy(len0).to(dev)
     # forked samples share their prompt blocks: say so to the library
     shape = P.DecodeShape(B, hq, hkv, d, bs, nb, maxb, max_len, ptok,
                           P.PA_BF16 if w.dtype == "bf16" else P.PA_F32,
@@ -223,22 +236,24 @@ def main() -> int:
     # partition) units from the lengths it just exported, into the same
     # staging buffer; the partition kernel's grid then holds only those.
     plan_cap = 0
-    if not args.no_plan and not fp8:
+    if not args.no_plan and (ptok != 0 or not fp8):
         try:
             P.pa_decode_plan(shape, np.minimum(ctx + 1, max_len).astype(np.int32))
             plan_cap = P.pa_decode_plan_capacity(shape)
         except P.PaError:
             plan_cap = 0                 # a shape on the per-tile kernel: full grid
+    # layout: slots | plan (16-byte aligned) | lengths | tables
     n_slots, n_lens, n_tab = 8 * B, 4 * B, 4 * B * maxb
-    plan_off = -(-(n_slots + n_lens + n_tab) // 16) * 16
-    base_bytes = n_slots + n_lens + n_tab
-    pack_bytes = plan_off + 16 * plan_cap
+    plan_off = -(-n_slots // 16) * 16
+    lens_off = plan_off + 16 * plan_cap
+    tab_off = lens_off + n_lens
+    pack_bytes = tab_off + n_tab
 
     def views(buf):
         return dict(slots=buf[:n_slots].view(torch.int64),
-                    lens=buf[n_slots:n_slots + n_lens].view(torch.int32),
-                    tables=buf[n_slots + n_lens:base_bytes].view(torch.int32).view(B, maxb),
-                    plan=buf[plan_off:pack_bytes].view(torch.int32))
+                    plan=buf[plan_off:lens_off].view(torch.int32),
+                    lens=buf[lens_off:tab_off].view(torch.int32),
+                    tables=buf[tab_off:pack_bytes].view(torch.int32).view(B, maxb))
 
     stage_raw = [torch.empty(pack_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(NBUF)]
     dev_raw = [torch.empty(pack_bytes, dtype=torch.uint8, device=dev) for _ in range(NBUF)]
@@ -286,10 +301,14 @@ def main() -> int:
             raise P.PaError(st, "pa_bm_append_slots")
         if ncow.value:
             raise RuntimeError("no copy-on-write expected in this workload")
-        st = Lh.pa_bm_export(bm._h, ids_ptr, B, maxb, sp["tables"], sp["lens"])
-        if st != 0:
-            raise P.PaError(st, "pa_bm_export")
+        if upload:
+            st = Lh.pa_bm_export(bm._h, ids_ptr, B, maxb, sp["tables"], sp["lens"])
+            if st != 0:
+                raise P.PaError(st, "pa_bm_export")
         bm_s[0] += time.perf_counter() - t_bm
+        lens_host[:] += 1                    # every sequence appended one token
+        if not upload:
+            lens_np[b][:] = lens_host
         if plan_cap:
             t_pl = time.perf_counter()
             st = Lh.pa_decode_plan(shape_ref, sp["lens"], sp["plan"], plan_cap,
@@ -335,21 +354,34 @@ def main() -> int:
     stage_base = [x.data_ptr() for x in stage_raw]
     dev_base = [x.data_ptr() for x in dev_raw]
 
+    tab_dev_ptr, len_dev_ptr = tables_dev.data_ptr(), lens_dev.data_ptr()
+
     def gpu_step(s: int, b: int, timed: bool):
-        db = dptr[b]
+        db = dict(dptr[b])
+        if not upload:
+            db["tables"], db["lens"] = tab_dev_ptr, len_dev_ptr
         if done[b] is not None:
             # step s-NBUF no longer reads device buffer b; waited on the host
             # (a GPU-side wait would make the runtime run the copy
             # synchronously), normally long since complete
             done[b].synchronize()
-        nbytes = plan_off + 16 * n_units[b] if plan_cap else base_bytes
+        nbytes = pack_bytes if upload else plan_off + 16 * n_units[b]
         if hip.hipMemcpyAsync(dev_base[b], stage_base[b], nbytes, HIP_H2D, copier_handle):
             raise RuntimeError("hipMemcpyAsync failed")
         copied[b] = copy_ev[b]
         copied[b].record(copier)
         compute.wait_event(copied[b])
         evs = time_ev[s - args.warmup] if timed else None
-        if fp8:
+        if not upload and fp8:
+            check(L.pa_append_tokens_e4m3(kn_all[s].data_ptr(), vn_all[s].data_ptr(), db["slots"],
+                                          kp_ptr, vp_ptr, db["tables"], db["lens"], B, maxb, hkv,
+                                          d, bs, nb, c_kscale, c_vscale, cs),
+                  "pa_append_tokens_e4m3")
+        elif not upload:
+            check(L.pa_append_tokens(kn_all[s].data_ptr(), vn_all[s].data_ptr(), db["slots"],
+                                     kp_ptr, vp_ptr, db["tables"], db["lens"], B, maxb, hkv, d,
+                                     bs, nb, dt_code, cs), "pa_append_tokens")
+        elif fp8:
             check(L.pa_reshape_and_cache_e4m3(kn_all[s].data_ptr(), vn_all[s].data_ptr(),
                                               db["slots"], kp_ptr, vp_ptr, B, hkv, d, bs, nb,
                                               c_kscale, c_vscale, cs), "pa_reshape_and_cache_e4m3")
@@ -359,7 +391,13 @@ def main() -> int:
                   "pa_reshape_and_cache")
         if timed:
             evs[0].record(compute)
-        if fp8:
+        if fp8 and plan_cap:
+            check(L.pa_decode_partition_e4m3_planned(q_all[s].data_ptr(), kp_ptr, vp_ptr,
+                                                     db["tables"], db["lens"], c_scale, c_kscale,
+                                                     c_vscale, out_ptr, shape_ref, db["plan"],
+                                                     n_units[b], ws_ptr, ws_bytes, cs),
+                  "pa_decode_partition_e4m3_planned")
+        elif fp8:
             check(L.pa_decode_partition_e4m3(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
                                              db["lens"], c_scale, c_kscale, c_vscale, out_ptr,
                                              shape_ref, ws_ptr, ws_bytes, cs),
@@ -402,6 +440,18 @@ def main() -> int:
     t1 = time.perf_counter()
     if P.pa_device_errors() != 0:
         raise RuntimeError("device index error during the timed steps")
+    b_last = (nsteps - 1) % NBUF
+    if not upload:
+        # the device tables and lengths must be the host block manager's
+        st_last = stage[b_last]
+        bm.export(list(range(B)), maxb, st_last["tables"].numpy(), st_last["lens"].numpy())
+        if not (np.array_equal(tables_dev.cpu().numpy(), st_last["tables"].numpy()) and
+                np.array_equal(lens_dev.cpu().numpy(), st_last["lens"].numpy())):
+            raise RuntimeError("device block tables / lengths differ from the host block manager")
+        devbuf[b_last]["tables"].copy_(tables_dev)
+        devbuf[b_last]["lens"].copy_(lens_dev)
+        torch.cuda.synchronize()
+        log("device tables and lengths match the host block manager")
 
     log(f"timed {args.steps} steps in {t1 - t0:.3f} s; host enqueue {1e6 * host_s[0] / args.steps:.0f} us/step")
     wall = t1 - t0
@@ -410,8 +460,9 @@ def main() -> int:
     gbs = total_bytes / wall / 1e9
     part_ms = [a.elapsed_time(b) for a, b in ev]
     # the slot write and the merge, timed separately on the last step's inputs
-    # (the slot write rewrites the same slots with the same rows)
-    b_last = (nsteps - 1) % NBUF
+    # (the slot write rewrites the same slots with the same rows; the table and
+    # length upkeep of pa_append_tokens is left out there, since repeating it
+    # would advance the lengths)
     db = dptr[b_last]
     cache_ms, red_ms = [], []
     for _ in range(20):
@@ -460,6 +511,7 @@ def main() -> int:
                                       if w.lengths[0] == "uniform" else f"{w.lengths}+step"),
                    "kernel": vname, "block_order": args.block_order,
                    "work_plan": bool(plan_cap),
+                   "device_tables": not upload,
                    "kv_storage": "e4m3" if fp8 else w.dtype,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),

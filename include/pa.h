@@ -60,7 +60,9 @@ typedef enum {
 /* Bits of the device error word (pa_device_errors). */
 #define PA_DEVERR_BLOCK_ID 0x1u   /* block table entry outside [0, num_blocks) */
 #define PA_DEVERR_SEQ_LEN 0x2u    /* seq_len < 0, > max_seq_len, or > table   */
-#define PA_DEVERR_SLOT 0x4u       /* slot >= num_blocks * block_size          */
+#define PA_DEVERR_SLOT 0x4u       /* slot >= num_blocks * block_size, or an
+                                     appended slot that does not fit its
+                                     sequence's position (pa_append_tokens) */
 #define PA_DEVERR_COPY_PAIR 0x8u  /* copy/swap pair id outside its pool         */
 #define PA_DEVERR_QUERY 0x10u     /* multi-query: bad query range or length    */
 #define PA_DEVERR_PREFIX 0x20u    /* shared-prefix decode: bad group or prefix  */
@@ -266,6 +268,26 @@ pa_status_t pa_decode_partition_e4m3(const void* q, const void* k_pool, const vo
                                      const pa_decode_shape_t* shape, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* pa_decode_e4m3 / pa_decode_partition_e4m3 over a work plan from
+ * pa_decode_plan (same rules as pa_decode_planned). The automatic partition
+ * length of 8-bit pools (1024) is not the one pa_decode_plan assumes for the
+ * shape, so shape->partition_tokens must be set explicitly, for the plan and
+ * for the call; 0 gives PA_EINVAL. */
+pa_status_t pa_decode_e4m3_planned(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   float scale, float k_scale, float v_scale, void* out,
+                                   const pa_decode_shape_t* shape, const int32_t* work_plan,
+                                   int32_t num_units, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+pa_status_t pa_decode_partition_e4m3_planned(const void* q, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_tables,
+                                             const int32_t* seq_lens, float scale, float k_scale,
+                                             float v_scale, void* out,
+                                             const pa_decode_shape_t* shape,
+                                             const int32_t* work_plan, int32_t num_units,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
 /* Second half of pa_decode: for every sequence with more than one partition,
  * out[i][h] = sum_j w_j o_j / sum_j w_j with w_j = l_j * exp(m_j - max_j m_j),
  * read from the workspace pa_decode_partition filled. */
@@ -381,6 +403,47 @@ pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                       int32_t num_blocks, float k_scale, float v_scale,
                                       void* stream);
+
+/*
+ * pa_append_tokens — one decode step's append for every sequence, on the
+ * device: the slot write of pa_reshape_and_cache plus the device copies of
+ * the block table and the length kept in step with the host block manager.
+ *
+ * [ZQ] single-decode-step pseudo-code: take a block when the position starts
+ * one, put the new K/V at (last block, position % bs), and the sequence
+ * grows by one token. The host decides (pa_bm_append_slots gives each
+ * sequence its slot, after any new block or copy-on-write); this call
+ * applies the decision to device-resident tables and lengths, so a decode
+ * loop need not upload whole tables every step. Token t belongs to sequence
+ * t. For t < num_seqs with slot_mapping[t] >= 0 and p = seq_lens[t]:
+ *     pools[slot / bs][h][slot % bs][:] = k[t][h][:], v[t][h][:]   (all h)
+ *     block_tables[t][p / bs] = slot / bs;   seq_lens[t] = p + 1
+ * That table entry is the new block when p % bs == 0, the replacement block
+ * after a copy-on-write, and otherwise the entry already there. Table
+ * changes of fork, free and swap are not appends: upload those rows.
+ * slot < 0: nothing happens for that sequence. A position p < 0 or past the
+ * table (p / bs >= max_blocks_per_seq), or a slot with slot % bs != p % bs,
+ * raises PA_DEVERR_SLOT and leaves table and length unchanged (the K/V row
+ * is still written to its slot).
+ *
+ *   k, v          [dev] [num_seqs][Hkv][D]
+ *   slot_mapping  [dev] int64 [num_seqs]
+ *   block_tables  [dev] int32 [num_seqs][max_blocks_per_seq], updated
+ *   seq_lens      [dev] int32 [num_seqs], updated
+ *   pools, sizes, dtype and stream as pa_reshape_and_cache; the _e4m3 form
+ *   writes 8-bit pools as pa_reshape_and_cache_e4m3 does.
+ */
+pa_status_t pa_append_tokens(const void* k, const void* v, const int64_t* slot_mapping,
+                             void* k_pool, void* v_pool, int32_t* block_tables,
+                             int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype, void* stream);
+pa_status_t pa_append_tokens_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
+                                  void* k_pool, void* v_pool, int32_t* block_tables,
+                                  int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  float k_scale, float v_scale, void* stream);
 
 /*
  * pa_copy_blocks — copy-on-write duplication of whole physical blocks.

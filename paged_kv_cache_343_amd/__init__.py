@@ -8,7 +8,7 @@ not been built, importing the binding's functions raises.
 Calls mirror the C ABI in include/pa.h:
     pa_decode, pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes,
     pa_decode_plan_capacity, pa_decode_plan, pa_decode_planned, pa_decode_partition_planned,
-    pa_reshape_and_cache, pa_copy_blocks, pa_swap_blocks, pa_device_errors,
+    pa_reshape_and_cache, pa_append_tokens, pa_copy_blocks, pa_swap_blocks, pa_device_errors,
     BlockManager (pa_bm_*).
 """
 from __future__ import annotations
@@ -24,6 +24,7 @@ __all__ = [
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_decode_e4m3", "pa_reshape_and_cache_e4m3", "PA_DEVERR_PLAN",
     "pa_decode_plan_capacity", "pa_decode_plan", "pa_decode_planned", "pa_decode_partition_planned",
+    "pa_append_tokens",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "PA_DECODE_SHARED_KV", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
@@ -53,7 +54,8 @@ EXPORTED_SYMBOLS = (
     "pa_decode_e4m3", "pa_decode_partition_e4m3",
     "pa_reshape_and_cache_e4m3",
     "pa_decode_plan_capacity", "pa_decode_plan", "pa_decode_planned",
-    "pa_decode_partition_planned",
+    "pa_decode_partition_planned", "pa_decode_e4m3_planned", "pa_decode_partition_e4m3_planned",
+    "pa_append_tokens", "pa_append_tokens_e4m3",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
     "pa_bm_set_swap_space", "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_num_free_swap",
@@ -114,6 +116,17 @@ _SIGS = {
     "pa_decode_partition_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
                                         ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp,
                                         _sz, _vp]),
+    "pa_decode_e4m3_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp, _i32,
+                                      _vp, _sz, _vp]),
+    "pa_decode_partition_e4m3_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                                ctypes.c_float, ctypes.c_float, _vp,
+                                                ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz,
+                                                _vp]),
+    "pa_append_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _vp]),
+    "pa_append_tokens_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, ctypes.c_float, ctypes.c_float, _vp]),
     "pa_reshape_and_cache_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                          ctypes.c_float, ctypes.c_float, _vp]),
     "pa_device_errors": (_i32, [ctypes.POINTER(ctypes.c_uint32), _vp]),
@@ -356,10 +369,12 @@ def pa_decode_reduce(q, k_pool, block_tables, seq_lens, out, *, max_seq_len, par
 
 def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_scale, out, *,
                    max_seq_len, partition_tokens=0, variant=PA_VARIANT_MFMA, workspace=None,
-                   stream=None):
+                   stream=None, work_plan=None):
     """pa_decode over 8-bit pools (include/pa.h pa_decode_e4m3): q, out bf16
     [B,Hq,D]; pools uint8 [NB,Hkv,bs,D] of FP8 E4M3 codes. `variant` may carry
-    PA_DECODE_SHARED_KV (the kernel is always the matrix-core one)."""
+    PA_DECODE_SHARED_KV (the kernel is always the matrix-core one). With
+    `work_plan` (device int32 [num_units, 4] from pa_decode_plan, built with
+    the same explicit partition_tokens) it calls pa_decode_e4m3_planned."""
     torch = _torch()
     dev = q.device
     _need(q, "q", dtype=torch.bfloat16, dim=3)
@@ -374,12 +389,18 @@ def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_
     need = pa_decode_workspace_bytes(shape)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    st = lib().pa_decode_e4m3(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                              block_tables.data_ptr(), seq_lens.data_ptr(), ctypes.c_float(scale),
-                              ctypes.c_float(k_scale), ctypes.c_float(v_scale), out.data_ptr(),
-                              ctypes.byref(shape), workspace.data_ptr(),
-                              workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
-    _check(st, "pa_decode_e4m3")
+    fn, plan_args = "pa_decode_e4m3", ()
+    if work_plan is not None:
+        _need(work_plan, "work_plan", dtype=torch.int32, dim=2, device=dev)
+        if work_plan.shape[1] != 4:
+            raise ValueError("work_plan must be [num_units, 4]")
+        fn, plan_args = "pa_decode_e4m3_planned", (work_plan.data_ptr(), int(work_plan.shape[0]))
+    st = getattr(lib(), fn)(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                            block_tables.data_ptr(), seq_lens.data_ptr(), ctypes.c_float(scale),
+                            ctypes.c_float(k_scale), ctypes.c_float(v_scale), out.data_ptr(),
+                            ctypes.byref(shape), *plan_args, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    _check(st, fn)
     return out
 
 
@@ -472,6 +493,40 @@ def pa_reshape_and_cache(k, v, slot_mapping, k_pool, v_pool, stream=None):
                                     k_pool.data_ptr(), v_pool.data_ptr(), T, hkv, d, bs, nb,
                                     _dtype_code(k_pool), _stream_ptr(stream, dev))
     _check(st, "pa_reshape_and_cache")
+
+
+def pa_append_tokens(k, v, slot_mapping, k_pool, v_pool, block_tables, seq_lens, stream=None,
+                     kv_scales=None):
+    """One token per sequence (include/pa.h pa_append_tokens): k/v [B,Hkv,D]
+    written at slot_mapping (int64 [B]), and the device block_tables (int32
+    [B,maxb]) and seq_lens (int32 [B]) updated in place. With uint8 pools of
+    FP8 codes pass kv_scales=(k_scale, v_scale) (pa_append_tokens_e4m3)."""
+    torch = _torch()
+    dev = k_pool.device
+    fp8 = k_pool.dtype == torch.uint8
+    _need(k, "k", dtype=torch.bfloat16 if fp8 else k_pool.dtype, dim=3, device=dev)
+    _need(v, "v", dtype=k.dtype, dim=3, device=dev)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, dim=1, device=dev)
+    _need(k_pool, "k_pool", dim=4)
+    _need(v_pool, "v_pool", dtype=k_pool.dtype, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=dev)
+    nb, hkv, bs, d = k_pool.shape
+    B = k.shape[0]
+    if (tuple(k.shape) != (B, hkv, d) or tuple(v.shape) != (B, hkv, d) or
+            slot_mapping.shape[0] != B or block_tables.shape[0] != B or seq_lens.shape[0] != B):
+        raise ValueError("shape mismatch")
+    common = (k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_pool.data_ptr(),
+              v_pool.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), B,
+              block_tables.shape[1], hkv, d, bs, nb)
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("8-bit pools need kv_scales")
+        st = lib().pa_append_tokens_e4m3(*common, ctypes.c_float(kv_scales[0]),
+                                         ctypes.c_float(kv_scales[1]), _stream_ptr(stream, dev))
+    else:
+        st = lib().pa_append_tokens(*common, _dtype_code(k_pool), _stream_ptr(stream, dev))
+    _check(st, "pa_append_tokens")
 
 
 def pa_copy_blocks(k_pool, v_pool, pairs, stream=None):

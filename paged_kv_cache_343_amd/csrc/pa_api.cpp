@@ -357,6 +357,32 @@ pa_status_t pa_decode_partition_e4m3(const void* q, const void* k_pool, const vo
                      workspace_bytes, stream, true, false, sc);
 }
 
+pa_status_t pa_decode_e4m3_planned(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   float scale, float k_scale, float v_scale, void* out,
+                                   const pa_decode_shape_t* shape, const int32_t* work_plan,
+                                   int32_t num_units, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (num_units < 0 || !shape || shape->partition_tokens == 0) return PA_EINVAL;
+  const float sc[2] = {k_scale, v_scale};
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, true, sc, work_plan, num_units);
+}
+
+pa_status_t pa_decode_partition_e4m3_planned(const void* q, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_tables,
+                                             const int32_t* seq_lens, float scale, float k_scale,
+                                             float v_scale, void* out,
+                                             const pa_decode_shape_t* shape,
+                                             const int32_t* work_plan, int32_t num_units,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (num_units < 0 || !shape || shape->partition_tokens == 0) return PA_EINVAL;
+  const float sc[2] = {k_scale, v_scale};
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
+                     workspace_bytes, stream, true, false, sc, work_plan, num_units);
+}
+
 pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode_shape_t* shape,
                              void* workspace, size_t workspace_bytes, void* stream) {
   Plan plan;
@@ -659,10 +685,11 @@ pa_status_t pa_multi_query_split(const void* q, const void* k_pool, const void* 
                           shape, sp, workspace, stream);
 }
 
-pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
-                                 void* k_pool, void* v_pool, int32_t num_tokens,
-                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                 int32_t num_blocks, int32_t dtype, void* stream) {
+static pa_status_t cache_impl(const void* k, const void* v, const int64_t* slot_mapping,
+                              void* k_pool, void* v_pool, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t dtype, const pa::AppendArgs& ap,
+                              void* stream) {
   const int eb = elem_bytes(dtype);
   if (eb == 0 || num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0)
@@ -683,7 +710,38 @@ pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* sl
   a.num_kv_heads = num_kv_heads;
   a.row_chunks = head_dim * eb / 16;
   a.block_size = block_size;
+  a.append = ap;
   return from_hip(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                                 void* k_pool, void* v_pool, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t dtype, void* stream) {
+  return cache_impl(k, v, slot_mapping, k_pool, v_pool, num_tokens, num_kv_heads, head_dim,
+                    block_size, num_blocks, dtype, pa::AppendArgs{}, stream);
+}
+
+static pa_status_t append_args(int32_t* block_tables, int32_t* seq_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, pa::AppendArgs* ap) {
+  if (num_seqs > 0 && (!block_tables || !seq_lens)) return PA_EINVAL;
+  if (max_blocks_per_seq <= 0) return PA_EINVAL;
+  ap->block_tables = block_tables;
+  ap->seq_lens = seq_lens;
+  ap->max_blocks = max_blocks_per_seq;
+  return PA_OK;
+}
+
+pa_status_t pa_append_tokens(const void* k, const void* v, const int64_t* slot_mapping,
+                             void* k_pool, void* v_pool, int32_t* block_tables,
+                             int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype, void* stream) {
+  pa::AppendArgs ap{};
+  pa_status_t st = append_args(block_tables, seq_lens, num_seqs, max_blocks_per_seq, &ap);
+  if (st != PA_OK) return st;
+  return cache_impl(k, v, slot_mapping, k_pool, v_pool, num_seqs, num_kv_heads, head_dim,
+                    block_size, num_blocks, dtype, ap, stream);
 }
 
 static pa_status_t copy_impl(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
@@ -709,11 +767,11 @@ static pa_status_t copy_impl(const void* src_k, const void* src_v, void* dst_k, 
   return from_hip(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
-pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
-                                      void* k_pool, void* v_pool, int32_t num_tokens,
-                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                      int32_t num_blocks, float k_scale, float v_scale,
-                                      void* stream) {
+static pa_status_t cache_e4m3_impl(const void* k, const void* v, const int64_t* slot_mapping,
+                                   void* k_pool, void* v_pool, int32_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, float k_scale, float v_scale,
+                                   const pa::AppendArgs& ap, void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 16 != 0 ||
       block_size <= 0 || num_blocks <= 0)
     return PA_EINVAL;
@@ -736,7 +794,30 @@ pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_
   a.num_kv_heads = num_kv_heads;
   a.row_groups = head_dim / 8;
   a.block_size = block_size;
+  a.append = ap;
   return from_hip(pa::launch_reshape_and_cache_e4m3(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
+                                      void* k_pool, void* v_pool, int32_t num_tokens,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, float k_scale, float v_scale,
+                                      void* stream) {
+  return cache_e4m3_impl(k, v, slot_mapping, k_pool, v_pool, num_tokens, num_kv_heads, head_dim,
+                         block_size, num_blocks, k_scale, v_scale, pa::AppendArgs{}, stream);
+}
+
+pa_status_t pa_append_tokens_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
+                                  void* k_pool, void* v_pool, int32_t* block_tables,
+                                  int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  float k_scale, float v_scale, void* stream) {
+  pa::AppendArgs ap{};
+  pa_status_t st = append_args(block_tables, seq_lens, num_seqs, max_blocks_per_seq, &ap);
+  if (st != PA_OK) return st;
+  return cache_e4m3_impl(k, v, slot_mapping, k_pool, v_pool, num_seqs, num_kv_heads, head_dim,
+                         block_size, num_blocks, k_scale, v_scale, ap, stream);
 }
 
 pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int64_t* pairs, int32_t num_pairs,

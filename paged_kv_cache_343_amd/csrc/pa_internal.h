@@ -50,6 +50,14 @@ struct DecodeArgs {
   int32_t num_units;
 };
 
+// Device copies of the block tables and lengths kept in step with the host
+// block manager's append (token t = sequence t): null tables = no upkeep.
+struct AppendArgs {
+  int32_t* block_tables;        // [num_tokens][max_blocks]
+  int32_t* seq_lens;            // [num_tokens]
+  int32_t max_blocks;
+};
+
 struct CacheArgs {
   const void* k;                // [T][Hkv][D]
   const void* v;
@@ -61,6 +69,7 @@ struct CacheArgs {
   int32_t num_kv_heads;
   int32_t row_chunks;           // 16-byte chunks per (token, head) row = D * elem / 16
   int32_t block_size;
+  AppendArgs append;            // table / length upkeep (pa_append_tokens) or none
 };
 
 // Slot write into FP8 E4M3 pools from bf16 rows.
@@ -77,6 +86,7 @@ struct CacheArgs8 {
   int32_t num_kv_heads;
   int32_t row_groups;           // 8-element groups per row = D / 8
   int32_t block_size;
+  AppendArgs append;
 };
 
 // Whole-block copies from (src_k, src_v) to (dst_k, dst_v): the same pools

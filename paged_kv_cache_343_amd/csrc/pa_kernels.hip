@@ -1191,6 +1191,23 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
 // Slot write and block copy
 // ---------------------------------------------------------------------------
 // One thread per 16-byte chunk of a (token, head) row, K and V together.
+// Table and length upkeep of an appended token (one thread per token): the
+// token of sequence t lands at position p = seq_lens[t], so the block of its
+// slot becomes table entry p / bs (a new block, a copy-on-write
+// replacement, or the entry already there) and the length becomes p + 1.
+// A position outside the table, or a slot whose offset is not p % bs, is
+// flagged and leaves table and length alone.
+__device__ __forceinline__ void append_upkeep(const AppendArgs& ap, int64_t t, int64_t slot,
+                                              int block_size) {
+  const int p = ap.seq_lens[t];
+  if (p < 0 || p / block_size >= ap.max_blocks || slot % block_size != p % block_size) {
+    flag_error(kErrSlot);
+    return;
+  }
+  ap.block_tables[t * ap.max_blocks + p / block_size] = (int32_t)(slot / block_size);
+  ap.seq_lens[t] = p + 1;
+}
+
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)a.num_kv_heads * a.row_chunks;
@@ -1205,6 +1222,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
     if (rem == 0) flag_error(kErrSlot);
     return;
   }
+  if (a.append.block_tables && rem == 0) append_upkeep(a.append, t, slot, a.block_size);
   const int64_t b = slot / a.block_size, o = slot - b * a.block_size;
   const int64_t dst = ((b * a.num_kv_heads + h) * a.block_size + o) * a.row_chunks + c;
   const int64_t src = idx;  // [T][Hkv][row_chunks] is exactly the thread order
@@ -1245,6 +1263,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_e4m3_kernel(CacheArgs8 
     if (rem == 0) flag_error(kErrSlot);
     return;
   }
+  if (a.append.block_tables && rem == 0) append_upkeep(a.append, t, slot, a.block_size);
   const int64_t b = slot / a.block_size, o = slot - b * a.block_size;
   const int64_t dst = ((b * a.num_kv_heads + h) * a.block_size + o) * a.row_groups + c;
   for (int pool = 0; pool < 2; ++pool) {

@@ -110,3 +110,31 @@ def test_nan_codes_outside_sequences_do_not_leak(dev):
     got = O.as_f64(to_storage_np(out), "bf16")
     assert np.isfinite(got).all()
     check_close(got, ref, "bf16", "e4m3 nan poison")
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (8, 8, 32), (32, 8, 64)])
+@pytest.mark.parametrize("ptok", [1024, 256, -1])
+def test_planned_decode_over_code_pools(dev, hq, hkv, bs, ptok):
+    """pa_decode_e4m3_planned: bitwise equal to pa_decode_e4m3 at the same
+    explicit partition length, within tolerance of the oracle."""
+    lens = [0, 1, 15, 16, 17, 33, 511, 512, 513, 1025, 2100, 1024]
+    c, kc, vc = _code_case(dev, hq, hkv, bs, lens)
+    kc_t, vc_t = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    shape = P._decode_shape(c.q, kc_t, c.tables, c.max_len, ptok, P.PA_VARIANT_MFMA)
+    plan = torch.from_numpy(P.pa_decode_plan(shape, c.olens)).to(dev)
+    outs = []
+    for wp in (None, plan):
+        out = torch.full_like(c.q, float("nan"))
+        P.pa_decode_e4m3(c.q, kc_t, vc_t, c.tables, c.lens, c.scale, 0.37, 0.11, out,
+                         max_seq_len=c.max_len, partition_tokens=ptok, work_plan=wp)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    ref = O.decode(O.as_f64(c.oq, "bf16"), O.dequantize_e4m3(kc, 0.37), O.dequantize_e4m3(vc, 0.11),
+                   c.otables, c.olens, c.scale)
+    check_close(O.as_f64(to_storage_np(outs[1]), "bf16"), ref, "bf16", f"e4m3 planned {ptok}")
+    # the automatic length of 8-bit pools is not the plan's: refused on the host
+    with pytest.raises(P.PaError):
+        P.pa_decode_e4m3(c.q, kc_t, vc_t, c.tables, c.lens, c.scale, 0.37, 0.11, outs[0],
+                         max_seq_len=c.max_len, partition_tokens=0, work_plan=plan)
