@@ -193,9 +193,10 @@ hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);
 #endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;
 // Waves per workgroup of the matrix-core decode kernel with 1, 2 or 4 query
-// heads per KV head (its shared-prefix walk keeps kDecodeWaves): two waves
-// make twice the workgroups, each walking 16 of a 512-position partition's
-// 32 chunks, which evens out the end of the grid.
+// heads per KV head on large grids (small grids and its shared-prefix walk
+// keep kDecodeWaves): two waves make twice the workgroups, each walking 16
+// of a 512-position partition's 32 chunks, which evens out the end of the
+// grid.
 #ifndef PA_MFMA_DECODE_WAVES
 #define PA_MFMA_DECODE_WAVES 2
 #endif

@@ -13,7 +13,8 @@
 // head and is read with full 16-byte, fully used loads.
 //
 // Work decomposition (one workgroup per (sequence, KV head, context
-// partition): 2 wave64s in the matrix-core kernel, 4 in the others):
+// partition): 2 wave64s in the matrix-core kernel when the shape's full grid
+// has 1024 or more workgroups, 4 otherwise and in the other kernels):
 //   * a partition covers part_tokens consecutive positions; its 16-position
 //     chunks are dealt round-robin to the waves; all G query heads of the KV
 //     head share every K/V load;
@@ -2156,23 +2157,39 @@ static PartitionKernel pick_valu_t(int d, int bs, int group) {
   return nullptr;
 }
 
-template <int BS, bool F8, int POL>
-static PartitionKernel pick_mfma_pol(int group) {
+template <int BS, bool F8, int POL, int NW>
+static PartitionKernel pick_mfma_nw(int group) {
   switch (group) {
-    case 1: return decode_partition_mfma<BS, 1, kMfmaDecodeWaves, F8, false, POL>;
-    case 2: return decode_partition_mfma<BS, 2, kMfmaDecodeWaves, F8, false, POL>;
-    case 4: return decode_partition_mfma<BS, 4, kMfmaDecodeWaves, F8, false, POL>;
+    case 1: return decode_partition_mfma<BS, 1, NW, F8, false, POL>;
+    case 2: return decode_partition_mfma<BS, 2, NW, F8, false, POL>;
+    case 4: return decode_partition_mfma<BS, 4, NW, F8, false, POL>;
     default: return nullptr;
   }
 }
 
-template <int BS, bool F8>
-static PartitionKernel pick_mfma(const DecodeKey& k) {
-  return k.cached_kv ? pick_mfma_pol<BS, F8, kKvCached>(k.group)
-                     : pick_mfma_pol<BS, F8, kKvStream>(k.group);
+// Waves per workgroup of the matrix-core kernel for a shape whose full grid
+// (sequences x KV heads x partitions) has `groups` workgroups:
+// kMfmaDecodeWaves on grids that fill the chip several times over,
+// kDecodeWaves on small batches, where a unit's latency (more chunks per
+// wave) matters more than the end of the grid.
+constexpr int64_t kMfmaNarrowMinGroups = 1024;
+static int mfma_waves(int64_t groups) {
+  return groups >= kMfmaNarrowMinGroups ? kMfmaDecodeWaves : kDecodeWaves;
 }
 
-static PartitionKernel pick_partition(const DecodeKey& k) {
+template <int BS, bool F8, int POL>
+static PartitionKernel pick_mfma_pol(int group, int waves) {
+  return waves == kMfmaDecodeWaves ? pick_mfma_nw<BS, F8, POL, kMfmaDecodeWaves>(group)
+                                   : pick_mfma_nw<BS, F8, POL, kDecodeWaves>(group);
+}
+
+template <int BS, bool F8>
+static PartitionKernel pick_mfma(const DecodeKey& k, int waves) {
+  return k.cached_kv ? pick_mfma_pol<BS, F8, kKvCached>(k.group, waves)
+                     : pick_mfma_pol<BS, F8, kKvStream>(k.group, waves);
+}
+
+static PartitionKernel pick_partition(const DecodeKey& k, int waves = kDecodeWaves) {
   if (k.variant == 1) {
     if (k.kv_fp8) return nullptr;
     if (k.dtype == 0) return pick_valu_t<float>(k.head_dim, k.block_size, k.group);
@@ -2183,19 +2200,19 @@ static PartitionKernel pick_partition(const DecodeKey& k) {
     if (k.dtype != 1 || k.head_dim != 128) return nullptr;
     if (k.kv_fp8) {
       switch (k.block_size) {
-        case 16: return pick_mfma<16, true>(k);
-        case 32: return pick_mfma<32, true>(k);
-        case 64: return pick_mfma<64, true>(k);
-        case 128: return pick_mfma<128, true>(k);
+        case 16: return pick_mfma<16, true>(k, waves);
+        case 32: return pick_mfma<32, true>(k, waves);
+        case 64: return pick_mfma<64, true>(k, waves);
+        case 128: return pick_mfma<128, true>(k, waves);
         default: return nullptr;
       }
     }
     switch (k.block_size) {
-      case 8: return pick_mfma<8, false>(k);
-      case 16: return pick_mfma<16, false>(k);
-      case 32: return pick_mfma<32, false>(k);
-      case 64: return pick_mfma<64, false>(k);
-      case 128: return pick_mfma<128, false>(k);
+      case 8: return pick_mfma<8, false>(k, waves);
+      case 16: return pick_mfma<16, false>(k, waves);
+      case 32: return pick_mfma<32, false>(k, waves);
+      case 64: return pick_mfma<64, false>(k, waves);
+      case 128: return pick_mfma<128, false>(k, waves);
       default: return nullptr;
     }
   }
@@ -2216,7 +2233,16 @@ static PartitionKernel pick_mfma_prefix(int group) {
 
 hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    hipStream_t stream) {
-  PartitionKernel kern = pick_partition(key);
+  const int64_t groups = (int64_t)args.num_kv_heads *
+                        (args.plan ? (int64_t)args.num_units
+                                   : (int64_t)args.num_seqs * args.max_parts);
+  // the wave count follows the shape's full grid, so that a planned call
+  // runs the same kernel as the unplanned one (bit-identical results)
+  const bool mfma = key.variant == 2 && !args.pos_start;
+  const int waves =
+      mfma ? mfma_waves((int64_t)args.num_kv_heads * args.num_seqs * args.max_parts)
+           : kDecodeWaves;
+  PartitionKernel kern = pick_partition(key, waves);
   if (args.pos_start) {
     // shared-prefix decode's per-sequence walk: bf16 matrix-core kernel only
     kern = nullptr;
@@ -2231,12 +2257,8 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
     }
   }
   if (!kern) return hipErrorInvalidValue;
-  const int64_t groups = (int64_t)args.num_kv_heads *
-                        (args.plan ? (int64_t)args.num_units
-                                   : (int64_t)args.num_seqs * args.max_parts);
   if (groups <= 0) return hipSuccess;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
-  const int waves = key.variant == 2 && !args.pos_start ? kMfmaDecodeWaves : kDecodeWaves;
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(waves * 64), 0, stream, args);
   return hipGetLastError();
 }
