@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstdlib>
 #include <vector>
 
@@ -289,27 +290,35 @@ pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_le
       e[3] = 0;
     }
   }
-  // tail units: bucketed by length, longest first, sequence order inside a bucket
-  std::vector<int32_t> count(pt + 1, 0), start(pt + 2, 0);
-  int64_t tails = 0;
-  for (int32_t i = 0; i < shape->num_seqs; ++i) {
-    const int32_t len = seq_lens[i];
-    if (len == 0 || len % pt != 0) {
-      ++count[len % pt];
-      ++tails;
-    }
-  }
+  // tail units: longest first, sequence order among equals
+  std::vector<int32_t> tail;   // sequences with a shorter last partition (or none at all)
+  for (int32_t i = 0; i < shape->num_seqs; ++i)
+    if (seq_lens[i] == 0 || seq_lens[i] % pt != 0) tail.push_back(i);
+  const int64_t tails = (int64_t)tail.size();
   if (n + tails > capacity) return PA_EINVAL;
-  for (int c = pt; c >= 0; --c) start[c] = (c == pt ? 0 : start[c + 1] + count[c + 1]);
-  for (int32_t i = 0; i < shape->num_seqs; ++i) {
-    const int32_t len = seq_lens[i];
-    if (len == 0 || len % pt != 0) {
-      int32_t* e = work_plan + 4 * (n + start[len % pt]++);
-      e[0] = i;
-      e[1] = len / pt;
-      e[2] = len;
-      e[3] = 0;
+  auto put = [&](int64_t u, int32_t i) {
+    int32_t* e = work_plan + 4 * u;
+    e[0] = i;
+    e[1] = seq_lens[i] / pt;
+    e[2] = seq_lens[i];
+    e[3] = 0;
+  };
+  if (pt <= 65536) {
+    // counting sort on the last partition's length
+    std::vector<int32_t> start(pt + 2, 0);
+    for (int32_t i : tail) ++start[seq_lens[i] % pt];
+    int32_t acc = 0;
+    for (int c = pt; c >= 0; --c) {
+      const int32_t k = start[c];
+      start[c] = acc;
+      acc += k;
     }
+    for (int32_t i : tail) put(n + start[seq_lens[i] % pt]++, i);
+  } else {
+    std::stable_sort(tail.begin(), tail.end(), [&](int32_t x, int32_t y) {
+      return seq_lens[x] % pt > seq_lens[y] % pt;
+    });
+    for (int64_t k = 0; k < tails; ++k) put(n + k, tail[k]);
   }
   n += tails;
   if (n > INT32_MAX) return PA_EINVAL;

@@ -83,3 +83,21 @@ def test_plan_unsupported_on_the_per_tile_route():
     plan = P.pa_decode_plan(_shape(2, 100, hq=64, hkv=8, variant=P.PA_VARIANT_VALU),
                             np.array([10, 20], dtype=np.int32))
     assert [tuple(u) for u in plan] == [(1, 0, 20, 0), (0, 0, 10, 0)]
+
+
+@pytest.mark.parametrize("max_len", [3000, 70_000])
+def test_plan_single_partition_per_sequence(max_len):
+    """partition_tokens -1: one partition of the whole (rounded) maximum
+    length; every unit is a sequence's only partition, longest first. The
+    long case takes the planner's comparison sort instead of its counting sort."""
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, max_len + 1, 200).astype(np.int32)
+    lens[:3] = [0, max_len, 1]
+    shape = _shape(len(lens), max_len, -1)
+    plan = P.pa_decode_plan(shape, lens)
+    pt = -(-max_len // 16) * 16
+    full, tails = _expected([int(x) for x in lens], pt)
+    want = [(i, j) for _, i, j in full] + [(i, j) for _, i, j in
+                                           sorted(tails, key=lambda t: (-t[0], t[1]))]
+    assert [tuple(map(int, u[:2])) for u in plan] == want
+    assert (plan[:, 1] == 0).all()
