@@ -606,10 +606,15 @@ struct KVChunk {                       // bf16 pools
 // Two FP8 E4M3 codes (bytes 0-1, or 2-3 with HI) of a word as a bf16 pair.
 // The hardware conversion is exact (an E4M3 value has 4 significant bits),
 // so is dropping the float's low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two E4M3 codes (bytes 0-1, or 2-3 with HI) to two bf16: one gfx950
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1.0. Exact: every E4M3 value,
+// subnormals included, is a bf16 value.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f[1]) & 0xffff0000u) | (__float_as_uint(f[0]) >> 16);
+  const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <bool HI>

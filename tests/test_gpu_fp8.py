@@ -138,3 +138,31 @@ def test_planned_decode_over_code_pools(dev, hq, hkv, bs, ptok):
     with pytest.raises(P.PaError):
         P.pa_decode_e4m3(c.q, kc_t, vc_t, c.tables, c.lens, c.scale, 0.37, 0.11, outs[0],
                          max_seq_len=c.max_len, partition_tokens=0, work_plan=plan)
+
+
+def test_subnormal_codes_reach_the_scores_and_outputs(dev):
+    """K and V codes drawn only from the E4M3 subnormals (2^-9 .. 7 * 2^-9)
+    and zero, scale 1: with large q the scores depend on them entirely, and the
+    outputs are of their size, so a conversion that flushed subnormals would
+    fail against the oracle."""
+    c, _, _ = _code_case(dev, 32, 8, 16, [1, 17, 300, 513, 1025])
+    rng = np.random.default_rng(419)
+    shape = (c.nb, c.hkv, 16, 128)
+    kc = (rng.integers(0, 8, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+    vc = (rng.integers(1, 8, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+    q_np = (W.normal_values(tuple(c.q.shape), rng, "f32") * 1024).astype(np.float32)
+    q_bits = W.to_bf16_bits(q_np)
+    q = to_device(q_bits, "bf16", dev)
+    out = torch.empty_like(q)
+    P.pa_decode_e4m3(q, torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev), c.tables,
+                     c.lens, c.scale, 1.0, 1.0, out, max_seq_len=c.max_len, partition_tokens=512)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    ref = O.decode(O.as_f64(q_bits, "bf16"), O.dequantize_e4m3(kc, 1.0),
+                   O.dequantize_e4m3(vc, 1.0), c.otables, c.olens, c.scale)
+    # the test bites: K flushed to zero would give uniform weights (the mean of
+    # the V rows), V flushed to zero would give zeros; both are far from ref
+    flat = O.decode(O.as_f64(q_bits, "bf16") * 0.0, O.dequantize_e4m3(kc, 1.0),
+                    O.dequantize_e4m3(vc, 1.0), c.otables, c.olens, c.scale)
+    assert np.abs(flat - ref).max() > 0.01 and np.abs(ref).max() > 0.01
+    check_close(O.as_f64(to_storage_np(out), "bf16"), ref, "bf16", "e4m3 subnormal codes")
