@@ -98,6 +98,8 @@ def main() -> int:
                     help="launch pa_decode's full grid instead of a host work plan")
     ap.add_argument("--event-every", type=int, default=5,
                     help="record the partition kernel's timing events on every n-th timed step")
+    ap.add_argument("--done-every", type=int, default=2,
+                    help="record the step-completion event (buffer reuse) every n-th step (n <= 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -272,7 +274,7 @@ def main() -> int:
     copier = torch.cuda.Stream(dev)
     torch.cuda.synchronize(dev)      # inputs drawn on the null stream are ready
     copied = [None] * NBUF    # H2D copy of staging buffer b done
-    done = [None] * NBUF      # kernels reading device buffer b done
+    done_step = [-1] * NBUF   # step whose completion event sits in done_ev[step % NBUF]
     n_units = [0] * NBUF      # work-plan units in staging / device buffer b
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
     step_bytes = []
@@ -365,11 +367,14 @@ def main() -> int:
         db = dict(dptr[b])
         if not upload:
             db["tables"], db["lens"] = tab_dev_ptr, len_dev_ptr
-        if done[b] is not None:
-            # step s-NBUF no longer reads device buffer b; waited on the host
-            # (a GPU-side wait would make the runtime run the copy
-            # synchronously), normally long since complete
-            done[b].synchronize()
+        # step s-NBUF must no longer read device buffer b: wait (on the host; a
+        # GPU-side wait would make the runtime run the copy synchronously) on
+        # the first completion event recorded at or after that step, normally
+        # long since complete
+        for t in range(max(0, s - NBUF), s):
+            if done_step[t % NBUF] == t:
+                done_ev[t % NBUF].synchronize()
+                break
         nbytes = pack_bytes if upload else plan_off + 16 * n_units[b]
         if hip.hipMemcpyAsync(dev_base[b], stage_base[b], nbytes, HIP_H2D, copier_handle):
             raise RuntimeError("hipMemcpyAsync failed")
@@ -430,8 +435,9 @@ def main() -> int:
             ev.append(evs)
         check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
               "pa_decode_reduce")
-        done[b] = done_ev[b]
-        done[b].record(compute)
+        if s % args.done_every == 0 or s == nsteps - 1:
+            done_ev[s % NBUF].record(compute)
+            done_step[s % NBUF] = s
 
     for s in range(args.warmup):
         host_step(s, s % NBUF)
