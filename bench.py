@@ -113,6 +113,10 @@ def main() -> int:
     args = ap.parse_args()
     if args.traffic_from:
         return summarise_traffic(args)
+    if args.event_every < 1 or not 1 <= args.done_every <= 4 or args.steps < 1 or args.warmup < 0:
+        print("need --event-every >= 1, 1 <= --done-every <= 4, --steps >= 1, --warmup >= 0",
+              file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by sequence or KV head with no exchange, see the design notes.",
