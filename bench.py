@@ -75,8 +75,8 @@ def recorded_traffic(variant_name: str, workload: str = "llama3_8b"):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=None)
@@ -546,7 +546,14 @@ def main() -> int:
         "seq_steps_per_s": round(B * K / wall, 1),
         "kernels_us": {"partition": round(1e3 * float(np.mean(part_ms)), 2),
                        "reduce": round(1e3 * float(np.mean(red_ms)), 2),
-                       "reshape_and_cache": round(1e3 * float(np.mean(cache_ms)), 2)},
+                       "reshape_and_cache": round(1e3 * float(np.mean(cache_ms)), 2),
+                       # spread of the sampled partition launches and step periods
+                       "partition_p10_p50_p90": [round(1e3 * float(x), 2) for x in
+                                                 np.percentile(part_ms, [10, 50, 90])],
+                       "step_period_p10_p50_p90": ([round(1e3 * float(x), 2) for x in
+                                                    np.percentile(period_ms, [10, 50, 90])]
+                                                   if period_ms else None),
+                       "partition_samples": len(part_ms)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(vname, w.name) if default_launch else None,
