@@ -83,16 +83,41 @@ def test_planned_equals_unplanned_and_oracle(dev, shape, ptok):
     assert not got[0].any() and not got[11].any()          # empty sequences give zeros
 
 
-def test_planned_llama3_8b_full_size_bitwise(dev):
-    """The headline workload in the bench's launch configuration: the planned
-    partition kernel + merge equals pa_decode bitwise on every output."""
-    w = W.get("llama3_8b")
+@pytest.mark.parametrize("name", ["llama3_8b", "llama2_13b"])
+def test_planned_full_size_bitwise(dev, name):
+    """The workloads at full size in the bench's launch configuration: the
+    planned partition kernel + merge equals pa_decode bitwise on every output
+    (pa_decode itself is checked against the oracle at full size in
+    test_gpu_workloads.py)."""
+    w = W.get(name)
     c = build(w, dev, pool_on_device=True)
+    print("planned full size", name, flush=True)
     ref_out = c.decode()
     out = _planned(c, split=True)
     torch.cuda.synchronize()
     assert P.pa_device_errors() == 0
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+
+
+def test_planned_e4m3_full_size_bitwise(dev):
+    """The headline shape over 8-bit pools (the bench's --kv-dtype e4m3 leg:
+    partitions of 1024 positions): planned = unplanned bitwise."""
+    w = W.get("llama3_8b")
+    c = build(w, dev, pool_on_device=True)
+    print("planned full size e4m3", flush=True)
+    kc = W.random_e4m3_codes_device(tuple(c.k_pool.shape), 901, dev)
+    vc = W.random_e4m3_codes_device(tuple(c.v_pool.shape), 902, dev)
+    shape = P._decode_shape(c.q, kc, c.tables, c.max_len, 1024, P.PA_VARIANT_MFMA)
+    plan = torch.from_numpy(P.pa_decode_plan(shape, c.olens)).to(dev)
+    outs = []
+    for wp in (None, plan):
+        out = torch.empty_like(c.q)
+        P.pa_decode_e4m3(c.q, kc, vc, c.tables, c.lens, c.scale, 0.05, 0.05, out,
+                         max_seq_len=c.max_len, partition_tokens=1024, work_plan=wp)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
 def test_bad_plan_entries_are_skipped_and_flagged(dev):
