@@ -653,9 +653,10 @@ struct KVChunk8 {                      // FP8 E4M3 pools: 128-byte rows
 #define PA_MFMA_BOUNDS(threads) __launch_bounds__(threads)
 #endif
 // Cache policies of the K/V loads (the buffer instructions' cache-policy
-// operand). Streaming (nt, non-temporal) is the default: each K/V line is
+// operand). Streaming (nt, non-temporal) is the default: each V line is
 // read once, and on the Llama-3-8B-shaped decode it takes about 4% off the
-// partition kernel. When sequences of one batch share blocks (forked samples,
+// partition kernel. K lines are read in two halves by consecutive loads;
+// with 2 or 4 query heads per KV head they keep the plain policy (mfma_unit). When sequences of one batch share blocks (forked samples,
 // a common prompt), a sequence reads lines that its neighbours in the grid
 // just brought into L2; the plain policy keeps them there.
 constexpr int kKvStream = 2;
@@ -695,7 +696,7 @@ __device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 // FP8 pools: K rows as two 16-byte loads per lane (dims 16R + 64h), V rows
 // as four 8-byte loads (dims 8c of rows 4R + jj); 2 KiB per chunk and pool.
-template <int BS, int POL = kKvStream>
+template <int BS, int POL = kKvStream, int KPOL = POL>
 __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, const char* vbase,
                                               int64_t blk_bytes, int phys, int tok_in_blk,
                                               uint32_t k_off, uint32_t v_off, bool live) {
@@ -703,8 +704,8 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, co
   const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live ? 16 * ROW : 0);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live ? 16 * ROW : 0);
-  c.k[0] = buf_ld16<POL>(kr, k_off, 0);
-  c.k[1] = buf_ld16<POL>(kr, k_off, 64);
+  c.k[0] = buf_ld16<KPOL>(kr, k_off, 0);    // the two halves of each K line
+  c.k[1] = buf_ld16<KPOL>(kr, k_off, 64);   // (see the 16-bit form below)
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld8<POL>(vr, v_off, jj * ROW);
 }
@@ -713,7 +714,7 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk8& c, const char* kbase, co
 // physical block `phys`. The chunk's base address is wave-uniform and goes
 // into the buffer descriptor (scalar registers); each lane only adds its own
 // fixed offset, so no per-lane 64-bit address is formed per chunk.
-template <int BS, int POL = kKvStream>
+template <int BS, int POL = kKvStream, int KPOL = POL>
 __device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, const char* vbase,
                                               int64_t blk_bytes, int phys, int tok_in_blk,
                                               uint32_t k_off, uint32_t v_off, bool live) {
@@ -721,8 +722,12 @@ __device__ __forceinline__ void load_kv_chunk(KVChunk& c, const char* kbase, con
   const int64_t base = (int64_t)phys * blk_bytes + (int64_t)tok_in_blk * ROW;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + base, live ? 16 * ROW : 0);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + base, live ? 16 * ROW : 0);
+  // K: one load covers 64 bytes of each of 16 token rows, so loads s and
+  // s + 1 read the two halves of the same 128-byte lines; with the plain
+  // policy (KPOL) the second half is an L1 hit, where streaming K loads
+  // fetch each line twice from L2. V loads cover whole rows and keep POL.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) c.k[s] = buf_ld16<POL>(kr, k_off, s * 64);
+  for (int s = 0; s < 4; ++s) c.k[s] = buf_ld16<KPOL>(kr, k_off, s * 64);
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) c.v[jj] = buf_ld16<POL>(vr, v_off, jj * ROW);
 }
@@ -841,6 +846,10 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
   using Chunk = typename std::conditional<F8, KVChunk8, KVChunk>::type;
   // register buffers in the K/V pipeline (an 8-bit chunk takes half the registers)
   constexpr int NBUF = BS == 8 ? 2 : (F8 ? PA_PIPE_F8 : PA_PIPE_BF16);
+  // K loads with the plain policy when a group shares them (G 2, 4): 410 vs
+  // 419 us on the Llama-3-8B shape, 234-237 vs 237-238 us with 8-bit pools;
+  // at G 1 streaming stays faster (555 vs 567 us on the Llama-2-13B shape)
+  constexpr int KPOL = G == 1 ? POL : kKvCached;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -891,8 +900,8 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
       if constexpr (BS == 8) {
         load_kv_chunk_bs8(buf, kbase, vbase, blk_bytes, phys, __builtin_amdgcn_readlane(ids.y, tt));
       } else {
-        load_kv_chunk<BS, POL>(buf, kbase, vbase, blk_bytes, phys, chunk_tok(win + tt) % BS,
-                               k_off, v_off, live);
+        load_kv_chunk<BS, POL, KPOL>(buf, kbase, vbase, blk_bytes, phys,
+                                     chunk_tok(win + tt) % BS, k_off, v_off, live);
       }
     };
     // one stage: issue chunk t + NBUF - 1 into `nxt`, compute chunk t from
