@@ -1519,8 +1519,11 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
       ids = checked_id(a.block_tables, a.num_blocks, trow_base, ((ch0 + win + lane) * 16) / BS);
     auto issue = [&](KVChunk& buf, int t) {
       const int phys = __builtin_amdgcn_readlane(ids, t);
-      load_kv_chunk<BS>(buf, kbase, vbase, blk_bytes, phys, ((ch0 + win + t) * 16) % BS, k_off,
-                        v_off, true);
+      // K with the plain policy (its lines are read in halves, see
+      // load_kv_chunk): decode at group 8 487-492 -> 477 us, speculative
+      // tokens over split contexts 499 -> 485 us; V streams
+      load_kv_chunk<BS, kKvStream, kKvCached>(buf, kbase, vbase, blk_bytes, phys,
+                                              ((ch0 + win + t) * 16) % BS, k_off, v_off, true);
     };
     KVChunk b0, b1;
     // chunks go in pairs (32 positions: one P.V step); the first chunk's
