@@ -152,3 +152,42 @@ def test_shared_prefix_workspace_bytes():
     assert P.pa_decode_shared_prefix_workspace_bytes(s, 0, 1024) == 0     # no group size
     assert P.pa_decode_shared_prefix_workspace_bytes(
         _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=-1), 4, 1024) == 0
+
+
+def test_planned_and_append_reject_before_launch():
+    lib = P.lib()
+    s = _shape(max_seq_len=4096, max_blocks_per_seq=256)
+    d = ctypes.c_void_p(4096)
+    big = 1 << 30
+    cap = lib.pa_decode_plan_capacity(ctypes.byref(s))
+    assert cap == 4 * 8
+    # negative or too many units, missing or misaligned plan
+    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d, -1,
+                                 d, big, None) == 1
+    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d,
+                                 cap + 1, d, big, None) == 1
+    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), None, 3,
+                                 d, big, None) == 1
+    assert lib.pa_decode_partition_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s),
+                                           ctypes.c_void_p(4104), 3, d, big, None) == 1
+    # 8-bit pools: the plan needs an explicit partition length
+    assert lib.pa_decode_e4m3_planned(d, d, d, d, d, ctypes.c_float(0.1), ctypes.c_float(1.0),
+                                      ctypes.c_float(1.0), d, ctypes.byref(s), d, 3, d, big,
+                                      None) == 1
+    s8 = _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=1024)
+    assert lib.pa_decode_partition_e4m3_planned(d, d, d, d, d, ctypes.c_float(0.1),
+                                                ctypes.c_float(1.0), ctypes.c_float(-1.0), d,
+                                                ctypes.byref(s8), d, 3, d, big, None) == 1
+    # group 8 on the matrix cores runs on the per-tile kernel: no plans there
+    s64 = _shape(num_q_heads=64, max_seq_len=4096, max_blocks_per_seq=256, variant=2)
+    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s64), d, 3,
+                                 d, big, None) == 2
+    # append: tables and lengths required, a positive table stride
+    assert lib.pa_append_tokens(d, d, d, d, d, None, d, 4, 8, 8, 128, 16, 10, 1, None) == 1
+    assert lib.pa_append_tokens(d, d, d, d, d, d, None, 4, 8, 8, 128, 16, 10, 1, None) == 1
+    assert lib.pa_append_tokens(d, d, d, d, d, d, d, 4, 0, 8, 128, 16, 10, 1, None) == 1
+    assert lib.pa_append_tokens(d, d, d, d, d, d, d, 4, 8, 8, 100, 16, 10, 1, None) == 1
+    assert lib.pa_append_tokens(None, None, None, None, None, d, d, 0, 8, 8, 128, 16, 10, 1,
+                                None) == 0
+    assert lib.pa_append_tokens_e4m3(d, d, d, d, d, d, d, 4, 8, 8, 128, 16, 10,
+                                     ctypes.c_float(0.0), ctypes.c_float(1.0), None) == 1
