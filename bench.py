@@ -94,6 +94,11 @@ def main() -> int:
     ap.add_argument("--gpu-wait-upload", action="store_true",
                     help="order each step's kernels after its upload with a stream wait "
                          "instead of on the host")
+    ap.add_argument("--prefix-decode", default="auto", choices=["auto", "pa_decode", "shared"],
+                    help="shared-prefix workloads: decode with pa_decode over a work plan, or "
+                         "with pa_decode_shared_prefix (each shared prompt block read once per "
+                         "group); auto = the latter unless the batch holds unshared long "
+                         "sequences")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch pa_decode's full grid instead of a host work plan")
     ap.add_argument("--event-every", type=int, default=5,
@@ -281,6 +286,21 @@ def main() -> int:
     done_step = [-1] * NBUF   # step whose completion event sits in done_ev[step % NBUF]
     n_units = [0] * NBUF      # work-plan units in staging / device buffer b
     ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8, device=dev)
+    # Shared-prefix decode in the step (shared-prefix workloads): the prompt
+    # groups and each sample's shared positions (the whole prompt blocks; a
+    # half-filled prompt block was copied on write at setup) stay fixed.
+    sp_mode = prefix and not fp8 and (
+        args.prefix_decode == "shared" or (args.prefix_decode == "auto" and n_long == 0))
+    if sp_mode:
+        shared = (plen // bs) * bs
+        sp_gs = torch.arange(0, ngroups * nsamp + 1, nsamp, dtype=torch.int32, device=dev)
+        sp_prefix = torch.zeros(B, dtype=torch.int32, device=dev)
+        sp_prefix[:ngroups * nsamp] = shared
+        sp_ws = torch.empty(max(16, P.pa_decode_shared_prefix_workspace_bytes(shape, nsamp, shared)),
+                            dtype=torch.uint8, device=dev)
+        sp_args = (ngroups, sp_gs.data_ptr(), sp_prefix.data_ptr(), nsamp, shared,
+                   sp_ws.data_ptr(), sp_ws.numel())
+        sp_ptrs = (sp_gs, sp_prefix, sp_ws)  # kept alive for the raw calls
     step_bytes = []
     host_s = [0.0]  # host time per timed step, waits excluded
     step_lens = []  # shared-prefix workloads: lengths per step, for the unique bytes
@@ -320,7 +340,7 @@ def main() -> int:
         lens_host[:] += 1                    # every sequence appended one token
         if not upload:
             lens_np[b][:] = lens_host
-        if plan_cap:
+        if plan_cap and not sp_mode:         # pa_decode_shared_prefix takes no plan
             t_pl = time.perf_counter()
             st = Lh.pa_decode_plan(shape_ref, sp["lens"], sp["plan"], plan_cap,
                                    ctypes.byref(nunits_c))
@@ -414,7 +434,12 @@ def main() -> int:
                   "pa_reshape_and_cache")
         if timed:
             evs[0].record(compute)
-        if fp8 and plan_cap:
+        if sp_mode:
+            # prefix pass and per-sequence walks in one launch, then the merge
+            check(L.pa_decode_shared_prefix(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
+                                            db["lens"], c_scale, out_ptr, shape_ref, *sp_args,
+                                            cs), "pa_decode_shared_prefix")
+        elif fp8 and plan_cap:
             check(L.pa_decode_partition_e4m3_planned(q_all[s].data_ptr(), kp_ptr, vp_ptr,
                                                      db["tables"], db["lens"], c_scale, c_kscale,
                                                      c_vscale, out_ptr, shape_ref, db["plan"],
@@ -437,8 +462,9 @@ def main() -> int:
         if timed:
             evs[1].record(compute)
             ev.append(evs)
-        check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
-              "pa_decode_reduce")
+        if not sp_mode:
+            check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
+                  "pa_decode_reduce")
         if s % args.done_every == 0 or s == nsteps - 1:
             done_ev[s % NBUF].record(compute)
             done_step[s % NBUF] = s
@@ -501,8 +527,9 @@ def main() -> int:
                                          db["slots"], kp_ptr, vp_ptr, B, hkv, d, bs, nb, dt_code, cs),
                   "pa_reshape_and_cache")
         e[1].record(compute)
-        check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
-              "pa_decode_reduce")
+        if not sp_mode:                      # (the shared-prefix call merges itself)
+            check(L.pa_decode_reduce(db["lens"], out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
+                  "pa_decode_reduce")
         e[2].record(compute)
         torch.cuda.synchronize()
         cache_ms.append(e[0].elapsed_time(e[1]))
@@ -538,14 +565,15 @@ def main() -> int:
                    "context_tokens": (f"U{{{w.lengths[1]}..{w.lengths[2]}}}+step"
                                       if w.lengths[0] == "uniform" else f"{w.lengths}+step"),
                    "kernel": vname, "block_order": args.block_order,
-                   "work_plan": bool(plan_cap),
+                   "work_plan": bool(plan_cap) and not sp_mode,
+                   "decode_call": "pa_decode_shared_prefix" if sp_mode else "pa_decode",
                    "device_tables": not upload,
                    "kv_storage": "e4m3" if fp8 else w.dtype,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(B * K / wall, 1),
         "kernels_us": {"partition": round(1e3 * float(np.mean(part_ms)), 2),
-                       "reduce": round(1e3 * float(np.mean(red_ms)), 2),
+                       "reduce": None if sp_mode else round(1e3 * float(np.mean(red_ms)), 2),
                        "reshape_and_cache": round(1e3 * float(np.mean(cache_ms)), 2),
                        # spread of the sampled partition launches and step periods
                        "partition_p10_p50_p90": [round(1e3 * float(x), 2) for x in
@@ -557,7 +585,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(vname, w.name) if default_launch else None,
-                     "kernel": "decode_partition_" + vname + ("_e4m3" if fp8 else ""),
+                     "kernel": ("shared_prefix_decode + decode_reduce (one call)" if sp_mode else
+                                "decode_partition_" + vname + ("_e4m3" if fp8 else "")),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
     }
     avg_len = total_bytes / K / (2 * hkv * d * pool_eb) / B
@@ -572,8 +601,11 @@ def main() -> int:
                                  "GBps": round(cache_bytes / (float(np.mean(cache_ms)) / 1e3) / 1e9, 1)},
         "a3_decode_partition": {"us": round(1e3 * float(np.mean(part_ms)), 2),
                                 "GBps": round(achieved, 1), "mean_len": round(avg_len, 1)},
-        "a4_decode_reduce": {"us": round(1e3 * float(np.mean(red_ms)), 2), "bytes_moved": int(red_bytes),
-                             "GBps": round(red_bytes / (float(np.mean(red_ms)) / 1e3) / 1e9, 1)},
+        "a4_decode_reduce": ({"us": None, "note": "merged inside the pa_decode_shared_prefix call "
+                                                  "(its time is in kernels_us.partition)"}
+                             if sp_mode else
+                             {"us": round(1e3 * float(np.mean(red_ms)), 2), "bytes_moved": int(red_bytes),
+                              "GBps": round(red_bytes / (float(np.mean(red_ms)) / 1e3) / 1e9, 1)}),
         "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
         "a6_fork_cow_host_us": fork_cow_host_us(P),
         "n2_multi_query": multi_query_rate(P, torch, dev, W),
