@@ -795,7 +795,8 @@ def shared_prefix_rate(P, torch, dev, w, q, k_pool, v_pool, db, plen, bs, max_le
 def group8_decode_rate(P, torch, dev, W) -> dict:
     """pa_decode at 8 query heads per KV head (64 query / 8 KV heads, D 128,
     bf16, block size 16, scattered blocks; 256 sequences of U{512..4096}):
-    the matrix-core default and the vector-ALU kernel."""
+    the matrix-core default (full grid and over a work plan) and the
+    vector-ALU kernel."""
     hq, hkv, d, bs = 64, 8, 128, 16
     rng = np.random.default_rng(19)
     lens = rng.integers(512, 4097, 256)
@@ -814,16 +815,28 @@ def group8_decode_rate(P, torch, dev, W) -> dict:
     tabd, lensd = torch.from_numpy(tab).to(dev), torch.from_numpy(lens.astype(np.int32)).to(dev)
     kv = int(lens.sum()) * 2 * hkv * d * 2
     res = {}
-    for name, variant in (("matrix_cores", P.PA_VARIANT_AUTO), ("vector_alu", P.PA_VARIANT_VALU)):
+    ml = int(lens.max())
+    shape = P._decode_shape(q, kp, tabd, ml, 0, P.PA_VARIANT_AUTO)
+    plan = torch.from_numpy(P.pa_decode_plan(shape, lens.astype(np.int32))).to(dev)
+    ws = torch.empty(max(16, P.pa_decode_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
+    for name, variant, wp in (("matrix_cores", P.PA_VARIANT_AUTO, None),
+                              ("matrix_cores_planned", P.PA_VARIANT_AUTO, plan),
+                              ("vector_alu", P.PA_VARIANT_VALU, None)):
         out = torch.empty_like(q)
+
+        def call():
+            if wp is None:
+                P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out, max_seq_len=ml,
+                            variant=variant)
+            else:
+                P.pa_decode_planned(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out,
+                                    work_plan=wp, max_seq_len=ml, variant=variant, workspace=ws)
         for _ in range(2):
-            P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out,
-                        max_seq_len=int(lens.max()), variant=variant)
+            call()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(10):
-            P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out,
-                        max_seq_len=int(lens.max()), variant=variant)
+            call()
         e1.record()
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 10 / 1e3

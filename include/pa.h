@@ -171,9 +171,9 @@ pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v
  *     entry (sequence, partition, that sequence's length, 0) per unit;
  *     *num_units [host] receives their count.
  *     PA_EINVAL if a length is negative or above min(max_seq_len,
- *     max_blocks_per_seq * block_size), or capacity is too small.
- *     PA_EUNSUPPORTED for shapes that run on the multi-token per-tile kernel
- *     (8 or 16 query heads per KV head with PA_VARIANT_MFMA/AUTO).
+ *     max_blocks_per_seq * block_size), or capacity is too small. Shapes
+ *     with 8 or 16 query heads per KV head on the matrix cores (the
+ *     multi-token per-tile kernel) take plans too: one wave per unit.
  *   pa_decode_planned / pa_decode_partition_planned: pa_decode /
  *     pa_decode_partition with work_plan [dev] (16-byte aligned, the
  *     pa_decode_plan output copied to the device) and its num_units. The

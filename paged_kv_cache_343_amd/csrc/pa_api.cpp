@@ -159,6 +159,41 @@ size_t pa_decode_workspace_bytes(const pa_decode_shape_t* shape) {
   return plan.ml_bytes + plan.o_bytes;
 }
 
+// Decode on the multi-token per-tile kernel (8 or 16 query heads per KV head
+// on the matrix cores), one token per sequence, in the same workspace
+// regions: per (sequence, query head, partition) the (max, exp-sum) pair
+// (within the statistics records' space) and the partial output in the
+// decode layout.
+static pa::MqArgs decode_mq_args(const pa::DecodeArgs& a, const pa_decode_shape_t& shape,
+                                 const Plan& plan) {
+  pa::MqArgs m{};
+  m.q = a.q;
+  m.k_pool = a.k_pool;
+  m.v_pool = a.v_pool;
+  m.block_tables = a.block_tables;
+  m.seq_lens = a.seq_lens;
+  m.out = a.out;
+  m.qscale = a.qscale;
+  m.num_seqs = a.num_seqs;
+  m.num_q_heads = a.num_q_heads;
+  m.num_kv_heads = a.num_kv_heads;
+  m.num_blocks = a.num_blocks;
+  m.max_blocks = a.max_blocks;
+  m.len_cap = a.len_cap;
+  m.max_query_len = 1;
+  m.num_tokens = a.num_seqs;
+  m.block_size = shape.block_size;
+  m.decode_mode = 1;
+  m.max_parts = plan.max_parts;
+  m.part_tokens = plan.max_parts > 1 ? plan.part_tokens : 0;
+  m.part_ml = a.part_ml;
+  m.part_o = a.part_o;
+  m.part_half = a.part_half;
+  m.plan = a.plan;
+  m.num_units = a.num_units;
+  return m;
+}
+
 static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_tables, const int32_t* seq_lens, float scale,
                                void* out, const pa_decode_shape_t* shape, void* workspace,
@@ -189,8 +224,7 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
     a.out_scale = fp8_scales[1];
   }
   if (num_units >= 0) {
-    // a work plan from pa_decode_plan (the per-tile route has its own grid)
-    if (plan.mq_route) return PA_EUNSUPPORTED;
+    // a work plan from pa_decode_plan
     if ((int64_t)num_units > (int64_t)shape->num_seqs * plan.max_parts) return PA_EINVAL;
     if (num_units > 0 && (!work_plan || !aligned16(work_plan)))
       return PA_EINVAL;
@@ -201,32 +235,7 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
   if (shape->num_seqs == 0) return PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.mq_route) {
-    // the same workspace regions: per (sequence, query head, partition) the
-    // (max, exp-sum) pair (within the statistics records' space) and the
-    // partial output in the decode layout
-    pa::MqArgs m{};
-    m.q = a.q;
-    m.k_pool = a.k_pool;
-    m.v_pool = a.v_pool;
-    m.block_tables = a.block_tables;
-    m.seq_lens = a.seq_lens;
-    m.out = a.out;
-    m.qscale = a.qscale;
-    m.num_seqs = a.num_seqs;
-    m.num_q_heads = a.num_q_heads;
-    m.num_kv_heads = a.num_kv_heads;
-    m.num_blocks = a.num_blocks;
-    m.max_blocks = a.max_blocks;
-    m.len_cap = a.len_cap;
-    m.max_query_len = 1;
-    m.num_tokens = a.num_seqs;
-    m.block_size = shape->block_size;
-    m.decode_mode = 1;
-    m.max_parts = plan.max_parts;
-    m.part_tokens = plan.max_parts > 1 ? plan.part_tokens : 0;
-    m.part_ml = a.part_ml;
-    m.part_o = a.part_o;
-    m.part_half = a.part_half;
+    const pa::MqArgs m = decode_mq_args(a, *shape, plan);
     if (do_partition) {
       st = from_hip(pa::launch_multi_query_tiles(shape->block_size, plan.group, m, s));
       if (st != PA_OK) return st;
@@ -269,7 +278,6 @@ pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_le
   Plan plan;
   pa_status_t st = make_plan(shape, &plan);
   if (st != PA_OK) return st;
-  if (plan.mq_route) return PA_EUNSUPPORTED;
   if (!num_units || (shape->num_seqs > 0 && (!seq_lens || !work_plan))) return PA_EINVAL;
   const int pt = plan.part_tokens;
   // Units with a full partition come first, in (sequence, partition) order;
@@ -416,6 +424,9 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
   a.len_cap = plan.len_cap;
   a.part_tokens = plan.part_tokens;
   a.max_parts = plan.max_parts;
+  if (plan.mq_route)   // the per-tile kernel's partials: its own merge
+    return from_hip(pa::launch_multi_query_reduce(plan.group, decode_mq_args(a, *shape, plan),
+                                                  static_cast<hipStream_t>(stream)));
   return from_hip(pa::launch_decode_reduce(shape->dtype, shape->head_dim, a,
                                            static_cast<hipStream_t>(stream)));
 }

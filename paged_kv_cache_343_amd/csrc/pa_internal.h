@@ -140,6 +140,10 @@ struct MqArgs {
   int32_t block_size;
   int32_t slot_stride;          // partial slots per row (0: max_parts)
   int32_t ml_records;           // mode 2: (max, exp-sum) in pa_decode's 128-byte records
+  // decode mode over a host work plan (pa_decode_plan): [num_units][4]
+  // (sequence, partition, length, 0), one wave each; null otherwise
+  const int32_t* plan;
+  int32_t num_units;
 };
 
 // The decode kernels keep the partial output of a partition in bf16 when it

@@ -656,8 +656,9 @@ struct KVChunk8 {                      // FP8 E4M3 pools: 128-byte rows
 // operand). Streaming (nt, non-temporal) is the default: each V line is
 // read once, and on the Llama-3-8B-shaped decode it takes about 4% off the
 // partition kernel. K lines are read in two halves by consecutive loads;
-// with 2 or 4 query heads per KV head they keep the plain policy (mfma_unit). When sequences of one batch share blocks (forked samples,
-// a common prompt), a sequence reads lines that its neighbours in the grid
+// with 2 or 4 query heads per KV head they keep the plain policy
+// (mfma_unit). When sequences of one batch share blocks (forked samples, a
+// common prompt), a sequence reads lines that its neighbours in the grid
 // just brought into L2; the plain policy keeps them there.
 constexpr int kKvStream = 2;
 constexpr int kKvCached = 0;
@@ -1381,11 +1382,29 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = lane >> 4, c = lane & 15;
-  const int i = bz, g = by;
-  // units (tile, context partition), partition fastest, one per wave
+  const int g = by;
+  // units (tile, context partition), partition fastest, one per wave; in
+  // decode mode over a host work plan, unit u = plan entry u (sequence,
+  // partition, length), one tile each, and the grid holds only those
   const int unit = bx * kMqWaves + w;
-  const int part = unit % a.max_parts;
-  const int tile = unit / a.max_parts;
+  int i = bz, part, tile, plan_len = -1;
+  if (a.plan) {
+    if (unit >= a.num_units) return;
+    const int4 e = reinterpret_cast<const int4*>(a.plan)[unit];
+    i = e.x;
+    part = e.y;
+    tile = 0;
+    plan_len = e.z;
+    const int np = a.part_tokens > 0 ? (plan_len + a.part_tokens - 1) / a.part_tokens : 1;
+    if ((unsigned)i >= (unsigned)a.num_seqs || (unsigned)plan_len > (unsigned)a.len_cap ||
+        part < 0 || part >= (np > 1 ? np : 1)) {
+      if (lane == 0) flag_error(kErrPlan);
+      return;
+    }
+  } else {
+    part = unit % a.max_parts;
+    tile = unit / a.max_parts;
+  }
 
   // validate the sequence's length and query range (device-resident). The
   // walk covers positions [wstart, npos) of the sequence (the tile's last
@@ -1395,8 +1414,9 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
   const int mode = a.mode ? a.mode : (a.decode_mode ? 1 : 0);
   if (mode == 1 || mode == 3) {
     // pa_decode: token i; a length outside [0, len_cap] is clamped and
-    // flagged, and an empty sequence gets zero rows
-    L = a.seq_lens[i];
+    // flagged, and an empty sequence gets zero rows (a plan's lengths were
+    // checked above)
+    L = plan_len >= 0 ? plan_len : a.seq_lens[i];
     q0 = i;
     tq = 1;
     if (L < 0 || L > a.len_cap) {
@@ -1404,7 +1424,7 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
       L = L < 0 ? 0 : a.len_cap;
     }
     if (L == 0) {
-      if (unit == 0)
+      if (a.plan ? part == 0 : unit == 0)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * R + r < G) {
@@ -2406,11 +2426,14 @@ hipError_t launch_multi_query_tiles(int block_size, int group, const MqArgs& arg
   if (args.max_parts < 1 || (args.max_parts > 1 && args.part_tokens <= 0))
     return hipErrorInvalidValue;
   const int64_t tiles = ((int64_t)args.max_query_len * group + 15) / 16;
-  const int64_t gx = (tiles * args.max_parts + kMqWaves - 1) / kMqWaves;
+  // a work plan (decode mode): one wave per listed unit, sequences from the plan
+  const int64_t gx = args.plan ? ((int64_t)args.num_units + kMqWaves - 1) / kMqWaves
+                               : (tiles * args.max_parts + kMqWaves - 1) / kMqWaves;
+  const int64_t gz = args.plan ? 1 : args.num_seqs;
   if (gx <= 0 || args.num_seqs <= 0) return hipSuccess;
   if (gx > 0x7fffffff || args.num_kv_heads > 65535 || args.num_seqs > 65535)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)args.num_kv_heads, (unsigned)args.num_seqs),
+  hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)args.num_kv_heads, (unsigned)gz),
                      dim3(kMqWaves * 64), 0, stream, args);
   return hipGetLastError();
 }

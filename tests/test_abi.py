@@ -178,10 +178,6 @@ def test_planned_and_append_reject_before_launch():
     assert lib.pa_decode_partition_e4m3_planned(d, d, d, d, d, ctypes.c_float(0.1),
                                                 ctypes.c_float(1.0), ctypes.c_float(-1.0), d,
                                                 ctypes.byref(s8), d, 3, d, big, None) == 1
-    # group 8 on the matrix cores runs on the per-tile kernel: no plans there
-    s64 = _shape(num_q_heads=64, max_seq_len=4096, max_blocks_per_seq=256, variant=2)
-    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s64), d, 3,
-                                 d, big, None) == 2
     # append: tables and lengths required, a positive table stride
     assert lib.pa_append_tokens(d, d, d, d, d, None, d, 4, 8, 8, 128, 16, 10, 1, None) == 1
     assert lib.pa_append_tokens(d, d, d, d, d, d, None, 4, 8, 8, 128, 16, 10, 1, None) == 1

@@ -56,6 +56,8 @@ SHAPES = [
     ("bf16", 32, 8, 128, 8, MFMA),
     ("bf16", 32, 8, 128, 128, MFMA),
     ("bf16", 64, 8, 128, 16, VALU),      # group 8 on the vector kernel
+    ("bf16", 64, 8, 128, 16, MFMA),      # group 8: the multi-token per-tile kernel
+    ("bf16", 16, 1, 128, 32, MFMA),      # group 16: the same, one tile per token
     ("f32", 8, 2, 128, 32, VALU),
     ("f32", 4, 4, 64, 16, VALU),
 ]
@@ -120,12 +122,14 @@ def test_planned_e4m3_full_size_bitwise(dev):
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-def test_bad_plan_entries_are_skipped_and_flagged(dev):
-    w = _custom("badplan", 132, 32, 8, 128, 16, "bf16")
+@pytest.mark.parametrize("hq", [32, 64])
+def test_bad_plan_entries_are_skipped_and_flagged(dev, hq):
+    w = _custom("badplan", 132, hq, 8, 128, 16, "bf16")
     c = build(w, dev, lens=[40, 700], append=False)
     shape = P._decode_shape(c.q, c.k_pool, c.tables, c.max_len, 0, MFMA)
     plan = P.pa_decode_plan(shape, c.olens)
-    assert plan.shape == (3, 4)
+    # group 4: 512-position partitions (700 -> 2); group 8: 1024 (one each)
+    assert plan.shape == ((3, 4) if hq == 32 else (2, 4))
     P.pa_device_errors()
     # sequence out of range, negative partition, a partition past the
     # sequence's last, a negative length, a length above the table's bound

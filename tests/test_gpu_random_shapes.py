@@ -45,14 +45,9 @@ def test_random_decode(dev, case):
     assert P.pa_device_errors() == 0
     check_close(O.as_f64(to_storage_np(out), "bf16"), c.oracle_all(), "bf16",
                 f"decode hq {hq} hkv {hkv} bs {bs} ptok {ptok} lens {lens}")
-    # the same decode over a host work plan: bit-identical (shapes on the
-    # multi-token per-tile kernel take no plan)
+    # the same decode over a host work plan: bit-identical
     shape = P._decode_shape(c.q, c.k_pool, c.tables, c.max_len, ptok, P.PA_VARIANT_AUTO)
-    try:
-        plan_np = P.pa_decode_plan(shape, c.olens)
-    except P.PaError as e:
-        assert e.name == "PA_EUNSUPPORTED" and hq // hkv in (8, 16)
-        return
+    plan_np = P.pa_decode_plan(shape, c.olens)
     out_p = torch.full_like(out, float("nan"))
     P.pa_decode_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out_p,
                         work_plan=torch.from_numpy(plan_np).to(dev), max_seq_len=c.max_len,

@@ -73,13 +73,14 @@ def test_plan_rejects_bad_lengths_and_small_capacity():
     assert st == 1
 
 
-def test_plan_unsupported_on_the_per_tile_route():
-    # 8 query heads per KV head on the matrix cores run on the multi-token kernel
-    with pytest.raises(P.PaError) as e:
-        P.pa_decode_plan(_shape(2, 100, hq=64, hkv=8, variant=P.PA_VARIANT_MFMA),
-                         np.array([10, 20], dtype=np.int32))
-    assert e.value.name == "PA_EUNSUPPORTED"
-    # the vector kernel takes plans at any group
+def test_plan_on_the_per_tile_route():
+    """8 query heads per KV head on the matrix cores run on the multi-token
+    per-tile kernel, whose automatic partition is 1024 positions; the plan
+    follows it."""
+    plan = P.pa_decode_plan(_shape(3, 3000, hq=64, hkv=8, variant=P.PA_VARIANT_MFMA),
+                            np.array([10, 2500, 1024], dtype=np.int32))
+    assert [tuple(u) for u in plan] == [(1, 0, 2500, 0), (1, 1, 2500, 0), (2, 0, 1024, 0),
+                                        (1, 2, 2500, 0), (0, 0, 10, 0)]
     plan = P.pa_decode_plan(_shape(2, 100, hq=64, hkv=8, variant=P.PA_VARIANT_VALU),
                             np.array([10, 20], dtype=np.int32))
     assert [tuple(u) for u in plan] == [(1, 0, 20, 0), (0, 0, 10, 0)]
