@@ -99,6 +99,9 @@ def main() -> int:
                          "with pa_decode_shared_prefix (each shared prompt block read once per "
                          "group); auto = the latter unless the batch holds unshared long "
                          "sequences")
+    ap.add_argument("--half-partials", action="store_true",
+                    help="store partial outputs in bf16 (PA_DECODE_HALF_PARTIALS; an option "
+                         "with a looser error bound, off by default)")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch pa_decode's full grid instead of a host work plan")
     ap.add_argument("--event-every", type=int, default=5,
@@ -247,7 +250,8 @@ def main() -> int:
     # forked samples share their prompt blocks: say so to the library
     shape = P.DecodeShape(B, hq, hkv, d, bs, nb, maxb, max_len, ptok,
                           P.PA_BF16 if w.dtype == "bf16" else P.PA_F32,
-                          variant | (P.PA_DECODE_SHARED_KV if prefix else 0))
+                          variant | (P.PA_DECODE_SHARED_KV if prefix else 0) |
+                          (P.PA_DECODE_HALF_PARTIALS if args.half_partials else 0))
     # Work plan (pa_decode_plan): the host lists the step's (sequence,
     # partition) units from the lengths it just exported, into the same
     # staging buffer; the partition kernel's grid then holds only those.
@@ -543,7 +547,8 @@ def main() -> int:
     # the counters were taken in the default launch configuration only
     default_launch = (not fp8 and args.block_size is None and args.block_order == "shuffled"
                       and args.partition_tokens is None and not args.no_plan
-                      and not args.upload_tables and args.variant == "auto")
+                      and not args.upload_tables and args.variant == "auto"
+                      and not args.half_partials)
     vname = {0: "auto", 1: "valu", 2: "mfma"}[variant]
     if variant == P.PA_VARIANT_AUTO:
         vname = "mfma" if (w.dtype == "bf16" and d == 128 and hq // hkv in (1, 2, 4)) else "valu"
@@ -569,6 +574,7 @@ def main() -> int:
                    "decode_call": "pa_decode_shared_prefix" if sp_mode else "pa_decode",
                    "device_tables": not upload,
                    "kv_storage": "e4m3" if fp8 else w.dtype,
+                   "partial_outputs": "bf16" if args.half_partials else "fp32",
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(B * K / wall, 1),
@@ -591,7 +597,8 @@ def main() -> int:
     }
     avg_len = total_bytes / K / (2 * hkv * d * pool_eb) / B
     parts = float(np.mean([-(-int(x) // ptok) for x in stage[0]["lens"].numpy()])) if ptok > 0 else 1.0
-    red_bytes = B * hq * (parts * d * eb + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
+    pe = 2 if (args.half_partials and eb == 2) else 4      # bytes per partial-output element
+    red_bytes = B * hq * (parts * d * pe + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
     cache_bytes = B * 2 * hkv * d * (eb + pool_eb)
     result["rows"] = {
         "a1_block_manager_host_us": round(1e6 * bm_s[0] / K, 1),
@@ -659,30 +666,40 @@ def main() -> int:
 
 def stream_read_peak(torch, dev) -> dict:
     """Practical HBM read ceiling: the streaming-read probe (libpa_probe.so)
-    over a 4 GiB buffer, best of three grid sizes, 10 timed launches each."""
+    over a 4 GiB buffer, best over a sweep of launch shapes (workgroups of 256
+    threads from 4 to 64 per CU, 1 to 8 independent 16-byte loads in flight
+    per lane, plain and streaming cache policy), 10 timed launches each."""
     path = os.path.join(ROOT, "paged_kv_cache_343_amd", "libpa_probe.so")
     lib = ctypes.CDLL(path)
     lib.pa_probe_stream_read.restype = ctypes.c_int
     lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                         ctypes.c_void_p, ctypes.c_void_p]
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream(dev).cuda_stream
-    best = 0.0
-    for grid in (1024, 2048, 4096):
-        for _ in range(2):
-            if lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, sink.data_ptr(), s):
-                raise RuntimeError("probe launch failed")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, sink.data_ptr(), s)
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, nbytes / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9)
+    sweep = {}
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        for loads in (1, 2, 4, 8):
+            for nt in (0, 1):
+                for _ in range(2):
+                    if lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, loads, nt,
+                                                sink.data_ptr(), s):
+                        raise RuntimeError("probe launch failed")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, loads, nt,
+                                             sink.data_ptr(), s)
+                e1.record()
+                torch.cuda.synchronize()
+                sweep[f"wg{grid}_loads{loads}_{'nt' if nt else 'plain'}"] = round(
+                    nbytes / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9, 1)
     del buf
-    return {"GBps": round(best, 1), "bytes": nbytes, "kernel": "pa_probe_stream_read"}
+    best = max(sweep, key=sweep.get)
+    return {"GBps": sweep[best], "bytes": nbytes, "kernel": "pa_probe_stream_read",
+            "best_launch": best, "sweep_GBps": sweep}
 
 
 def copy_blocks_rate(P, torch, dev) -> dict:

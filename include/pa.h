@@ -85,6 +85,16 @@ typedef enum {
  * faster when every block belongs to one sequence. Results are identical
  * either way. */
 #define PA_DECODE_SHARED_KV 0x100
+/* Option OR-ed into pa_decode_shape_t.variant (bf16 q/out, group 1, 2 or 4
+ * on the matrix cores): partitions of 256 or more positions store their
+ * normalised partial output in bf16 instead of fp32 (the (max, exp-sum)
+ * statistics and the merge stay fp32). This halves the partial-output bytes
+ * but adds a rounding of each partial: the output may then differ from the
+ * exact result by up to 2^-8 * sum_j w_j |o_j| (w_j = partition j's weight in
+ * the merge, o_j its partial output), which is far above the bf16 tolerance
+ * when partials of opposite sign cancel. Off by default: partials are fp32
+ * and the merge adds only fp32 rounding. */
+#define PA_DECODE_HALF_PARTIALS 0x200
 
 /* Shape of one pa_decode call. */
 typedef struct {
@@ -104,12 +114,14 @@ typedef struct {
                                  -1 = one partition per sequence, else a
                                  positive multiple of block_size               */
   int32_t dtype;              /* pa_dtype_t                                    */
-  int32_t variant;            /* PA_VARIANT_*, optionally | PA_DECODE_SHARED_KV */
+  int32_t variant;            /* PA_VARIANT_*, optionally | PA_DECODE_SHARED_KV
+                                 | PA_DECODE_HALF_PARTIALS                     */
 } pa_decode_shape_t;
 
 /* Bytes of scratch workspace pa_decode needs for `shape`: the partial softmax
- * statistics (fp32) and the normalised partial outputs (in `dtype`; they are
- * merged in fp32). 0 if the shape is invalid. */
+ * statistics and the normalised partial outputs (fp32-sized slots; bf16
+ * data with PA_DECODE_HALF_PARTIALS), merged in fp32. 0 if the shape is
+ * invalid. */
 size_t pa_decode_workspace_bytes(const pa_decode_shape_t* shape);
 
 /*
@@ -216,7 +228,8 @@ pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const
  *   shape          as pa_decode: bf16, head_dim 128, G in {1, 2, 4, 8, 16},
  *                  block size 16-128; partition_tokens 0 = 256 positions
  *                  (both passes split their range into partitions), -1 is
- *                  not accepted; variant ignored
+ *                  not accepted; of variant only PA_DECODE_HALF_PARTIALS
+ *                  is read (it applies to the walks after the prefix)
  *   group_start    [dev] int32 [num_groups + 1], non-decreasing, last <= B;
  *                  sequences outside every group need prefix_lens 0
  *   prefix_lens    [dev] int32 [B]: shared positions of each sequence, a
@@ -392,10 +405,10 @@ pa_status_t pa_reshape_and_cache(const void* k, const void* v, const int64_t* sl
 /*
  * pa_reshape_and_cache_e4m3 — the slot write into 8-bit pools. For t with
  * slot_mapping[t] >= 0 and every head h and dim d:
- *     k_pool[slot / bs][h][slot % bs][d] = E4M3(k[t][h][d] * (1 / k_scale))
- * (and v with v_scale), where 1 / k_scale and the product are rounded to
- * float32 and E4M3 picks the nearest code (ties to the even mantissa),
- * saturating at +-448, NaN to 0x7F. k, v [dev] bf16 [num_tokens][Hkv][D];
+ *     k_pool[slot / bs][h][slot % bs][d] = E4M3(k[t][h][d] / k_scale)
+ * (and v with v_scale), where E4M3 picks the code nearest to the exact
+ * quotient (ties to the even mantissa), saturating at +-448, NaN to 0x7F
+ * with the input's sign. k, v [dev] bf16 [num_tokens][Hkv][D];
  * head_dim a multiple of 16; scales finite and positive.
  */
 pa_status_t pa_reshape_and_cache_e4m3(const void* k, const void* v, const int64_t* slot_mapping,
@@ -483,9 +496,14 @@ pa_status_t pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, vo
                            const int64_t* pairs, int32_t num_pairs, int64_t block_bytes,
                            int32_t src_num_blocks, int32_t dst_num_blocks, void* stream);
 
-/* Waits for `stream`, then returns the current device's error word in
- * *flags (PA_DEVERR_* bits, 0 = clean) and clears it. Returns PA_EDEVICE if
- * any bit was set, PA_EHIP if a HIP call failed. */
+/* Returns the current device's error word in *flags (PA_DEVERR_* bits,
+ * 0 = clean) as it stands once the work already enqueued on `stream` has
+ * finished, and clears it: a one-thread kernel on `stream` fetches and
+ * clears the word in one atomic exchange, then the call waits for the
+ * value. A bit raised meanwhile by work on another stream is kept for the
+ * next call. Returns PA_EDEVICE if any bit was set, PA_EHIP if a HIP call
+ * failed. Concurrent calls from several host threads race on the fetched
+ * copy. */
 pa_status_t pa_device_errors(uint32_t* flags, void* stream);
 
 /* Human-readable name of a status code (static storage). */

@@ -184,11 +184,25 @@ class OracleBlockManager:
         self.tables[seq] = [self._take() for _ in range(need)]
         self.ntok[seq] = int(num_tokens)
 
-    def _append_needs_block(self, seq: int) -> bool:
-        p = self.ntok[seq]
-        if p % self.block_size == 0:
-            return True
-        return self.ref[self.tables[seq][p // self.block_size]] > 1
+    def _blocks_for_appends(self, seqs) -> int:
+        """Blocks that appending one token to each listed sequence takes, in
+        order: one for a position that starts a block, one for a write into
+        a block still shared with another holder at that point (its copy
+        gives up the writer's reference, so the last holder of a shared
+        block writes in place and takes none)."""
+        refs = dict()
+        need = 0
+        for s in seqs:
+            p = self.ntok[s]
+            if p % self.block_size == 0:
+                need += 1
+                continue
+            b = self.tables[s][p // self.block_size]
+            r = refs.get(b, self.ref[b])
+            if r > 1:
+                need += 1
+                refs[b] = r - 1
+        return need
 
     def append_slot(self, seq: int):
         """Reserve the slot of the next token of `seq`.
@@ -201,9 +215,9 @@ class OracleBlockManager:
         """append_slot for each listed sequence in order; all or nothing."""
         if any(s in self.swapped for s in seqs):
             raise ValueError("a swapped-out sequence cannot be appended to")
-        need = sum(1 for s in seqs if self._append_needs_block(s)) if len(set(seqs)) == len(seqs) else None
-        if need is None:
+        if len(set(seqs)) != len(seqs):
             raise ValueError("a sequence may appear once per batch")
+        need = self._blocks_for_appends(seqs)
         if need > len(self.free):
             raise OracleNoBlocks(f"need {need}, free {len(self.free)}")
         out = []
@@ -529,9 +543,10 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
 # --------------------------------------------------------------------------
 # [ZQ] summary: paged attention composes with KV quantization; the pages give
 # no scheme. Reading taken: OCP FP8 E4M3 ("fn": no infinities, S.1111.111 is
-# NaN, largest finite 448), one scale per pool (K and V), a value x stored as
-# the code nearest to x / scale (ties to the even code), saturating to +-448;
-# the code's value times the scale is what attention reads.
+# NaN, largest finite 448), one float32 scale per pool (K and V); a value x is
+# stored as the code nearest to the exact quotient x / scale (ties to the code
+# with an even mantissa), saturating to +-448; the code's value times the
+# scale is what attention reads.
 
 E4M3_MAX = 448.0
 
@@ -555,30 +570,43 @@ def e4m3_values(codes) -> np.ndarray:
     return table[np.asarray(codes, dtype=np.uint8)]
 
 
-def e4m3_encode(x) -> np.ndarray:
-    """Nearest FP8 E4M3 code to each float32 value of x (ties to the code with
-    an even mantissa), saturating at +-448; NaN gives 0x7F with the input's
-    sign. Written as a search over the 127 non-negative finite codes."""
-    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+def _nearest_code(y) -> np.ndarray:
+    """Nearest FP8 E4M3 code to each float64 value of y (ties to the code with
+    an even mantissa), saturating at +-448; NaN gives 0x7F with y's sign.
+    Written as a search over the 127 non-negative finite codes."""
+    y = np.asarray(y, dtype=np.float64)
     mags = np.array([e4m3_value(c) for c in range(0x7F)])        # codes 0x00..0x7E, ascending
-    a = np.minimum(np.abs(x), E4M3_MAX)
+    a = np.minimum(np.abs(y), E4M3_MAX)
     hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)  # first magnitude >= a
     lo = np.maximum(hi - 1, 0)
     d_lo, d_hi = a - mags[lo], mags[hi] - a
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
-    code = np.where(np.isnan(x), np.where(np.signbit(x), 0xFF, 0x7F), code).astype(np.uint8)
+    code = np.where(np.signbit(y), code | 0x80, code).astype(np.uint8)
+    code = np.where(np.isnan(y), np.where(np.signbit(y), 0xFF, 0x7F), code).astype(np.uint8)
     return code
 
 
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest FP8 E4M3 code to each float32 value of x (ties to the code with
+    an even mantissa), saturating at +-448; NaN gives 0x7F with the input's
+    sign."""
+    return _nearest_code(np.asarray(x, dtype=np.float32).astype(np.float64))
+
+
 def quantize_e4m3(x, scale: float) -> np.ndarray:
-    """Codes of x / scale: x (float32 values, e.g. from bf16) times the
-    float32 reciprocal of the float32 scale, the product rounded to float32,
-    then e4m3_encode."""
-    inv = np.float32(1.0) / np.float32(scale)
-    y = (np.asarray(x, dtype=np.float32) * inv).astype(np.float32)
-    return e4m3_encode(y)
+    """Codes of x / scale: the code nearest to the exact quotient of each
+    float32 value of x (e.g. from bf16) by the float32 scale.
+
+    The quotient is formed in float64. That decides every case as the exact
+    quotient would: a midpoint between two codes has at most 5 significant
+    bits, so the exact quotient x / s of two float32 values is either that
+    midpoint exactly (a tie) or differs from it by at least 2^-29 of its
+    size, far more than the 2^-53 of one float64 rounding; the rounded
+    quotient therefore lies on the same side of every midpoint."""
+    q = (np.asarray(x, dtype=np.float32).astype(np.float64) /
+         np.float64(np.float32(scale)))
+    return _nearest_code(q)
 
 
 def reshape_and_cache_e4m3(k_new, v_new, slot_mapping, k_codes, v_codes, k_scale, v_scale):

@@ -23,6 +23,12 @@ def _load():
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+        lib.pa_oracle_decode_e4m3.restype = ctypes.c_int
+        lib.pa_oracle_decode_e4m3.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
         lib.pa_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -54,4 +60,28 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale, dtype, num_threads=
         ctypes.c_float(scale), out.ctypes.data, int(num_threads))
     if rc != 0:
         raise RuntimeError(f"pa_oracle_decode failed: {rc}")
+    return out
+
+
+def decode_e4m3(q, k_codes, v_codes, k_scale, v_scale, block_tables, seq_lens, scale,
+                num_threads=0):
+    """pa_oracle.decode over 8-bit pools: q as uint16 bf16 bit patterns
+    [B, Hq, D], pools of FP8 E4M3 codes (uint8) read as code value times their
+    pool's float32 scale. Returns float64 [B, Hq, D]."""
+    lib = _load()
+    q = np.ascontiguousarray(q).view(np.uint16)
+    k_codes = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    v_codes = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_codes.shape
+    assert d == d2 and v_codes.shape == k_codes.shape and bt.shape[0] == B and sl.shape == (B,)
+    out = np.zeros((B, hq, d), dtype=np.float64)
+    rc = lib.pa_oracle_decode_e4m3(
+        q.ctypes.data, k_codes.ctypes.data, v_codes.ctypes.data, ctypes.c_float(k_scale),
+        ctypes.c_float(v_scale), bt.ctypes.data, bt.shape[1], sl.ctypes.data, B, hq, hkv, d, bs,
+        nb, ctypes.c_float(scale), out.ctypes.data, int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"pa_oracle_decode_e4m3 failed: {rc}")
     return out

@@ -28,7 +28,7 @@ __all__ = [
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "PA_DECODE_SHARED_KV", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
-    "BlockManager", "EXPORTED_SYMBOLS",
+    "BlockManager", "EXPORTED_SYMBOLS", "PA_DECODE_HALF_PARTIALS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -42,6 +42,8 @@ PA_DEVERR_PLAN = 0x40
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 # hint OR-ed into `variant`: the batch's sequences share blocks (pa.h)
 PA_DECODE_SHARED_KV = 0x100
+# option OR-ed into `variant`: bf16 partial outputs (pa.h; off by default)
+PA_DECODE_HALF_PARTIALS = 0x200
 _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
            4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
 

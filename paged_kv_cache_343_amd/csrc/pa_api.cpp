@@ -72,7 +72,8 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
       s->block_size != 128)
     return PA_EUNSUPPORTED;
   const int group = s->num_q_heads / s->num_kv_heads;
-  if (s->variant & ~(kVariantMask | PA_DECODE_SHARED_KV)) return PA_EINVAL;
+  if (s->variant & ~(kVariantMask | PA_DECODE_SHARED_KV | PA_DECODE_HALF_PARTIALS))
+    return PA_EINVAL;
   const int base = s->variant & kVariantMask;
   int variant = base == PA_VARIANT_AUTO ? auto_variant(*s, group) : base;
   if (variant != PA_VARIANT_VALU && variant != PA_VARIANT_MFMA) return PA_EINVAL;
@@ -102,9 +103,10 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   const size_t recs = (size_t)s->num_seqs * s->num_kv_heads * plan->max_parts;
   if (plan->max_parts > 1) {
     plan->ml_bytes = round_up(recs * pa::kMlRecord * sizeof(float), 256);
-    // bf16 partials only for full-length partitions of the decode kernels
-    // (the per-tile multi-token kernel keeps fp32)
-    plan->part_half = s->dtype == PA_BF16 && pt >= pa::kHalfPartialMinTokens && !plan->mq_route;
+    // bf16 partials only on request, for full-length partitions of the
+    // decode kernels (the per-tile multi-token kernel keeps fp32)
+    plan->part_half = (s->variant & PA_DECODE_HALF_PARTIALS) && s->dtype == PA_BF16 &&
+                      pt >= pa::kHalfPartialMinTokens && !plan->mq_route;
     plan->o_bytes = round_up(rows * (size_t)s->head_dim * 4, 256);
   }
   return PA_OK;
@@ -431,6 +433,10 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
                                            static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
 // Shared-prefix decode plan: partitions of the prefix pass, then of the
 // per-sequence pass, in one partial array per (sequence, query head).
 struct PrefixPlan {
@@ -444,7 +450,7 @@ pa_status_t prefix_plan(const pa_decode_shape_t* s, int32_t max_group_size,
                         int32_t max_prefix_len, PrefixPlan* pp) {
   if (!s || max_group_size <= 0 || max_prefix_len < 0) return PA_EINVAL;
   pa_decode_shape_t s2 = *s;
-  s2.variant = PA_VARIANT_MFMA;
+  s2.variant = PA_VARIANT_MFMA | (s->variant & PA_DECODE_HALF_PARTIALS);
   if (s2.partition_tokens == -1) return PA_EINVAL;
   pa_status_t st = make_plan(&s2, &pp->base);
   if (st != PA_OK) return st;
@@ -466,9 +472,10 @@ pa_status_t prefix_plan(const pa_decode_shape_t* s, int32_t max_group_size,
   pp->ml_bytes = round_up((size_t)s->num_seqs * s->num_kv_heads * slots * pa::kMlRecord *
                               sizeof(float), 256);
   pp->o_bytes = round_up((size_t)s->num_seqs * s->num_q_heads * slots * s->head_dim * 4, 256);
-  // the decode kernel's own partitions may keep bf16 partials (prefix pass: fp32)
-  pp->base.part_half = s->dtype == PA_BF16 && pt >= pa::kHalfPartialMinTokens &&
-                       group <= 4;
+  // the decode kernel's own partitions keep bf16 partials on request (prefix
+  // pass: fp32)
+  pp->base.part_half = (s->variant & PA_DECODE_HALF_PARTIALS) && s->dtype == PA_BF16 &&
+                       pt >= pa::kHalfPartialMinTokens && group <= 4;
   return PA_OK;
 }
 
@@ -808,8 +815,8 @@ static pa_status_t cache_e4m3_impl(const void* k, const void* v, const int64_t* 
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.num_slots = (int64_t)num_blocks * block_size;
-  a.k_inv = 1.0f / k_scale;
-  a.v_inv = 1.0f / v_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.num_tokens = num_tokens;
   a.num_kv_heads = num_kv_heads;
   a.row_groups = head_dim / 8;

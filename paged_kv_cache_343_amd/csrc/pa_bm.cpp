@@ -35,6 +35,9 @@ struct pa_bm {
   std::unordered_map<int32_t, Seq> seqs;
   uint64_t epoch = 0;                          // append call counter
   std::vector<Seq*> batch;                     // scratch of pa_bm_append_slots
+  std::vector<int32_t> dropped;                // per block: references the batch
+                                               //   being counted gives up
+  std::vector<int32_t> touched;                // blocks with dropped != 0
 
   int32_t take() {
     const int32_t b = free_list.front();
@@ -42,11 +45,29 @@ struct pa_bm {
     ref[b] = 1;
     return b;
   }
-  // Does appending one token to `s` need a block (new block or CoW copy)?
-  bool append_needs_block(const Seq& s) const {
-    const int32_t off = s.ntok % block_size;
-    if (off == 0) return true;
-    return ref[s.table[s.ntok / block_size]] > 1;
+  // Blocks that appending one token to each of batch[0 .. n) takes: one per
+  // position that starts a block, and one per write into a block that some
+  // other holder still shares at that point. Writers into one shared block
+  // are served in batch order and each copy gives up the writer's reference,
+  // so the last holder writes in place and takes none.
+  int64_t blocks_for_appends(int32_t n) {
+    int64_t need = 0;
+    if (dropped.size() != ref.size()) dropped.assign(ref.size(), 0);
+    touched.clear();
+    for (int32_t k = 0; k < n; ++k) {
+      const Seq& s = *batch[(size_t)k];
+      if (s.ntok % block_size == 0) {
+        ++need;
+        continue;
+      }
+      const int32_t b = s.table[s.ntok / block_size];
+      if (ref[b] - dropped[b] > 1) {
+        ++need;
+        if (dropped[b]++ == 0) touched.push_back(b);
+      }
+    }
+    for (int32_t b : touched) dropped[b] = 0;
+    return need;
   }
 };
 
@@ -114,8 +135,8 @@ pa_status_t pa_bm_append_slots(pa_bm_t* bm, const int32_t* seq_ids, int32_t n, i
     if (it->second.ntok == INT32_MAX || it->second.swapped) return PA_EINVAL;
     it->second.stamp = epoch;
     batch[k] = &it->second;
-    need += bm->append_needs_block(it->second) ? 1 : 0;
   }
+  need = bm->blocks_for_appends(n);
   if (need > (int64_t)bm->free_list.size()) return PA_ENOBLOCKS;
   const int32_t bs = bm->block_size;
   int32_t ncow = 0;

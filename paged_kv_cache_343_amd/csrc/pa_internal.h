@@ -80,8 +80,8 @@ struct CacheArgs8 {
   void* k_pool;                 // [NB][Hkv][bs][D] codes
   void* v_pool;
   int64_t num_slots;            // num_blocks * block_size
-  float k_inv;                  // float32 1 / k_scale
-  float v_inv;
+  float k_scale;                // a value x is stored as the code of x / k_scale
+  float v_scale;
   int32_t num_tokens;
   int32_t num_kv_heads;
   int32_t row_groups;           // 8-element groups per row = D / 8
@@ -146,10 +146,10 @@ struct MqArgs {
   int32_t num_units;
 };
 
-// The decode kernels keep the partial output of a partition in bf16 when it
-// covers at least this many positions and the output is bf16 (an average
-// over many positions stays far from the size of single values); shorter
-// partials, and those of the multi-token kernels, stay fp32.
+// When the caller asks for bf16 partials (part_half), the decode kernels
+// keep the partial output of a partition in bf16 if it covers at least this
+// many positions and the output is bf16; shorter partials, those of the
+// multi-token kernels, and all partials by default stay fp32.
 constexpr int kHalfPartialMinTokens = 256;
 
 // Kernel selection key for pa_decode_partition.
@@ -188,7 +188,8 @@ hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& 
 // kernel (which never splits the context).
 bool multi_query_tiled(int group, int max_query_len);
 hipError_t launch_copy_blocks(const CopyArgs& args, hipStream_t stream);
-// Synchronises `stream`, returns the device error word and clears it.
+// Fetches and clears the device error word in one atomic exchange, ordered
+// after the work already enqueued on `stream`, and waits for the value.
 hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream);
 
 // Workgroup size (waves) of the partition kernels.

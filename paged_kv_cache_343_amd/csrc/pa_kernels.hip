@@ -1246,25 +1246,29 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
   reinterpret_cast<uint4*>(a.v_pool)[dst] = reinterpret_cast<const uint4*>(a.v)[src];
 }
 
-// FP8 E4M3 code of y: nearest code, ties to the even mantissa, saturating at
-// +-448, NaN to 0x7F (with y's sign). Normal range: the float's mantissa is
-// rounded to 3 bits on its bit pattern (carry into the exponent included)
-// and the exponent rebased from 127 to 7; below 2^-6 the code is the
-// subnormal count round(|y| * 2^9).
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (a != a) return 0x7fu | sign;
-  if (a >= 448.0f) return 0x7eu | sign;
-  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f) | sign;
-  const uint32_t b = __float_as_uint(a);
-  const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
-  return ((r >> 20) - (120u << 3)) | sign;
+// FP8 E4M3 code of the exact quotient x / s (s > 0 and finite): the nearest
+// code, ties to the even mantissa, saturating at +-448, NaN to 0x7F with x's
+// sign. The quotient is formed in double, which decides every case as the
+// exact quotient would: a midpoint between two codes has at most 5
+// significant bits, so the quotient of two floats is either such a midpoint
+// exactly or at least 2^-29 of its size away from it, far more than one
+// double rounding moves it. In the normal range the double's mantissa is
+// then rounded to 3 bits on its bit pattern (carry into the exponent
+// included) and the exponent rebased from 1023 to 7; below 2^-6 the code is
+// the subnormal count round(x / s * 2^9), ties to even.
+__device__ __forceinline__ uint32_t e4m3_code_of_quotient(float x, float s) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  if (x != x) return 0x7fu | sign;
+  const double a = fabs((double)x) / (double)s;
+  if (a >= 448.0) return 0x7eu | sign;
+  if (a < 0.015625) return (uint32_t)__builtin_rint(a * 512.0) | sign;
+  const uint64_t b = (uint64_t)__double_as_longlong(a);
+  const uint64_t r = b + 0xffffffffffffull + ((b >> 49) & 1u);
+  return (uint32_t)((r >> 49) - (1016ull << 3)) | sign;
 }
 
 // One thread per 8 elements of a (token, head) row, K and V together: 16
-// bytes of bf16 in, 8 bytes of codes out. x * inv is rounded to float32
-// before the code is chosen.
+// bytes of bf16 in, 8 bytes of codes out.
 __global__ __launch_bounds__(256) void reshape_and_cache_e4m3_kernel(CacheArgs8 a) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_token = (int64_t)a.num_kv_heads * a.row_groups;
@@ -1284,12 +1288,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_e4m3_kernel(CacheArgs8 
   const int64_t dst = ((b * a.num_kv_heads + h) * a.block_size + o) * a.row_groups + c;
   for (int pool = 0; pool < 2; ++pool) {
     const uint4 x = reinterpret_cast<const uint4*>(pool ? a.v : a.k)[idx];
-    const float inv = pool ? a.v_inv : a.k_inv;
+    const float sc = pool ? a.v_scale : a.k_scale;
     float f[8];
     Elem<uint16_t>::unpack(x, f);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_code(f[e] * inv) << (8 * (e & 3));
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_code_of_quotient(f[e], sc) << (8 * (e & 3));
     reinterpret_cast<uint2*>(pool ? a.v_pool : a.k_pool)[dst] = make_uint2(w[0], w[1]);
   }
 }
@@ -2500,17 +2504,26 @@ bool multi_query_tiled(int group, int max_query_len) {
   return (int64_t)max_query_len * group >= kFaRows;
 }
 
+// Copy of the error word taken by take_errors_kernel.
+__device__ uint32_t g_error_snapshot;
+
+// Fetches and clears the error word in one atomic exchange, so that a bit
+// raised by work still running elsewhere (another stream) stays set for the
+// next read instead of being lost between a read and a separate clear.
+__global__ void take_errors_kernel() {
+  if (threadIdx.x == 0) g_error_snapshot = atomicExch(&g_error_word, 0u);
+}
+
 hipError_t read_and_clear_errors(uint32_t* flags, hipStream_t stream) {
-  hipError_t e = hipStreamSynchronize(stream);
+  hipLaunchKernelGGL(take_errors_kernel, dim3(1), dim3(64), 0, stream);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint32_t v = 0;
-  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_error_word), sizeof(v), 0, hipMemcpyDeviceToHost);
+  e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_error_snapshot), sizeof(v), 0,
+                               hipMemcpyDeviceToHost, stream);
   if (e != hipSuccess) return e;
-  if (v != 0) {
-    const uint32_t zero = 0;
-    e = hipMemcpyToSymbol(HIP_SYMBOL(g_error_word), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return e;
-  }
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
   *flags = v;
   return hipSuccess;
 }

@@ -17,6 +17,7 @@ import torch
 import paged_kv_cache_343_amd as P
 import workloads as W
 from oracle import pa_oracle as O
+from oracle import ref as R
 
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}   # (abs, rel): |d| <= abs + rel*|ref|
 
@@ -90,23 +91,16 @@ class Case:
                     variant=variant)
         return out
 
-    def oracle_rows(self, pairs):
-        """Oracle outputs (float64) for the listed (seq, q_head) pairs."""
-        q64 = O.as_f64(self.oq, self.dtype)
-        res = []
-        for i, h in pairs:
-            g = O.kv_head_of(h, self.hq, self.hkv)
-            L = int(self.olens[i])
-            phys, off = O.positions_to_rows(self.otables[i], L, self.bs)
-            kk = O.as_f64(self.ok_pool[phys, g, off, :], self.dtype)
-            vv = O.as_f64(self.ov_pool[phys, g, off, :], self.dtype)
-            if L == 0:
-                res.append(np.zeros(self.d))
-                continue
-            s = self.scale * (kk @ q64[i, h])
-            e = np.exp(s - s.max())
-            res.append((e @ vv) / e.sum())
-        return np.stack(res)
+    def oracle_c(self):
+        """Oracle outputs (float64 [B, Hq, D]) for every (sequence, head) row,
+        from the plain-C float64 oracle over the host pools and tables."""
+        return R.decode(self.oq, self.ok_pool, self.ov_pool, self.otables, self.olens,
+                        self.scale, self.dtype)
+
+    def oracle_c_e4m3(self, k_codes, v_codes, k_scale, v_scale, q=None):
+        """oracle_c over 8-bit pools of codes (q in bf16)."""
+        return R.decode_e4m3(self.oq if q is None else q, k_codes, v_codes, k_scale, v_scale,
+                             self.otables, self.olens, self.scale)
 
     def oracle_all(self):
         q64 = O.as_f64(self.oq, self.dtype)
@@ -180,11 +174,12 @@ def build(w: W.Workload, device, *, lens=None, pool_on_device=False, append=True
 
 
 def build_shared_prefix(w: W.Workload, device, *, prefix_len=None, groups=None, long_seqs=None,
-                        pool_on_device=True):
+                        pool_on_device=True, final_append=True):
     """Shared-prefix workload: per group, one parent holds the prompt, the
     other samples fork it; every sample then appends its private suffix
     (copy-on-write on the first write into the shared partial block), and a
-    final decode step appends one token per sequence."""
+    final decode step appends one token per sequence (left to the caller
+    with final_append=False; the tables have room for it either way)."""
     rng = np.random.default_rng(w.seed)
     suffix = W.draw_lengths(w, rng)
     samples = w.extra["samples"]
@@ -237,19 +232,23 @@ def build_shared_prefix(w: W.Workload, device, *, prefix_len=None, groups=None, 
         all_pairs += pairs.tolist()
         oslots += [s for s, _ in ores]
         opairs += [list(cw) for _, cw in ores if cw is not None]
-    slots, pairs = c.bm.append_slots(list(range(B)))
-    ores = c.obm.append_slots(list(range(B)))
-    all_slots += slots.tolist(); all_pairs += pairs.tolist()
-    oslots += [s for s, _ in ores]; opairs += [list(cw) for _, cw in ores if cw is not None]
+    if final_append:
+        slots, pairs = c.bm.append_slots(list(range(B)))
+        ores = c.obm.append_slots(list(range(B)))
+        all_slots += slots.tolist(); all_pairs += pairs.tolist()
+        oslots += [s for s, _ in ores]; opairs += [list(cw) for _, cw in ores if cw is not None]
     assert all_slots == oslots and all_pairs == opairs, "allocation differs from the oracle"
     c.extra["cow_pairs"] = np.array(all_pairs, dtype=np.int64).reshape(-1, 2)
     if all_pairs:
         P.pa_copy_blocks(c.k_pool, c.v_pool, torch.tensor(all_pairs, dtype=torch.int64, device=device))
         O.copy_blocks(c.ok_pool, c.ov_pool, np.array(opairs))
-    P.pa_reshape_and_cache(to_device(knew, dtype, device), to_device(vnew, dtype, device),
-                           torch.tensor(all_slots, dtype=torch.int64, device=device),
-                           c.k_pool, c.v_pool)
-    O.reshape_and_cache(knew, vnew, np.array(oslots), c.ok_pool, c.ov_pool)
+    n_w = len(all_slots)
+    if n_w:
+        P.pa_reshape_and_cache(to_device(knew[:n_w], dtype, device),
+                               to_device(vnew[:n_w], dtype, device),
+                               torch.tensor(all_slots, dtype=torch.int64, device=device),
+                               c.k_pool, c.v_pool)
+        O.reshape_and_cache(knew[:n_w], vnew[:n_w], np.array(oslots), c.ok_pool, c.ov_pool)
     tab, ln = c.bm.export(list(range(B)), maxb)
     otab, oln = c.obm.export(list(range(B)), maxb)
     assert np.array_equal(tab, otab) and np.array_equal(ln, oln)
@@ -260,3 +259,69 @@ def build_shared_prefix(w: W.Workload, device, *, prefix_len=None, groups=None, 
     c.extra["samples"] = samples
     c.extra["groups"] = ngroups
     return c
+
+
+def bench_step(c: Case, *, seed=0, q_scale=1, shared_prefix=False, variant=P.PA_VARIANT_AUTO):
+    """One decode step launched the way bench.py launches it, checked step by
+    step against the oracle side. The host block manager reserves every
+    sequence's next slot (its oracle mirror must agree), the host builds the
+    work plan from its own lengths, pa_append_tokens writes the new K/V rows
+    and advances the device-resident tables and lengths (which must then
+    equal the mirror's export), and pa_decode_partition_planned +
+    pa_decode_reduce decode (pa_decode_shared_prefix with shared_prefix=True,
+    over the groups and prompt length recorded in c.extra). q_scale multiplies
+    q (a power of two keeps it exact). Returns the output tensor; the oracle
+    side (pools, tables, lengths, q) is updated to the same step."""
+    dev = c.device
+    rng = np.random.default_rng(10_000 + seed)
+    B, dtype = c.B, c.dtype
+    knew = W.normal_values((B, c.hkv, c.d), rng, dtype)
+    vnew = W.normal_values((B, c.hkv, c.d), rng, dtype)
+    if q_scale != 1:
+        q32 = (O.as_f64(c.oq, dtype) * q_scale).astype(np.float32)
+        c.oq = q32 if dtype == "f32" else W.to_bf16_bits(q32)
+        assert np.array_equal(O.as_f64(c.oq, dtype), O.as_f64(to_storage_np(c.q), dtype) * q_scale)
+        c.q = to_device(c.oq, dtype, dev)
+    ids = list(range(B))
+    slots, pairs = c.bm.append_slots(ids)
+    ores = c.obm.append_slots(ids)
+    assert slots.tolist() == [x for x, _ in ores], "slot mapping differs from the oracle"
+    assert pairs.shape[0] == 0 and all(cw is None for _, cw in ores)
+    otab, oln = c.obm.export(ids, c.maxb)
+    # device side, in the bench's order
+    shape = P._decode_shape(c.q, c.k_pool, c.tables, int(oln.max()), c.w.partition_tokens
+                            if not shared_prefix else 0,
+                            variant | (P.PA_DECODE_SHARED_KV if "samples" in c.extra else 0))
+    plan = None if shared_prefix else torch.from_numpy(P.pa_decode_plan(shape, oln)).to(dev)
+    P.pa_append_tokens(to_device(knew, dtype, dev), to_device(vnew, dtype, dev),
+                       torch.from_numpy(slots).to(dev), c.k_pool, c.v_pool, c.tables, c.lens)
+    out = torch.full_like(c.q, float("nan"))
+    if shared_prefix:
+        samples, groups = c.extra["samples"], c.extra["groups"]
+        shared = (c.extra["prefix_len"] // c.bs) * c.bs
+        gs = torch.arange(0, groups * samples + 1, samples, dtype=torch.int32, device=dev)
+        pref = torch.zeros(B, dtype=torch.int32, device=dev)
+        pref[:groups * samples] = shared
+        P.pa_decode_shared_prefix(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
+                                  group_start=gs, prefix_lens=pref, max_group_size=samples,
+                                  max_prefix_len=shared, max_seq_len=int(oln.max()),
+                                  partition_tokens=c.w.partition_tokens)
+    else:
+        ws = torch.empty(max(16, P.pa_decode_workspace_bytes(shape)), dtype=torch.uint8,
+                         device=dev)
+        P.pa_decode_partition_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
+                                      work_plan=plan, max_seq_len=shape.max_seq_len,
+                                      partition_tokens=shape.partition_tokens,
+                                      variant=shape.variant, workspace=ws)
+        P.pa_decode_reduce(c.q, c.k_pool, c.tables, c.lens, out, max_seq_len=shape.max_seq_len,
+                           partition_tokens=shape.partition_tokens, variant=shape.variant,
+                           workspace=ws)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    # oracle side of the same step
+    O.reshape_and_cache(knew, vnew, np.array([x for x, _ in ores]), c.ok_pool, c.ov_pool)
+    assert np.array_equal(c.tables.cpu().numpy(), otab), "device tables differ from the oracle's"
+    assert np.array_equal(c.lens.cpu().numpy(), oln), "device lengths differ from the oracle's"
+    c.otables, c.olens = otab, oln
+    c.max_len = int(oln.max())
+    return out

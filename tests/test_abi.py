@@ -69,7 +69,10 @@ def test_workspace_bytes():
     for v in (P.PA_VARIANT_AUTO, P.PA_VARIANT_MFMA, P.PA_VARIANT_VALU):
         assert (P.pa_decode_workspace_bytes(_shape(variant=v | P.PA_DECODE_SHARED_KV, **big)) ==
                 P.pa_decode_workspace_bytes(_shape(variant=v, **big)) > 0)
-    assert P.pa_decode_workspace_bytes(_shape(variant=0x200, **big)) == 0     # unknown flag
+    # bf16 partials (an option) use the same fp32-sized slots
+    assert (P.pa_decode_workspace_bytes(_shape(variant=P.PA_DECODE_HALF_PARTIALS, **big)) ==
+            P.pa_decode_workspace_bytes(_shape(**big)))
+    assert P.pa_decode_workspace_bytes(_shape(variant=0x400, **big)) == 0     # unknown flag
     assert P.pa_decode_workspace_bytes(_shape(variant=3, **big)) == 0         # unknown kernel
 
 

@@ -1,6 +1,7 @@
 """GPU parity of the 8-bit (FP8 E4M3) KV pool: the quantized slot write bit
-for bit against the oracle's codes, and decode over code pools against the
-float64 oracle on the dequantized pools."""
+for bit against the oracle's codes (nearest code to the exact quotient, also
+right at the rounding boundaries), and decode over pools of every finite code
+against the float64 oracle on the dequantized pools."""
 import numpy as np
 import pytest
 import torch
@@ -48,12 +49,61 @@ def test_quantized_slot_write_bitwise(dev, k_scale, v_scale):
         assert ((okc & 0x78) == 0).sum() > 0               # subnormal / zero codes exercised
 
 
+def test_quantized_slot_write_near_rounding_boundaries(dev):
+    """Inputs whose quotient x / scale lies within 2^-24 of a midpoint between
+    two codes, or on one: the kernel's codes equal the oracle's (nearest code
+    to the exact quotient) bit for bit, including the cases where rounding
+    x * float32(1 / scale) instead would pick the other code."""
+    rng = np.random.default_rng(403)
+    mags = [O.e4m3_value(c) for c in range(0x7F)]
+    hkv, d, nb, bs = 2, 128, 4, 16
+    differ = 0
+    for j in range(48):
+        # x (bf16) and a midpoint m; the scale float32(x / m) puts x / scale
+        # within one float32 rounding of m, and so do x * 2^k for the other
+        # midpoints m * 2^k in the normal range
+        k = int(rng.integers(8, 0x76))
+        m = (mags[k] + mags[k + 1]) / 2
+        x0 = float(O.as_f64(W.to_bf16_bits(np.float32([rng.uniform(0.5, 2.0)])), "bf16")[0])
+        if j % 4:
+            s = float(np.float32(x0 / m))
+        else:
+            s = 2.0 ** -int(rng.integers(0, 6))      # power-of-two scale:
+            x0 = m * s                               # x / s = m exactly, a tie
+        row = np.array([x0 * 2.0 ** e for e in range(-6, 6)], dtype=np.float32)
+        row = np.concatenate([row, -row])
+        vals = np.resize(row, (2, hkv, d)).astype(np.float32)
+        bits = W.to_bf16_bits(vals)
+        assert np.array_equal(O.as_f64(bits, "bf16"), vals.astype(np.float64))
+        slots = np.array([3, 40], dtype=np.int64)
+        kc = torch.zeros((nb, hkv, bs, d), dtype=torch.uint8, device=dev)
+        vc = torch.zeros_like(kc)
+        kb = to_device(bits, "bf16", dev)
+        P.pa_reshape_and_cache_e4m3(kb, kb, torch.from_numpy(slots).to(dev), kc, vc, s, s)
+        okc = np.zeros((nb, hkv, bs, d), dtype=np.uint8)
+        ovc = np.zeros_like(okc)
+        O.reshape_and_cache_e4m3(vals, vals, slots, okc, ovc, s, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(kc.cpu().numpy(), okc), f"case {j}: scale {s!r}, x {x0!r}"
+        assert np.array_equal(vc.cpu().numpy(), ovc)
+        inv = np.float32(1) / np.float32(s)
+        differ += int((O.e4m3_encode((vals * inv).astype(np.float32)) != O.quantize_e4m3(vals, s)).sum())
+    assert P.pa_device_errors() == 0
+    assert differ > 0            # the reciprocal rule would have failed somewhere
+
+
 def _code_case(dev, hq, hkv, bs, lens, seed=411):
+    """A decode case over code pools holding every finite code of both signs
+    (magnitudes 2^-9 .. 448). q is scaled by 1/16 (exact in bf16) so that
+    scores over codes up to 448 x k_scale stay a few units wide and the
+    softmax mixes several positions."""
     w = W.Workload("f8", seed, 0, hq, hkv, 128, bs, "bf16", ("fixed", 0), ("factor", 1.3))
     c = build(w, dev, lens=lens, append=False)
     rng = np.random.default_rng(seed + 7)
     kc = W.random_e4m3_codes((c.nb, hkv, bs, 128), rng)
     vc = W.random_e4m3_codes((c.nb, hkv, bs, 128), rng)
+    c.oq = W.to_bf16_bits((O.as_f64(c.oq, "bf16") / 16).astype(np.float32))
+    c.q = to_device(c.oq, "bf16", dev)
     return c, kc, vc
 
 

@@ -1,7 +1,8 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the
-bench times: every allocation and cache write bit-exact over the whole pool,
-decode outputs compared with the oracle on sampled (sequence, head) rows plus
-every head of the shortest and longest sequences."""
+"""GPU parity at the workloads' full sizes through pa_decode (unplanned, both
+kernels): every allocation and cache write bit-exact over the whole pool,
+every decode output element compared with the plain-C float64 oracle. (The
+bench's own launch, planned and with device-side appends, is covered in
+test_gpu_full_parity.py.)"""
 import numpy as np
 import pytest
 import torch
@@ -21,17 +22,10 @@ def dev():
     return torch.device("cuda", 0)
 
 
-def _sampled_check(c, out, n_samples=192, seed=0, what=""):
-    rng = np.random.default_rng(seed)
-    lens = c.olens
-    pairs = {(int(i), int(h)) for i, h in zip(rng.integers(0, c.B, n_samples), rng.integers(0, c.hq, n_samples))}
-    for i in (int(np.argmin(lens)), int(np.argmax(lens))):
-        pairs |= {(i, h) for h in range(c.hq)}
-    pairs = sorted(pairs)
-    got_all = O.as_f64(to_storage_np(out), c.dtype)
-    got = np.stack([got_all[i, h] for i, h in pairs])
-    ref = c.oracle_rows(pairs)
-    return check_close(got, ref, c.dtype, what)
+def _full_check(c, out, what=""):
+    """Every output element against the plain-C float64 oracle."""
+    got = O.as_f64(to_storage_np(out), c.dtype)
+    return check_close(got, c.oracle_c(), c.dtype, what)
 
 
 @pytest.mark.parametrize("variant", [P.PA_VARIANT_AUTO, P.PA_VARIANT_VALU])
@@ -42,7 +36,7 @@ def test_llama3_8b_gqa(dev, variant):
     assert np.array_equal(to_storage_np(c.v_pool), c.ov_pool)
     out = c.decode(variant=variant)
     assert P.pa_device_errors() == 0
-    print("llama3_8b", variant, _sampled_check(c, out, what="llama3_8b"), flush=True)
+    print("llama3_8b", variant, _full_check(c, out, what="llama3_8b"), flush=True)
 
 
 @pytest.mark.parametrize("variant", [P.PA_VARIANT_AUTO, P.PA_VARIANT_VALU])
@@ -52,7 +46,7 @@ def test_llama2_13b_mha(dev, variant):
     assert np.array_equal(to_storage_np(c.k_pool), c.ok_pool)
     out = c.decode(variant=variant)
     assert P.pa_device_errors() == 0
-    print("llama2_13b", variant, _sampled_check(c, out, what="llama2_13b"), flush=True)
+    print("llama2_13b", variant, _full_check(c, out, what="llama2_13b"), flush=True)
 
 
 @pytest.mark.parametrize("prefix_len", [1040, 1024])
@@ -75,7 +69,7 @@ def test_shared_prefix_cow(dev, prefix_len):
         assert all(c.bm.refcount(int(b)) == 4 for b in rows[0])
     out = c.decode()
     assert P.pa_device_errors() == 0
-    print("shared_prefix", prefix_len, _sampled_check(c, out, what="shared_prefix"), flush=True)
+    print("shared_prefix", prefix_len, _full_check(c, out, what="shared_prefix"), flush=True)
     # samples of one group with equal q and equal suffix would be identical;
     # here they differ, so only check determinism across a second call
     out2 = c.decode()
@@ -88,4 +82,4 @@ def test_shared_prefix_long(dev):
     assert c.max_len == 32769
     out = c.decode()
     assert P.pa_device_errors() == 0
-    print("shared_prefix_long", _sampled_check(c, out, n_samples=64, what="long"), flush=True)
+    print("shared_prefix_long", _full_check(c, out, what="long"), flush=True)

@@ -251,3 +251,56 @@ def test_swap_errors_leave_state_unchanged():
     back = bm.swap_in(0)
     assert back[:, 0].tolist() == moves[:, 1].tolist() and not bm.is_swapped(0)
     assert bm.num_tokens(0) == 100 and bm.num_free_swap() == 8
+
+
+@pytest.mark.parametrize("spare", [0, 1])
+def test_exactly_enough_blocks_for_writes_into_a_shared_block(spare):
+    """Four samples share a 40-token prompt (two full 16-token blocks and a
+    half-filled one, refcount 4). One token appended to all four: the first
+    three writers copy the shared partial block and the fourth, then its
+    only holder, writes in place, so the batch takes exactly three blocks and
+    succeeds with three free; with two free it fails and changes nothing.
+    Listing only two of the four holders takes two blocks."""
+    bs, prompt = 16, 40
+    nb = 3 + 3 + spare
+    order = np.arange(nb, dtype=np.int32)
+    bm, ob = P.BlockManager(nb, bs, order), O.OracleBlockManager(nb, bs, order)
+    for m in (bm, ob):
+        m.add_seq(0, prompt)
+        for child in (1, 2, 3):
+            m.fork(0, child)
+    assert bm.num_free() == ob.num_free() == 3 + spare
+    slots, pairs = bm.append_slots([0, 1, 2, 3])
+    ores = ob.append_slots([0, 1, 2, 3])
+    assert slots.tolist() == [s for s, _ in ores]
+    assert [tuple(p) for p in pairs.tolist()] == [c for _, c in ores if c is not None]
+    assert pairs.shape == (3, 2) and bm.num_free() == spare
+    assert slots[3] == 2 * bs + prompt % bs            # the last holder kept block 2
+    _same_state(bm, ob, [0, 1, 2, 3], 4)
+    # two of four holders of a shared partial block: both copy
+    bm2, ob2 = P.BlockManager(5, bs, np.arange(5)), O.OracleBlockManager(5, bs, np.arange(5))
+    for m in (bm2, ob2):
+        m.add_seq(0, prompt)
+        for child in (1, 2, 3):
+            m.fork(0, child)
+    _, pairs2 = bm2.append_slots([1, 3])
+    ob2.append_slots([1, 3])
+    assert pairs2.shape == (2, 2) and bm2.num_free() == 0
+    _same_state(bm2, ob2, [0, 1, 2, 3], 4)
+
+
+def test_one_block_short_for_writes_into_a_shared_block():
+    bs, prompt = 16, 40
+    order = np.arange(5, dtype=np.int32)                # 3 held, 2 free: one short
+    bm, ob = P.BlockManager(5, bs, order), O.OracleBlockManager(5, bs, order)
+    for m in (bm, ob):
+        m.add_seq(0, prompt)
+        for child in (1, 2, 3):
+            m.fork(0, child)
+    with pytest.raises(P.PaError) as e:
+        bm.append_slots([0, 1, 2, 3])
+    assert e.value.name == "PA_ENOBLOCKS"
+    with pytest.raises(O.OracleNoBlocks):
+        ob.append_slots([0, 1, 2, 3])
+    _same_state(bm, ob, [0, 1, 2, 3], 4)
+    assert bm.num_free() == 2 and all(bm.refcount(b) == 4 for b in range(3))

@@ -39,3 +39,22 @@ def test_c_oracle_rejects_bad_block_id():
     tab[0, 1] = kp.shape[0] + 3
     with pytest.raises(RuntimeError):
         R.decode(q, kp, vp, tab, sl, 1.0, "f32")
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(8, 2, 16), (4, 4, 32)])
+def test_c_oracle_e4m3_matches_numpy(hq, hkv, bs):
+    """8-bit pools over every finite code of both signs: the C oracle reads
+    code value times its pool's scale, as the numpy oracle's dequantized
+    pools do."""
+    rng = np.random.default_rng(33)
+    lens = [0, 1, 33, 70, 5]
+    q, kp, _, tab, sl = _build(rng, len(lens), hq, hkv, 32, bs, lens, "bf16")
+    kc = W.random_e4m3_codes(kp.shape, rng)
+    vc = W.random_e4m3_codes(kp.shape, rng)
+    q = W.to_bf16_bits(O.as_f64(q, "bf16").astype(np.float32) / 64)
+    scale, ks, vs = 0.125, 0.37, 0.11
+    a = O.decode(O.as_f64(q, "bf16"), O.dequantize_e4m3(kc, ks), O.dequantize_e4m3(vc, vs),
+                 tab, sl, scale)
+    b = R.decode_e4m3(q, kc, vc, ks, vs, tab, sl, scale, num_threads=2)
+    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-12)
+    assert np.abs(a).max() > 1.0

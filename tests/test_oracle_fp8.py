@@ -1,6 +1,10 @@
 """Pins of the oracle's FP8 E4M3 arithmetic (8-bit KV pool) against the OCP
-definition's fixed points, brute force over every code, and torch's own
-float8_e4m3fn conversion (a library routine) inside the finite range."""
+definition's fixed points, brute force over every code, torch's own
+float8_e4m3fn conversion (a library routine) inside the finite range, and
+exact rational arithmetic for the quantization rule (nearest code to the
+exact quotient x / scale)."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -64,14 +68,82 @@ def test_matches_torch_float8_e4m3fn_in_range():
     assert np.array_equal(O.e4m3_encode(x), ref)
 
 
-def test_quantize_uses_float32_reciprocal_and_product():
+def _torch_code_values():
+    """Values of the 127 non-negative finite codes from torch's own
+    float8_e4m3fn type (a library routine, independent of the oracle)."""
+    vals = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    return [Fraction(float(v)) for v in vals]
+
+
+def _exact_code(x: float, s: float, values) -> int:
+    """Nearest code to the exact rational x / s (ties to the even code),
+    saturating at 448, by exact comparison with every code value."""
+    q = Fraction(x) / Fraction(s)
+    a = min(abs(q), values[-1])
+    best = min(range(0x7F), key=lambda c: (abs(values[c] - a), c % 2))
+    return best | (0x80 if q < 0 or (q == 0 and np.signbit(x)) else 0)
+
+
+def _near_midpoint_inputs(scales, rng):
+    """float32 values x within a few ulps of m * s for every midpoint m
+    between adjacent codes and every scale s (so x / s sits on or right
+    beside a rounding boundary), both signs."""
+    values = [float(v) for v in _torch_code_values()]
+    xs, ss = [], []
+    for s in scales:
+        s32 = np.float32(s)
+        for k in range(0x7E):
+            m = (values[k] + values[k + 1]) / 2
+            c = np.float32(m * float(s32))
+            for step in (-2, -1, 0, 1, 2):
+                x = c
+                for _ in range(abs(step)):
+                    x = np.nextafter(x, np.float32(np.inf if step > 0 else -np.inf))
+                sign = np.float32(-1 if rng.random() < 0.5 else 1)
+                xs.append(np.float32(x * sign))
+                ss.append(s32)
+    return np.array(xs, dtype=np.float32), np.array(ss, dtype=np.float32)
+
+
+SCALES = [0.37, 0.11, 0.0123, 1 / 3, 0.005, 1.0, 3.0, 7e-3, 0.125, 2.0 ** -20, 1234.5]
+
+
+def test_quantize_is_nearest_code_of_exact_quotient():
+    """quantize_e4m3 against exact rational arithmetic: for inputs on or
+    beside every rounding boundary of 11 scales, the code is the nearest one
+    to the exact x / scale (ties to the even code)."""
     rng = np.random.default_rng(9)
-    x = rng.standard_normal(1000).astype(np.float32)
-    scale = 0.0123
-    inv = np.float32(1) / np.float32(scale)
-    assert np.array_equal(O.quantize_e4m3(x, scale), O.e4m3_encode((x * inv).astype(np.float32)))
+    values = _torch_code_values()
+    xs, ss = _near_midpoint_inputs(SCALES, rng)
+    got = np.concatenate([O.quantize_e4m3(xs[ss == s], float(s)) for s in np.unique(ss)])
+    xs_o = np.concatenate([xs[ss == s] for s in np.unique(ss)])
+    ss_o = np.concatenate([ss[ss == s] for s in np.unique(ss)])
+    want = [_exact_code(float(x), float(s), values) for x, s in zip(xs_o, ss_o)]
+    assert got.tolist() == want
+    # exact ties (power-of-two scales make m * s a float32): ties go to the
+    # even code
+    ties = [(np.float32(m * 0.125), 0.125) for m in (1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10)]
+    for x, s in ties:
+        assert int(O.quantize_e4m3(np.array([x]), s)[0]) == _exact_code(float(x), s, values)
+    assert [int(O.quantize_e4m3(np.array([x]), s)[0]) for x, s in ties] == [0x38, 0x3A, 0x00, 0x02]
+
+
+def test_quantize_rule_is_the_quotient_not_the_reciprocal_product():
+    """Inputs where x / s and x * float32(1 / s) (rounded to float32) round to
+    different codes: the oracle gives the quotient's code, so the test says
+    which rule is in force."""
+    rng = np.random.default_rng(10)
+    values = _torch_code_values()
+    xs, ss = _near_midpoint_inputs(SCALES, rng)
+    recip = np.array([O.e4m3_encode([np.float32(x * (np.float32(1) / s))])[0]
+                      for x, s in zip(xs, ss)])
+    exact = np.array([_exact_code(float(x), float(s), values) for x, s in zip(xs, ss)])
+    differ = recip != exact
+    assert differ.sum() >= 20
+    got = np.array([O.quantize_e4m3(np.array([x]), float(s))[0] for x, s in zip(xs[differ], ss[differ])])
+    assert np.array_equal(got, exact[differ])
     # a value at the pool's largest magnitude maps to 448's code
-    assert int(O.quantize_e4m3(np.float32([448 * scale]), scale)[0]) in (0x7E,)
+    assert int(O.quantize_e4m3(np.float32([448 * 0.0123]), 0.0123)[0]) == 0x7E
 
 
 def test_cache_write_and_dequantized_decode():

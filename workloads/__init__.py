@@ -154,10 +154,10 @@ def normal_values(shape, rng: np.random.Generator, dtype: str) -> np.ndarray:
 
 
 def random_e4m3_codes(shape, rng: np.random.Generator) -> np.ndarray:
-    """Random FP8 E4M3 bytes for an 8-bit pool: a random sign bit over the
-    low 80 code points of each sign (the codes of magnitude below 4), drawn
-    uniformly. Raw bytes; the format's arithmetic is not used here."""
-    low = rng.integers(0, 0x50, size=shape, dtype=np.uint8)
+    """Random FP8 E4M3 bytes for an 8-bit pool: every finite code point of
+    either sign (0x00..0x7E, then a random sign bit), drawn uniformly over
+    code points. Raw bytes; the format's arithmetic is not used here."""
+    low = rng.integers(0, 0x7F, size=shape, dtype=np.uint8)
     sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
     return (low | sign).astype(np.uint8)
 
@@ -168,7 +168,7 @@ def random_e4m3_codes_device(shape, seed: int, device):
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
-    low = torch.randint(0, 0x50, tuple(shape), generator=g, device=device, dtype=torch.int32)
+    low = torch.randint(0, 0x7F, tuple(shape), generator=g, device=device, dtype=torch.int32)
     sign = torch.randint(0, 2, tuple(shape), generator=g, device=device, dtype=torch.int32)
     return (low | (sign << 7)).to(torch.uint8)
 
