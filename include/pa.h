@@ -153,6 +153,29 @@ pa_status_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
                       void* out, const pa_decode_shape_t* shape, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same operation, arguments and outputs as pa_decode (the
+ * same kernels, bit-identical results) without the workspace arguments: the
+ * partials live in a device array inside libpa, PA_NOALLOC_SCRATCH_BYTES per
+ * GPU, which each GPU holds from the library's first call on it until the
+ * process ends. The call allocates nothing.
+ *   - PA_EWORKSPACE (nothing enqueued) if pa_decode_workspace_bytes(shape)
+ *     exceeds PA_NOALLOC_SCRATCH_BYTES (256 sequences x 32 query heads x 8 KV
+ *     heads x head_dim 128, for instance, fit 15 partitions: 7,680 positions
+ *     at 512 per partition).
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams, or threads without ordering) race and
+ *     their outputs are undefined. Calls ordered on one stream are safe. No
+ *     part of the array needs to start at zero: a call writes every partial
+ *     it reads.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status_t pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
+                              void* out, const pa_decode_shape_t* shape, void* stream);
+
 /* First half of pa_decode: one workgroup per (sequence, KV head, partition)
  * writes that partition's max score, exp-sum and normalised partial output
  * to `workspace`; a sequence with a single partition gets its final `out`

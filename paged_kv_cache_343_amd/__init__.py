@@ -28,7 +28,8 @@ __all__ = [
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "PA_DECODE_SHARED_KV", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
-    "BlockManager", "EXPORTED_SYMBOLS", "PA_DECODE_HALF_PARTIALS",
+    "BlockManager", "EXPORTED_SYMBOLS", "PA_DECODE_HALF_PARTIALS", "pa_decode_noalloc",
+    "PA_NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -44,12 +45,15 @@ PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 PA_DECODE_SHARED_KV = 0x100
 # option OR-ed into `variant`: bf16 partial outputs (pa.h; off by default)
 PA_DECODE_HALF_PARTIALS = 0x200
+# size of the device array pa_decode_noalloc keeps its partials in (pa.h)
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 _STATUS = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE",
            4: "PA_ENOBLOCKS", 5: "PA_EREFCOUNT", 6: "PA_EHIP", 7: "PA_EDEVICE"}
 
 # Every function include/pa.h declares.
 EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
+    "pa_decode_noalloc",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
     "pa_status_str", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_multi_query_split", "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
@@ -92,6 +96,8 @@ _SIGS = {
     "pa_decode_partition": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                    ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                 ctypes.POINTER(DecodeShape), _vp]),
     "pa_decode_plan_capacity": (_i64, [ctypes.POINTER(DecodeShape)]),
     "pa_decode_plan": (_i32, [ctypes.POINTER(DecodeShape), _vp, _vp, _i64,
                               ctypes.POINTER(_i32)]),
@@ -304,6 +310,32 @@ def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_
     return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                         max_seq_len=max_seq_len, partition_tokens=partition_tokens,
                         variant=variant, workspace=workspace, stream=stream)
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,
+                      partition_tokens=0, variant=PA_VARIANT_AUTO, stream=None):
+    """pa_decode with its partials in libpa's own device array instead of a
+    caller workspace (include/pa.h pa_decode_noalloc): allocates nothing.
+    Calls that may overlap on one GPU race."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", dim=3)
+    _need(k_pool, "k_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(v_pool, "v_pool", dtype=q.dtype, dim=4, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, dim=1, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if block_tables.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise ValueError("batch mismatch")
+    shape = _decode_shape(q, k_pool, block_tables, max_seq_len, partition_tokens, variant)
+    st = lib().pa_decode_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                 block_tables.data_ptr(), seq_lens.data_ptr(),
+                                 ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
+                                 _stream_ptr(stream, dev))
+    _check(st, "pa_decode_noalloc")
+    return out
 
 
 def pa_decode_shared_prefix_workspace_bytes(shape: DecodeShape, max_group_size: int,

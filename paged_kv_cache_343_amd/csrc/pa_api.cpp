@@ -6,7 +6,9 @@
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "pa.h"
@@ -434,6 +436,62 @@ pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: pa_decode with its workspace in a file-scope device array
+// ---------------------------------------------------------------------------
+// Each GPU the library runs on holds its own copy of `scratch`, from the
+// first call on that GPU until the process ends. In host code the name
+// `scratch` is a host-side stand-in, not device memory: the kernels get the
+// address hipGetSymbolAddress returns on the current device, resolved once
+// per device and kept in g_scratch_addr.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's `scratch`.
+pa_status_t scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_EHIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return PA_EUNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_EHIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                         const int32_t* block_tables, const int32_t* seq_lens,
+                                         float scale, void* out, const pa_decode_shape_t* shape,
+                                         void* stream) {
+  Plan plan;
+  pa_status_t st = make_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  const size_t need = plan.ml_bytes + plan.o_bytes;
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_EWORKSPACE;
+  // every partial the merge reads is written earlier in the same call, so
+  // nothing in the array has to start at zero
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, ws, need,
+                     stream, true, true);
+}
 
 namespace {
 
