@@ -59,9 +59,10 @@ def kernel_source_hash() -> str:
 
 
 def recorded_traffic(variant_name: str, workload: str = "llama3_8b"):
-    """HBM bytes per partition-kernel launch measured with rocprofv3 counters
-    for the current kernel source and this workload (in the bench's default
-    launch configuration), or None."""
+    """The traffic record (HBM bytes per partition-kernel launch measured
+    with rocprofv3 counters, and the algorithmic K/V bytes of the same
+    launches) for the current kernel source and this workload in the bench's
+    default launch configuration, or None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:
@@ -69,7 +70,7 @@ def recorded_traffic(variant_name: str, workload: str = "llama3_8b"):
     if (rec.get("source_hash") != kernel_source_hash() or rec.get("variant") != variant_name
             or rec.get("workload") != workload):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def main() -> int:
@@ -118,7 +119,28 @@ def main() -> int:
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                          "this script with --copy-calibration-mib into a traffic record")
     ap.add_argument("--traffic-out", default=None)
+    ap.add_argument("--configs", default="auto", choices=["auto", "on", "off"],
+                    help="after the headline workload, run the other workloads (single_fp32, "
+                         "small_mha, llama2_13b, shared_prefix, shared_prefix_long) through the "
+                         "same step loop and report them under 'configs'; auto = on for the "
+                         "default headline launch")
+    ap.add_argument("--config-steps", type=int, default=50,
+                    help="timed steps per workload under 'configs' (5 warm-up steps each)")
+    ap.add_argument("--side-rows", default="on", choices=["on", "off"],
+                    help="measure the rows outside the step (block copies, fork, multi-token "
+                         "queries, group 8, swapping, the read probe) after the timed steps")
+    ap.add_argument("--scrub", action="store_true",
+                    help="also time the step's decode alone with 512 MiB written between "
+                         "iterations (outside the timed region), and without")
     args = ap.parse_args()
+    if args.configs == "auto":
+        args.configs = ("on" if (args.workload == "llama3_8b" and args.variant == "auto" and
+                                 args.partition_tokens is None and args.block_size is None and
+                                 args.kv_dtype == "native" and args.block_order == "shuffled" and
+                                 not args.upload_tables and not args.no_plan and
+                                 not args.half_partials and args.copy_calibration_mib == 0)
+                        else "off")
+    args.configs = args.configs == "on"
     if args.traffic_from:
         return summarise_traffic(args)
     if args.event_every < 1 or not 1 <= args.done_every <= 4 or args.steps < 1 or args.warmup < 0:
@@ -140,6 +162,20 @@ def main() -> int:
         return 1
     P.lib()  # fail loudly if libpa.so is missing
     dev = torch.device("cuda", 0)
+    result = run_workload(args, torch, P, W, dev, side_rows=args.side_rows == "on")
+    if args.configs:
+        result["configs"] = other_configs(args, torch, P, W, dev, result)
+    result["run"] = run_metadata(torch, W.get(args.workload), result)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
+    """Build one workload, run its warm-up and timed steps and return the
+    result record (the JSON line's fields for this workload). side_rows adds
+    the measurements of the rows outside the step (block copies, fork,
+    multi-token queries, group 8, swapping, the read-bandwidth probe, the CPU
+    baseline)."""
     w = W.get(args.workload)
     prefix = w.lengths[0] == "prefix_suffix"
     variant = {"auto": P.PA_VARIANT_AUTO, "valu": P.PA_VARIANT_VALU, "mfma": P.PA_VARIANT_MFMA}[args.variant]
@@ -538,6 +574,59 @@ def main() -> int:
         torch.cuda.synchronize()
         cache_ms.append(e[0].elapsed_time(e[1]))
         red_ms.append(e[1].elapsed_time(e[2]))
+    scrub_us = None
+    if args.scrub:
+        # the last step's decode again on its own inputs, timed alone: after
+        # 512 MiB were written (L2 and the 256 MB MALL then hold other
+        # lines, so K/V come from HBM), and back to back without that
+        tabs_p = db["tables"] if upload else tab_dev_ptr
+        lens_p = db["lens"] if upload else len_dev_ptr
+        qp = q_all[nsteps - 1].data_ptr()
+
+        def decode_last():
+            if sp_mode:
+                check(L.pa_decode_shared_prefix(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale,
+                                                out_ptr, shape_ref, *sp_args, cs),
+                      "pa_decode_shared_prefix")
+                return
+            if fp8 and plan_cap:
+                check(L.pa_decode_partition_e4m3_planned(qp, kp_ptr, vp_ptr, tabs_p, lens_p,
+                                                         c_scale, c_kscale, c_vscale, out_ptr,
+                                                         shape_ref, db["plan"], n_units[b_last],
+                                                         ws_ptr, ws_bytes, cs), "partition")
+            elif fp8:
+                check(L.pa_decode_partition_e4m3(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale,
+                                                 c_kscale, c_vscale, out_ptr, shape_ref, ws_ptr,
+                                                 ws_bytes, cs), "partition")
+            elif plan_cap:
+                check(L.pa_decode_partition_planned(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale,
+                                                    out_ptr, shape_ref, db["plan"],
+                                                    n_units[b_last], ws_ptr, ws_bytes, cs),
+                      "partition")
+            else:
+                check(L.pa_decode_partition(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale, out_ptr,
+                                            shape_ref, ws_ptr, ws_bytes, cs), "partition")
+            check(L.pa_decode_reduce(lens_p, out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
+                  "pa_decode_reduce")
+
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        scrub_us = {}
+        for mode in ("unscrubbed", "scrubbed"):
+            ts = []
+            for k in range(22):
+                if mode == "scrubbed":
+                    junk.fill_(k + 1)
+                torch.cuda.synchronize()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(compute)
+                decode_last()
+                e[1].record(compute)
+                torch.cuda.synchronize()
+                ts.append(e[0].elapsed_time(e[1]))
+            scrub_us[mode] = 1e3 * float(np.median(ts[2:]))
+        del junk
+        if P.pa_device_errors() != 0:
+            raise RuntimeError("device index error in the scrub measurement")
     period_ms = [ev[k][0].elapsed_time(ev[k + 1][0]) / args.event_every
                  for k in range(len(ev) - 1)]
     log(f"GPU step period {1e3 * np.mean(period_ms):.1f} us")
@@ -590,12 +679,23 @@ def main() -> int:
                        "partition_samples": len(part_ms)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(vname, w.name) if default_launch else None,
+                     "traffic": None,
                      "kernel": ("shared_prefix_decode + decode_reduce (one call)" if sp_mode else
                                 "decode_partition_" + vname + ("_e4m3" if fp8 else "")),
                      "algorithmic_bytes_per_launch": int(bytes_per_launch)},
     }
     avg_len = total_bytes / K / (2 * hkv * d * pool_eb) / B
+    result["sum_L_per_step"] = round(avg_len * B, 1)
+    rec = recorded_traffic(vname, w.name) if default_launch else None
+    if rec is not None:
+        # the counters' run had its own step mix (its steps and warm-up): its
+        # traffic is set against its own algorithmic bytes
+        rf = result["roofline"]
+        rf["traffic"] = rec["bytes_per_launch"]
+        if rec.get("algorithmic_bytes_per_launch"):
+            rf["traffic_run_algorithmic_bytes"] = rec["algorithmic_bytes_per_launch"]
+            rf["traffic_over_algorithmic"] = round(
+                rec["bytes_per_launch"] / rec["algorithmic_bytes_per_launch"], 4)
     parts = float(np.mean([-(-int(x) // ptok) for x in stage[0]["lens"].numpy()])) if ptok > 0 else 1.0
     pe = 2 if (args.half_partials and eb == 2) else 4      # bytes per partial-output element
     red_bytes = B * hq * (parts * d * pe + d * eb) + B * hkv * parts * 128 if parts > 1 else 0
@@ -613,14 +713,19 @@ def main() -> int:
                              if sp_mode else
                              {"us": round(1e3 * float(np.mean(red_ms)), 2), "bytes_moved": int(red_bytes),
                               "GBps": round(red_bytes / (float(np.mean(red_ms)) / 1e3) / 1e9, 1)}),
-        "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
-        "a6_fork_cow_host_us": fork_cow_host_us(P),
-        "n2_multi_query": multi_query_rate(P, torch, dev, W),
-        "decode_group8": group8_decode_rate(P, torch, dev, W),
-        "n3_swap_blocks": swap_rate(P, torch, dev),
     }
-    peak = stream_read_peak(torch, dev)
-    result["practical_peak"] = dict(peak, partition_frac=round(achieved / peak["GBps"], 4))
+    if side_rows:
+        result["rows"].update({
+            "a5_copy_blocks": copy_blocks_rate(P, torch, dev),
+            "a6_fork_cow_host_us": fork_cow_host_us(P),
+            "n2_multi_query": multi_query_rate(P, torch, dev, W),
+            "decode_group8": group8_decode_rate(P, torch, dev, W),
+            "n3_swap_blocks": swap_rate(P, torch, dev),
+        })
+        peak = stream_read_peak(torch, dev)
+        result["practical_peak"] = dict(peak, partition_frac=round(achieved / peak["GBps"], 4),
+                                        partition_frac_of_random_4k=round(
+                                            achieved / peak["random_4k_GBps"], 4))
     if prefix:
         # bytes of distinct cached rows read per step: a shared prompt block is
         # read once per step however many sequences point at it
@@ -652,54 +757,140 @@ def main() -> int:
         rf.update({"achieved": round(uach, 1), "frac": round(uach / HBM_PEAK_GBS, 4),
                    "algorithmic_bytes_per_launch": int(ub), "bytes": "unique K/V rows",
                    "logical_achieved": round(achieved, 1)})
-        result["practical_peak"]["partition_frac"] = round(uach / result["practical_peak"]["GBps"], 4)
+        if "practical_peak" in result:
+            result["practical_peak"]["partition_frac"] = round(
+                uach / result["practical_peak"]["GBps"], 4)
+    if scrub_us is not None:
+        nbytes = int(uniq[-1]) if prefix else int(step_bytes[-1])
+        result["scrub"] = {
+            "decode_us_unscrubbed": round(scrub_us["unscrubbed"], 2),
+            "decode_us_scrubbed": round(scrub_us["scrubbed"], 2),
+            "bytes": nbytes, "bytes_kind": "unique K/V rows" if prefix else "K/V rows",
+            "GBps_unscrubbed": round(nbytes / scrub_us["unscrubbed"] / 1e3, 1),
+            "GBps_scrubbed": round(nbytes / scrub_us["scrubbed"] / 1e3, 1),
+            "frac_scrubbed": round(nbytes / scrub_us["scrubbed"] / 1e3 / HBM_PEAK_GBS, 4),
+            "what": "the last step's decode (partition + merge) timed alone, median of 20, "
+                    "with 512 MiB written between iterations outside the timed region, and "
+                    "back to back without"}
     if args.copy_calibration_mib > 0:
         result["copy_calibration"] = copy_calibration(P, torch, dev, args.copy_calibration_mib,
                                                       hkv * bs * d * eb)
-    if not args.no_cpu_baseline:
+    if side_rows and not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, kp_host, vp_host, storage_np(q_all[nsteps - 1]),
                                               ctx, order, nb, nsteps, scale, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
-    return 0
+    return result
+
+
+# The workloads reported under 'configs' beside the headline, with their tags.
+OTHER_CONFIGS = (("single_fp32", "C1"), ("small_mha", "C2"), ("llama2_13b", "C3"),
+                 ("shared_prefix", "C5"), ("shared_prefix_long", "C5-long"))
+# cache-resident working sets (below the 256 MB MALL, or near it): also timed
+# with the caches scrubbed
+SCRUBBED_CONFIGS = ("small_mha", "shared_prefix")
+
+
+def other_configs(args, torch, P, W, dev, head: dict) -> dict:
+    """Every other workload through the same step loop (fewer steps), one
+    summary row each."""
+    out = {}
+    for name, tag in OTHER_CONFIGS:
+        sub = argparse.Namespace(**vars(args))
+        sub.workload, sub.steps, sub.warmup = name, args.config_steps, 5
+        sub.no_cpu_baseline, sub.copy_calibration_mib = True, 0
+        sub.scrub = name in SCRUBBED_CONFIGS
+        log(f"config {tag}: {name}")
+        r = run_workload(sub, torch, P, W, dev, side_rows=False)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        rf = r["roofline"]
+        row = {"config": tag, "workload": name, "dtype": r["dtype"], "steps": sub.steps,
+               "decode_call": r["config"]["decode_call"], "ms_per_step": r["ms_per_step"],
+               "step_GBps": r["value"], "seq_steps_per_s": r["seq_steps_per_s"],
+               "partition_us": r["kernels_us"]["partition"], "reduce_us": r["kernels_us"]["reduce"],
+               "kernel_GBps": rf["achieved"], "frac": rf["frac"],
+               "bytes": rf.get("bytes", "K/V rows"), "sum_L_per_step": r["sum_L_per_step"]}
+        if "shared_prefix" in r:
+            sp = r["shared_prefix"]
+            row["logical_kernel_GBps"] = rf.get("logical_achieved")
+            row["shared_prefix"] = {k: sp[k] for k in (
+                "logical_bytes_per_step", "unique_bytes_per_step", "unique_GBps",
+                "pct_of_hbm_peak_unique", "partition_unique_GBps")}
+        if "scrub" in r:
+            row["scrub"] = r["scrub"]
+        if "practical_peak" in head:
+            row["practical_frac"] = round(rf["achieved"] / head["practical_peak"]["GBps"], 4)
+        out[name] = row
+    return out
+
+
+def run_metadata(torch, w, result: dict) -> dict:
+    """Versions, device and host facts, and the draw seed of the run."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rocm = fh.read().strip()
+    except OSError:
+        pass
+    with open(os.path.abspath(__file__), "rb") as fh:
+        bench_sha = hashlib.sha256(fh.read()).hexdigest()[:16]
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_bytes": int(props.total_memory),
+            "rocm": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": cpu_model(), "host_affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "workload_seed": w.seed, "sum_L_per_step": result.get("sum_L_per_step"),
+            "kernel_source_hash": kernel_source_hash(), "bench_sha16": bench_sha}
+
+
+PROBE_PATTERNS = {0: ("stride", (1, 2, 4, 8)), 1: ("wavetile", (1, 2, 4, 8)),
+                  2: ("random4k", (4, 8))}
 
 
 def stream_read_peak(torch, dev) -> dict:
-    """Practical HBM read ceiling: the streaming-read probe (libpa_probe.so)
-    over a 4 GiB buffer, best over a sweep of launch shapes (workgroups of 256
-    threads from 4 to 64 per CU, 1 to 8 independent 16-byte loads in flight
-    per lane, plain and streaming cache policy), 10 timed launches each."""
+    """Practical HBM read ceiling: the read probe (libpa_probe.so) over a
+    4 GiB buffer, best over a sweep of launch shapes (workgroups of 256
+    threads from 4 to 64 per CU; 1 to 8 independent 16-byte loads in flight
+    per lane; plain and streaming cache policy) and access patterns
+    (grid-stride, consecutive tiles per wave, random 4 KiB tiles of two
+    pools), 10 timed launches each. The best random-tile rate, the pattern of
+    paged decode's gather, is reported beside the overall best."""
     path = os.path.join(ROOT, "paged_kv_cache_343_amd", "libpa_probe.so")
     lib = ctypes.CDLL(path)
     lib.pa_probe_stream_read.restype = ctypes.c_int
     lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                         ctypes.c_void_p]
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream(dev).cuda_stream
     sweep = {}
-    for grid in (1024, 2048, 4096, 8192, 16384):
-        for loads in (1, 2, 4, 8):
-            for nt in (0, 1):
-                for _ in range(2):
-                    if lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, loads, nt,
-                                                sink.data_ptr(), s):
-                        raise RuntimeError("probe launch failed")
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(10):
-                    lib.pa_probe_stream_read(buf.data_ptr(), nbytes, grid, loads, nt,
-                                             sink.data_ptr(), s)
-                e1.record()
-                torch.cuda.synchronize()
-                sweep[f"wg{grid}_loads{loads}_{'nt' if nt else 'plain'}"] = round(
-                    nbytes / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9, 1)
+    for pattern, (pname, loads_set) in PROBE_PATTERNS.items():
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            for loads in loads_set:
+                for nt in (0, 1):
+                    args = (buf.data_ptr(), nbytes, grid, loads, nt, pattern, sink.data_ptr(), s)
+                    for _ in range(2):
+                        if lib.pa_probe_stream_read(*args):
+                            raise RuntimeError("probe launch failed")
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(10):
+                        lib.pa_probe_stream_read(*args)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    # (4 GiB splits into two halves of 2^19 4-KiB tiles, all read)
+                    sweep[f"{pname}_wg{grid}_loads{loads}_{'nt' if nt else 'plain'}"] = round(
+                        nbytes / (e0.elapsed_time(e1) / 10 / 1e3) / 1e9, 1)
     del buf
     best = max(sweep, key=sweep.get)
+    rnd = max((k for k in sweep if k.startswith("random4k")), key=sweep.get)
     return {"GBps": sweep[best], "bytes": nbytes, "kernel": "pa_probe_stream_read",
-            "best_launch": best, "sweep_GBps": sweep}
+            "best_launch": best, "random_4k_GBps": sweep[rnd], "random_4k_best_launch": rnd,
+            "sweep_GBps": sweep}
 
 
 def copy_blocks_rate(P, torch, dev) -> dict:
@@ -1027,6 +1218,17 @@ def _finish_traffic(args, out) -> int:
         total += c["partition_bytes"]
     out["bytes_per_launch"] = round(total)
     out["calibration_bytes_each_way"] = int(2 * n * block_bytes)
+    # algorithmic K/V bytes of the same launches: the seeded lengths plus one
+    # token per step, at the counted (timed) steps
+    if w_.lengths[0] != "prefix_suffix":
+        ctx = __import__("workloads").draw_lengths(
+            w_, np.random.default_rng(w_.seed)).astype(np.int64)
+        per_tok = 2 * w_.num_kv_heads * w_.head_dim * w_.elem_bytes
+        steps = range(args.warmup, args.warmup + args.steps)
+        out["algorithmic_bytes_per_launch"] = round(float(np.mean(
+            [int((ctx + s + 1).sum()) * per_tok for s in steps])))
+        out["steps"], out["warmup"] = args.steps, args.warmup
+        out["traffic_over_algorithmic"] = round(total / out["algorithmic_bytes_per_launch"], 4)
     text = json.dumps(out, indent=1)
     print(text)
     if args.traffic_out:
@@ -1064,15 +1266,25 @@ def cpu_baseline(w, kp_host, vp_host, q_host, ctx, order, nb, nsteps, scale, sec
     sample = seqs[:n_seq]
     maxb = max(len(obm.table(i)) for i in sample)
     tables, lens = obm.export(sample, maxb)
-    threads = min(16, len(os.sched_getaffinity(0)))
+    # all the cores this process may run on, but no more than the host's
+    # share for it (OMP_NUM_THREADS, set to the machine's CPU share)
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS") or affinity)
+    threads = max(1, min(affinity, share))
     R.decode(q_host[:n_seq], kp_host, vp_host, tables, lens, scale, w.dtype, num_threads=threads)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        R.decode(q_host[:n_seq], kp_host, vp_host, tables, lens, scale, w.dtype, num_threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
+    # three timed runs of about seconds / 3 each; the median rate is reported
+    runs, reps, el = [], 0, 0.0
+    for _ in range(3):
+        r, t0 = 0, time.perf_counter()
+        while True:
+            R.decode(q_host[:n_seq], kp_host, vp_host, tables, lens, scale, w.dtype,
+                     num_threads=threads)
+            r += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds / 3 or r >= 400:
+                break
+        runs.append(n_seq * r / dt)
+        reps, el = reps + r, el + dt
     kv_bytes = int(lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
     # the same oracle on one thread, for a third of the time
     reps1, t1 = 0, time.perf_counter()
@@ -1082,15 +1294,19 @@ def cpu_baseline(w, kp_host, vp_host, q_host, ctx, order, nb, nsteps, scale, sec
         el1 = time.perf_counter() - t1
         if el1 >= seconds / 3 or reps1 >= 1000:
             break
-    return {"value": round(n_seq * reps / el, 2), "unit": "seq-steps/s", "cores": threads,
-            "kind": "oracle",
-            "kv_gb_per_s": round(kv_bytes * reps / el / 1e9, 3),
+    med = float(np.median(runs))
+    return {"value": round(med, 2), "unit": "seq-steps/s", "cores": threads,
+            "kind": "oracle", "affinity_cpus": affinity,
+            "thread_rule": ("OpenMP over (sequence, query head) pairs on min(affinity set, "
+                            "OMP_NUM_THREADS) threads"),
+            "runs_seq_steps_per_s": [round(x, 2) for x in runs],
+            "kv_gb_per_s": round(kv_bytes * med / n_seq / 1e9, 3),
             "cpu_model": cpu_model(),
             "single_thread": {"value": round(n_seq * reps1 / el1, 2), "unit": "seq-steps/s",
                               "repetitions": reps1, "seconds": round(el1, 1)},
             "sample": (f"first {n_seq} of {len(ctx)} {w.name} sequences at the last timed step "
                        f"(sum of lengths {int(lens.sum())}), plain C float64 oracle, "
-                       f"{reps} repetitions in {el:.1f} s")}
+                       f"median of 3 runs, {reps} repetitions in {el:.1f} s")}
 
 
 if __name__ == "__main__":

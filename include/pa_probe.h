@@ -2,16 +2,24 @@
  * pa_probe.h — measurement aid shipped beside libpa (libpa_probe.so), not
  * part of the decode path.
  *
- * pa_probe_stream_read: enqueues one streaming read of `bytes` bytes of
- * device memory at `buf` (16-byte aligned) on `stream` (hipStream_t as void*,
- * NULL = null stream) with `workgroups` workgroups of 256 threads. Each lane
- * keeps `loads_per_lane` (1, 2, 4 or 8) independent 16-byte loads in flight,
- * with the streaming (non-temporal) cache policy if `nontemporal` is
- * nonzero, else the plain one. The best rate over a sweep of these shapes is
- * the practical HBM read ceiling that the decode kernels' rates are compared
- * with. `sink` is a device word written only if the folded data equal a
- * sentinel (keeps the reads live). Returns 0, 1 for a bad argument (nothing
- * enqueued), 6 if the launch failed.
+ * pa_probe_stream_read: enqueues one read of `bytes` bytes of device memory
+ * at `buf` (16-byte aligned) on `stream` (hipStream_t as void*, NULL = null
+ * stream) with `workgroups` workgroups of 256 threads. Each lane keeps
+ * `loads_per_lane` independent 16-byte loads in flight, with the streaming
+ * (non-temporal) cache policy if `nontemporal` is nonzero, else the plain
+ * one. `pattern`: 0 = grid-stride (loads 1, 2, 4, 8; each wave load covers
+ * 1 KiB of consecutive bytes), 1 = each wave reads loads_per_lane KiB of
+ * consecutive bytes per iteration (loads 1, 2, 4, 8), 2 = random 4 KiB tiles
+ * from each half of the buffer at one pseudo-random tile index per
+ * iteration, like paged decode's K and V blocks (loads 4: one tile at a
+ * time, 8: both halves' tiles together; bytes >= 8 KiB; the tiles covered
+ * per half are a power of two, so up to half of the buffer is read: the
+ * achieved rate counts the bytes actually read, see the bench). The best
+ * rate over a sweep of these shapes is the practical HBM read ceiling that
+ * the decode kernels' rates are compared with. `sink` is a device word
+ * written only if the folded data equal a sentinel (keeps the reads live).
+ * Returns 0, 1 for a bad argument (nothing enqueued), 6 if the launch
+ * failed.
  */
 #ifndef PA_PROBE_H
 #define PA_PROBE_H
@@ -23,7 +31,7 @@ extern "C" {
 #endif
 
 int pa_probe_stream_read(const void* buf, size_t bytes, int workgroups, int loads_per_lane,
-                         int nontemporal, void* sink, void* stream);
+                         int nontemporal, int pattern, void* sink, void* stream);
 
 #ifdef __cplusplus
 }
