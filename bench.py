@@ -98,8 +98,8 @@ def main() -> int:
     ap.add_argument("--prefix-decode", default="auto", choices=["auto", "pa_decode", "shared"],
                     help="shared-prefix workloads: decode with pa_decode over a work plan, or "
                          "with pa_decode_shared_prefix (each shared prompt block read once per "
-                         "group); auto = the latter unless the batch holds unshared long "
-                         "sequences")
+                         "group, the walks after the prompts over a work plan); auto = the "
+                         "latter")
     ap.add_argument("--half-partials", action="store_true",
                     help="store partial outputs in bf16 (PA_DECODE_HALF_PARTIALS; an option "
                          "with a looser error bound, off by default)")
@@ -329,17 +329,19 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
     # Shared-prefix decode in the step (shared-prefix workloads): the prompt
     # groups and each sample's shared positions (the whole prompt blocks; a
     # half-filled prompt block was copied on write at setup) stay fixed.
-    sp_mode = prefix and not fp8 and (
-        args.prefix_decode == "shared" or (args.prefix_decode == "auto" and n_long == 0))
+    sp_mode = prefix and not fp8 and args.prefix_decode in ("shared", "auto")
+    walk_start_ptr = None           # host prefix lengths: the plan's walk starts
     if sp_mode:
         shared = (plen // bs) * bs
         sp_gs = torch.arange(0, ngroups * nsamp + 1, nsamp, dtype=torch.int32, device=dev)
-        sp_prefix = torch.zeros(B, dtype=torch.int32, device=dev)
-        sp_prefix[:ngroups * nsamp] = shared
+        sp_prefix_host = np.zeros(B, dtype=np.int32)
+        sp_prefix_host[:ngroups * nsamp] = shared
+        sp_prefix = torch.from_numpy(sp_prefix_host).to(dev)
+        walk_start_ptr = sp_prefix_host.ctypes.data
         sp_ws = torch.empty(max(16, P.pa_decode_shared_prefix_workspace_bytes(shape, nsamp, shared)),
                             dtype=torch.uint8, device=dev)
-        sp_args = (ngroups, sp_gs.data_ptr(), sp_prefix.data_ptr(), nsamp, shared,
-                   sp_ws.data_ptr(), sp_ws.numel())
+        sp_args = (ngroups, sp_gs.data_ptr(), sp_prefix.data_ptr(), nsamp, shared)
+        sp_ws_args = (sp_ws.data_ptr(), sp_ws.numel())
         sp_ptrs = (sp_gs, sp_prefix, sp_ws)  # kept alive for the raw calls
     step_bytes = []
     host_s = [0.0]  # host time per timed step, waits excluded
@@ -380,9 +382,10 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
         lens_host[:] += 1                    # every sequence appended one token
         if not upload:
             lens_np[b][:] = lens_host
-        if plan_cap and not sp_mode:         # pa_decode_shared_prefix takes no plan
+        if plan_cap:
+            # (pa_decode_shared_prefix: the walks after each prefix)
             t_pl = time.perf_counter()
-            st = Lh.pa_decode_plan(shape_ref, sp["lens"], sp["plan"], plan_cap,
+            st = Lh.pa_decode_plan(shape_ref, sp["lens"], walk_start_ptr, sp["plan"], plan_cap,
                                    ctypes.byref(nunits_c))
             if st != 0:
                 raise P.PaError(st, "pa_decode_plan")
@@ -474,31 +477,22 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
                   "pa_reshape_and_cache")
         if timed:
             evs[0].record(compute)
+        plan_ptr, plan_n = (db["plan"], n_units[b]) if plan_cap else (None, 0)
         if sp_mode:
             # prefix pass and per-sequence walks in one launch, then the merge
             check(L.pa_decode_shared_prefix(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
                                             db["lens"], c_scale, out_ptr, shape_ref, *sp_args,
-                                            cs), "pa_decode_shared_prefix")
-        elif fp8 and plan_cap:
-            check(L.pa_decode_partition_e4m3_planned(q_all[s].data_ptr(), kp_ptr, vp_ptr,
-                                                     db["tables"], db["lens"], c_scale, c_kscale,
-                                                     c_vscale, out_ptr, shape_ref, db["plan"],
-                                                     n_units[b], ws_ptr, ws_bytes, cs),
-                  "pa_decode_partition_e4m3_planned")
+                                            plan_ptr, plan_n, *sp_ws_args, cs),
+                  "pa_decode_shared_prefix")
         elif fp8:
             check(L.pa_decode_partition_e4m3(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
                                              db["lens"], c_scale, c_kscale, c_vscale, out_ptr,
-                                             shape_ref, ws_ptr, ws_bytes, cs),
+                                             shape_ref, plan_ptr, plan_n, ws_ptr, ws_bytes, cs),
                   "pa_decode_partition_e4m3")
-        elif plan_cap:
-            check(L.pa_decode_partition_planned(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
-                                                db["lens"], c_scale, out_ptr, shape_ref, db["plan"],
-                                                n_units[b], ws_ptr, ws_bytes, cs),
-                  "pa_decode_partition_planned")
         else:
             check(L.pa_decode_partition(q_all[s].data_ptr(), kp_ptr, vp_ptr, db["tables"],
-                                        db["lens"], c_scale, out_ptr, shape_ref, ws_ptr, ws_bytes,
-                                        cs), "pa_decode_partition")
+                                        db["lens"], c_scale, out_ptr, shape_ref, plan_ptr,
+                                        plan_n, ws_ptr, ws_bytes, cs), "pa_decode_partition")
         if timed:
             evs[1].record(compute)
             ev.append(evs)
@@ -584,28 +578,21 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
         qp = q_all[nsteps - 1].data_ptr()
 
         def decode_last():
+            plan_ptr, plan_n = (db["plan"], n_units[b_last]) if plan_cap else (None, 0)
             if sp_mode:
                 check(L.pa_decode_shared_prefix(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale,
-                                                out_ptr, shape_ref, *sp_args, cs),
-                      "pa_decode_shared_prefix")
+                                                out_ptr, shape_ref, *sp_args, plan_ptr, plan_n,
+                                                *sp_ws_args, cs), "pa_decode_shared_prefix")
                 return
-            if fp8 and plan_cap:
-                check(L.pa_decode_partition_e4m3_planned(qp, kp_ptr, vp_ptr, tabs_p, lens_p,
-                                                         c_scale, c_kscale, c_vscale, out_ptr,
-                                                         shape_ref, db["plan"], n_units[b_last],
-                                                         ws_ptr, ws_bytes, cs), "partition")
-            elif fp8:
+            if fp8:
                 check(L.pa_decode_partition_e4m3(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale,
-                                                 c_kscale, c_vscale, out_ptr, shape_ref, ws_ptr,
-                                                 ws_bytes, cs), "partition")
-            elif plan_cap:
-                check(L.pa_decode_partition_planned(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale,
-                                                    out_ptr, shape_ref, db["plan"],
-                                                    n_units[b_last], ws_ptr, ws_bytes, cs),
+                                                 c_kscale, c_vscale, out_ptr, shape_ref,
+                                                 plan_ptr, plan_n, ws_ptr, ws_bytes, cs),
                       "partition")
             else:
                 check(L.pa_decode_partition(qp, kp_ptr, vp_ptr, tabs_p, lens_p, c_scale, out_ptr,
-                                            shape_ref, ws_ptr, ws_bytes, cs), "partition")
+                                            shape_ref, plan_ptr, plan_n, ws_ptr, ws_bytes, cs),
+                      "partition")
             check(L.pa_decode_reduce(lens_p, out_ptr, shape_ref, ws_ptr, ws_bytes, cs),
                   "pa_decode_reduce")
 
@@ -1033,12 +1020,8 @@ def group8_decode_rate(P, torch, dev, W) -> dict:
         out = torch.empty_like(q)
 
         def call():
-            if wp is None:
-                P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out, max_seq_len=ml,
-                            variant=variant)
-            else:
-                P.pa_decode_planned(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out,
-                                    work_plan=wp, max_seq_len=ml, variant=variant, workspace=ws)
+            P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out, max_seq_len=ml,
+                        variant=variant, workspace=ws, work_plan=wp)
         for _ in range(2):
             call()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -146,12 +146,15 @@ size_t pa_decode_workspace_bytes(const pa_decode_shape_t* shape);
  *   seq_lens      [dev] int32 [B]
  *   scale         softmax scale applied to q.k (e.g. 1/sqrt(D))
  *   out           [dev] [B][Hq][D], written; rounded to nearest-even for bf16
+ *   work_plan     [dev] NULL (with num_units 0) for the full grid, or a work
+ *                 plan from pa_decode_plan and its unit count (below)
  *   workspace     [dev] >= pa_decode_workspace_bytes(shape) bytes
  */
 pa_status_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                      void* out, const pa_decode_shape_t* shape, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      void* out, const pa_decode_shape_t* shape, const int32_t* work_plan,
+                      int32_t num_units, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * pa_decode_noalloc — pa_decode for callers that cannot allocate device
@@ -183,58 +186,54 @@ pa_status_t pa_decode_noalloc(const void* q, const void* k_pool, const void* v_p
 pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 float scale, void* out, const pa_decode_shape_t* shape,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                const int32_t* work_plan, int32_t num_units, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
- * Work plans: pa_decode with a grid built on the host from the lengths.
+ * Work plans: the decode's grid built on the host from the lengths.
  *
- * Same operation as pa_decode (same definition and citations). pa_decode's
- * grid covers every (sequence, partition) pair up to max_seq_len, and the
- * pairs past a sequence's own length exit at once. When the caller knows
- * the lengths on the host (its block manager produced them), pa_decode_plan
- * lists only the pairs that hold positions: every full partition first, in
- * (sequence, partition) order, then each sequence's last, shorter partition,
- * longest first (an empty sequence gets one unit that writes its zeros).
- * The planned calls launch one workgroup per (unit, KV head) in that order.
- * Each unit computes exactly what it computes in pa_decode, so the outputs
- * are bit-identical to pa_decode's.
+ * Same operation as pa_decode (same definition and citations). Without a
+ * plan the grid covers every (sequence, partition) pair up to max_seq_len,
+ * and the pairs past a sequence's own length exit at once. When the caller
+ * knows the lengths on the host (its block manager produced them),
+ * pa_decode_plan lists only the pairs that hold positions: every full
+ * partition first, in (sequence, partition) order, then each sequence's
+ * last, shorter partition, longest first (an empty sequence gets one unit
+ * that writes its zeros). A decode call given the plan (work_plan and
+ * num_units of pa_decode, pa_decode_partition, the _e4m3 forms and
+ * pa_decode_shared_prefix) launches one workgroup per (unit, KV head) in
+ * that order. Each unit computes exactly what it computes without the plan,
+ * so the outputs are bit-identical.
  *
  *   pa_decode_plan_capacity: units a plan for `shape` can hold at most
  *     (num_seqs x partitions of max_seq_len); 0 if the shape is invalid.
  *   pa_decode_plan: seq_lens [host] int32 [B], the same values the device
- *     copy will hold; work_plan [host] int32 [capacity][4] receives one
- *     entry (sequence, partition, that sequence's length, 0) per unit;
- *     *num_units [host] receives their count.
- *     PA_EINVAL if a length is negative or above min(max_seq_len,
- *     max_blocks_per_seq * block_size), or capacity is too small. Shapes
- *     with 8 or 16 query heads per KV head on the matrix cores (the
- *     multi-token per-tile kernel) take plans too: one wave per unit.
- *   pa_decode_planned / pa_decode_partition_planned: pa_decode /
- *     pa_decode_partition with work_plan [dev] (16-byte aligned, the
- *     pa_decode_plan output copied to the device) and its num_units. The
- *     partition kernel takes each unit's length from its entry (seq_lens
- *     serves the merge and the unplanned path). An entry whose sequence is
- *     outside [0, B), whose length is negative or above the bound above, or
- *     whose partition holds no position is skipped and raises
- *     PA_DEVERR_PLAN. A plan built from other lengths than seq_lens leaves
- *     outputs undefined (a partition missing from it is never computed,
- *     and nothing is read outside the buffers). pa_decode_reduce
- *     completes a pa_decode_partition_planned call as it does an unplanned
- *     one.
+ *     copy will hold; walk_start [host] int32 [B] or NULL: the partitions of
+ *     sequence i tile positions [walk_start[i], seq_lens[i]) (for
+ *     pa_decode_shared_prefix: its prefix_lens; NULL = 0 for the other
+ *     calls); work_plan [host] int32 [capacity][4] receives one entry
+ *     (sequence, partition, that sequence's length, its walk start) per
+ *     unit; *num_units [host] receives their count. A walk that starts at
+ *     its sequence's end gets no unit. PA_EINVAL if a length is negative or
+ *     above min(max_seq_len, max_blocks_per_seq * block_size), a start is
+ *     negative or past its length, or capacity is too small. Shapes with 8
+ *     or 16 query heads per KV head on the matrix cores (the multi-token
+ *     per-tile kernel) take plans too: one wave per unit.
+ *   In a decode call, work_plan [dev] is the pa_decode_plan output copied to
+ *     the device (16-byte aligned) and num_units its count. The partition
+ *     kernel takes each unit's length from its entry (seq_lens serves the
+ *     merge and the unplanned path). An entry whose sequence is outside
+ *     [0, B), whose length is negative or above the bound above, or whose
+ *     partition holds no position is skipped and raises PA_DEVERR_PLAN. A
+ *     plan built from other lengths (or starts) than the device's leaves
+ *     outputs undefined (a partition missing from it is never computed, and
+ *     nothing is read outside the buffers). pa_decode_reduce completes a
+ *     planned pa_decode_partition call as it does an unplanned one.
  */
 int64_t pa_decode_plan_capacity(const pa_decode_shape_t* shape);
 pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_lens,
-                           int32_t* work_plan, int64_t capacity, int32_t* num_units);
-pa_status_t pa_decode_planned(const void* q, const void* k_pool, const void* v_pool,
-                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                              void* out, const pa_decode_shape_t* shape, const int32_t* work_plan,
-                              int32_t num_units, void* workspace, size_t workspace_bytes,
-                              void* stream);
-pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const void* v_pool,
-                                        const int32_t* block_tables, const int32_t* seq_lens,
-                                        float scale, void* out, const pa_decode_shape_t* shape,
-                                        const int32_t* work_plan, int32_t num_units,
-                                        void* workspace, size_t workspace_bytes, void* stream);
+                           const int32_t* walk_start, int32_t* work_plan, int64_t capacity,
+                           int32_t* num_units);
 
 /*
  * pa_decode_shared_prefix — pa_decode for a batch whose sequences come in
@@ -249,10 +248,12 @@ pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const
  * statistics and outputs (log-sum-exp, fp32).
  *
  *   shape          as pa_decode: bf16, head_dim 128, G in {1, 2, 4, 8, 16},
- *                  block size 16-128; partition_tokens 0 = 256 positions
- *                  (both passes split their range into partitions), -1 is
- *                  not accepted; of variant only PA_DECODE_HALF_PARTIALS
- *                  is read (it applies to the walks after the prefix)
+ *                  block size 16-128; both passes split their range into
+ *                  partitions: partition_tokens 0 = 256 positions for the
+ *                  prefix pass and pa_decode's automatic length for the
+ *                  walks after it, else that length for both; -1 is not
+ *                  accepted; of variant only PA_DECODE_HALF_PARTIALS is read
+ *                  (it applies to the walks after the prefix)
  *   group_start    [dev] int32 [num_groups + 1], non-decreasing, last <= B;
  *                  sequences outside every group need prefix_lens 0
  *   prefix_lens    [dev] int32 [B]: shared positions of each sequence, a
@@ -260,6 +261,10 @@ pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const
  *                  seq_lens[i] and max_prefix_len; 0 = none
  *   max_group_size host bound on group sizes (sizes the grid)
  *   max_prefix_len host bound on prefix_lens, a multiple of block_size
+ *   work_plan      [dev] NULL (num_units 0): the walks after the prefix run
+ *                  over the full (sequence, partition) grid; else a work
+ *                  plan from pa_decode_plan built with walk_start =
+ *                  prefix_lens (host copies), for G in {1, 2, 4} only
  *   workspace      [dev] >= pa_decode_shared_prefix_workspace_bytes(shape,
  *                  max_group_size, max_prefix_len) bytes
  * A group whose members do not share the prefix (lengths differ, blocks
@@ -275,8 +280,9 @@ pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const voi
                                     float scale, void* out, const pa_decode_shape_t* shape,
                                     int32_t num_groups, const int32_t* group_start,
                                     const int32_t* prefix_lens, int32_t max_group_size,
-                                    int32_t max_prefix_len, void* workspace,
-                                    size_t workspace_bytes, void* stream);
+                                    int32_t max_prefix_len, const int32_t* work_plan,
+                                    int32_t num_units, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * 8-bit KV pools (FP8 E4M3). [ZQ] summary: paged attention composes with KV
@@ -290,39 +296,24 @@ pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const voi
  * must be PA_BF16 (q, out), head_dim 128, group 1, 2 or 4, block size 16,
  * 32, 64 or 128; the matrix-core kernel runs whatever shape->variant says
  * (PA_VARIANT_VALU gives PA_EUNSUPPORTED; PA_DECODE_SHARED_KV applies as in
- * pa_decode). Workspace as pa_decode; the
- * second half is pa_decode_reduce unchanged.
+ * pa_decode). Workspace and work plan as pa_decode; the second half is
+ * pa_decode_reduce unchanged. The automatic partition length of 8-bit pools
+ * (1024) is not the one pa_decode_plan assumes for the shape, so with a work
+ * plan shape->partition_tokens must be set explicitly, for the plan and for
+ * the call; 0 then gives PA_EINVAL.
  */
 pa_status_t pa_decode_e4m3(const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, const int32_t* seq_lens, float scale,
                            float k_scale, float v_scale, void* out,
-                           const pa_decode_shape_t* shape, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           const pa_decode_shape_t* shape, const int32_t* work_plan,
+                           int32_t num_units, void* workspace, size_t workspace_bytes,
+                           void* stream);
 pa_status_t pa_decode_partition_e4m3(const void* q, const void* k_pool, const void* v_pool,
                                      const int32_t* block_tables, const int32_t* seq_lens,
                                      float scale, float k_scale, float v_scale, void* out,
-                                     const pa_decode_shape_t* shape, void* workspace,
-                                     size_t workspace_bytes, void* stream);
-
-/* pa_decode_e4m3 / pa_decode_partition_e4m3 over a work plan from
- * pa_decode_plan (same rules as pa_decode_planned). The automatic partition
- * length of 8-bit pools (1024) is not the one pa_decode_plan assumes for the
- * shape, so shape->partition_tokens must be set explicitly, for the plan and
- * for the call; 0 gives PA_EINVAL. */
-pa_status_t pa_decode_e4m3_planned(const void* q, const void* k_pool, const void* v_pool,
-                                   const int32_t* block_tables, const int32_t* seq_lens,
-                                   float scale, float k_scale, float v_scale, void* out,
-                                   const pa_decode_shape_t* shape, const int32_t* work_plan,
-                                   int32_t num_units, void* workspace, size_t workspace_bytes,
-                                   void* stream);
-pa_status_t pa_decode_partition_e4m3_planned(const void* q, const void* k_pool,
-                                             const void* v_pool, const int32_t* block_tables,
-                                             const int32_t* seq_lens, float scale, float k_scale,
-                                             float v_scale, void* out,
-                                             const pa_decode_shape_t* shape,
-                                             const int32_t* work_plan, int32_t num_units,
-                                             void* workspace, size_t workspace_bytes,
-                                             void* stream);
+                                     const pa_decode_shape_t* shape, const int32_t* work_plan,
+                                     int32_t num_units, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /* Second half of pa_decode: for every sequence with more than one partition,
  * out[i][h] = sum_j w_j o_j / sum_j w_j with w_j = l_j * exp(m_j - max_j m_j),

@@ -7,7 +7,7 @@ not been built, importing the binding's functions raises.
 
 Calls mirror the C ABI in include/pa.h:
     pa_decode, pa_decode_partition, pa_decode_reduce, pa_decode_workspace_bytes,
-    pa_decode_plan_capacity, pa_decode_plan, pa_decode_planned, pa_decode_partition_planned,
+    pa_decode_plan_capacity, pa_decode_plan (the decode calls take its plan as work_plan),
     pa_reshape_and_cache, pa_append_tokens, pa_copy_blocks, pa_swap_blocks, pa_device_errors,
     BlockManager (pa_bm_*).
 """
@@ -23,7 +23,7 @@ __all__ = [
     "PA_DEVERR_SLOT", "PA_DEVERR_COPY_PAIR", "PA_DEVERR_QUERY", "PA_DEVERR_PREFIX",
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "MultiQueryShape", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_decode_e4m3", "pa_reshape_and_cache_e4m3", "PA_DEVERR_PLAN",
-    "pa_decode_plan_capacity", "pa_decode_plan", "pa_decode_planned", "pa_decode_partition_planned",
+    "pa_decode_plan_capacity", "pa_decode_plan",
     "pa_append_tokens",
     "PA_VARIANT_AUTO", "PA_VARIANT_VALU", "PA_VARIANT_MFMA", "PA_DECODE_SHARED_KV", "DecodeShape",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
@@ -59,8 +59,7 @@ EXPORTED_SYMBOLS = (
     "pa_multi_query_split", "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
     "pa_decode_e4m3", "pa_decode_partition_e4m3",
     "pa_reshape_and_cache_e4m3",
-    "pa_decode_plan_capacity", "pa_decode_plan", "pa_decode_planned",
-    "pa_decode_partition_planned", "pa_decode_e4m3_planned", "pa_decode_partition_e4m3_planned",
+    "pa_decode_plan_capacity", "pa_decode_plan",
     "pa_append_tokens", "pa_append_tokens_e4m3",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_append_slots", "pa_bm_fork",
     "pa_bm_free_seq", "pa_bm_export", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_num_tokens",
@@ -92,20 +91,15 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 _SIGS = {
     "pa_decode_workspace_bytes": (_sz, [ctypes.POINTER(DecodeShape)]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
-                         ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+                         ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz, _vp]),
     "pa_decode_partition": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
-                                   ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+                                   ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
     "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                  ctypes.POINTER(DecodeShape), _vp]),
     "pa_decode_plan_capacity": (_i64, [ctypes.POINTER(DecodeShape)]),
-    "pa_decode_plan": (_i32, [ctypes.POINTER(DecodeShape), _vp, _vp, _i64,
+    "pa_decode_plan": (_i32, [ctypes.POINTER(DecodeShape), _vp, _vp, _vp, _i64,
                               ctypes.POINTER(_i32)]),
-    "pa_decode_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
-                                 ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz, _vp]),
-    "pa_decode_partition_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
-                                           ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz,
-                                           _vp]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i64, _i32, _vp]),
@@ -116,21 +110,15 @@ _SIGS = {
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [ctypes.POINTER(DecodeShape), _i32, _i32]),
     "pa_decode_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                        ctypes.POINTER(DecodeShape), _i32, _vp, _vp, _i32, _i32,
-                                       _vp, _sz, _vp]),
+                                       _vp, _i32, _vp, _sz, _vp]),
     "pa_multi_query_split": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                     ctypes.POINTER(MultiQueryShape), _i32, _vp, _sz, _vp]),
     "pa_decode_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
-                              ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp, _sz, _vp]),
+                              ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp, _i32, _vp,
+                              _sz, _vp]),
     "pa_decode_partition_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
                                         ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp,
-                                        _sz, _vp]),
-    "pa_decode_e4m3_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
-                                      ctypes.c_float, _vp, ctypes.POINTER(DecodeShape), _vp, _i32,
-                                      _vp, _sz, _vp]),
-    "pa_decode_partition_e4m3_planned": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float,
-                                                ctypes.c_float, ctypes.c_float, _vp,
-                                                ctypes.POINTER(DecodeShape), _vp, _i32, _vp, _sz,
-                                                _vp]),
+                                        _i32, _vp, _sz, _vp]),
     "pa_append_tokens": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _vp]),
     "pa_append_tokens_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -232,19 +220,37 @@ def pa_decode_plan_capacity(shape: DecodeShape) -> int:
     return int(lib().pa_decode_plan_capacity(ctypes.byref(shape)))
 
 
-def pa_decode_plan(shape: DecodeShape, seq_lens_host) -> np.ndarray:
+def pa_decode_plan(shape: DecodeShape, seq_lens_host, walk_start=None) -> np.ndarray:
     """Host work plan of a decode call (include/pa.h pa_decode_plan):
-    int32 [num_units, 4] entries (sequence, partition, length, 0), built
-    from the host lengths (int32 array-like [B])."""
+    int32 [num_units, 4] entries (sequence, partition, length, walk start),
+    built from the host lengths (int32 array-like [B]) and, for
+    pa_decode_shared_prefix, the host prefix lengths as walk_start."""
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     if lens.shape != (shape.num_seqs,):
         raise ValueError("seq_lens must hold num_seqs lengths")
+    starts = None
+    if walk_start is not None:
+        starts = np.ascontiguousarray(np.asarray(walk_start, dtype=np.int32))
+        if starts.shape != lens.shape:
+            raise ValueError("walk_start must hold num_seqs positions")
     cap = pa_decode_plan_capacity(shape)
     plan = np.zeros((max(cap, 1), 4), dtype=np.int32)
     n = ctypes.c_int32(0)
-    _check(lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data, plan.ctypes.data, cap,
-                                ctypes.byref(n)), "pa_decode_plan")
+    _check(lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data,
+                                None if starts is None else starts.ctypes.data,
+                                plan.ctypes.data, cap, ctypes.byref(n)), "pa_decode_plan")
     return plan[:n.value].copy()
+
+
+def _plan_args(work_plan, dev):
+    """(pointer, unit count) of an optional device work plan."""
+    if work_plan is None:
+        return None, 0
+    torch = _torch()
+    _need(work_plan, "work_plan", dtype=torch.int32, dim=2, device=dev)
+    if work_plan.shape[1] != 4:
+        raise ValueError("work_plan must be [num_units, 4]")
+    return work_plan.data_ptr(), int(work_plan.shape[0])
 
 
 def _decode_call(fn_name, q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
@@ -268,12 +274,7 @@ def _decode_call(fn_name, q, k_pool, v_pool, block_tables, seq_lens, scale, out,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    plan_args = ()
-    if work_plan is not None:
-        _need(work_plan, "work_plan", dtype=torch.int32, dim=2, device=dev)
-        if work_plan.shape[1] != 4:
-            raise ValueError("work_plan must be [num_units, 4]")
-        plan_args = (work_plan.data_ptr(), int(work_plan.shape[0]))
+    plan_args = _plan_args(work_plan, dev)
     st = getattr(lib(), fn_name)(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
         seq_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
@@ -282,34 +283,18 @@ def _decode_call(fn_name, q, k_pool, v_pool, block_tables, seq_lens, scale, out,
     return out
 
 
-def pa_decode_planned(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, work_plan,
-                      max_seq_len, partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None,
-                      stream=None):
-    """pa_decode over a host-built work plan (include/pa.h
-    pa_decode_planned); work_plan: the pa_decode_plan output as a device
-    int32 tensor [num_units, 4]."""
-    return _decode_call("pa_decode_planned", q, k_pool, v_pool, block_tables, seq_lens, scale,
-                        out, max_seq_len=max_seq_len, partition_tokens=partition_tokens,
-                        variant=variant, workspace=workspace, stream=stream, work_plan=work_plan)
-
-
-def pa_decode_partition_planned(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
-                                work_plan, max_seq_len, partition_tokens=0,
-                                variant=PA_VARIANT_AUTO, workspace, stream=None):
-    """First half of pa_decode_planned; pa_decode_reduce completes it."""
-    return _decode_call("pa_decode_partition_planned", q, k_pool, v_pool, block_tables, seq_lens,
-                        scale, out, max_seq_len=max_seq_len, partition_tokens=partition_tokens,
-                        variant=variant, workspace=workspace, stream=stream, work_plan=work_plan)
-
-
 def pa_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,
-              partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None, stream=None):
+              partition_tokens=0, variant=PA_VARIANT_AUTO, workspace=None, stream=None,
+              work_plan=None):
     """Paged decode attention (include/pa.h pa_decode). q [B,Hq,D]; pools
     [NB,Hkv,bs,D]; block_tables int32 [B,maxb]; seq_lens int32 [B]; out
-    [B,Hq,D]. Enqueues on `stream` (default: torch's current stream)."""
+    [B,Hq,D]; work_plan: None, or the pa_decode_plan output as a device int32
+    tensor [num_units, 4]. Enqueues on `stream` (default: torch's current
+    stream)."""
     return _decode_call("pa_decode", q, k_pool, v_pool, block_tables, seq_lens, scale, out,
                         max_seq_len=max_seq_len, partition_tokens=partition_tokens,
-                        variant=variant, workspace=workspace, stream=stream)
+                        variant=variant, workspace=workspace, stream=stream,
+                        work_plan=work_plan)
 
 
 def pa_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,
@@ -346,10 +331,13 @@ def pa_decode_shared_prefix_workspace_bytes(shape: DecodeShape, max_group_size: 
 
 def pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *,
                             group_start, prefix_lens, max_group_size, max_prefix_len,
-                            max_seq_len, partition_tokens=0, workspace=None, stream=None):
+                            max_seq_len, partition_tokens=0, workspace=None, stream=None,
+                            work_plan=None):
     """pa_decode for groups of sequences sharing a prompt (include/pa.h
     pa_decode_shared_prefix). group_start int32 [G+1] and prefix_lens int32
-    [B] on the device; the workspace is allocated here unless given."""
+    [B] on the device; the workspace is allocated here unless given;
+    work_plan: None, or a pa_decode_plan output built with walk_start = the
+    host prefix lengths, as a device int32 tensor [num_units, 4]."""
     torch = _torch()
     dev = q.device
     _need(q, "q", dtype=torch.bfloat16, dim=3)
@@ -375,18 +363,22 @@ def pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, seq_lens, scale, ou
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(),
         seq_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), ctypes.byref(shape),
         group_start.shape[0] - 1, group_start.data_ptr(), prefix_lens.data_ptr(),
-        int(max_group_size), int(max_prefix_len), workspace.data_ptr(),
+        int(max_group_size), int(max_prefix_len), *_plan_args(work_plan, dev),
+        workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
     _check(st, "pa_decode_shared_prefix")
     return out
 
 
 def pa_decode_partition(q, k_pool, v_pool, block_tables, seq_lens, scale, out, *, max_seq_len,
-                        partition_tokens=0, variant=PA_VARIANT_AUTO, workspace, stream=None):
-    """First half of pa_decode (per-partition kernel)."""
+                        partition_tokens=0, variant=PA_VARIANT_AUTO, workspace, stream=None,
+                        work_plan=None):
+    """First half of pa_decode (per-partition kernel); pa_decode_reduce
+    completes it."""
     return _decode_call("pa_decode_partition", q, k_pool, v_pool, block_tables, seq_lens, scale,
                         out, max_seq_len=max_seq_len, partition_tokens=partition_tokens,
-                        variant=variant, workspace=workspace, stream=stream)
+                        variant=variant, workspace=workspace, stream=stream,
+                        work_plan=work_plan)
 
 
 def pa_decode_reduce(q, k_pool, block_tables, seq_lens, out, *, max_seq_len, partition_tokens=0,
@@ -408,7 +400,7 @@ def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_
     [B,Hq,D]; pools uint8 [NB,Hkv,bs,D] of FP8 E4M3 codes. `variant` may carry
     PA_DECODE_SHARED_KV (the kernel is always the matrix-core one). With
     `work_plan` (device int32 [num_units, 4] from pa_decode_plan, built with
-    the same explicit partition_tokens) it calls pa_decode_e4m3_planned."""
+    the same explicit partition_tokens) the grid follows the plan."""
     torch = _torch()
     dev = q.device
     _need(q, "q", dtype=torch.bfloat16, dim=3)
@@ -423,12 +415,7 @@ def pa_decode_e4m3(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_
     need = pa_decode_workspace_bytes(shape)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    fn, plan_args = "pa_decode_e4m3", ()
-    if work_plan is not None:
-        _need(work_plan, "work_plan", dtype=torch.int32, dim=2, device=dev)
-        if work_plan.shape[1] != 4:
-            raise ValueError("work_plan must be [num_units, 4]")
-        fn, plan_args = "pa_decode_e4m3_planned", (work_plan.data_ptr(), int(work_plan.shape[0]))
+    fn, plan_args = "pa_decode_e4m3", _plan_args(work_plan, dev)
     st = getattr(lib(), fn)(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                             block_tables.data_ptr(), seq_lens.data_ptr(), ctypes.c_float(scale),
                             ctypes.c_float(k_scale), ctypes.c_float(v_scale), out.data_ptr(),

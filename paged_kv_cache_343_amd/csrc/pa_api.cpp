@@ -255,20 +255,31 @@ static pa_status_t decode_impl(const void* q, const void* k_pool, const void* v_
   return st;
 }
 
+// A work plan argument: null = the full grid (num_units must be 0), else a
+// device array of num_units >= 0 entries from pa_decode_plan.
+static bool plan_args_ok(const int32_t* work_plan, int32_t num_units) {
+  return work_plan ? num_units >= 0 : num_units == 0;
+}
+
 pa_status_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                      void* out, const pa_decode_shape_t* shape, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      void* out, const pa_decode_shape_t* shape, const int32_t* work_plan,
+                      int32_t num_units, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan_args_ok(work_plan, num_units)) return PA_EINVAL;
   return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, true);
+                     workspace_bytes, stream, true, true, nullptr, work_plan,
+                     work_plan ? num_units : -1);
 }
 
 pa_status_t pa_decode_partition(const void* q, const void* k_pool, const void* v_pool,
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 float scale, void* out, const pa_decode_shape_t* shape,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                const int32_t* work_plan, int32_t num_units, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!plan_args_ok(work_plan, num_units)) return PA_EINVAL;
   return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, false);
+                     workspace_bytes, stream, true, false, nullptr, work_plan,
+                     work_plan ? num_units : -1);
 }
 
 int64_t pa_decode_plan_capacity(const pa_decode_shape_t* shape) {
@@ -278,58 +289,66 @@ int64_t pa_decode_plan_capacity(const pa_decode_shape_t* shape) {
 }
 
 pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_lens,
-                           int32_t* work_plan, int64_t capacity, int32_t* num_units) {
+                           const int32_t* walk_start, int32_t* work_plan, int64_t capacity,
+                           int32_t* num_units) {
   Plan plan;
   pa_status_t st = make_plan(shape, &plan);
   if (st != PA_OK) return st;
   if (!num_units || (shape->num_seqs > 0 && (!seq_lens || !work_plan))) return PA_EINVAL;
   const int pt = plan.part_tokens;
+  // positions [start, len) of each sequence are split into partitions
+  auto start_of = [&](int32_t i) { return walk_start ? walk_start[i] : 0; };
+  for (int32_t i = 0; i < shape->num_seqs; ++i) {
+    const int32_t len = seq_lens[i], st0 = start_of(i);
+    if (len < 0 || len > plan.len_cap || st0 < 0 || st0 > len) return PA_EINVAL;
+  }
   // Units with a full partition come first, in (sequence, partition) order;
   // then each sequence's last, shorter partition (and the zero-output unit
   // of an empty sequence), longest first, so that the grid ends on the
-  // shortest work.
+  // shortest work. A walk that starts at its sequence's end has no unit.
   int64_t n = 0;
   for (int32_t i = 0; i < shape->num_seqs; ++i) {
-    const int32_t len = seq_lens[i];
-    if (len < 0 || len > plan.len_cap) return PA_EINVAL;
-    const int full = len / pt;
+    const int32_t len = seq_lens[i], st0 = start_of(i);
+    const int full = (len - st0) / pt;
     if (n + full > capacity) return PA_EINVAL;
     for (int j = 0; j < full; ++j) {
       int32_t* e = work_plan + 4 * n++;
       e[0] = i;
       e[1] = j;
       e[2] = len;
-      e[3] = 0;
+      e[3] = st0;
     }
   }
   // tail units: longest first, sequence order among equals
   std::vector<int32_t> tail;   // sequences with a shorter last partition (or none at all)
-  for (int32_t i = 0; i < shape->num_seqs; ++i)
-    if (seq_lens[i] == 0 || seq_lens[i] % pt != 0) tail.push_back(i);
+  for (int32_t i = 0; i < shape->num_seqs; ++i) {
+    const int32_t rest = seq_lens[i] - start_of(i);
+    if (seq_lens[i] == 0 || rest % pt != 0) tail.push_back(i);
+  }
   const int64_t tails = (int64_t)tail.size();
   if (n + tails > capacity) return PA_EINVAL;
   auto put = [&](int64_t u, int32_t i) {
     int32_t* e = work_plan + 4 * u;
     e[0] = i;
-    e[1] = seq_lens[i] / pt;
+    e[1] = (seq_lens[i] - start_of(i)) / pt;
     e[2] = seq_lens[i];
-    e[3] = 0;
+    e[3] = start_of(i);
   };
+  auto rem = [&](int32_t i) { return (seq_lens[i] - start_of(i)) % pt; };
   if (pt <= 65536) {
     // counting sort on the last partition's length
     std::vector<int32_t> start(pt + 2, 0);
-    for (int32_t i : tail) ++start[seq_lens[i] % pt];
+    for (int32_t i : tail) ++start[rem(i)];
     int32_t acc = 0;
     for (int c = pt; c >= 0; --c) {
       const int32_t k = start[c];
       start[c] = acc;
       acc += k;
     }
-    for (int32_t i : tail) put(n + start[seq_lens[i] % pt]++, i);
+    for (int32_t i : tail) put(n + start[rem(i)]++, i);
   } else {
-    std::stable_sort(tail.begin(), tail.end(), [&](int32_t x, int32_t y) {
-      return seq_lens[x] % pt > seq_lens[y] % pt;
-    });
+    std::stable_sort(tail.begin(), tail.end(),
+                     [&](int32_t x, int32_t y) { return rem(x) > rem(y); });
     for (int64_t k = 0; k < tails; ++k) put(n + k, tail[k]);
   }
   n += tails;
@@ -338,70 +357,32 @@ pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_le
   return PA_OK;
 }
 
-pa_status_t pa_decode_planned(const void* q, const void* k_pool, const void* v_pool,
-                              const int32_t* block_tables, const int32_t* seq_lens, float scale,
-                              void* out, const pa_decode_shape_t* shape, const int32_t* work_plan,
-                              int32_t num_units, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  if (num_units < 0) return PA_EINVAL;
-  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, true, nullptr, work_plan, num_units);
-}
-
-pa_status_t pa_decode_partition_planned(const void* q, const void* k_pool, const void* v_pool,
-                                        const int32_t* block_tables, const int32_t* seq_lens,
-                                        float scale, void* out, const pa_decode_shape_t* shape,
-                                        const int32_t* work_plan, int32_t num_units,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_units < 0) return PA_EINVAL;
-  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, false, nullptr, work_plan, num_units);
-}
-
 pa_status_t pa_decode_e4m3(const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, const int32_t* seq_lens, float scale,
                            float k_scale, float v_scale, void* out,
-                           const pa_decode_shape_t* shape, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           const pa_decode_shape_t* shape, const int32_t* work_plan,
+                           int32_t num_units, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!plan_args_ok(work_plan, num_units)) return PA_EINVAL;
+  if (work_plan && (!shape || shape->partition_tokens == 0)) return PA_EINVAL;
   const float sc[2] = {k_scale, v_scale};
   return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, true, sc);
+                     workspace_bytes, stream, true, true, sc, work_plan,
+                     work_plan ? num_units : -1);
 }
 
 pa_status_t pa_decode_partition_e4m3(const void* q, const void* k_pool, const void* v_pool,
                                      const int32_t* block_tables, const int32_t* seq_lens,
                                      float scale, float k_scale, float v_scale, void* out,
-                                     const pa_decode_shape_t* shape, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+                                     const pa_decode_shape_t* shape, const int32_t* work_plan,
+                                     int32_t num_units, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (!plan_args_ok(work_plan, num_units)) return PA_EINVAL;
+  if (work_plan && (!shape || shape->partition_tokens == 0)) return PA_EINVAL;
   const float sc[2] = {k_scale, v_scale};
   return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, false, sc);
-}
-
-pa_status_t pa_decode_e4m3_planned(const void* q, const void* k_pool, const void* v_pool,
-                                   const int32_t* block_tables, const int32_t* seq_lens,
-                                   float scale, float k_scale, float v_scale, void* out,
-                                   const pa_decode_shape_t* shape, const int32_t* work_plan,
-                                   int32_t num_units, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
-  if (num_units < 0 || !shape || shape->partition_tokens == 0) return PA_EINVAL;
-  const float sc[2] = {k_scale, v_scale};
-  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, true, sc, work_plan, num_units);
-}
-
-pa_status_t pa_decode_partition_e4m3_planned(const void* q, const void* k_pool,
-                                             const void* v_pool, const int32_t* block_tables,
-                                             const int32_t* seq_lens, float scale, float k_scale,
-                                             float v_scale, void* out,
-                                             const pa_decode_shape_t* shape,
-                                             const int32_t* work_plan, int32_t num_units,
-                                             void* workspace, size_t workspace_bytes,
-                                             void* stream) {
-  if (num_units < 0 || !shape || shape->partition_tokens == 0) return PA_EINVAL;
-  const float sc[2] = {k_scale, v_scale};
-  return decode_impl(q, k_pool, v_pool, block_tables, seq_lens, scale, out, shape, workspace,
-                     workspace_bytes, stream, true, false, sc, work_plan, num_units);
+                     workspace_bytes, stream, true, false, sc, work_plan,
+                     work_plan ? num_units : -1);
 }
 
 pa_status_t pa_decode_reduce(const int32_t* seq_lens, void* out, const pa_decode_shape_t* shape,
@@ -553,11 +534,16 @@ pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const voi
                                     float scale, void* out, const pa_decode_shape_t* shape,
                                     int32_t num_groups, const int32_t* group_start,
                                     const int32_t* prefix_lens, int32_t max_group_size,
-                                    int32_t max_prefix_len, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+                                    int32_t max_prefix_len, const int32_t* work_plan,
+                                    int32_t num_units, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   PrefixPlan pp;
   pa_status_t st = prefix_plan(shape, max_group_size, max_prefix_len, &pp);
   if (st != PA_OK) return st;
+  if (!plan_args_ok(work_plan, num_units)) return PA_EINVAL;
+  if (work_plan && ((int64_t)num_units > (int64_t)shape->num_seqs * pp.suf_parts ||
+                    (num_units > 0 && !aligned16(work_plan))))
+    return PA_EINVAL;
   if (num_groups < 0 || (num_groups > 0 && !group_start) || !prefix_lens) return PA_EINVAL;
   if (shape->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out) return PA_EINVAL;
@@ -599,6 +585,7 @@ pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const voi
   m.slot_stride = pp.pref_parts + pp.suf_parts;
   m.part_half = 0;
   const bool decode_kernel = group <= 4;   // the walks on pa_decode's kernel
+  if (work_plan && !decode_kernel) return PA_EINVAL;   // plans serve those walks only
   pa::MqArgs m2 = m;
   m2.mode = 2;
   m2.part_tokens = pp.pref_tokens;
@@ -629,6 +616,10 @@ pa_status_t pa_decode_shared_prefix(const void* q, const void* k_pool, const voi
     a.slot_stride = pp.pref_parts + pp.suf_parts;
     a.max_prefix = max_prefix_len;
     a.block_size = shape->block_size;
+    if (work_plan) {
+      a.plan = work_plan;
+      a.num_units = num_units;
+    }
     st = from_hip(pa::launch_shared_prefix_decode(shape->block_size, group, m2, a, s));
     if (st != PA_OK) return st;
     return from_hip(pa::launch_decode_reduce(shape->dtype, shape->head_dim, a, s));

@@ -417,9 +417,11 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
 template <typename T, int D, int BS, int G, int NW, bool PFX = false>
 __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWork& wk,
                                                 int id) {
-  if (!PFX && a.plan) {
-    // entry (sequence, partition, sequence length, 0): the length comes with
-    // the unit, so no dependent load of seq_lens precedes the table window
+  if (a.plan) {
+    // entry (sequence, partition, sequence length, walk start): the length
+    // comes with the unit, so no dependent load of seq_lens precedes the
+    // table window (the start of a shared-prefix walk is read from
+    // pos_start, as without a plan)
     int4 e;
     if (a.num_kv_heads % 8 == 0) {
       const int x = id & 7, r = id >> 3, nb8 = a.num_kv_heads >> 3;
@@ -432,9 +434,14 @@ __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWo
     wk.i = e.x;
     wk.j = e.y;
     wk.len = e.z;
-    const int np = (wk.len + a.part_tokens - 1) / a.part_tokens;
-    if ((unsigned)wk.i >= (unsigned)a.num_seqs || (unsigned)wk.len > (unsigned)a.len_cap ||
-        wk.j < 0 || wk.j >= (np > 1 ? np : 1)) {
+    bool bad = (unsigned)wk.i >= (unsigned)a.num_seqs || (unsigned)wk.len > (unsigned)a.len_cap ||
+               wk.j < 0;
+    if (!bad) {
+      const int st = PFX && wk.len > 0 ? walk_start(a, wk.i, wk.len, false) : 0;
+      const int np = (wk.len - st + a.part_tokens - 1) / a.part_tokens;
+      bad = wk.j >= (np > 1 ? np : 1);
+    }
+    if (bad) {
       if (threadIdx.x == 0) flag_error(kErrPlan);
       return false;
     }
@@ -450,7 +457,7 @@ __device__ __forceinline__ bool setup_partition(const DecodeArgs& a, PartitionWo
     wk.g = rest % a.num_kv_heads;
     wk.i = rest / a.num_kv_heads;
   }
-  if (PFX || !a.plan) wk.len = checked_len(a, wk.i);
+  if (!a.plan) wk.len = checked_len(a, wk.i);
   if (wk.len == 0) {
     if (wk.j == 0) write_zero_rows<T, D, G, NW>(a, wk.i, wk.g);
     return false;
@@ -2490,7 +2497,11 @@ hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& 
   const int64_t tiles = ((int64_t)pre.max_query_len * group + 15) / 16;
   const int64_t pre_gx = pre.max_parts > 0 ? (tiles * pre.max_parts + kMqWaves - 1) / kMqWaves : 0;
   const int64_t n_prefix = pre_gx * pre.num_kv_heads * pre.num_seqs;
-  const int64_t n_walk = (int64_t)walk.num_kv_heads * walk.num_seqs * walk.max_parts;
+  // the walks: one workgroup per (unit, KV head) of a work plan, else the
+  // full (sequence, partition, KV head) grid
+  const int64_t n_walk = (int64_t)walk.num_kv_heads *
+                         (walk.plan ? (int64_t)walk.num_units
+                                    : (int64_t)walk.num_seqs * walk.max_parts);
   if (n_prefix + n_walk <= 0) return hipSuccess;
   if (n_prefix + n_walk > 0x7fffffff) return hipErrorInvalidValue;
   ca.n_prefix = (int32_t)n_prefix;

@@ -267,9 +267,10 @@ def bench_step(c: Case, *, seed=0, q_scale=1, shared_prefix=False, variant=P.PA_
     sequence's next slot (its oracle mirror must agree), the host builds the
     work plan from its own lengths, pa_append_tokens writes the new K/V rows
     and advances the device-resident tables and lengths (which must then
-    equal the mirror's export), and pa_decode_partition_planned +
+    equal the mirror's export), and pa_decode_partition over the plan +
     pa_decode_reduce decode (pa_decode_shared_prefix with shared_prefix=True,
-    over the groups and prompt length recorded in c.extra). q_scale multiplies
+    over the groups and prompt length recorded in c.extra, its walks after
+    the prompts over a plan). q_scale multiplies
     q (a power of two keeps it exact). Returns the output tensor; the oracle
     side (pools, tables, lengths, q) is updated to the same step."""
     dev = c.device
@@ -289,27 +290,31 @@ def bench_step(c: Case, *, seed=0, q_scale=1, shared_prefix=False, variant=P.PA_
     assert pairs.shape[0] == 0 and all(cw is None for _, cw in ores)
     otab, oln = c.obm.export(ids, c.maxb)
     # device side, in the bench's order
-    shape = P._decode_shape(c.q, c.k_pool, c.tables, int(oln.max()), c.w.partition_tokens
-                            if not shared_prefix else 0,
+    shape = P._decode_shape(c.q, c.k_pool, c.tables, int(oln.max()), c.w.partition_tokens,
                             variant | (P.PA_DECODE_SHARED_KV if "samples" in c.extra else 0))
-    plan = None if shared_prefix else torch.from_numpy(P.pa_decode_plan(shape, oln)).to(dev)
+    if shared_prefix:
+        # the walks after each sequence's prompt: their plan starts there
+        samples, groups = c.extra["samples"], c.extra["groups"]
+        shared = (c.extra["prefix_len"] // c.bs) * c.bs
+        pref_host = np.zeros(B, dtype=np.int32)
+        pref_host[:groups * samples] = shared
+        plan = torch.from_numpy(P.pa_decode_plan(shape, oln, walk_start=pref_host)).to(dev)
+    else:
+        plan = torch.from_numpy(P.pa_decode_plan(shape, oln)).to(dev)
     P.pa_append_tokens(to_device(knew, dtype, dev), to_device(vnew, dtype, dev),
                        torch.from_numpy(slots).to(dev), c.k_pool, c.v_pool, c.tables, c.lens)
     out = torch.full_like(c.q, float("nan"))
     if shared_prefix:
-        samples, groups = c.extra["samples"], c.extra["groups"]
-        shared = (c.extra["prefix_len"] // c.bs) * c.bs
         gs = torch.arange(0, groups * samples + 1, samples, dtype=torch.int32, device=dev)
-        pref = torch.zeros(B, dtype=torch.int32, device=dev)
-        pref[:groups * samples] = shared
+        pref = torch.from_numpy(pref_host).to(dev)
         P.pa_decode_shared_prefix(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
                                   group_start=gs, prefix_lens=pref, max_group_size=samples,
                                   max_prefix_len=shared, max_seq_len=int(oln.max()),
-                                  partition_tokens=c.w.partition_tokens)
+                                  partition_tokens=c.w.partition_tokens, work_plan=plan)
     else:
         ws = torch.empty(max(16, P.pa_decode_workspace_bytes(shape)), dtype=torch.uint8,
                          device=dev)
-        P.pa_decode_partition_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
+        P.pa_decode_partition(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
                                       work_plan=plan, max_seq_len=shape.max_seq_len,
                                       partition_tokens=shape.partition_tokens,
                                       variant=shape.variant, workspace=ws)

@@ -87,7 +87,7 @@ def test_decode_rejects_before_launch(kw, status):
     s = _shape(**kw)
     dummy = ctypes.c_void_p(16)
     st = lib.pa_decode(dummy, dummy, dummy, dummy, dummy, ctypes.c_float(0.1), dummy,
-                       ctypes.byref(s), None, 0, None)
+                       ctypes.byref(s), None, 0, None, 0, None)
     assert st == status
 
 
@@ -95,15 +95,17 @@ def test_decode_null_and_workspace_checks():
     lib = P.lib()
     s = _shape(max_seq_len=4096, max_blocks_per_seq=256)
     d = ctypes.c_void_p(4096)
-    assert lib.pa_decode(None, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d, 1 << 30, None) == 1
+    assert lib.pa_decode(None, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), None, 0, d,
+                         1 << 30, None) == 1
     # workspace too small
-    assert lib.pa_decode(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d, 16, None) == 3
+    assert lib.pa_decode(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), None, 0, d, 16,
+                         None) == 3
     # misaligned q
     assert lib.pa_decode(ctypes.c_void_p(4100), d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s),
-                         d, 1 << 30, None) == 1
+                         None, 0, d, 1 << 30, None) == 1
     # non-finite scale
     assert lib.pa_decode(d, d, d, d, d, ctypes.c_float(float("nan")), d, ctypes.byref(s),
-                         d, 1 << 30, None) == 1
+                         None, 0, d, 1 << 30, None) == 1
 
 
 def test_cache_and_copy_reject_before_launch():
@@ -164,23 +166,30 @@ def test_planned_and_append_reject_before_launch():
     big = 1 << 30
     cap = lib.pa_decode_plan_capacity(ctypes.byref(s))
     assert cap == 4 * 8
-    # negative or too many units, missing or misaligned plan
-    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d, -1,
-                                 d, big, None) == 1
-    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d,
-                                 cap + 1, d, big, None) == 1
-    assert lib.pa_decode_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), None, 3,
-                                 d, big, None) == 1
-    assert lib.pa_decode_partition_planned(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s),
-                                           ctypes.c_void_p(4104), 3, d, big, None) == 1
+    # negative or too many units, missing or misaligned plan, units without a plan
+    assert lib.pa_decode(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d, -1,
+                         d, big, None) == 1
+    assert lib.pa_decode(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), d,
+                         cap + 1, d, big, None) == 1
+    assert lib.pa_decode(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s), None, 3,
+                         d, big, None) == 1
+    assert lib.pa_decode_partition(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s),
+                                   ctypes.c_void_p(4104), 3, d, big, None) == 1
     # 8-bit pools: the plan needs an explicit partition length
-    assert lib.pa_decode_e4m3_planned(d, d, d, d, d, ctypes.c_float(0.1), ctypes.c_float(1.0),
-                                      ctypes.c_float(1.0), d, ctypes.byref(s), d, 3, d, big,
-                                      None) == 1
+    assert lib.pa_decode_e4m3(d, d, d, d, d, ctypes.c_float(0.1), ctypes.c_float(1.0),
+                              ctypes.c_float(1.0), d, ctypes.byref(s), d, 3, d, big,
+                              None) == 1
     s8 = _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=1024)
-    assert lib.pa_decode_partition_e4m3_planned(d, d, d, d, d, ctypes.c_float(0.1),
-                                                ctypes.c_float(1.0), ctypes.c_float(-1.0), d,
-                                                ctypes.byref(s8), d, 3, d, big, None) == 1
+    assert lib.pa_decode_partition_e4m3(d, d, d, d, d, ctypes.c_float(0.1),
+                                        ctypes.c_float(1.0), ctypes.c_float(-1.0), d,
+                                        ctypes.byref(s8), d, 3, d, big, None) == 1
+    # shared-prefix decode: the same plan checks, and plans only for group <= 4
+    assert lib.pa_decode_shared_prefix(d, d, d, d, d, ctypes.c_float(0.1), d, ctypes.byref(s),
+                                       1, d, d, 4, 1024, None, 5, d, big, None) == 1
+    s16 = _shape(num_q_heads=128, max_seq_len=4096, max_blocks_per_seq=256)
+    assert lib.pa_decode_shared_prefix(d, d, d, d, d, ctypes.c_float(0.1), d,
+                                       ctypes.byref(s16), 1, d, d, 4, 1024, d, 3, d, big,
+                                       None) == 1
     # append: tables and lengths required, a positive table stride
     assert lib.pa_append_tokens(d, d, d, d, d, None, d, 4, 8, 8, 128, 16, 10, 1, None) == 1
     assert lib.pa_append_tokens(d, d, d, d, d, d, None, 4, 8, 8, 128, 16, 10, 1, None) == 1

@@ -7,8 +7,9 @@ one decode step the way bench.py does: the host block manager reserves the
 slots (its oracle mirror must agree), the host builds the work plan from its
 lengths, pa_append_tokens writes the new rows and advances the device-resident
 tables and lengths (which must equal the mirror's export afterwards), and
-pa_decode_partition_planned + pa_decode_reduce decode (pa_decode_shared_prefix
-for the shared-prefix batch). Every output element is then compared with the
+pa_decode_partition over the plan + pa_decode_reduce decode
+(pa_decode_shared_prefix, its walks over a plan, for the shared-prefix
+batches). Every output element is then compared with the
 oracle under |got - ref| <= 2e-3 + 1e-2 |ref|, and max-abs / max-rel are
 printed per case.
 
@@ -64,15 +65,14 @@ def test_bench_launch_every_row(dev, name, q_scale):
 @pytest.mark.parametrize("name", ["shared_prefix", "shared_prefix_long"])
 def test_shared_prefix_bench_launch_every_row(dev, name):
     """The shared-prefix batch (64 groups x 4 samples of a 1040-token prompt,
-    copy-on-write of the half-filled prompt block at setup) through
-    pa_decode_shared_prefix, as the bench runs it; with the 16 unshared
-    32,768-token sequences through the planned pa_decode with the
-    shared-blocks hint."""
+    copy-on-write of the half-filled prompt block at setup), alone and with
+    16 unshared 32,768-token sequences, through pa_decode_shared_prefix with
+    its walks over a plan, as the bench runs it."""
     w = W.get(name)
     print(f"full parity {name}: building", flush=True)
     c = build_shared_prefix(w, dev, final_append=False)
     assert c.extra["cow_pairs"].shape == (64 * 3, 2)
-    out = bench_step(c, seed=w.seed, shared_prefix=(name == "shared_prefix"))
+    out = bench_step(c, seed=w.seed, shared_prefix=True)
     _full_check(c, out, name)
 
 

@@ -35,12 +35,12 @@ def _planned(c, variant=P.PA_VARIANT_AUTO, ptok=0, split=False):
     if split:
         ws = torch.empty(max(P.pa_decode_workspace_bytes(shape), 16), dtype=torch.uint8,
                          device=c.device)
-        P.pa_decode_partition_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
+        P.pa_decode_partition(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
                                       workspace=ws, **kw)
         P.pa_decode_reduce(c.q, c.k_pool, c.tables, c.lens, out, max_seq_len=c.max_len,
                            partition_tokens=ptok, variant=variant, workspace=ws)
     else:
-        P.pa_decode_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out, **kw)
+        P.pa_decode(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out, **kw)
     return out
 
 
@@ -139,7 +139,7 @@ def test_bad_plan_entries_are_skipped_and_flagged(dev, hq):
         p[1] = bad                                   # replaces one valid unit
         pt = torch.from_numpy(p).to(dev)
         out = torch.zeros_like(c.q)
-        P.pa_decode_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
+        P.pa_decode(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
                             work_plan=pt, max_seq_len=c.max_len, variant=MFMA)
         torch.cuda.synchronize()
         assert P.pa_device_errors() == P.PA_DEVERR_PLAN, bad

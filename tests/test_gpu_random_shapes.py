@@ -49,7 +49,7 @@ def test_random_decode(dev, case):
     shape = P._decode_shape(c.q, c.k_pool, c.tables, c.max_len, ptok, P.PA_VARIANT_AUTO)
     plan_np = P.pa_decode_plan(shape, c.olens)
     out_p = torch.full_like(out, float("nan"))
-    P.pa_decode_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out_p,
+    P.pa_decode(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out_p,
                         work_plan=torch.from_numpy(plan_np).to(dev), max_seq_len=c.max_len,
                         partition_tokens=ptok)
     torch.cuda.synchronize()

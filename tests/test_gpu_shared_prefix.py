@@ -97,6 +97,23 @@ def test_groups_all_outputs(dev, hq, hkv, bs, partition_tokens):
     assert P.pa_device_errors() == 0
     check_close(got, ref, "bf16", f"shared prefix {hq}/{hkv} bs {bs} pt {partition_tokens}")
     check_close(got, dec, "bf16", "shared prefix vs pa_decode")
+    if hq // hkv <= 4:
+        # the walks after the prompts over a work plan: the same bits
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        q = to_device(c["q"], "bf16", dev)
+        kp, vp = to_device(c["kp"], "bf16", dev), to_device(c["vp"], "bf16", dev)
+        ml = int(c["lens"].max())
+        shape = P._decode_shape(q, kp, t(c["tab"]), ml, partition_tokens, P.PA_VARIANT_AUTO)
+        plan = t(P.pa_decode_plan(shape, c["lens"], walk_start=c["prefix"]))
+        out = torch.full_like(q, float("nan"))
+        P.pa_decode_shared_prefix(q, kp, vp, t(c["tab"]), t(c["lens"]), scale_for(c["d"]), out,
+                                  group_start=t(c["gs"]), prefix_lens=t(c["prefix"]),
+                                  max_group_size=c["max_group"], max_prefix_len=c["max_prefix"],
+                                  max_seq_len=ml, partition_tokens=partition_tokens,
+                                  work_plan=plan)
+        torch.cuda.synchronize()
+        assert P.pa_device_errors() == 0
+        assert np.array_equal(O.as_f64(to_storage_np(out), "bf16"), got)
 
 
 def test_broken_groups_are_flagged(dev):
@@ -135,9 +152,18 @@ def test_shared_prefix_workloads(dev, name):
     P.pa_decode_shared_prefix(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out,
                               group_start=gs, prefix_lens=prefix, max_group_size=samples,
                               max_prefix_len=shared, max_seq_len=c.max_len)
+    # the walks after the prompts over a work plan: the same bits
+    shape = P._decode_shape(c.q, c.k_pool, c.tables, c.max_len, 0, P.PA_VARIANT_AUTO)
+    plan = torch.from_numpy(P.pa_decode_plan(shape, c.olens,
+                                             walk_start=prefix.cpu().numpy())).to(dev)
+    out_p = torch.full_like(out, float("nan"))
+    P.pa_decode_shared_prefix(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out_p,
+                              group_start=gs, prefix_lens=prefix, max_group_size=samples,
+                              max_prefix_len=shared, max_seq_len=c.max_len, work_plan=plan)
     dec = c.decode()
     torch.cuda.synchronize()
     assert P.pa_device_errors() == 0
+    assert torch.equal(out.view(torch.int16), out_p.view(torch.int16))
     check_close(O.as_f64(to_storage_np(out), "bf16"), O.as_f64(to_storage_np(dec), "bf16"),
                 "bf16", f"{name}: shared-prefix vs pa_decode")
     # every row against the plain-C float64 oracle

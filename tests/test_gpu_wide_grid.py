@@ -43,7 +43,7 @@ def test_bf16_wide_grid(dev, bs, hq, hkv):
     out = c.decode(variant=MFMA)
     plan = torch.from_numpy(P.pa_decode_plan(shape, c.olens)).to(dev)
     out_p = torch.empty_like(out)
-    P.pa_decode_planned(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out_p,
+    P.pa_decode(c.q, c.k_pool, c.v_pool, c.tables, c.lens, c.scale, out_p,
                         work_plan=plan, max_seq_len=c.max_len, variant=MFMA)
     torch.cuda.synchronize()
     assert P.pa_device_errors() == 0

@@ -65,10 +65,10 @@ def test_plan_rejects_bad_lengths_and_small_capacity():
     shape = _shape(2, 600)
     buf = np.zeros((3, 4), dtype=np.int32)
     n = ctypes.c_int32(0)
-    st = P.lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data, buf.ctypes.data, 3,
+    st = P.lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data, None, buf.ctypes.data, 3,
                                 ctypes.byref(n))
     assert st == 1                                    # PA_EINVAL: 4 units do not fit in 3
-    st = P.lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data, buf.ctypes.data, 1,
+    st = P.lib().pa_decode_plan(ctypes.byref(shape), lens.ctypes.data, None, buf.ctypes.data, 1,
                                 ctypes.byref(n))
     assert st == 1
 
@@ -102,3 +102,44 @@ def test_plan_single_partition_per_sequence(max_len):
                                            sorted(tails, key=lambda t: (-t[0], t[1]))]
     assert [tuple(map(int, u[:2])) for u in plan] == want
     assert (plan[:, 1] == 0).all()
+
+
+def _expected_walks(lens, starts, ptok):
+    """Units of walks over positions [start, L): partition j covers
+    [start + j*P, min(L, start + (j+1)*P)); an empty sequence (L = 0) gets
+    its zero unit, a walk with no positions (start = L > 0) none."""
+    full, tails = [], []
+    for i, (L, s0) in enumerate(zip(lens, starts)):
+        if L == 0:
+            tails.append((0, i, 0))
+            continue
+        rest = L - s0
+        for j in range(-(-rest // ptok)):
+            size = min(ptok, rest - j * ptok)
+            (full if size == ptok else tails).append((size, i, j))
+    return full, tails
+
+
+@pytest.mark.parametrize("ptok", [512, 64])
+def test_plan_of_walks_after_a_shared_prefix(ptok):
+    """The walks of pa_decode_shared_prefix: partitions tile the positions
+    after each sequence's prefix; entries carry the walk start."""
+    rng = np.random.default_rng(8)
+    lens = rng.integers(0, 3000, 200).astype(np.int32)
+    starts = np.minimum(lens, rng.integers(0, 40, 200) * 32).astype(np.int32)
+    lens[:4] = [0, 64, 1040, 1100]
+    starts[:4] = [0, 64, 1024, 0]
+    shape = _shape(len(lens), 3000, ptok)
+    plan = P.pa_decode_plan(shape, lens, walk_start=starts)
+    full, tails = _expected_walks([int(x) for x in lens], [int(x) for x in starts], ptok)
+    assert (plan[:, 2] == lens[plan[:, 0]]).all() and (plan[:, 3] == starts[plan[:, 0]]).all()
+    units = [tuple(map(int, u[:2])) for u in plan]
+    assert len(units) == len(full) + len(tails) == len(set(units))
+    assert units[:len(full)] == [(i, j) for _, i, j in full]
+    assert units[len(full):] == [(i, j) for _, i, j in sorted(tails, key=lambda t: (-t[0], t[1]))]
+    assert 1 not in {u[0] for u in units}                 # walk with no positions: no unit
+    # a start past its length, or negative, is refused
+    with pytest.raises(P.PaError):
+        P.pa_decode_plan(shape, lens, walk_start=np.where(np.arange(200) == 5, lens + 1, starts))
+    with pytest.raises(P.PaError):
+        P.pa_decode_plan(shape, lens, walk_start=np.where(np.arange(200) == 5, -1, starts))
