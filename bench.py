@@ -642,7 +642,8 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
         "dtype": w.dtype if not fp8 else "bf16 q/out, e4m3 K/V",
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": B, "num_q_heads": hq, "num_kv_heads": hkv,
-                   "head_dim": d, "block_size": bs, "partition_tokens": ptok,
+                   "head_dim": d, "block_size": bs,
+                   "partition_tokens": ptok if ptok else "automatic (library)",
                    "context_tokens": (f"U{{{w.lengths[1]}..{w.lengths[2]}}}+step"
                                       if w.lengths[0] == "uniform" else f"{w.lengths}+step"),
                    "kernel": vname, "block_order": args.block_order,
@@ -1013,11 +1014,12 @@ def group8_decode_rate(P, torch, dev, W) -> dict:
     ml = int(lens.max())
     shape = P._decode_shape(q, kp, tabd, ml, 0, P.PA_VARIANT_AUTO)
     plan = torch.from_numpy(P.pa_decode_plan(shape, lens.astype(np.int32))).to(dev)
-    ws = torch.empty(max(16, P.pa_decode_workspace_bytes(shape)), dtype=torch.uint8, device=dev)
     for name, variant, wp in (("matrix_cores", P.PA_VARIANT_AUTO, None),
                               ("matrix_cores_planned", P.PA_VARIANT_AUTO, plan),
                               ("vector_alu", P.PA_VARIANT_VALU, None)):
         out = torch.empty_like(q)
+        ws = torch.empty(max(16, P.pa_decode_workspace_bytes(
+            P._decode_shape(q, kp, tabd, ml, 0, variant))), dtype=torch.uint8, device=dev)
 
         def call():
             P.pa_decode(q, kp, vp, tabd, lensd, 1.0 / math.sqrt(d), out, max_seq_len=ml,

@@ -109,8 +109,9 @@ typedef struct {
   int32_t max_seq_len;        /* host bound on every seq_lens[i]; sizes the
                                  grid and the workspace                        */
   int32_t partition_tokens;   /* context partition length: 0 = automatic (512;
-                                 1024 for 8-bit pools and when G is 8 or 16 on
-                                 the matrix cores),
+                                 1024 for 8-bit pools, when G is 8 or 16 on
+                                 the matrix cores, and when max_seq_len is
+                                 above 8192),
                                  -1 = one partition per sequence, else a
                                  positive multiple of block_size               */
   int32_t dtype;              /* pa_dtype_t                                    */
@@ -249,11 +250,10 @@ pa_status_t pa_decode_plan(const pa_decode_shape_t* shape, const int32_t* seq_le
  *
  *   shape          as pa_decode: bf16, head_dim 128, G in {1, 2, 4, 8, 16},
  *                  block size 16-128; both passes split their range into
- *                  partitions: partition_tokens 0 = 256 positions for the
- *                  prefix pass and pa_decode's automatic length for the
- *                  walks after it, else that length for both; -1 is not
- *                  accepted; of variant only PA_DECODE_HALF_PARTIALS is read
- *                  (it applies to the walks after the prefix)
+ *                  partitions of partition_tokens positions (0: pa_decode's
+ *                  automatic length); -1 is not accepted; of variant only
+ *                  PA_DECODE_HALF_PARTIALS is read (it applies to the walks
+ *                  after the prefix)
  *   group_start    [dev] int32 [num_groups + 1], non-decreasing, last <= B;
  *                  sequences outside every group need prefix_lens 0
  *   prefix_lens    [dev] int32 [B]: shared positions of each sequence, a

@@ -17,11 +17,15 @@
 namespace {
 
 constexpr int kDefaultPartitionTokens = 512;
+// Contexts longer than this get automatic partitions of kLongPartitionTokens:
+// every partition writes a partial output (HBM writes in the middle of the
+// streaming K/V reads, which cost far more than their bytes), and a long
+// context has many (a 32,768-position sequence: 64 of 512 positions).
+constexpr int kLongContext = 8192;
+constexpr int kLongPartitionTokens = 1024;
 // pa_multi_query_split: one wave walks a partition for a whole 16-row tile,
 // so partitions are longer than decode's (measured best on 4-token chunks)
 constexpr int kDefaultMqPartitionTokens = 1024;
-// pa_decode_shared_prefix: a prefix is walked once per group
-constexpr int kDefaultPrefixPartitionTokens = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -82,10 +86,13 @@ pa_status_t make_plan(const pa_decode_shape_t* s, Plan* plan, bool kv_fp8 = fals
   plan->mq_route = decode_on_multi_query(*s, group, variant, kv_fp8);
   int pt = s->partition_tokens;
   // automatic length: 512 positions; 1024 on the per-tile kernel (one wave
-  // walks a partition for the whole group; measured best at group 8) and
-  // for 8-bit pools (the same bytes per workgroup as 512 bf16 positions)
+  // walks a partition for the whole group; measured best at group 8), for
+  // 8-bit pools (the same bytes per workgroup as 512 bf16 positions) and for
+  // contexts beyond kLongContext (fewer partial outputs)
   if (pt == 0)
-    pt = plan->mq_route || kv_fp8 ? kDefaultMqPartitionTokens : kDefaultPartitionTokens;
+    pt = plan->mq_route || kv_fp8 ? kDefaultMqPartitionTokens
+         : s->max_seq_len > kLongContext ? kLongPartitionTokens
+                                         : kDefaultPartitionTokens;
   if (pt == -1) {
     // one partition per sequence
     pt = s->max_seq_len > 0 ? (int)round_up((size_t)s->max_seq_len, (size_t)s->block_size)
@@ -498,11 +505,14 @@ pa_status_t prefix_plan(const pa_decode_shape_t* s, int32_t max_group_size,
     return PA_EUNSUPPORTED;
   if (max_prefix_len % s->block_size != 0 || max_prefix_len > s->max_seq_len) return PA_EINVAL;
   if ((int64_t)max_group_size * group > (1 << 24)) return PA_EINVAL;
-  // the walks after the prefix use pa_decode's partitions; the prefix pass
-  // (read once per group, so it needs shorter partitions to spread over the
-  // GPU) uses 256 positions unless partition_tokens is given
+  // both passes use pa_decode's partitions: shorter prefix partitions would
+  // spread the prefix pass over more waves but write more partial outputs
+  // (the prefix pass runs beside the walks in one launch; 256-position
+  // prefix partitions measured 95.5 vs 93.5 us on 64 x 4 samples of a
+  // 1040-position prompt, 488 vs 475 us with 16 more 32,768-position
+  // sequences)
   const int pt = pp->base.part_tokens;
-  pp->pref_tokens = s->partition_tokens == 0 ? kDefaultPrefixPartitionTokens : pt;
+  pp->pref_tokens = pt;
   pp->pref_parts = (max_prefix_len + pp->pref_tokens - 1) / pp->pref_tokens;
   pp->suf_parts = s->max_seq_len == 0 ? 1 : (s->max_seq_len + pt - 1) / pt;
   const size_t slots = (size_t)(pp->pref_parts + pp->suf_parts);

@@ -1383,7 +1383,7 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) { return to_bf16(f); }
 
 // The per-tile kernel's work for workgroup (bx, by = KV head, bz = sequence
 // or group), staging V^T in s_vt.
-template <int BS, int G>
+template <int BS, int G, int NWV = kMqWaves>
 __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz,
                                          uint16_t (*s_vt)[128][kMqVtRow]) {
   constexpr int D = 128, ROW = 256;
@@ -1397,7 +1397,7 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
   // units (tile, context partition), partition fastest, one per wave; in
   // decode mode over a host work plan, unit u = plan entry u (sequence,
   // partition, length), one tile each, and the grid holds only those
-  const int unit = bx * kMqWaves + w;
+  const int unit = bx * NWV + w;
   int i = bz, part, tile, plan_len = -1;
   if (a.plan) {
     if (unit >= a.num_units) return;
@@ -1726,20 +1726,28 @@ struct CascadeArgs {
   int32_t pre_gx;        // its grid: pre_gx x num_kv_heads x num_groups
 };
 
+// Waves per workgroup of the shared-prefix decode: one 16-row tile each in
+// the prefix pass, two per (sequence, KV head, partition) unit in the walks
+// (as the decode kernel on large grids: twice the workgroups of a 4-wave
+// walk, which evens out the end of the grid; a 32,768-position sequence
+// makes 64 units per KV head).
+constexpr int kCascadeWaves = 2;
+
 template <int BS, int G>
-__global__ __launch_bounds__(kMqWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kCascadeWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void shared_prefix_decode(CascadeArgs ca) {
-  __shared__ __align__(16) uint16_t s_vt[kMqWaves][128][kMqVtRow];
+  __shared__ __align__(16) uint16_t s_vt[kCascadeWaves][128][kMqVtRow];
   const int id = blockIdx.x;
   if (id < ca.n_prefix) {
     const int bx = id % ca.pre_gx, r = id / ca.pre_gx;
-    mq_tiles<BS, G>(ca.pre, bx, r % ca.pre.num_kv_heads, r / ca.pre.num_kv_heads, s_vt);
+    mq_tiles<BS, G, kCascadeWaves>(ca.pre, bx, r % ca.pre.num_kv_heads,
+                                   r / ca.pre.num_kv_heads, s_vt);
     return;
   }
   PartitionWork wk;
-  if (!setup_partition<uint16_t, 128, BS, G, kDecodeWaves, true>(ca.walk, wk, id - ca.n_prefix))
+  if (!setup_partition<uint16_t, 128, BS, G, kCascadeWaves, true>(ca.walk, wk, id - ca.n_prefix))
     return;
-  mfma_unit<BS, G, kDecodeWaves, false, true>(ca.walk, wk);
+  mfma_unit<BS, G, kCascadeWaves, false, true>(ca.walk, wk);
 }
 
 // Merge of the context partitions of pa_multi_query's split form: one wave
@@ -2495,7 +2503,8 @@ hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& 
   ca.pre = pre;
   ca.walk = walk;
   const int64_t tiles = ((int64_t)pre.max_query_len * group + 15) / 16;
-  const int64_t pre_gx = pre.max_parts > 0 ? (tiles * pre.max_parts + kMqWaves - 1) / kMqWaves : 0;
+  const int64_t pre_gx =
+      pre.max_parts > 0 ? (tiles * pre.max_parts + kCascadeWaves - 1) / kCascadeWaves : 0;
   const int64_t n_prefix = pre_gx * pre.num_kv_heads * pre.num_seqs;
   // the walks: one workgroup per (unit, KV head) of a work plan, else the
   // full (sequence, partition, KV head) grid
@@ -2506,7 +2515,7 @@ hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& 
   if (n_prefix + n_walk > 0x7fffffff) return hipErrorInvalidValue;
   ca.n_prefix = (int32_t)n_prefix;
   ca.pre_gx = (int32_t)(pre_gx > 0 ? pre_gx : 1);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(n_prefix + n_walk)), dim3(kMqWaves * 64), 0, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(n_prefix + n_walk)), dim3(kCascadeWaves * 64), 0, stream,
                      ca);
   return hipGetLastError();
 }

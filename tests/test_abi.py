@@ -149,7 +149,7 @@ def test_multi_query_workspace_bytes():
 
 def test_shared_prefix_workspace_bytes():
     s = _shape(max_seq_len=4096, max_blocks_per_seq=256)
-    slots = 1024 // 256 + 4096 // 512              # prefix pass (256) + walks (512) partitions
+    slots = 1024 // 512 + 4096 // 512              # prefix pass + walks: 512-position partitions
     # 128-byte statistics records per (sequence, KV head, slot); fp32 partial outputs
     want = -(-4 * 8 * slots * 128 // 256) * 256 + -(-4 * 32 * slots * 128 * 4 // 256) * 256
     assert P.pa_decode_shared_prefix_workspace_bytes(s, 4, 1024) == want
@@ -157,6 +157,12 @@ def test_shared_prefix_workspace_bytes():
     assert P.pa_decode_shared_prefix_workspace_bytes(s, 0, 1024) == 0     # no group size
     assert P.pa_decode_shared_prefix_workspace_bytes(
         _shape(max_seq_len=4096, max_blocks_per_seq=256, partition_tokens=-1), 4, 1024) == 0
+    # contexts beyond 8192 positions: automatic partitions of 1024
+    s = _shape(max_seq_len=32768, max_blocks_per_seq=2048)
+    slots = 1024 // 1024 + 32768 // 1024
+    want = -(-4 * 8 * slots * 128 // 256) * 256 + -(-4 * 32 * slots * 128 * 4 // 256) * 256
+    assert P.pa_decode_shared_prefix_workspace_bytes(s, 4, 1024) == want
+    assert P.pa_decode_plan_capacity(s) == 4 * 32
 
 
 def test_planned_and_append_reject_before_launch():

@@ -229,7 +229,7 @@ def test_variants_agree(dev):
 @pytest.mark.parametrize("ptok", [-1, 16, 128, 512])
 def test_large_groups_partition_lengths(dev, hq, hkv, ptok):
     # group 8 / 16 decode runs on the multi-token per-tile kernel with its
-    # context partitions (fp32 partials below 256 positions, bf16 above)
+    # context partitions (fp32 partials)
     w = _custom("groups", 110, hq, hkv, 128, 16, "bf16")
     c = build(w, dev, lens=[0, 1, 100, 511, 700, 2047, 2500], append=False)
     out = c.decode(variant=MFMA, partition_tokens=ptok)

@@ -25,7 +25,9 @@ The five workload shapes:
                 32, bf16; each group's prompt (1040 tokens: 32 full blocks and
                 one half-filled block) is shared by its 4 samples, then each
                 sample appends a private suffix of U{16..256} tokens.
-                The long variant adds 16 sequences of 32768 tokens.
+                The long variant adds 16 sequences of 32768 tokens. No
+                partition length is fixed for these two (partition_tokens 0:
+                the library's automatic choice).
 
 Draw order for every workload (one numpy Generator seeded with the workload's
 seed): lengths -> free-list order -> q -> new k/v -> pool contents.
@@ -78,9 +80,10 @@ WORKLOADS = {
                           ("uniform", 512, 4096), ("factor", 1.1)),
     "shared_prefix": Workload("shared_prefix", 5, 256, 32, 8, 128, 32, "bf16",
                               ("prefix_suffix", 1040, (16, 256), 4), ("factor", 1.1),
-                              extra={"groups": 64, "samples": 4}),
+                              partition_tokens=0, extra={"groups": 64, "samples": 4}),
     "shared_prefix_long": Workload("shared_prefix_long", 5, 272, 32, 8, 128, 32, "bf16",
                                    ("prefix_suffix", 1040, (16, 256), 4), ("factor", 1.1),
+                                   partition_tokens=0,
                                    extra={"groups": 64, "samples": 4,
                                           "long_seqs": 16, "long_len": 32768}),
 }
