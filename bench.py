@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: effective KV GB/s (% of HBM peak) + seq-steps/s"
+_KEEP_ALIVE = []   # device allocations made outside torch, held until the process ends
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b.json")
 
@@ -103,6 +104,11 @@ def main() -> int:
     ap.add_argument("--half-partials", action="store_true",
                     help="store partial outputs in bf16 (PA_DECODE_HALF_PARTIALS; an option "
                          "with a looser error bound, off by default)")
+    ap.add_argument("--workspace-memory", default="default",
+                    choices=["default", "finegrained", "uncached"],
+                    help="device memory kind of the decode workspace (partials): a torch "
+                         "tensor, or hipExtMallocWithFlags fine-grained or uncached memory "
+                         "(never freed: the process ends after the run)")
     ap.add_argument("--no-plan", action="store_true",
                     help="launch pa_decode's full grid instead of a host work plan")
     ap.add_argument("--event-every", type=int, default=5,
@@ -401,6 +407,19 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
     c_scale = ctypes.c_float(scale)
     c_kscale, c_vscale = ctypes.c_float(k_scale), ctypes.c_float(v_scale)
     ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+    if args.workspace_memory != "default":
+        # the partials in fine-grained or uncached device memory; uncached
+        # memory is kept to the end of the process once a kernel has used it
+        hipx = ctypes.CDLL("libamdhip64.so")
+        hipx.hipExtMallocWithFlags.restype = ctypes.c_int
+        hipx.hipExtMallocWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                               ctypes.c_uint]
+        wsp = ctypes.c_void_p()
+        flag = {"finegrained": 0x1, "uncached": 0x3}[args.workspace_memory]
+        if hipx.hipExtMallocWithFlags(ctypes.byref(wsp), ws_bytes, flag) != 0 or not wsp.value:
+            raise RuntimeError("hipExtMallocWithFlags failed")
+        ws_ptr = wsp.value
+        _KEEP_ALIVE.append(wsp)
     kp_ptr, vp_ptr, out_ptr = k_pool.data_ptr(), v_pool.data_ptr(), out.data_ptr()
     dt_code = P.PA_BF16 if w.dtype == "bf16" else P.PA_F32
     cs = compute.cuda_stream
@@ -624,7 +643,7 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
     default_launch = (not fp8 and args.block_size is None and args.block_order == "shuffled"
                       and args.partition_tokens is None and not args.no_plan
                       and not args.upload_tables and args.variant == "auto"
-                      and not args.half_partials)
+                      and not args.half_partials and args.workspace_memory == "default")
     vname = {0: "auto", 1: "valu", 2: "mfma"}[variant]
     if variant == P.PA_VARIANT_AUTO:
         vname = "mfma" if (w.dtype == "bf16" and d == 128 and hq // hkv in (1, 2, 4)) else "valu"
@@ -652,6 +671,7 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
                    "device_tables": not upload,
                    "kv_storage": "e4m3" if fp8 else w.dtype,
                    "partial_outputs": "bf16" if args.half_partials else "fp32",
+                   "workspace_memory": args.workspace_memory,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(B * K / wall, 1),

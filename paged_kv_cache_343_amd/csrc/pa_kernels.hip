@@ -993,24 +993,40 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
   // partial k (see finish_partition for its storage type)
   const float* po = reinterpret_cast<const float*>(a.part_o) +
                     ((int64_t)i * a.num_q_heads + hq) * stride * D;
-  // (branch-free, so that the loads of a batch can all be issued first: one
-  // 8-byte load at the lane's bf16 or fp32 position, decoded by a select;
-  // the bf16 case reads 4 bytes past its pair, still inside the slot)
-  auto load_part = [&](int k, float (&f)[D / 64]) {
-    const float* slot = po + (int64_t)slot_of(k) * D;
+  // The lane's slice of partial k in two steps, so that the loads of a
+  // batch can all be issued before any is decoded: raw_part loads the raw
+  // words (D 128: one 8-byte load at the lane's bf16 or fp32 position, the
+  // bf16 case reading 4 bytes past its pair, still inside the slot; D 64:
+  // one 4-byte fp32 or 2-byte bf16 load), decode_part turns them into
+  // floats.
+  auto half_of = [&](int k) {
     const int t0 = start + (k - np_pref) * pt;
-    const bool half = (!PFX || k >= np_pref) && a.part_half &&
-                      min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+    return (!PFX || k >= np_pref) && a.part_half &&
+           min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+  };
+  auto raw_part = [&](int k, bool half) {
+    const char* slot = reinterpret_cast<const char*>(po + (int64_t)slot_of(k) * D);
+    uint2 w = make_uint2(0u, 0u);
     if constexpr (D / 64 == 2) {
-      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(slot) +
-                                                      (half ? 4 : 8) * lane);
+      w = *reinterpret_cast<const uint2*>(slot + (half ? 4 : 8) * lane);
+    } else if (half) {
+      w.x = *reinterpret_cast<const uint16_t*>(slot + 2 * lane);
+    } else {
+      w.x = *reinterpret_cast<const uint32_t*>(slot + 4 * lane);
+    }
+    return w;
+  };
+  auto decode_part = [&](uint2 w, bool half, float (&f)[D / 64]) {
+    if constexpr (D / 64 == 2) {
       f[0] = half ? lo_bf16(w.x) : __uint_as_float(w.x);
       f[1] = half ? hi_bf16(w.x) : __uint_as_float(w.y);
-    } else if (half) {
-      load_elems<uint16_t, D / 64>(reinterpret_cast<const uint16_t*>(slot) + lane * (D / 64), f);
     } else {
-      load_elems<float, D / 64>(slot + lane * (D / 64), f);
+      f[0] = half ? lo_bf16(w.x) : __uint_as_float(w.x);
     }
+  };
+  auto load_part = [&](int k, float (&f)[D / 64]) {
+    const bool half = half_of(k);
+    decode_part(raw_part(k, half), half, f);
   };
   constexpr int DPL = D / 64;
   float o[DPL];
@@ -1021,15 +1037,19 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
     // every load up front: lane j's statistics, then each partition's slice
     const float mj = lane < np ? ml[(int64_t)slot_of(lane) * kMlRecord] : -INFINITY;
     const float lj = lane < np ? ml[(int64_t)slot_of(lane) * kMlRecord + 1] : 0.0f;
-    float v[kReduceFast][DPL];
+    // every load first; partitions past np (a wave-uniform test) load
+    // nothing and count as zeros
+    uint2 raw[kReduceFast];
+    bool hf[kReduceFast];
 #pragma unroll
     for (int j = 0; j < kReduceFast; ++j) {
-      // partitions past np read partition 0's slice (in bounds) and drop it
-      float f[DPL];
-      load_part(j < np ? j : 0, f);
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) v[j][k] = j < np ? f[k] : 0.0f;
+      hf[j] = half_of(j);
+      raw[j] = make_uint2(0u, 0u);
+      if (j < np) raw[j] = raw_part(j, hf[j]);
     }
+    float v[kReduceFast][DPL];
+#pragma unroll
+    for (int j = 0; j < kReduceFast; ++j) decode_part(raw[j], hf[j], v[j]);
     float big = mj;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
@@ -1146,32 +1166,37 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
   float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   // batch of partitions j0 .. j0 + 15 with weights wj (lane c: partition j0 + c)
   auto accumulate = [&](int j0, float wj) {
-    float v[R][8];
+    // every load of the batch first; partitions past np (a wave-uniform
+    // test) load nothing
+    uint4 w0[R], w1[R];
+    bool half[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      // past np: partition j0's slice again (in bounds), weight 0
-      const int j = j0 + u < np ? j0 + u : j0;
+      const int j = j0 + u;
       const int t0 = j * pt;
-      const bool half = a.part_half && min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
-      const char* sl = po + (int64_t)j * D * 4 + (half ? 16 : 32) * c;
-      const uint4 w0 = *reinterpret_cast<const uint4*>(sl);
-      const uint4 w1 = *reinterpret_cast<const uint4*>(sl + 16);
-      float f[8];
-      Elem<uint16_t>::unpack(w0, f);
-      v[u][0] = half ? f[0] : __uint_as_float(w0.x);
-      v[u][1] = half ? f[1] : __uint_as_float(w0.y);
-      v[u][2] = half ? f[2] : __uint_as_float(w0.z);
-      v[u][3] = half ? f[3] : __uint_as_float(w0.w);
-      v[u][4] = half ? f[4] : __uint_as_float(w1.x);
-      v[u][5] = half ? f[5] : __uint_as_float(w1.y);
-      v[u][6] = half ? f[6] : __uint_as_float(w1.z);
-      v[u][7] = half ? f[7] : __uint_as_float(w1.w);
+      half[u] = a.part_half && min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+      w0[u] = w1[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < np) {
+        const char* sl = po + (int64_t)j * D * 4 + (half[u] ? 16 : 32) * c;
+        w0[u] = *reinterpret_cast<const uint4*>(sl);
+        w1[u] = *reinterpret_cast<const uint4*>(sl + 16);
+      }
     }
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const float w = __shfl(wj, (lane & 48) | u);
+      float f[8];
+      Elem<uint16_t>::unpack(w0[u], f);
+      const float v[8] = {half[u] ? f[0] : __uint_as_float(w0[u].x),
+                          half[u] ? f[1] : __uint_as_float(w0[u].y),
+                          half[u] ? f[2] : __uint_as_float(w0[u].z),
+                          half[u] ? f[3] : __uint_as_float(w0[u].w),
+                          half[u] ? f[4] : __uint_as_float(w1[u].x),
+                          half[u] ? f[5] : __uint_as_float(w1[u].y),
+                          half[u] ? f[6] : __uint_as_float(w1[u].z),
+                          half[u] ? f[7] : __uint_as_float(w1[u].w)};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, v[u][e], o[e]);
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, v[e], o[e]);
     }
   };
   auto row_max = [](float x) {
@@ -1205,6 +1230,113 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D + 8 * c;
+  store4<uint16_t>(out, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  store4<uint16_t>(out + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+}
+
+// The same merge (bf16 out, head dim 128, 4 query heads per KV head) for
+// rows with many partitions, and for the shared-prefix decode's slots: one
+// workgroup of kWideReduceWaves waves per (sequence, KV head). Every wave
+// finds the row's maximum over all partitions; wave w then takes partitions
+// w, w + kWideReduceWaves, ... in batches of 16 (lane c of a 16-lane row:
+// partition number c of the batch, whose 16 loads are all issued first),
+// and the waves' sums meet in LDS. A 65-partition row is one batch per wave
+// instead of five in a row (decode_reduce_g4), and a shared-prefix row is
+// read per KV head rather than per query head (decode_reduce<PFX>).
+constexpr int kWideReduceWaves = 4;
+
+template <bool PFX>
+__global__ __launch_bounds__(kWideReduceWaves * 64) void decode_reduce_g4_wide(DecodeArgs a) {
+  constexpr int D = 128, G = 4, R = 16, NW = kWideReduceWaves;
+  const int unit = blockIdx.x;
+  if (unit >= a.num_seqs * a.num_kv_heads) return;
+  const int g = unit % a.num_kv_heads, i = unit / a.num_kv_heads;
+  int len = a.seq_lens[i];
+  len = len < 0 ? 0 : min(len, a.len_cap);
+  if (len == 0) return;                          // (every wave of the workgroup)
+  const int pt = a.part_tokens;
+  // partials k = 0 .. np - 1 of the row: with shared-prefix decode first the
+  // prefix pass's np_pref slots (fp32), then the walk's own partitions
+  const int start = PFX ? walk_start(a, i, len, false) : 0;
+  const int np_pref = PFX ? (start + a.prefix_part_tokens - 1) / a.prefix_part_tokens : 0;
+  const int np = np_pref + (len - start + pt - 1) / pt;
+  if (!PFX && np <= 1) return;                   // written by the partition kernel
+  const int64_t stride = PFX ? a.slot_stride : a.max_parts;
+  auto slot_of = [&](int k) { return PFX && k >= np_pref ? a.slot0 + (k - np_pref) : k; };
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 4, c = lane & 15;
+  const float* rec = a.part_ml + ((int64_t)i * a.num_kv_heads + g) * stride * kMlRecord + 2 * h;
+  const int64_t row = (int64_t)i * a.num_q_heads + g * G + h;
+  const char* po = reinterpret_cast<const char*>(a.part_o) + row * stride * D * 4;
+  auto row_max = [](float x) {
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+  };
+  float big = -INFINITY;
+  for (int k = c; k < np; k += R) big = fmaxf(big, rec[(int64_t)slot_of(k) * kMlRecord]);
+  big = row_max(big);
+  float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float wsum = 0.0f;
+  for (int b0 = w; b0 < np; b0 += NW * R) {
+    // lane c's partition of the batch and its weight
+    const int kc = b0 + NW * c;
+    const float wj = kc < np ? rec[(int64_t)slot_of(kc) * kMlRecord + 1] *
+                                   merge_weight(rec[(int64_t)slot_of(kc) * kMlRecord], big)
+                             : 0.0f;
+    // the batch's loads, all issued before any is used; partitions past np
+    // (a wave-uniform test) load nothing
+    uint4 w0[R], w1[R];
+    bool half[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = b0 + NW * u;
+      const int t0 = start + (k - np_pref) * pt;
+      half[u] = (!PFX || k >= np_pref) && a.part_half &&
+                min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+      w0[u] = w1[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (k < np) {
+        const char* sl = po + (int64_t)slot_of(k) * D * 4 + (half[u] ? 16 : 32) * c;
+        w0[u] = *reinterpret_cast<const uint4*>(sl);
+        w1[u] = *reinterpret_cast<const uint4*>(sl + 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const float wu = __shfl(wj, (lane & 48) | u);
+      float f[8];
+      Elem<uint16_t>::unpack(w0[u], f);
+      const float v[8] = {half[u] ? f[0] : __uint_as_float(w0[u].x),
+                          half[u] ? f[1] : __uint_as_float(w0[u].y),
+                          half[u] ? f[2] : __uint_as_float(w0[u].z),
+                          half[u] ? f[3] : __uint_as_float(w0[u].w),
+                          half[u] ? f[4] : __uint_as_float(w1[u].x),
+                          half[u] ? f[5] : __uint_as_float(w1[u].y),
+                          half[u] ? f[6] : __uint_as_float(w1[u].z),
+                          half[u] ? f[7] : __uint_as_float(w1[u].w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(wu, v[e], o[e]);
+    }
+    wsum += wj;
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  __shared__ __align__(16) float s_o[NW][64][8];
+  __shared__ float s_w[NW][G];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_o[w][lane][e] = o[e];
+  if (c == 0) s_w[w][h] = wsum;
+  __syncthreads();
+  if (w != 0) return;
+  float tot = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    tot += s_w[k][h];
+    if (k == 0) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += s_o[k][lane][e];
+  }
+  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D + 8 * c;
   store4<uint16_t>(out, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
   store4<uint16_t>(out + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
@@ -2333,11 +2465,22 @@ hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
   if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
   if (args.pos_start) kern = dtype == 1 && head_dim == 128 ? decode_reduce<uint16_t, 128, true> : nullptr;
   if (!kern) return hipErrorInvalidValue;
-  if (!args.pos_start && dtype == 1 && head_dim == 128 && args.num_q_heads == 4 * args.num_kv_heads) {
-    // one wave per (sequence, KV head)
+  // the shared-prefix decode's slots: prefix pass and walks
+  const int64_t slots = args.pos_start ? (int64_t)args.slot_stride : args.max_parts;
+  if (dtype == 1 && head_dim == 128 && args.num_q_heads == 4 * args.num_kv_heads &&
+      (!args.pos_start || slots > kReduceFast)) {
     const int64_t units = (int64_t)args.num_seqs * args.num_kv_heads;
-    hipLaunchKernelGGL(decode_reduce_g4, dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
-                       dim3(kReduceWaves * 64), 0, stream, args);
+    if (!args.pos_start && args.max_parts <= kReduceFast) {
+      // one wave per (sequence, KV head), every partition in one batch
+      hipLaunchKernelGGL(decode_reduce_g4,
+                         dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
+                         dim3(kReduceWaves * 64), 0, stream, args);
+      return hipGetLastError();
+    }
+    // many partitions: a workgroup per (sequence, KV head)
+    if (units > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(args.pos_start ? decode_reduce_g4_wide<true> : decode_reduce_g4_wide<false>,
+                       dim3((unsigned)units), dim3(kWideReduceWaves * 64), 0, stream, args);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kReduceWaves * 64), 0, stream, args);
