@@ -1509,7 +1509,12 @@ __device__ __forceinline__ void split_bf16x8(const float (&p)[8], uint4& hi, uin
 }
 
 constexpr int kMqWaves = 4;
-constexpr int kMqVtRow = 40;     // bf16 elements per staged V^T row (32 positions + 8 pad)
+// Staged V^T: row = dim, 40 bf16 per row (32 positions + 8 pad). The four
+// 16-byte chunks of rows 64..127 sit in the order 2, 3, 0, 1 (chunk index
+// XOR 2): the transposing 8-byte writes of a wave cover rows 8c + k for
+// c = 0..15, which without the swap fall on only 16 of the 64 LDS banks.
+constexpr int kMqVtRow = 40;
+__device__ __forceinline__ int mq_vt_chunk(int row, int chunk) { return chunk ^ ((row >> 5) & 2); }
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return to_bf16(f); }
 
@@ -1733,8 +1738,9 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
       __builtin_amdgcn_wave_barrier();   // the staged V^T rows are complete (in-order per wave)
 #pragma unroll
       for (int t2 = 0; t2 < 8; ++t2) {
+        const int row = 16 * t2 + c;
         const bf16x8_t vb = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[w][16 * t2 + c][8 * R]));
+            bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[w][row][8 * mq_vt_chunk(row, R)]));
         acc[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, phi), vb,
                                                           acc[t2], 0, 0, 0);
         acc[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, plo), vb,
@@ -1756,7 +1762,8 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
         v[r][2] = x.z;
         v[r][3] = x.w;
       }
-      const int slot = 8 * R + 4 * h;
+      // rows 8c .. 8c + 7 share one chunk order
+      const int slot = 8 * mq_vt_chunk(8 * c, R) + 4 * h;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint2 lo = make_uint2((v[0][e] & 0xffffu) | (v[1][e] << 16),
