@@ -196,6 +196,24 @@ __device__ __forceinline__ void quad_spread(float x, float (&out)[G]) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one v_max3_f32. For matrix-core results the compiler
+// otherwise quiets each operand with a max of the value with itself before
+// every two-input max (it cannot tell they hold no signalling NaN).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Two bf16 halves of 32-bit words into one word: the low halves of lo_src
+// (bits 0-15) and hi_src (bits 16-31), or their high halves, in one v_perm_b32.
+__device__ __forceinline__ uint32_t pack_low_halves(uint32_t lo_src, uint32_t hi_src) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_high_halves(uint32_t lo_src, uint32_t hi_src) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
+}
+
 // Weight of a softmax stream with running max m when merged under max M.
 __device__ __forceinline__ float merge_weight(float m, float big_m) {
   return m == -INFINITY ? 0.0f : exp2_fast(m - big_m);
@@ -1766,10 +1784,10 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
       const int slot = 8 * mq_vt_chunk(8 * c, R) + 4 * h;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint2 lo = make_uint2((v[0][e] & 0xffffu) | (v[1][e] << 16),
-                                    (v[2][e] & 0xffffu) | (v[3][e] << 16));
-        const uint2 hi = make_uint2((v[0][e] >> 16) | (v[1][e] & 0xffff0000u),
-                                    (v[2][e] >> 16) | (v[3][e] & 0xffff0000u));
+        const uint2 lo = make_uint2(pack_low_halves(v[0][e], v[1][e]),
+                                    pack_low_halves(v[2][e], v[3][e]));
+        const uint2 hi = make_uint2(pack_high_halves(v[0][e], v[1][e]),
+                                    pack_high_halves(v[2][e], v[3][e]));
         *reinterpret_cast<uint2*>(&s_vt[w][8 * c + 2 * e][slot]) = lo;
         *reinterpret_cast<uint2*>(&s_vt[w][8 * c + 2 * e + 1][slot]) = hi;
       }
@@ -2135,9 +2153,8 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // dims 8 dv + 2e (low halves) and + 2e + 1 (high halves) of positions 0..3
-      const uint2 lo = make_uint2((v0[e] & 0xffffu) | (v1[e] << 16), (v2[e] & 0xffffu) | (v3[e] << 16));
-      const uint2 hi = make_uint2((v0[e] >> 16) | (v1[e] & 0xffff0000u),
-                                  (v2[e] >> 16) | (v3[e] & 0xffff0000u));
+      const uint2 lo = make_uint2(pack_low_halves(v0[e], v1[e]), pack_low_halves(v2[e], v3[e]));
+      const uint2 hi = make_uint2(pack_high_halves(v0[e], v1[e]), pack_high_halves(v2[e], v3[e]));
       *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e][slot]) = lo;
       *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e + 1][slot]) = hi;
     }
@@ -2199,70 +2216,84 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
           sc[rt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s2], qop[rt][s2], sc[rt][sl], 0, 0, 0);
       }
     }
-    const bool full = p0 + kFaPos <= vis_w;     // no position of the block is masked for this wave
     uint4 phi[2][2], plo[2][2];                 // [rt][32-position step]
     bool rescale = false;
     float alpha[2];
+    // the softmax of the block's scores, with a per-position mask (kMasked:
+    // the block reaches past some row's last position) or without
+    auto softmax = [&](auto masked_tag) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      // scores stay unscaled until the exponent: qs >= 0 (a negative scale
-      // was folded into q's sign), so the row maximum scales with them
-      float bm = -INFINITY;
-      if (full) {
+      for (int rt = 0; rt < 2; ++rt) {
+        // scores stay unscaled until the exponent: qs >= 0 (a negative scale
+        // was folded into q's sign), so the row maximum scales with them
+        float bm = -INFINITY;
+        if constexpr (kMasked) {
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
+          for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sc[rt][sl][r]);
-      } else {
+            for (int r = 0; r < 4; ++r)
+              bm = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? fmaxf(bm, sc[rt][sl][r]) : bm;
+        } else {
+          float b0 = -INFINITY, b1 = -INFINITY;
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            bm = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? fmaxf(bm, sc[rt][sl][r]) : bm;
-      }
-      bm = fmaxf(bm, xor_lanes<16>(bm));
-      bm = fmaxf(bm, xor_lanes<32>(bm));
-      // the reference maximum moves only when a score exceeds it by more
-      // than 2^8 (so p <= 256): rows rarely need rescaling after the first
-      // block
-      const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
-      const float mn = bms > m[rt] + kFaLazy ? bms : m[rt];
-      alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
-      rescale |= alpha[rt] != 1.0f;
-      m[rt] = mn;
-      float p[16], ps = 0.0f;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[4 * sl + r] = exp2_fast(fmaf(sc[rt][sl][r], qs, -mn));
-      if (!full) {
-        // masked positions (and every position while the row has none) get 0
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            p[4 * sl + r] = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? p[4 * sl + r] : 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) ps += p[e];
-      lsum[rt] = lsum[rt] * alpha[rt] + ps;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        // k-slots 8R + 4h + r <- position 32 st + 16 h + 4R + r = p[4 (2 st + h) + r]
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = p[8 * st + e];
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-          lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
-                              f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+          for (int sl = 0; sl < 4; sl += 2) {
+            b0 = max3f(b0, sc[rt][sl][0], sc[rt][sl][1]);
+            b0 = max3f(b0, sc[rt][sl][2], sc[rt][sl][3]);
+            b1 = max3f(b1, sc[rt][sl + 1][0], sc[rt][sl + 1][1]);
+            b1 = max3f(b1, sc[rt][sl + 1][2], sc[rt][sl + 1][3]);
+          }
+          bm = fmaxf(b0, b1);
         }
-        phi[rt][st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-        plo[rt][st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+        bm = fmaxf(bm, xor_lanes<16>(bm));
+        bm = fmaxf(bm, xor_lanes<32>(bm));
+        // the reference maximum moves only when a score exceeds it by more
+        // than 2^8 (so p <= 256): rows rarely need rescaling after the first
+        // block
+        const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
+        const float mn = bms > m[rt] + kFaLazy ? bms : m[rt];
+        alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
+        rescale |= alpha[rt] != 1.0f;
+        m[rt] = mn;
+        float p[16], ps = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[4 * sl + r] = exp2_fast(fmaf(sc[rt][sl][r], qs, -mn));
+        if constexpr (kMasked) {
+          // masked positions (and every position while the row has none) get 0
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              p[4 * sl + r] = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? p[4 * sl + r] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ps += p[e];
+        lsum[rt] = lsum[rt] * alpha[rt] + ps;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          // k-slots 8R + 4h + r <- position 32 st + 16 h + 4R + r = p[4 (2 st + h) + r]
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = p[8 * st + e];
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+            lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
+                                f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+          }
+          phi[rt][st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+          plo[rt][st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+        }
       }
-    }
+    };
+    // no position of the block is masked for this wave
+    if (p0 + kFaPos <= vis_w)
+      softmax(std::false_type{});
+    else
+      softmax(std::true_type{});
     // rescale output rows 4R + r of each tile by their rows' alpha (row c's
     // alpha sits in lane c); skipped when no row's maximum moved
     if (__ballot(rescale) != 0) {
