@@ -154,6 +154,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        # libpa.so takes whichever HIP runtime (soname libamdhip64.so.7) the
+        # process has loaded. torch ships its own copy, which owns the device
+        # memory and streams handed to libpa: load it first, or libpa would
+        # bring in a second runtime to which torch's pointers mean nothing
+        import torch  # noqa: F401
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(handle, name)
