@@ -1253,113 +1253,6 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
   store4<uint16_t>(out + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
-// The same merge (bf16 out, head dim 128, 4 query heads per KV head) for
-// rows with many partitions, and for the shared-prefix decode's slots: one
-// workgroup of kWideReduceWaves waves per (sequence, KV head). Every wave
-// finds the row's maximum over all partitions; wave w then takes partitions
-// w, w + kWideReduceWaves, ... in batches of 16 (lane c of a 16-lane row:
-// partition number c of the batch, whose 16 loads are all issued first),
-// and the waves' sums meet in LDS. A 65-partition row is one batch per wave
-// instead of five in a row (decode_reduce_g4), and a shared-prefix row is
-// read per KV head rather than per query head (decode_reduce<PFX>).
-constexpr int kWideReduceWaves = 4;
-
-template <bool PFX>
-__global__ __launch_bounds__(kWideReduceWaves * 64) void decode_reduce_g4_wide(DecodeArgs a) {
-  constexpr int D = 128, G = 4, R = 16, NW = kWideReduceWaves;
-  const int unit = blockIdx.x;
-  if (unit >= a.num_seqs * a.num_kv_heads) return;
-  const int g = unit % a.num_kv_heads, i = unit / a.num_kv_heads;
-  int len = a.seq_lens[i];
-  len = len < 0 ? 0 : min(len, a.len_cap);
-  if (len == 0) return;                          // (every wave of the workgroup)
-  const int pt = a.part_tokens;
-  // partials k = 0 .. np - 1 of the row: with shared-prefix decode first the
-  // prefix pass's np_pref slots (fp32), then the walk's own partitions
-  const int start = PFX ? walk_start(a, i, len, false) : 0;
-  const int np_pref = PFX ? (start + a.prefix_part_tokens - 1) / a.prefix_part_tokens : 0;
-  const int np = np_pref + (len - start + pt - 1) / pt;
-  if (!PFX && np <= 1) return;                   // written by the partition kernel
-  const int64_t stride = PFX ? a.slot_stride : a.max_parts;
-  auto slot_of = [&](int k) { return PFX && k >= np_pref ? a.slot0 + (k - np_pref) : k; };
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 4, c = lane & 15;
-  const float* rec = a.part_ml + ((int64_t)i * a.num_kv_heads + g) * stride * kMlRecord + 2 * h;
-  const int64_t row = (int64_t)i * a.num_q_heads + g * G + h;
-  const char* po = reinterpret_cast<const char*>(a.part_o) + row * stride * D * 4;
-  auto row_max = [](float x) {
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-  };
-  float big = -INFINITY;
-  for (int k = c; k < np; k += R) big = fmaxf(big, rec[(int64_t)slot_of(k) * kMlRecord]);
-  big = row_max(big);
-  float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  float wsum = 0.0f;
-  for (int b0 = w; b0 < np; b0 += NW * R) {
-    // lane c's partition of the batch and its weight
-    const int kc = b0 + NW * c;
-    const float wj = kc < np ? rec[(int64_t)slot_of(kc) * kMlRecord + 1] *
-                                   merge_weight(rec[(int64_t)slot_of(kc) * kMlRecord], big)
-                             : 0.0f;
-    // the batch's loads, all issued before any is used; partitions past np
-    // (a wave-uniform test) load nothing
-    uint4 w0[R], w1[R];
-    bool half[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int k = b0 + NW * u;
-      const int t0 = start + (k - np_pref) * pt;
-      half[u] = (!PFX || k >= np_pref) && a.part_half &&
-                min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
-      w0[u] = w1[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (k < np) {
-        const char* sl = po + (int64_t)slot_of(k) * D * 4 + (half[u] ? 16 : 32) * c;
-        w0[u] = *reinterpret_cast<const uint4*>(sl);
-        w1[u] = *reinterpret_cast<const uint4*>(sl + 16);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const float wu = __shfl(wj, (lane & 48) | u);
-      float f[8];
-      Elem<uint16_t>::unpack(w0[u], f);
-      const float v[8] = {half[u] ? f[0] : __uint_as_float(w0[u].x),
-                          half[u] ? f[1] : __uint_as_float(w0[u].y),
-                          half[u] ? f[2] : __uint_as_float(w0[u].z),
-                          half[u] ? f[3] : __uint_as_float(w0[u].w),
-                          half[u] ? f[4] : __uint_as_float(w1[u].x),
-                          half[u] ? f[5] : __uint_as_float(w1[u].y),
-                          half[u] ? f[6] : __uint_as_float(w1[u].z),
-                          half[u] ? f[7] : __uint_as_float(w1[u].w)};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = fmaf(wu, v[e], o[e]);
-    }
-    wsum += wj;
-  }
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
-  __shared__ __align__(16) float s_o[NW][64][8];
-  __shared__ float s_w[NW][G];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s_o[w][lane][e] = o[e];
-  if (c == 0) s_w[w][h] = wsum;
-  __syncthreads();
-  if (w != 0) return;
-  float tot = 0.0f;
-#pragma unroll
-  for (int k = 0; k < NW; ++k) {
-    tot += s_w[k][h];
-    if (k == 0) continue;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] += s_o[k][lane][e];
-  }
-  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D + 8 * c;
-  store4<uint16_t>(out, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-  store4<uint16_t>(out + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
-}
-
 // ---------------------------------------------------------------------------
 // Slot write and block copy
 // ---------------------------------------------------------------------------
@@ -2503,22 +2396,12 @@ hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
   if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
   if (args.pos_start) kern = dtype == 1 && head_dim == 128 ? decode_reduce<uint16_t, 128, true> : nullptr;
   if (!kern) return hipErrorInvalidValue;
-  // the shared-prefix decode's slots: prefix pass and walks
-  const int64_t slots = args.pos_start ? (int64_t)args.slot_stride : args.max_parts;
   if (dtype == 1 && head_dim == 128 && args.num_q_heads == 4 * args.num_kv_heads &&
-      (!args.pos_start || slots > kReduceFast)) {
+      !args.pos_start && args.max_parts <= kReduceFast) {
+    // one wave per (sequence, KV head), every partition in one batch
     const int64_t units = (int64_t)args.num_seqs * args.num_kv_heads;
-    if (!args.pos_start && args.max_parts <= kReduceFast) {
-      // one wave per (sequence, KV head), every partition in one batch
-      hipLaunchKernelGGL(decode_reduce_g4,
-                         dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
-                         dim3(kReduceWaves * 64), 0, stream, args);
-      return hipGetLastError();
-    }
-    // many partitions: a workgroup per (sequence, KV head)
-    if (units > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(args.pos_start ? decode_reduce_g4_wide<true> : decode_reduce_g4_wide<false>,
-                       dim3((unsigned)units), dim3(kWideReduceWaves * 64), 0, stream, args);
+    hipLaunchKernelGGL(decode_reduce_g4, dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
+                       dim3(kReduceWaves * 64), 0, stream, args);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(kReduceWaves * 64), 0, stream, args);
