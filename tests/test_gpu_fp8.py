@@ -165,7 +165,7 @@ def test_nan_codes_outside_sequences_do_not_leak(dev):
 @pytest.mark.parametrize("hq,hkv,bs", [(32, 8, 16), (8, 8, 32), (32, 8, 64)])
 @pytest.mark.parametrize("ptok", [1024, 256, -1])
 def test_planned_decode_over_code_pools(dev, hq, hkv, bs, ptok):
-    """pa_decode_e4m3_planned: bitwise equal to pa_decode_e4m3 at the same
+    """pa_decode_e4m3 over a work plan: bitwise equal to the unplanned call at the same
     explicit partition length, within tolerance of the oracle."""
     lens = [0, 1, 15, 16, 17, 33, 511, 512, 513, 1025, 2100, 1024]
     c, kc, vc = _code_case(dev, hq, hkv, bs, lens)

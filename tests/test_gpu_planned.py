@@ -1,5 +1,5 @@
-"""GPU parity of the planned decode (pa_decode_plan + pa_decode_planned /
-pa_decode_partition_planned): each work unit computes what it computes in
+"""GPU parity of the planned decode (pa_decode_plan, then pa_decode or
+pa_decode_partition with the work_plan argument): each work unit computes what it computes in
 pa_decode, so outputs must be bitwise equal to pa_decode's, and within
 tolerance of the float64 oracle; bad plan entries are skipped and flagged."""
 import numpy as np
