@@ -1166,6 +1166,9 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce(DecodeArgs a)
 // and dims 8 (l % 16) .. + 7, so the group's statistics record is read once
 // and a partial slice is one 16-byte (bf16) or 32-byte (fp32) read per lane.
 // Lane c of a row holds the statistics of partition c of each batch of 16.
+// PFX: the shared-prefix decode's slots, as in decode_reduce<PFX>: first the
+// prefix pass's (fp32), then the walk's own partitions from slot0.
+template <bool PFX>
 __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs a) {
   constexpr int D = 128, G = 4, R = kReduceFast;
   static_assert(R == 16, "one partition per lane of a 16-lane row");
@@ -1174,13 +1177,18 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
   const int g = unit % a.num_kv_heads, i = unit / a.num_kv_heads;
   int len = a.seq_lens[i];
   len = len < 0 ? 0 : min(len, a.len_cap);
+  if (PFX && len == 0) return;
   const int pt = a.part_tokens;
-  const int np = (len + pt - 1) / pt;
-  if (np <= 1) return;                           // written by the partition kernel
+  const int start = PFX ? walk_start(a, i, len, false) : 0;
+  const int np_pref = PFX ? (start + a.prefix_part_tokens - 1) / a.prefix_part_tokens : 0;
+  const int np = np_pref + (len - start + pt - 1) / pt;
+  if (!PFX && np <= 1) return;                   // written by the partition kernel
+  const int64_t stride = PFX ? a.slot_stride : a.max_parts;
+  auto slot_of = [&](int k) { return PFX && k >= np_pref ? a.slot0 + (k - np_pref) : k; };
   const int lane = threadIdx.x & 63, h = lane >> 4, c = lane & 15;
-  const float* rec = a.part_ml + ((int64_t)i * a.num_kv_heads + g) * a.max_parts * kMlRecord + 2 * h;
+  const float* rec = a.part_ml + ((int64_t)i * a.num_kv_heads + g) * stride * kMlRecord + 2 * h;
   const int64_t row = (int64_t)i * a.num_q_heads + g * G + h;
-  const char* po = reinterpret_cast<const char*>(a.part_o) + row * a.max_parts * D * 4;
+  const char* po = reinterpret_cast<const char*>(a.part_o) + row * stride * D * 4;
   float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   // batch of partitions j0 .. j0 + 15 with weights wj (lane c: partition j0 + c)
   auto accumulate = [&](int j0, float wj) {
@@ -1191,11 +1199,12 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int j = j0 + u;
-      const int t0 = j * pt;
-      half[u] = a.part_half && min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
+      const int t0 = start + (j - np_pref) * pt;
+      half[u] = (!PFX || j >= np_pref) && a.part_half &&
+                min(len, t0 + pt) - t0 >= kHalfPartialMinTokens;
       w0[u] = w1[u] = make_uint4(0u, 0u, 0u, 0u);
       if (j < np) {
-        const char* sl = po + (int64_t)j * D * 4 + (half[u] ? 16 : 32) * c;
+        const char* sl = po + (int64_t)slot_of(j) * D * 4 + (half[u] ? 16 : 32) * c;
         w0[u] = *reinterpret_cast<const uint4*>(sl);
         w1[u] = *reinterpret_cast<const uint4*>(sl + 16);
       }
@@ -1225,22 +1234,21 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_g4(DecodeArgs
   float wsum;
   if (np <= R) {
     // every read up front
-    const float mj = c < np ? rec[(int64_t)c * kMlRecord] : -INFINITY;
-    const float lj = c < np ? rec[(int64_t)c * kMlRecord + 1] : 0.0f;
+    const float mj = c < np ? rec[(int64_t)slot_of(c) * kMlRecord] : -INFINITY;
+    const float lj = c < np ? rec[(int64_t)slot_of(c) * kMlRecord + 1] : 0.0f;
     const float wj = lj * merge_weight(mj, row_max(mj));
     accumulate(0, wj);
     wsum = wj;
   } else {
     float big = -INFINITY;
     for (int j0 = 0; j0 < np; j0 += R)
-      if (j0 + c < np) big = fmaxf(big, rec[(int64_t)(j0 + c) * kMlRecord]);
+      if (j0 + c < np) big = fmaxf(big, rec[(int64_t)slot_of(j0 + c) * kMlRecord]);
     big = row_max(big);
     wsum = 0.0f;
     for (int j0 = 0; j0 < np; j0 += R) {
       const int j = j0 + c;
-      const float wj =
-          j < np ? rec[(int64_t)j * kMlRecord + 1] * merge_weight(rec[(int64_t)j * kMlRecord], big)
-                 : 0.0f;
+      const float* rj = rec + (int64_t)slot_of(j) * kMlRecord;
+      const float wj = j < np ? rj[1] * merge_weight(rj[0], big) : 0.0f;
       accumulate(j0, wj);
       wsum += wj;
     }
@@ -2396,11 +2404,14 @@ hipError_t launch_decode_reduce(int dtype, int head_dim, const DecodeArgs& args,
   if (dtype == 1 && head_dim == 128) kern = decode_reduce<uint16_t, 128>;
   if (args.pos_start) kern = dtype == 1 && head_dim == 128 ? decode_reduce<uint16_t, 128, true> : nullptr;
   if (!kern) return hipErrorInvalidValue;
+  // the shared-prefix decode's slots: prefix pass and walks
+  const int64_t slots = args.pos_start ? (int64_t)args.slot_stride : args.max_parts;
   if (dtype == 1 && head_dim == 128 && args.num_q_heads == 4 * args.num_kv_heads &&
-      !args.pos_start && args.max_parts <= kReduceFast) {
+      slots <= kReduceFast) {
     // one wave per (sequence, KV head), every partition in one batch
     const int64_t units = (int64_t)args.num_seqs * args.num_kv_heads;
-    hipLaunchKernelGGL(decode_reduce_g4, dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
+    hipLaunchKernelGGL(args.pos_start ? decode_reduce_g4<true> : decode_reduce_g4<false>,
+                       dim3((unsigned)((units + kReduceWaves - 1) / kReduceWaves)),
                        dim3(kReduceWaves * 64), 0, stream, args);
     return hipGetLastError();
   }
