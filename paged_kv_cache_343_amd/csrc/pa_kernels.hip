@@ -196,6 +196,13 @@ __device__ __forceinline__ void quad_spread(float x, float (&out)[G]) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Online softmax with a lazy reference maximum: a stream's reference m (log2
+// units) moves only when a new score exceeds it by more than kLazyMax, so
+// after its first positions a stream almost never rescales its output, and
+// each exponent exp2(s - m) stays at most 2^kLazyMax. The result is the same
+// softmax for any reference (m only scales the terms and the sum alike).
+constexpr float kLazyMax = 8.0f;
+
 // max(a, b, c) in one v_max3_f32. For matrix-core results the compiler
 // otherwise quiets each operand with a max of the value with itself before
 // every two-input max (it cannot tell they hold no signalling NaN).
@@ -825,7 +832,7 @@ __device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4]
     ok[r] = full || (tokc + 4 * R + r < tok1);
     bm = ok[r] ? fmaxf(bm, sv[r]) : bm;
   }
-  const float mn = fmaxf(m, bm);
+  const float mn = bm > m + kLazyMax ? bm : m;
   const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
   m = mn;
   float p[4];
@@ -836,14 +843,18 @@ __device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4]
     psum += p[r];
   }
   lsum = lsum * alpha + psum;
-  float al[G], ph[4][G];
-  quad_spread<G>(alpha, al);
+  float ph[4][G];
 #pragma unroll
   for (int r = 0; r < 4; ++r) quad_spread<G>(p[r], ph[r]);
+  // rescale only when some stream of the wave moved its reference
+  if (__ballot(alpha != 1.0f) != 0) {
+    float al[G];
+    quad_spread<G>(alpha, al);
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+  }
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float vf[8];
@@ -1631,7 +1642,7 @@ __device__ __forceinline__ void mq_tiles(const MqArgs& a, int bx, int by, int bz
         }
       bm = fmaxf(bm, xor_lanes<16>(bm));
       bm = fmaxf(bm, xor_lanes<32>(bm));
-      const float mn = fmaxf(m, bm);
+      const float mn = bm > m + kLazyMax ? bm : m;
       const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
       m = mn;
       float p[8], ps = 0.0f;
@@ -1917,7 +1928,6 @@ constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad
 #define PA_FA_BUFS 2
 #endif
 constexpr int kFaBufs = PA_FA_BUFS;   // LDS stages of K and V^T
-constexpr float kFaLazy = 8.0f;       // log2 headroom of the softmax reference maximum
 
 
 // Slot of position j (0..63) of a block in a staged V^T row: inside each
@@ -2148,11 +2158,10 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
         }
         bm = fmaxf(bm, xor_lanes<16>(bm));
         bm = fmaxf(bm, xor_lanes<32>(bm));
-        // the reference maximum moves only when a score exceeds it by more
-        // than 2^8 (so p <= 256): rows rarely need rescaling after the first
-        // block
+        // lazy reference maximum (kLazyMax): rows rarely need rescaling
+        // after the first block
         const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
-        const float mn = bms > m[rt] + kFaLazy ? bms : m[rt];
+        const float mn = bms > m[rt] + kLazyMax ? bms : m[rt];
         alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
         rescale |= alpha[rt] != 1.0f;
         m[rt] = mn;
@@ -2348,16 +2357,6 @@ static PartitionKernel pick_partition(const DecodeKey& k, int waves = kDecodeWav
 
 bool decode_partition_supported(const DecodeKey& key) { return pick_partition(key) != nullptr; }
 
-template <int BS>
-static PartitionKernel pick_mfma_prefix(int group) {
-  switch (group) {
-    case 1: return decode_partition_mfma<BS, 1, kDecodeWaves, false, true>;
-    case 2: return decode_partition_mfma<BS, 2, kDecodeWaves, false, true>;
-    case 4: return decode_partition_mfma<BS, 4, kDecodeWaves, false, true>;
-    default: return nullptr;
-  }
-}
-
 hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    hipStream_t stream) {
   const int64_t groups = (int64_t)args.num_kv_heads *
@@ -2365,24 +2364,13 @@ hipError_t launch_decode_partition(const DecodeKey& key, const DecodeArgs& args,
                                    : (int64_t)args.num_seqs * args.max_parts);
   // the wave count follows the shape's full grid, so that a planned call
   // runs the same kernel as the unplanned one (bit-identical results)
-  const bool mfma = key.variant == 2 && !args.pos_start;
+  // (the shared-prefix walks run inside launch_shared_prefix_decode)
+  if (args.pos_start) return hipErrorInvalidValue;
+  const bool mfma = key.variant == 2;
   const int waves =
       mfma ? mfma_waves((int64_t)args.num_kv_heads * args.num_seqs * args.max_parts)
            : kDecodeWaves;
   PartitionKernel kern = pick_partition(key, waves);
-  if (args.pos_start) {
-    // shared-prefix decode's per-sequence walk: bf16 matrix-core kernel only
-    kern = nullptr;
-    if (key.dtype == 1 && key.head_dim == 128 && key.variant == 2 && !key.kv_fp8) {
-      switch (key.block_size) {
-        case 16: kern = pick_mfma_prefix<16>(key.group); break;
-        case 32: kern = pick_mfma_prefix<32>(key.group); break;
-        case 64: kern = pick_mfma_prefix<64>(key.group); break;
-        case 128: kern = pick_mfma_prefix<128>(key.group); break;
-        default: break;
-      }
-    }
-  }
   if (!kern) return hipErrorInvalidValue;
   if (groups <= 0) return hipSuccess;
   if (groups > 0x7fffffff) return hipErrorInvalidValue;
