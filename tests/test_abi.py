@@ -205,3 +205,29 @@ def test_planned_and_append_reject_before_launch():
                                 None) == 0
     assert lib.pa_append_tokens_e4m3(d, d, d, d, d, d, d, 4, 8, 8, 128, 16, 10,
                                      ctypes.c_float(0.0), ctypes.c_float(1.0), None) == 1
+
+
+def test_binding_and_torch_share_one_hip_runtime():
+    """libpa.so takes whichever HIP runtime the process has loaded; torch
+    ships its own copy, which owns the tensors' memory and streams. The
+    binding loads torch first, so a process that calls lib() before using
+    torch still maps exactly one HIP runtime (loading libpa.so before torch
+    maps two, and torch's pointers then mean nothing to libpa's)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        "import paged_kv_cache_343_amd as P\n"
+        "P.lib()\n"
+        "assert 'torch' in sys.modules\n"
+        "paths = set()\n"
+        "for line in open('/proc/self/maps'):\n"
+        "    f = line.split()\n"
+        "    if len(f) >= 6 and 'libamdhip64' in f[5]:\n"
+        "        paths.add(f[5])\n"
+        "print(len(paths))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1"
