@@ -12,8 +12,9 @@ fixed step per position:
   second chunk or so, and exponents up to 2^8 pile up in between.
 
 Decode at 1, 4 and 8 query heads per KV head (the decode kernel and the
-per-tile kernel, split partitions and not) and multi-token chunks (the
-per-tile and the workgroup-tiled kernels) against the float64 oracle under
+per-tile kernel, split partitions and not), decode over 8-bit pools, and
+multi-token chunks (the per-tile and the workgroup-tiled kernels) against the
+float64 oracle under
 the bf16 tolerance. The math is ordinary attention ("Walk through paged
 attention end to end ...", single-decode-step pseudo-code and "Red flags")."""
 import math
@@ -104,3 +105,31 @@ def test_multi_query_rising_scores(dev, ramp, hq, hkv, tq, split):
     got = O.as_f64(to_storage_np(out), "bf16")
     assert np.isfinite(got).all()
     check_close(got, ref, "bf16", f"multi-query {ramp} tq {tq} split {split}")
+
+
+@pytest.mark.parametrize("ramp", sorted(RAMPS))
+def test_decode_e4m3_rising_scores(dev, ramp):
+    """The same over 8-bit pools: key dimension 0 holds the E4M3 code of
+    slope * p / k_scale (the oracle's quantizer; other dimensions small random
+    codes), so the scores climb in the format's coarse steps."""
+    hq, hkv, bs, lens = 32, 8, 16, [1, 17, 300, 513, 1100, 2048]
+    c = _ramp_case(dev, hq, hkv, bs, lens, RAMPS[ramp], 421)
+    c.oq = _ramp_queries((len(lens), hq, 128), 422)
+    c.q = to_device(c.oq, "bf16", dev)
+    rng = np.random.default_rng(423)
+    ks, vs = 16.0, 0.11
+    kc = O.quantize_e4m3(O.as_f64(c.ok_pool, "bf16").astype(np.float32), ks)
+    vc = W.random_e4m3_codes((c.nb, hkv, bs, 128), rng)
+    # the slope's codes in dimension 0 (max 448 * 16 = 7168), small codes elsewhere
+    small = W.random_e4m3_codes((c.nb, hkv, bs, 128), rng) & np.uint8(0x9F)
+    kc[..., 1:] = small[..., 1:]
+    out = torch.full_like(c.q, float("nan"))
+    P.pa_decode_e4m3(c.q, torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev), c.tables,
+                     c.lens, c.scale, ks, vs, out, max_seq_len=c.max_len)
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    ref = O.decode(O.as_f64(c.oq, "bf16"), O.dequantize_e4m3(kc, ks), O.dequantize_e4m3(vc, vs),
+                   c.otables, c.olens, c.scale)
+    got = O.as_f64(to_storage_np(out), "bf16")
+    assert np.isfinite(got).all()
+    check_close(got, ref, "bf16", f"e4m3 decode {ramp}")
