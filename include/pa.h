@@ -523,6 +523,12 @@ pa_status_t pa_device_errors(uint32_t* flags, void* stream);
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_str(pa_status_t status);
 
+/* Name of the HIP error behind the calling thread's most recent PA_EHIP
+ * (hipGetErrorName; static storage), "hipSuccess" if the thread has had
+ * none. Diagnostic only: a failed HIP call leaves the operation's outputs
+ * undefined whatever its name. */
+const char* pa_last_hip_error(void);
+
 /* ------------------------------------------------------------------------
  * Host block manager: free pool, block tables, reference counts, fork and
  * copy-on-write decisions. Host memory only, no GPU calls, not thread-safe.

@@ -55,7 +55,7 @@ EXPORTED_SYMBOLS = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partition", "pa_decode_reduce",
     "pa_decode_noalloc",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_device_errors",
-    "pa_status_str", "pa_multi_query", "pa_multi_query_workspace_bytes",
+    "pa_status_str", "pa_last_hip_error", "pa_multi_query", "pa_multi_query_workspace_bytes",
     "pa_multi_query_split", "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
     "pa_decode_e4m3", "pa_decode_partition_e4m3",
     "pa_reshape_and_cache_e4m3",
@@ -72,7 +72,11 @@ class PaError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
         self.name = _STATUS.get(status, str(status))
-        super().__init__(f"{what}: {self.name}" if what else self.name)
+        msg = f"{what}: {self.name}" if what else self.name
+        if self.name == "PA_EHIP" and _lib is not None:
+            # the HIP error behind it (the calling thread's most recent one)
+            msg += f" ({_lib.pa_last_hip_error().decode()})"
+        super().__init__(msg)
 
 
 class DecodeShape(ctypes.Structure):
@@ -127,6 +131,7 @@ _SIGS = {
                                          ctypes.c_float, ctypes.c_float, _vp]),
     "pa_device_errors": (_i32, [ctypes.POINTER(ctypes.c_uint32), _vp]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
+    "pa_last_hip_error": (ctypes.c_char_p, []),
     "pa_bm_create": (_i32, [_i32, _i32, _vp, ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_seq": (_i32, [_vp, _i32, _i32]),

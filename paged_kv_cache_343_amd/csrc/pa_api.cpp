@@ -158,7 +158,14 @@ pa_status_t fill_args(const void* q, const void* k_pool, const void* v_pool,
   return PA_OK;
 }
 
-pa_status_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+// The HIP error behind the calling thread's most recent PA_EHIP.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+pa_status_t from_hip(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  g_last_hip_error = e;
+  return PA_EHIP;
+}
 
 }  // namespace
 
@@ -444,14 +451,15 @@ std::mutex g_scratch_mu;
 // Device address of the current device's `scratch`.
 pa_status_t scratch_address(void** addr) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return PA_EHIP;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return from_hip(e);
   if (dev < 0 || dev >= kMaxScratchDevices) return PA_EUNSUPPORTED;
   void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
   if (!p) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     p = g_scratch_addr[dev].load(std::memory_order_relaxed);
     if (!p) {
-      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_EHIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return from_hip(e != hipSuccess ? e : hipErrorInvalidSymbol);
       g_scratch_addr[dev].store(p, std::memory_order_release);
     }
   }
@@ -942,9 +950,11 @@ pa_status_t pa_device_errors(uint32_t* flags, void* stream) {
   if (!flags) return PA_EINVAL;
   *flags = 0;
   hipError_t e = pa::read_and_clear_errors(flags, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return PA_EHIP;
+  if (e != hipSuccess) return from_hip(e);
   return *flags ? PA_EDEVICE : PA_OK;
 }
+
+const char* pa_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
 
 const char* pa_status_str(pa_status_t status) {
   switch (status) {

@@ -231,3 +231,21 @@ def test_binding_and_torch_share_one_hip_runtime():
                        timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_last_hip_error_names_the_failure():
+    """PA_EHIP keeps the HIP error behind it for the calling thread: on a
+    machine without a GPU, reading the device error word fails with
+    hipErrorNoDevice, and the binding's exception names it. (Host only; on a
+    GPU machine the call succeeds and the test has nothing to check.)"""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call does not fail")
+    L = P.lib()
+    flags = ctypes.c_uint32(0)
+    st = L.pa_device_errors(ctypes.byref(flags), None)
+    assert st == 6                                     # PA_EHIP
+    name = L.pa_last_hip_error().decode()
+    assert name.startswith("hipError") and name != "hipSuccess"
+    with pytest.raises(P.PaError, match=name):
+        P._check(st, "pa_device_errors")
