@@ -743,6 +743,7 @@ def run_workload(args, torch, P, W, dev, side_rows=True) -> dict:
             "n2_multi_query": multi_query_rate(P, torch, dev, W),
             "decode_group8": group8_decode_rate(P, torch, dev, W),
             "n3_swap_blocks": swap_rate(P, torch, dev),
+            "mfma_valu_overlap": mfma_valu_overlap(torch, dev),
         })
         peak = stream_read_peak(torch, dev)
         result["practical_peak"] = dict(peak, partition_frac=round(achieved / peak["GBps"], 4),
@@ -916,6 +917,51 @@ def stream_read_peak(torch, dev) -> dict:
     return {"GBps": sweep[best], "bytes": nbytes, "kernel": "pa_probe_stream_read",
             "best_launch": best, "random_4k_GBps": sweep[rnd], "random_4k_best_launch": rnd,
             "sweep_GBps": sweep}
+
+
+OVERLAP_MODES = {0: "mfma_only", 1: "fma_only", 2: "both_in_every_wave",
+                 3: "mfma_waves_beside_fma_waves", 4: "mfma_one_chain", 5: "exp2_only"}
+
+
+def mfma_valu_overlap(torch, dev) -> dict:
+    """How far matrix-core and vector work overlap on one SIMD: the overlap
+    probe of libpa_probe.so (16 independent v_mfma_f32_16x16x32_bf16 and/or
+    64 fp32 FMAs per iteration, by mode), 1024 workgroups of 8 waves x 2000
+    iterations (8 waves per SIMD), 5 timed launches per mode. Reported per
+    mode: milliseconds, and SIMD cycles at 2.4 GHz per iteration of the
+    waves that run it. The two ratios compare running both kinds of work
+    against running them one after the other (1.0: no overlap, 0.5: full
+    overlap of equal halves)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_343_amd", "libpa_probe.so"))
+    lib.pa_probe_mfma_valu.restype = ctypes.c_int
+    lib.pa_probe_mfma_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    grid, iters = 1024, 2000
+    out = torch.empty(grid * 512, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    wave_iters = grid * 8 * iters / 1024            # per SIMD (1024 SIMDs)
+    res = {}
+    for mode, name in OVERLAP_MODES.items():
+        args = (mode, grid, iters, out.data_ptr(), s)
+        if lib.pa_probe_mfma_valu(*args):
+            raise RuntimeError("overlap probe launch failed")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            lib.pa_probe_mfma_valu(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        waves = wave_iters / 2 if mode == 3 else wave_iters
+        res[name] = {"ms": round(ms, 3),
+                     "simd_cycles_per_iteration": round(ms * 1e-3 * 2.4e9 / waves, 1)}
+    m, f = res["mfma_only"]["ms"], res["fma_only"]["ms"]
+    res["both_in_every_wave_vs_serial"] = round(res["both_in_every_wave"]["ms"] / (m + f), 3)
+    # mode 3 does half of each kind of work
+    res["beside_vs_serial"] = round(res["mfma_waves_beside_fma_waves"]["ms"] / ((m + f) / 2), 3)
+    del out
+    return res
 
 
 def copy_blocks_rate(P, torch, dev) -> dict:

@@ -20,6 +20,18 @@
  * written only if the folded data equal a sentinel (keeps the reads live).
  * Returns 0, 1 for a bad argument (nothing enqueued), 6 if the launch
  * failed.
+ *
+ * pa_probe_mfma_valu: enqueues `workgroups` workgroups of 8 waves on
+ * `stream`; each wave runs `iters` iterations of matrix-core work (16
+ * independent v_mfma_f32_16x16x32_bf16 on four accumulators) and/or vector
+ * work (64 fp32 FMAs on eight independent chains), by `mode`: 0 MFMAs only,
+ * 1 FMAs only, 2 both in every wave, interleaved, 3 waves 0-3 MFMAs and
+ * waves 4-7 FMAs (one wave of each kind per SIMD), 4 MFMAs only as one
+ * dependent chain, 5 16 exp2 per iteration only. Timing the modes shows how
+ * far the two kinds of work overlap on one SIMD. `out` [dev] float
+ * [workgroups * 512] receives one value per thread (keeps the work live).
+ * Returns 0, 1 for a bad argument (nothing enqueued), 6 if the launch
+ * failed.
  */
 #ifndef PA_PROBE_H
 #define PA_PROBE_H
@@ -32,6 +44,7 @@ extern "C" {
 
 int pa_probe_stream_read(const void* buf, size_t bytes, int workgroups, int loads_per_lane,
                          int nontemporal, int pattern, void* sink, void* stream);
+int pa_probe_mfma_valu(int mode, int workgroups, int iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

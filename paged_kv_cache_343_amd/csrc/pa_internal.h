@@ -144,6 +144,8 @@ struct MqArgs {
   // (sequence, partition, length, 0), one wave each; null otherwise
   const int32_t* plan;
   int32_t num_units;
+  // workgroup-tiled multi-token kernel: this call's ticket (set by its launcher)
+  uint64_t fa_ticket;
 };
 
 // When the caller asks for bf16 partials (part_half), the decode kernels

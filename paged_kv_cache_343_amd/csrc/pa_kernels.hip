@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "pa_internal.h"
@@ -64,6 +65,7 @@ __device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_wor
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -1424,6 +1426,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
 }
 
+// Two floats as an fp16 pair (round to nearest even), low element first.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+  const f32x2v_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2v_t));
+}
+
 // p as two bf16 terms hi + lo (lo = the bf16 rounding of p - hi), 8 values
 // per operand: ~16 significant bits instead of bf16's 8.
 __device__ __forceinline__ void split_bf16x8(const float (&p)[8], uint4& hi, uint4& lo) {
@@ -1915,9 +1925,10 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
 // S^T product leaves lane (R, c) the scores of row c at positions 4R .. 4R+3
 // of the slice; with the two slices of a 32-position step these are exactly
 // the lane's 8 k-slots (8R .. 8R+7) of the P.V step, so P goes from the
-// softmax to the matrix cores without leaving the lane (as two bf16 terms,
-// p = hi + lo, for ~16 significant bits). The next block's K/V loads are
-// issued before the current block is computed. Workgroup ids: every tile of
+// softmax to the matrix cores without leaving the lane: in fp16, with V^T
+// staged in fp16 (11 significant bits, 8x finer than bf16), or, on the exact
+// pass, as two bf16 terms p = hi + lo (~16 significant bits) against bf16 V^T.
+// The next block's K/V loads are issued before the current block is computed. Workgroup ids: every tile of
 // one (sequence, KV head) lands on the same XCD (XCD = id % 8), so the tiles
 // share that XCD's L2 copy of the context; heavier (later) tiles first.
 constexpr int kFaRows = 128;     // query rows per workgroup
@@ -1937,14 +1948,19 @@ __device__ __forceinline__ int fa_vt_slot(int j) {
   return 32 * half + 8 * R + 4 * h + r;
 }
 
-template <int BS, int G>
-__global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
+typedef uint16_t FaKStage[kFaPos][kFaKRow];
+typedef uint16_t FaVtStage[128][kFaVRow];
+
+// One workgroup's tile. F16: P and V^T in fp16 on v_mfma_f32_16x16x32_f16;
+// returns false (and writes nothing) when some V value of the tile's context
+// is at least 2^16 in magnitude or infinite, which fp16 cannot hold. Otherwise
+// P as two bf16 terms on the bf16 matrix product, for any input.
+template <int BS, int G, bool F16>
+__device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s_kb, FaVtStage* s_vtb) {
   constexpr int D = 128, ROW = 256;
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS % 16 == 0 && kFaRows % (2 * 16) == 0 && 16 % G == 0,
                 "whole 4-position groups per block, whole tokens per 16-row tile");
-  __shared__ __align__(16) uint16_t s_kb[kFaBufs][kFaPos][kFaKRow];
-  __shared__ __align__(16) uint16_t s_vtb[kFaBufs][D][kFaVRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1956,7 +1972,7 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
   const int id = blockIdx.x, x = id & 7, rr = id >> 3;
   const int tile = ntiles - 1 - rr % ntiles;
   const int pair = (rr / ntiles) * 8 + x;
-  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  if (pair >= a.num_seqs * a.num_kv_heads) return true;
   const int g = pair % a.num_kv_heads, i = pair / a.num_kv_heads;
 
   // validate the sequence's length and query range (device-resident)
@@ -1966,11 +1982,11 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
   if (L < 0 || L > a.len_cap || q0 < 0 || q1 > a.num_tokens || tq < 0 || tq > L ||
       tq > a.max_query_len) {
     if (tid == 0 && g == 0 && tile == ntiles - 1) flag_error(kErrQuery);
-    return;
+    return true;
   }
   const int rows = tq * G;
   const int row0 = tile * kFaRows;
-  if (row0 >= rows) return;
+  if (row0 >= rows) return true;
   const int t_last = min(tq - 1, (row0 + kFaRows - 1) / G);
   const int npos = L - tq + t_last + 1;          // positions the tile's last token sees
   const int nblk = (npos + kFaPos - 1) / kFaPos;
@@ -2051,6 +2067,9 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
       }
     }
   };
+  // V^T is staged as loaded (bf16, two-term path) or converted to fp16
+  // (round to nearest: exact for every bf16 value below 2^16 in magnitude,
+  // larger ones become infinite)
   auto stage = [&](int buf) {
     uint16_t(*s_k)[kFaKRow] = s_kb[buf];
     uint16_t(*s_vt)[kFaVRow] = s_vtb[buf];
@@ -2064,205 +2083,292 @@ __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // dims 8 dv + 2e (low halves) and + 2e + 1 (high halves) of positions 0..3
-      const uint2 lo = make_uint2(pack_low_halves(v0[e], v1[e]), pack_low_halves(v2[e], v3[e]));
-      const uint2 hi = make_uint2(pack_high_halves(v0[e], v1[e]), pack_high_halves(v2[e], v3[e]));
+      uint2 lo, hi;
+      if constexpr (F16) {
+        const float a0 = __uint_as_float(v0[e] << 16), a1 = __uint_as_float(v1[e] << 16);
+        const float a2 = __uint_as_float(v2[e] << 16), a3 = __uint_as_float(v3[e] << 16);
+        const float b0 = __uint_as_float(v0[e] & 0xffff0000u), b1 = __uint_as_float(v1[e] & 0xffff0000u);
+        const float b2 = __uint_as_float(v2[e] & 0xffff0000u), b3 = __uint_as_float(v3[e] & 0xffff0000u);
+        lo = make_uint2(pack_f16x2(a0, a1), pack_f16x2(a2, a3));
+        hi = make_uint2(pack_f16x2(b0, b1), pack_f16x2(b2, b3));
+      } else {
+        lo = make_uint2(pack_low_halves(v0[e], v1[e]), pack_low_halves(v2[e], v3[e]));
+        hi = make_uint2(pack_high_halves(v0[e], v1[e]), pack_high_halves(v2[e], v3[e]));
+      }
       *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e][slot]) = lo;
       *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e + 1][slot]) = hi;
     }
   };
 
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
-  f32x4_t acc[2][8];
+  {
+    // fp16 weights carry a factor 2^7 (the largest, 2^kLazyMax, becomes 2^15)
+    // so that weights down to 2^-21 of the reference stay normal numbers; the
+    // factor cancels in O / l
+    constexpr float kPBias = F16 ? 7.0f : 0.0f;
+    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+    f32x4_t acc[2][8];
+    // fp16 path: the row sums of P come from the matrix cores too, as P times
+    // a column of ones; lane (R, c) holds the sums of rows 4R .. 4R+3, like
+    // the output accumulators
+    f32x4_t acc_l[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
+      acc_l[rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  int idk, idv;
-  block_ids(0, idk, idv);
-  fetch(0, idk, idv);
-  if (nblk > 1) block_ids(1, idk, idv);
-#if PA_FA_BUFS == 2
-  // two LDS buffers: block b + 1 is staged while others may still compute
-  // block b, so one barrier per block suffices
-  stage(0);
-  if (nblk > 1) {
-    fetch(1, idk, idv);
-    if (nblk > 2) block_ids(2, idk, idv);
-  }
-  __syncthreads();
-#endif
-  for (int blk = 0; blk < nblk; ++blk) {
-#if PA_FA_BUFS == 2
-    const uint16_t(*s_k)[kFaKRow] = s_kb[blk & 1];
-    const uint16_t(*s_vt)[kFaVRow] = s_vtb[blk & 1];
-#else
-    if (blk > 0) __syncthreads();          // every wave is done with the previous block
-    stage(0);
-    __syncthreads();
-    if (blk + 1 < nblk) {
-      fetch(blk + 1, idk, idv);
-      if (blk + 2 < nblk) block_ids(blk + 2, idk, idv);
+      for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    const uint16_t(*s_k)[kFaKRow] = s_kb[0];
-    const uint16_t(*s_vt)[kFaVRow] = s_vtb[0];
-#endif
-    const int p0 = blk * kFaPos;
+    const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
-    // S^T for the block: sc[rt][sl] = scores of row c (tile rt) at positions
-    // p0 + 16 sl + 4R + r
-    f32x4_t sc[2][4];
+    int idk, idv;
+    block_ids(0, idk, idv);
+    fetch(0, idk, idv);
+    if (nblk > 1) block_ids(1, idk, idv);
+#if PA_FA_BUFS == 2
+    // two LDS buffers: block b + 1 is staged while others may still compute
+    // block b, so one barrier per block suffices
+    stage(0);
+    if (nblk > 1) {
+      fetch(1, idk, idv);
+      if (nblk > 2) block_ids(2, idk, idv);
+    }
+    __syncthreads();
+#endif
+    for (int blk = 0; blk < nblk; ++blk) {
+#if PA_FA_BUFS == 2
+      const uint16_t(*s_k)[kFaKRow] = s_kb[blk & 1];
+      const uint16_t(*s_vt)[kFaVRow] = s_vtb[blk & 1];
+#else
+      if (blk > 0) __syncthreads();          // every wave is done with the previous block
+      stage(0);
+      __syncthreads();
+      if (blk + 1 < nblk) {
+        fetch(blk + 1, idk, idv);
+        if (blk + 2 < nblk) block_ids(blk + 2, idk, idv);
+      }
+      const uint16_t(*s_k)[kFaKRow] = s_kb[0];
+      const uint16_t(*s_vt)[kFaVRow] = s_vtb[0];
+#endif
+      const int p0 = blk * kFaPos;
+
+      // S^T for the block: sc[rt][sl] = scores of row c (tile rt) at positions
+      // p0 + 16 sl + 4R + r
+      f32x4_t sc[2][4];
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      bf16x8_t kop[4];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-        kop[s2] = __builtin_bit_cast(bf16x8_t,
-                                     *reinterpret_cast<const uint4*>(&s_k[16 * sl + c][8 * R + 32 * s2]));
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        sc[rt][sl] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sl = 0; sl < 4; ++sl) {
+        bf16x8_t kop[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2)
-          sc[rt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s2], qop[rt][s2], sc[rt][sl], 0, 0, 0);
+          kop[s2] = __builtin_bit_cast(bf16x8_t,
+                                       *reinterpret_cast<const uint4*>(&s_k[16 * sl + c][8 * R + 32 * s2]));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          sc[rt][sl] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            sc[rt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s2], qop[rt][s2], sc[rt][sl], 0, 0, 0);
+        }
       }
-    }
-    uint4 phi[2][2], plo[2][2];                 // [rt][32-position step]
-    bool rescale = false;
-    float alpha[2];
-    // the softmax of the block's scores, with a per-position mask (kMasked:
-    // the block reaches past some row's last position) or without
-    auto softmax = [&](auto masked_tag) {
-      constexpr bool kMasked = decltype(masked_tag)::value;
+      uint4 phi[2][2], plo[2][2];                 // [rt][32-position step]
+      bool rescale = false;
+      float alpha[2];
+      // the softmax of the block's scores, with a per-position mask (kMasked:
+      // the block reaches past some row's last position) or without
+      auto softmax = [&](auto masked_tag) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        // scores stay unscaled until the exponent: qs >= 0 (a negative scale
-        // was folded into q's sign), so the row maximum scales with them
-        float bm = -INFINITY;
-        if constexpr (kMasked) {
+        for (int rt = 0; rt < 2; ++rt) {
+          // scores stay unscaled until the exponent: qs >= 0 (a negative scale
+          // was folded into q's sign), so the row maximum scales with them
+          float bm = -INFINITY;
+          if constexpr (kMasked) {
 #pragma unroll
-          for (int sl = 0; sl < 4; ++sl)
+            for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              bm = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? fmaxf(bm, sc[rt][sl][r]) : bm;
-        } else {
-          float b0 = -INFINITY, b1 = -INFINITY;
+              for (int r = 0; r < 4; ++r)
+                bm = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? fmaxf(bm, sc[rt][sl][r]) : bm;
+          } else {
+            float b0 = -INFINITY, b1 = -INFINITY;
 #pragma unroll
-          for (int sl = 0; sl < 4; sl += 2) {
-            b0 = max3f(b0, sc[rt][sl][0], sc[rt][sl][1]);
-            b0 = max3f(b0, sc[rt][sl][2], sc[rt][sl][3]);
-            b1 = max3f(b1, sc[rt][sl + 1][0], sc[rt][sl + 1][1]);
-            b1 = max3f(b1, sc[rt][sl + 1][2], sc[rt][sl + 1][3]);
+            for (int sl = 0; sl < 4; sl += 2) {
+              b0 = max3f(b0, sc[rt][sl][0], sc[rt][sl][1]);
+              b0 = max3f(b0, sc[rt][sl][2], sc[rt][sl][3]);
+              b1 = max3f(b1, sc[rt][sl + 1][0], sc[rt][sl + 1][1]);
+              b1 = max3f(b1, sc[rt][sl + 1][2], sc[rt][sl + 1][3]);
+            }
+            bm = fmaxf(b0, b1);
           }
-          bm = fmaxf(b0, b1);
-        }
-        bm = fmaxf(bm, xor_lanes<16>(bm));
-        bm = fmaxf(bm, xor_lanes<32>(bm));
-        // lazy reference maximum (kLazyMax): rows rarely need rescaling
-        // after the first block
-        const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
-        const float mn = bms > m[rt] + kLazyMax ? bms : m[rt];
-        alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
-        rescale |= alpha[rt] != 1.0f;
-        m[rt] = mn;
-        float p[16], ps = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[4 * sl + r] = exp2_fast(fmaf(sc[rt][sl][r], qs, -mn));
-        if constexpr (kMasked) {
-          // masked positions (and every position while the row has none) get 0
+          bm = fmaxf(bm, xor_lanes<16>(bm));
+          bm = fmaxf(bm, xor_lanes<32>(bm));
+          // lazy reference maximum (kLazyMax): rows rarely need rescaling
+          // after the first block
+          const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
+          const float mn = bms > m[rt] + kLazyMax ? bms : m[rt];
+          alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
+          rescale |= alpha[rt] != 1.0f;
+          m[rt] = mn;
+          const float mo = kPBias - mn;
+          float p[16];
 #pragma unroll
           for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              p[4 * sl + r] = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? p[4 * sl + r] : 0.0f;
-        }
+            for (int r = 0; r < 4; ++r) p[4 * sl + r] = exp2_fast(fmaf(sc[rt][sl][r], qs, mo));
+          if constexpr (kMasked) {
+            // masked positions (and every position while the row has none) get 0
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ps += p[e];
-        lsum[rt] = lsum[rt] * alpha[rt] + ps;
+            for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                p[4 * sl + r] = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? p[4 * sl + r] : 0.0f;
+          }
+          if constexpr (!F16) {
+            float ps = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ps += p[e];
+            lsum[rt] = lsum[rt] * alpha[rt] + ps;
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            // k-slots 8R + 4h + r <- position 32 st + 16 h + 4R + r = p[4 (2 st + h) + r]
+            const float* f = p + 8 * st;
+            if constexpr (F16) {
+              phi[rt][st] = make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
+                                       pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7]));
+            } else {
+              uint32_t hb[4], lb[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+                lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
+                                    f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+              }
+              phi[rt][st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+              plo[rt][st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+            }
+          }
+        }
+      };
+      // no position of the block is masked for this wave
+      if (p0 + kFaPos <= vis_w)
+        softmax(std::false_type{});
+      else
+        softmax(std::true_type{});
+      // rescale output rows 4R + r of each tile by their rows' alpha (row c's
+      // alpha sits in lane c); skipped when no row's maximum moved
+      if (__ballot(rescale) != 0) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha[rt], 4 * R + r);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[rt][t][r] *= ar;
+            if constexpr (F16) acc_l[rt][r] *= ar;
+          }
+      }
+      // O += P V over 8 tiles of 16 dims and two 32-position steps
+      if constexpr (F16) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            acc_l[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, phi[rt][st]),
+                                                               ones, acc_l[rt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          // k-slots 8R + 4h + r <- position 32 st + 16 h + 4R + r = p[4 (2 st + h) + r]
-          float f[8];
+          const uint4 vb = *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = p[8 * st + e];
-          uint32_t hb[4], lb[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-            lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
-                                f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+          for (int rt = 0; rt < 2; ++rt) {
+            if constexpr (F16) {
+              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(f16x8_t, phi[rt][st]), __builtin_bit_cast(f16x8_t, vb), acc[rt][t],
+                  0, 0, 0);
+            } else {
+              const bf16x8_t vbb = __builtin_bit_cast(bf16x8_t, vb);
+              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, phi[rt][st]), vbb, acc[rt][t], 0, 0, 0);
+              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, plo[rt][st]), vbb, acc[rt][t], 0, 0, 0);
+            }
           }
-          phi[rt][st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-          plo[rt][st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+        }
+#if PA_FA_BUFS == 2
+      if (blk + 1 < nblk) {
+        // every wave finished block b - 1 before the barrier that ended it, so
+        // its buffer ((b + 1) & 1) is free
+        stage((blk + 1) & 1);
+        if (blk + 2 < nblk) {
+          fetch(blk + 2, idk, idv);
+          if (blk + 3 < nblk) block_ids(blk + 3, idk, idv);
         }
       }
-    };
-    // no position of the block is masked for this wave
-    if (p0 + kFaPos <= vis_w)
-      softmax(std::false_type{});
-    else
-      softmax(std::true_type{});
-    // rescale output rows 4R + r of each tile by their rows' alpha (row c's
-    // alpha sits in lane c); skipped when no row's maximum moved
-    if (__ballot(rescale) != 0) {
+      __syncthreads();
+#endif
+    }
+    // A V value that fp16 cannot hold became infinite at staging; every wave
+    // multiplied it into its rows (a zero weight gives 0 * inf = NaN), so some
+    // accumulator of the tile is not finite. The caller then walks the tile
+    // again on the two-term bf16 path; non-finite inputs take that path too,
+    // where they give what they give there.
+    if constexpr (F16) {
+      bool bad = false;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha[rt], 4 * R + r);
+          bad |= !__builtin_isfinite(acc_l[rt][r]);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) acc[rt][t][r] *= ar;
+          for (int t = 0; t < 8; ++t) bad |= !__builtin_isfinite(acc[rt][t][r]);
         }
+      if (__syncthreads_or(bad)) return false;
     }
-    // O += P V over 8 tiles of 16 dims and two 32-position steps
+    // out[row] = O[row] / l[row]; lane holds rows 4R + r of each tile, dims 16 t + c
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8_t vb = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]));
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, phi[rt][st]), vb, acc[rt][t], 0, 0, 0);
-          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, plo[rt][st]), vb, acc[rt][t], 0, 0, 0);
-        }
+    for (int rt = 0; rt < 2; ++rt) {
+      float l = lsum[rt];
+      if constexpr (!F16) {
+        l += xor_lanes<16>(l);
+        l += xor_lanes<32>(l);
       }
-#if PA_FA_BUFS == 2
-    if (blk + 1 < nblk) {
-      // every wave finished block b - 1 before the barrier that ended it, so
-      // its buffer ((b + 1) & 1) is free
-      stage((blk + 1) & 1);
-      if (blk + 2 < nblk) {
-        fetch(blk + 2, idk, idv);
-        if (blk + 3 < nblk) block_ids(blk + 3, idk, idv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float lr = F16 ? acc_l[rt][r] : __shfl(l, 4 * R + r);
+        const int row = roww + 16 * rt + 4 * R + r;
+        if (row >= rows) continue;
+        const int t = row / G, h = row % G;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                        ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + c;
+        const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[rt][t2][r] * inv);
       }
     }
-    __syncthreads();
-#endif
   }
-  // out[row] = O[row] / l[row]; lane holds rows 4R + r of each tile, dims 16 t + c
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    float l = lsum[rt];
-    l += xor_lanes<16>(l);
-    l += xor_lanes<32>(l);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float lr = __shfl(l, 4 * R + r);
-      const int row = roww + 16 * rt + 4 * R + r;
-      if (row >= rows) continue;
-      const int t = row / G, h = row % G;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
-                      ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + c;
-      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-#pragma unroll
-      for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[rt][t2][r] * inv);
-    }
+  return true;
+}
+
+// Ticket of the latest multi-token call whose fp16 walk met a V value fp16
+// cannot hold (tickets only grow; 0: none yet), one per device.
+__device__ unsigned long long g_fa_exact_ticket;
+
+// F16: the fast pass; a tile that meets an out-of-range V value writes
+// nothing and raises the call's ticket. !F16: the exact pass, launched right
+// after on the same stream; it walks every tile again, but only when the
+// ticket shows that some fp16 tile of this call (or of a later one, which
+// costs a redundant pass and nothing else) gave up.
+template <int BS, int G, bool F16>
+__global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
+  __shared__ __align__(16) uint16_t s_kb[kFaBufs][kFaPos][kFaKRow];
+  __shared__ __align__(16) uint16_t s_vtb[kFaBufs][128][kFaVRow];
+  if constexpr (!F16) {
+    if (__hip_atomic_load(&g_fa_exact_ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+        a.fa_ticket)
+      return;
   }
+  if (!multi_query_fa_tile<BS, G, F16>(a, s_kb, s_vtb) && threadIdx.x == 0)
+    atomicMax(&g_fa_exact_ticket, a.fa_ticket);
 }
 
 }  // namespace
@@ -2457,36 +2563,44 @@ static PartitionKernelMq pick_mq(int group) {
 
 bool multi_query_tiled(int group, int max_query_len);
 
-template <int BS>
+template <int BS, bool F16>
 static PartitionKernelMq pick_fa(int group) {
   switch (group) {
-    case 1: return multi_query_fa<BS, 1>;
-    case 2: return multi_query_fa<BS, 2>;
-    case 4: return multi_query_fa<BS, 4>;
-    case 8: return multi_query_fa<BS, 8>;
-    case 16: return multi_query_fa<BS, 16>;
+    case 1: return multi_query_fa<BS, 1, F16>;
+    case 2: return multi_query_fa<BS, 2, F16>;
+    case 4: return multi_query_fa<BS, 4, F16>;
+    case 8: return multi_query_fa<BS, 8, F16>;
+    case 16: return multi_query_fa<BS, 16, F16>;
     default: return nullptr;
   }
 }
 
+// process-wide source of the tickets of multi-token calls on the tiled path
+static std::atomic<unsigned long long> g_fa_tickets{0};
+
 hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hipStream_t stream) {
   if (multi_query_tiled(group, args.max_query_len)) {
     // many rows per (sequence, KV head): workgroup tiles sharing staged K/V
-    PartitionKernelMq kern = nullptr;
+    PartitionKernelMq kern = nullptr, exact = nullptr;
     switch (block_size) {
-      case 16: kern = pick_fa<16>(group); break;
-      case 32: kern = pick_fa<32>(group); break;
-      case 64: kern = pick_fa<64>(group); break;
-      case 128: kern = pick_fa<128>(group); break;
+      case 16: kern = pick_fa<16, true>(group); exact = pick_fa<16, false>(group); break;
+      case 32: kern = pick_fa<32, true>(group); exact = pick_fa<32, false>(group); break;
+      case 64: kern = pick_fa<64, true>(group); exact = pick_fa<64, false>(group); break;
+      case 128: kern = pick_fa<128, true>(group); exact = pick_fa<128, false>(group); break;
       default: break;
     }
-    if (!kern) return hipErrorInvalidValue;
+    if (!kern || !exact) return hipErrorInvalidValue;
     const int64_t tiles = ((int64_t)args.max_query_len * group + kFaRows - 1) / kFaRows;
     const int64_t pairs = (int64_t)args.num_seqs * args.num_kv_heads;
     if (pairs <= 0) return hipSuccess;
     const int64_t gx = 8 * tiles * ((pairs + 7) / 8);
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), 0, stream, args);
+    MqArgs a = args;
+    a.fa_ticket = ++g_fa_tickets;
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(exact, dim3((unsigned)gx), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   hipError_t e = launch_multi_query_tiles(block_size, group, args, stream);

@@ -16,6 +16,15 @@
 // The words are folded into a value that is stored only if it matches a
 // sentinel, so the reads cannot be dropped and nothing but the reads touches
 // memory.
+//
+// A second probe times how far matrix-core and vector work overlap on one
+// SIMD: workgroups of 8 waves repeat, per iteration, 16 independent
+// v_mfma_f32_16x16x32_bf16 (four accumulators) and/or 64 dependent-in-eights
+// fp32 FMAs, in these modes:
+//   0 MFMAs only; 1 FMAs only; 2 both in every wave, interleaved;
+//   3 waves 0-3 MFMAs and waves 4-7 FMAs (one of each kind per SIMD);
+//   4 MFMAs only, one dependent chain; 5 16 exp2 per iteration only.
+// Each thread stores one float at the end; nothing else touches memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -114,6 +123,60 @@ __global__ __launch_bounds__(256) void random_tile_kernel(const u32x4_t* __restr
   if (x == 0x9e3779b9u) sink[0] = x;
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+__global__ __launch_bounds__(512) void overlap_kernel(float* out, int iters) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(lane * 0.001f + i);
+    b[i] = (__bf16)(w * 0.01f + i * 0.5f);
+  }
+  f32x4_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = lane * 0.01f + i;
+  const bool do_m = MODE == 0 || MODE == 4 || (MODE == 3 && w < 4);
+  const bool do_v = MODE == 1 || (MODE == 3 && w >= 4);
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j & 3], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[(4 * j + v) & 7] = fmaf(x[(4 * j + v) & 7], 1.0001f, 0.5f);
+      }
+    } else {
+      if (do_m) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int k = MODE == 4 ? 0 : (j & 3);
+          acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[k], 0, 0, 0);
+        }
+      }
+      if (do_v) {
+#pragma unroll
+        for (int v = 0; v < 64; ++v) x[v & 7] = fmaf(x[v & 7], 1.0001f, 0.5f);
+      }
+      if constexpr (MODE == 5) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v & 7] = __builtin_amdgcn_exp2f(x[v & 7]);
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = s;
+}
+
 using ProbeKernel = void (*)(const u32x4_t*, size_t, uint32_t*);
 
 template <bool NT>
@@ -147,5 +210,23 @@ extern "C" int pa_probe_stream_read(const void* buf, size_t bytes, int workgroup
   hipLaunchKernelGGL(kern, dim3((unsigned)workgroups), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4_t*>(buf),
                      bytes / 16, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// out: workgroups * 512 floats.
+extern "C" int pa_probe_mfma_valu(int mode, int workgroups, int iters, float* out, void* stream) {
+  if (!out || workgroups <= 0 || iters <= 0) return 1;
+  void (*kern)(float*, int) = nullptr;
+  switch (mode) {
+    case 0: kern = overlap_kernel<0>; break;
+    case 1: kern = overlap_kernel<1>; break;
+    case 2: kern = overlap_kernel<2>; break;
+    case 3: kern = overlap_kernel<3>; break;
+    case 4: kern = overlap_kernel<4>; break;
+    case 5: kern = overlap_kernel<5>; break;
+    default: return 1;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)workgroups), dim3(512), 0,
+                     static_cast<hipStream_t>(stream), out, iters);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }

@@ -7,7 +7,7 @@ import torch
 import paged_kv_cache_343_amd as P
 import workloads as W
 from oracle import pa_oracle as O
-from tests.paged_case import build, check_close, to_device, to_storage_np
+from tests.paged_case import TOL, build, check_close, to_device, to_storage_np
 
 pytestmark = pytest.mark.gpu
 
@@ -170,3 +170,117 @@ def test_split_context_skips_bad_ranges(dev):
     torch.cuda.synchronize()
     assert P.pa_device_errors() == P.PA_DEVERR_QUERY
     assert torch.count_nonzero(out2[4:49]) == 0
+
+
+def _tiled_case(dev, seed, lens, tqs):
+    w = W.Workload("mq", seed, 0, 32, 8, 128, 16, "bf16", ("fixed", 0), ("factor", 1.3))
+    c = build(w, dev, lens=lens, append=False)
+    rng = np.random.default_rng(seed + 1)
+    qs = np.concatenate([[0], np.cumsum(tqs)]).astype(np.int32)
+    return c, rng, qs
+
+
+def _run_tiled(dev, c, q_np, qs, kp, vp, tag):
+    """pa_multi_query with 4 query heads per KV head and chunks of >= 32 tokens
+    (>= 128 rows per KV head: the workgroup-tiled kernel) against the oracle."""
+    c.k_pool.copy_(to_device(kp, "bf16", dev)); c.v_pool.copy_(to_device(vp, "bf16", dev))
+    out = torch.full((int(qs[-1]), 32, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    P.pa_multi_query(to_device(q_np, "bf16", dev), c.k_pool, c.v_pool, c.tables, c.lens,
+                     torch.from_numpy(qs).to(dev), c.scale, out, max_seq_len=c.max_len,
+                     max_query_len=int(np.diff(qs).max()))
+    torch.cuda.synchronize()
+    assert P.pa_device_errors() == 0
+    ref = O.multi_query(O.as_f64(q_np, "bf16"), O.as_f64(kp, "bf16"), O.as_f64(vp, "bf16"),
+                        c.otables, c.olens, qs, c.scale)
+    got = O.as_f64(to_storage_np(out), "bf16")
+    check_close(got, ref, "bf16", tag)
+    return got, ref
+
+
+def test_tiled_kernel_values_beyond_fp16_range(dev):
+    """The tiled kernel holds P and V in fp16 (exact for every bf16 value below
+    2^16 in magnitude). V values of 2^16 and more, here 70000, 3e6 and -1e9 in
+    one sequence's context and 1e30 in another's, send the call through the
+    exact pass (two-term bf16 P), which must still match the oracle; the next
+    call with ordinary values takes the fast pass again."""
+    lens, tqs = [300, 1100, 700], [40, 64, 33]
+    c, rng, qs = _tiled_case(dev, 331, lens, tqs)
+    q_np = W.normal_values((int(qs[-1]), 32, 128), rng, "bf16")
+    kp, vp = to_storage_np(c.k_pool).copy(), to_storage_np(c.v_pool).copy()
+    big = vp.copy()
+    vals = np.array([70000.0, 3e6, -1e9], dtype=np.float32)
+    phys, off = O.positions_to_rows(c.otables[1], lens[1], 16)
+    for j, p in enumerate([5, 600, 1090]):         # before, inside and after the chunk
+        big[phys[p], j % 8, off[p], 7 + j] = W.to_bf16_bits(vals[j:j + 1])[0]
+    phys, off = O.positions_to_rows(c.otables[2], lens[2], 16)
+    big[phys[100], 3, off[100], 0] = W.to_bf16_bits(np.array([1e30], np.float32))[0]
+    _run_tiled(dev, c, q_np, qs, kp, big, "V beyond fp16")
+    _run_tiled(dev, c, q_np, qs, kp, vp, "ordinary V after the exact pass")
+
+
+def test_tiled_kernel_keeps_tiny_weights(dev):
+    """One position 16 (log2 units) above ~1000-4000 others in every row: each
+    of the others weighs 2^-16 of it (an fp16 subnormal without the kernel's
+    2^7 scale on P), together 2-6% of the output, which differs in sign from
+    the dominant position's V."""
+    lens, tqs = [1100, 4096, 2000], [40, 64, 100]
+    c, rng, qs = _tiled_case(dev, 341, lens, tqs)
+    Q0, gap = 4.0, 16.0
+    q_np = np.zeros((int(qs[-1]), 32, 128), np.float32)
+    q_np[..., 0] = Q0
+    q_np = W.to_bf16_bits(q_np)
+    kp = np.zeros((c.nb, 8, 16, 128), np.float32)
+    vp = np.ones((c.nb, 8, 16, 128), np.float32)
+    a = gap / (Q0 * c.scale * np.log2(np.e))       # score gap of position 0, log2 units
+    a = float(O.as_f64(W.to_bf16_bits(np.array([a], np.float32)), "bf16")[0])
+    gap = Q0 * a * c.scale * np.log2(np.e)         # the gap the bf16 key carries
+    for i, L in enumerate(lens):
+        phys, off = O.positions_to_rows(c.otables[i], L, 16)
+        kp[phys[0], :, off[0], 0] = a
+        vp[phys[0], :, off[0], :] = -1.0
+    got, _ = _run_tiled(dev, c, q_np, qs, W.to_bf16_bits(kp), W.to_bf16_bits(vp), "tiny weights")
+    # the last token of the longest context: 4095 others at 2^-16 each
+    last = got[int(qs[2]) - 1, 0, 0]
+    n = lens[1] - 1
+    expect = (-1.0 + n * 2.0 ** -gap) / (1.0 + n * 2.0 ** -gap)
+    assert abs(last - expect) < 4e-3, (last, expect)
+
+
+def _tolerance_use(got, ref):
+    atol, rtol = TOL["bf16"]
+    return float((np.abs(got - ref) / (atol + rtol * np.abs(ref))).max())
+
+
+@pytest.mark.parametrize("case", ["prefill", "prefill_v4", "chunk512", "steep", "gentle"])
+def test_tiled_kernel_tolerance_margin(dev, case):
+    """The fp16 weights of the tiled kernel on the cases most sensitive to
+    them: whole prompts (rows of 1 to 200 positions), the same with V scaled
+    by 4, a 512-token chunk over 4096 positions, and scores that rise along
+    the context (steeply and gently). The worst element must use at most
+    three quarters of the tolerance (it is printed)."""
+    lens, tqs, ramp, vscale = {"prefill": ([200, 150, 64], [200, 150, 64], None, 1.0),
+                               "prefill_v4": ([200, 150], [200, 150], None, 4.0),
+                               "chunk512": ([4096, 3000], [512, 512], None, 1.0),
+                               "steep": ([700, 1500, 2100], [160] * 3, 1.5, 1.0),
+                               "gentle": ([700, 1500, 2100], [160] * 3, 0.25, 1.0)}[case]
+    c, rng, qs = _tiled_case(dev, 351, lens, tqs)
+    kp = O.as_f64(c.ok_pool, "bf16").astype(np.float32)
+    vp = O.as_f64(c.ov_pool, "bf16").astype(np.float32) * vscale
+    if ramp is None:
+        q_np = W.normal_values((int(qs[-1]), 32, 128), rng, "bf16")
+    else:
+        # key dimension 0 = slope * p, query dimension 0 = 4: the score grows
+        # by `ramp` (log2 units) per position
+        slope = ramp / (4.0 * c.scale * np.log2(np.e))
+        kp *= 0.1
+        for i, L in enumerate(lens):
+            phys, off = O.positions_to_rows(c.otables[i], L, 16)
+            kp[phys, :, off, 0] = (slope * np.arange(L))[:, None]
+        q = rng.standard_normal((int(qs[-1]), 32, 128)).astype(np.float32) * 0.1
+        q[..., 0] = 4.0
+        q_np = W.to_bf16_bits(q)
+    kb, vb = W.to_bf16_bits(kp), W.to_bf16_bits(vp)
+    got, ref = _run_tiled(dev, c, q_np, qs, kb, vb, case)
+    use = _tolerance_use(got, ref)
+    print(f"{case}: worst element uses {use:.3f} of the tolerance")
+    assert use <= 0.75, use
