@@ -352,13 +352,13 @@ typedef struct {
  * positions 0 .. p:
  *     out[row][h] = sum_{p' <= p} softmax_p'(scale * q[row][h] . K[p']) V[p']
  * With one token per sequence this is pa_decode. Both products run on the
- * matrix cores with fp32 accumulation; the weights enter P.V with at least
- * 11 significant bits. From 128 query rows per KV head (max_query_len * G
- * >= 128) the call makes two launches on `stream`: the first holds P and V
- * in fp16 (exact for bf16 values below 2^16 in magnitude); a tile whose
- * context holds a larger or non-finite V value writes nothing there, and
- * the second launch, which otherwise exits at once, redoes the call with
- * P as two bf16 terms. A sequence whose query range is invalid (Tq_i < 0,
+ * matrix cores with fp32 accumulation. From 128 query rows per KV head
+ * (max_query_len * G >= 128) the call makes two launches on `stream`: the
+ * first holds P and V in fp16 and serves the tiles whose context holds V
+ * values within +-8 only; a tile with a larger (or non-finite) V value
+ * writes nothing there, and the second launch, which otherwise exits at
+ * once, redoes the call with P as two bf16 terms (as the call takes for
+ * fewer rows). A sequence whose query range is invalid (Tq_i < 0,
  * Tq_i > seq_lens[i], > max_query_len, or past num_tokens) is skipped and
  * flagged (PA_DEVERR_QUERY).
  *

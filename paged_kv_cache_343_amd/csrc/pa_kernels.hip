@@ -66,6 +66,7 @@ __device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_wor
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -211,6 +212,12 @@ constexpr float kLazyMax = 8.0f;
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max(a, |b|, |c|) in one v_max3_f32 with absolute-value operand modifiers
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 
@@ -1926,11 +1933,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
 // of the slice; with the two slices of a 32-position step these are exactly
 // the lane's 8 k-slots (8R .. 8R+7) of the P.V step, so P goes from the
 // softmax to the matrix cores without leaving the lane: in fp16, with V^T
-// staged in fp16 (11 significant bits, 8x finer than bf16), or, on the exact
-// pass, as two bf16 terms p = hi + lo (~16 significant bits) against bf16 V^T.
-// The next block's K/V loads are issued before the current block is computed. Workgroup ids: every tile of
-// one (sequence, KV head) lands on the same XCD (XCD = id % 8), so the tiles
-// share that XCD's L2 copy of the context; heavier (later) tiles first.
+// staged in fp16 (11 significant bits, 8x finer than bf16; for tiles whose V
+// values stay within +-kFaF16VMax), or, on the exact pass, as two bf16 terms
+// p = hi + lo (~16 significant bits) against bf16 V^T. The next block's K/V
+// loads are issued before the current block is computed. Workgroup ids: every
+// tile of one (sequence, KV head) lands on the same XCD (XCD = id % 8), so the
+// tiles share that XCD's L2 copy of the context; heavier (later) tiles first.
 constexpr int kFaRows = 128;     // query rows per workgroup
 constexpr int kFaPos = 64;       // positions per block
 constexpr int kFaKRow = 136;     // bf16 elements per staged K row (128 + 8 pad)
@@ -1939,6 +1947,11 @@ constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad
 #define PA_FA_BUFS 2
 #endif
 constexpr int kFaBufs = PA_FA_BUFS;   // LDS stages of K and V^T
+// The fp16 pass serves tiles whose context holds V values within
+// +-kFaF16VMax only (its weights' rounding then moves an output by at most
+// 2^-10 * 2 * kFaF16VMax, and in practice as little as the two-term P does);
+// a tile that meets a larger value leaves it to the exact pass.
+constexpr float kFaF16VMax = 8.0f;
 
 
 // Slot of position j (0..63) of a block in a staged V^T row: inside each
@@ -1952,11 +1965,12 @@ typedef uint16_t FaKStage[kFaPos][kFaKRow];
 typedef uint16_t FaVtStage[128][kFaVRow];
 
 // One workgroup's tile. F16: P and V^T in fp16 on v_mfma_f32_16x16x32_f16;
-// returns false (and writes nothing) when some V value of the tile's context
-// is at least 2^16 in magnitude or infinite, which fp16 cannot hold. Otherwise
-// P as two bf16 terms on the bf16 matrix product, for any input.
+// returns false (and writes nothing) as soon as a staged block holds a V value
+// beyond +-kFaF16VMax (infinite ones included). Otherwise P as two bf16 terms
+// on the bf16 matrix product, for any input.
 template <int BS, int G, bool F16>
-__device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s_kb, FaVtStage* s_vtb) {
+__device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s_kb, FaVtStage* s_vtb,
+                                                    int* s_big) {
   constexpr int D = 128, ROW = 256;
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS % 16 == 0 && kFaRows % (2 * 16) == 0 && 16 % G == 0,
@@ -2068,11 +2082,13 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
     }
   };
   // V^T is staged as loaded (bf16, two-term path) or converted to fp16
-  // (round to nearest: exact for every bf16 value below 2^16 in magnitude,
-  // larger ones become infinite)
-  auto stage = [&](int buf) {
+  // (round to nearest: exact for every bf16 value below 2^16 in magnitude)
+  // stage(buf, b): block b into LDS buffer buf; on the fp16 pass a thread
+  // that staged a V value beyond +-kFaF16VMax stamps the buffer with b
+  auto stage = [&](int buf, int b) {
     uint16_t(*s_k)[kFaKRow] = s_kb[buf];
     uint16_t(*s_vt)[kFaVRow] = s_vtb[buf];
+    float vmax = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&s_k[4 * tk + r][8 * dk]) = kreg[r];
     const int slot = fa_vt_slot(4 * tv);
@@ -2091,12 +2107,19 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
         const float b2 = __uint_as_float(v2[e] & 0xffff0000u), b3 = __uint_as_float(v3[e] & 0xffff0000u);
         lo = make_uint2(pack_f16x2(a0, a1), pack_f16x2(a2, a3));
         hi = make_uint2(pack_f16x2(b0, b1), pack_f16x2(b2, b3));
+        vmax = max3_abs(vmax, a0, a1);
+        vmax = max3_abs(vmax, a2, a3);
+        vmax = max3_abs(vmax, b0, b1);
+        vmax = max3_abs(vmax, b2, b3);
       } else {
         lo = make_uint2(pack_low_halves(v0[e], v1[e]), pack_low_halves(v2[e], v3[e]));
         hi = make_uint2(pack_high_halves(v0[e], v1[e]), pack_high_halves(v2[e], v3[e]));
       }
       *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e][slot]) = lo;
       *reinterpret_cast<uint2*>(&s_vt[8 * dv + 2 * e + 1][slot]) = hi;
+    }
+    if constexpr (F16) {
+      if (vmax > kFaF16VMax) s_big[buf] = b;
     }
   };
 
@@ -2123,10 +2146,15 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
     block_ids(0, idk, idv);
     fetch(0, idk, idv);
     if (nblk > 1) block_ids(1, idk, idv);
+    if constexpr (F16) {
+      // no block stamps yet (LDS keeps what an earlier workgroup left)
+      if (tid < kFaBufs) s_big[tid] = -1;
+      __syncthreads();
+    }
 #if PA_FA_BUFS == 2
     // two LDS buffers: block b + 1 is staged while others may still compute
     // block b, so one barrier per block suffices
-    stage(0);
+    stage(0, 0);
     if (nblk > 1) {
       fetch(1, idk, idv);
       if (nblk > 2) block_ids(2, idk, idv);
@@ -2137,9 +2165,10 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
 #if PA_FA_BUFS == 2
       const uint16_t(*s_k)[kFaKRow] = s_kb[blk & 1];
       const uint16_t(*s_vt)[kFaVRow] = s_vtb[blk & 1];
+      const int cur = blk & 1;
 #else
       if (blk > 0) __syncthreads();          // every wave is done with the previous block
-      stage(0);
+      stage(0, blk);
       __syncthreads();
       if (blk + 1 < nblk) {
         fetch(blk + 1, idk, idv);
@@ -2147,8 +2176,15 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
       }
       const uint16_t(*s_k)[kFaKRow] = s_kb[0];
       const uint16_t(*s_vt)[kFaVRow] = s_vtb[0];
+      const int cur = 0;
 #endif
       const int p0 = blk * kFaPos;
+      // fp16 pass: a V value of this block lies beyond +-kFaF16VMax. Every
+      // wave reads the same stamp after the same barrier, so the whole
+      // workgroup leaves the tile here, to the exact pass.
+      if constexpr (F16) {
+        if (__builtin_amdgcn_readfirstlane(s_big[cur]) == blk) return false;
+      }
 
       // S^T for the block: sc[rt][sl] = scores of row c (tile rt) at positions
       // p0 + 16 sl + 4R + r
@@ -2273,32 +2309,38 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
           for (int rt = 0; rt < 2; ++rt)
             acc_l[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, phi[rt][st]),
                                                                ones, acc_l[rt], 0, 0, 0);
-      }
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const uint4 vb = *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]);
+          for (int st = 0; st < 2; ++st) {
+            const f16x8_t vb = __builtin_bit_cast(
+                f16x8_t, *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]));
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            if constexpr (F16) {
-              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                  __builtin_bit_cast(f16x8_t, phi[rt][st]), __builtin_bit_cast(f16x8_t, vb), acc[rt][t],
-                  0, 0, 0);
-            } else {
-              const bf16x8_t vbb = __builtin_bit_cast(bf16x8_t, vb);
+            for (int rt = 0; rt < 2; ++rt)
+              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, phi[rt][st]),
+                                                                  vb, acc[rt][t], 0, 0, 0);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const bf16x8_t vb = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]));
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
               acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, phi[rt][st]), vbb, acc[rt][t], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8_t, phi[rt][st]), vb, acc[rt][t], 0, 0, 0);
               acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, plo[rt][st]), vbb, acc[rt][t], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8_t, plo[rt][st]), vb, acc[rt][t], 0, 0, 0);
             }
           }
-        }
+      }
 #if PA_FA_BUFS == 2
       if (blk + 1 < nblk) {
         // every wave finished block b - 1 before the barrier that ended it, so
         // its buffer ((b + 1) & 1) is free
-        stage((blk + 1) & 1);
+        stage((blk + 1) & 1, blk + 1);
         if (blk + 2 < nblk) {
           fetch(blk + 2, idk, idv);
           if (blk + 3 < nblk) block_ids(blk + 3, idk, idv);
@@ -2306,23 +2348,6 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
       }
       __syncthreads();
 #endif
-    }
-    // A V value that fp16 cannot hold became infinite at staging; every wave
-    // multiplied it into its rows (a zero weight gives 0 * inf = NaN), so some
-    // accumulator of the tile is not finite. The caller then walks the tile
-    // again on the two-term bf16 path; non-finite inputs take that path too,
-    // where they give what they give there.
-    if constexpr (F16) {
-      bool bad = false;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bad |= !__builtin_isfinite(acc_l[rt][r]);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) bad |= !__builtin_isfinite(acc[rt][t][r]);
-        }
-      if (__syncthreads_or(bad)) return false;
     }
     // out[row] = O[row] / l[row]; lane holds rows 4R + r of each tile, dims 16 t + c
 #pragma unroll
@@ -2349,11 +2374,11 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
   return true;
 }
 
-// Ticket of the latest multi-token call whose fp16 walk met a V value fp16
-// cannot hold (tickets only grow; 0: none yet), one per device.
+// Ticket of the latest multi-token call whose fp16 walk gave up on a tile
+// (tickets only grow; 0: none yet), one per device.
 __device__ unsigned long long g_fa_exact_ticket;
 
-// F16: the fast pass; a tile that meets an out-of-range V value writes
+// F16: the fast pass; a tile that meets a V value beyond +-kFaF16VMax writes
 // nothing and raises the call's ticket. !F16: the exact pass, launched right
 // after on the same stream; it walks every tile again, but only when the
 // ticket shows that some fp16 tile of this call (or of a later one, which
@@ -2362,12 +2387,13 @@ template <int BS, int G, bool F16>
 __global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
   __shared__ __align__(16) uint16_t s_kb[kFaBufs][kFaPos][kFaKRow];
   __shared__ __align__(16) uint16_t s_vtb[kFaBufs][128][kFaVRow];
+  __shared__ int s_big[kFaBufs];
   if constexpr (!F16) {
     if (__hip_atomic_load(&g_fa_exact_ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
         a.fa_ticket)
       return;
   }
-  if (!multi_query_fa_tile<BS, G, F16>(a, s_kb, s_vtb) && threadIdx.x == 0)
+  if (!multi_query_fa_tile<BS, G, F16>(a, s_kb, s_vtb, s_big) && threadIdx.x == 0)
     atomicMax(&g_fa_exact_ticket, a.fa_ticket);
 }
 

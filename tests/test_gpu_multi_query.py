@@ -197,23 +197,25 @@ def _run_tiled(dev, c, q_np, qs, kp, vp, tag):
     return got, ref
 
 
-def test_tiled_kernel_values_beyond_fp16_range(dev):
-    """The tiled kernel holds P and V in fp16 (exact for every bf16 value below
-    2^16 in magnitude). V values of 2^16 and more, here 70000, 3e6 and -1e9 in
-    one sequence's context and 1e30 in another's, send the call through the
-    exact pass (two-term bf16 P), which must still match the oracle; the next
-    call with ordinary values takes the fast pass again."""
+@pytest.mark.parametrize("vals", [(70000.0, 3e6, -1e9, 1e30), (9.5, -20.0, 8.5, -300.0)])
+def test_tiled_kernel_values_beyond_fast_pass_range(dev, vals):
+    """The tiled kernel's fast pass holds P and V in fp16 and serves contexts
+    whose V values stay within +-8. Larger values, here three in one
+    sequence's context (before, inside and after its chunk) and one in
+    another's, beyond fp16's range or just past the bound, send the tiles
+    through the exact pass (two-term bf16 P), which must match the oracle; the
+    next call with ordinary values takes the fast pass again."""
     lens, tqs = [300, 1100, 700], [40, 64, 33]
     c, rng, qs = _tiled_case(dev, 331, lens, tqs)
     q_np = W.normal_values((int(qs[-1]), 32, 128), rng, "bf16")
     kp, vp = to_storage_np(c.k_pool).copy(), to_storage_np(c.v_pool).copy()
     big = vp.copy()
-    vals = np.array([70000.0, 3e6, -1e9], dtype=np.float32)
+    vals = np.array(vals, dtype=np.float32)
     phys, off = O.positions_to_rows(c.otables[1], lens[1], 16)
     for j, p in enumerate([5, 600, 1090]):         # before, inside and after the chunk
         big[phys[p], j % 8, off[p], 7 + j] = W.to_bf16_bits(vals[j:j + 1])[0]
     phys, off = O.positions_to_rows(c.otables[2], lens[2], 16)
-    big[phys[100], 3, off[100], 0] = W.to_bf16_bits(np.array([1e30], np.float32))[0]
+    big[phys[100], 3, off[100], 0] = W.to_bf16_bits(vals[3:4])[0]
     _run_tiled(dev, c, q_np, qs, kp, big, "V beyond fp16")
     _run_tiled(dev, c, q_np, qs, kp, vp, "ordinary V after the exact pass")
 
@@ -251,18 +253,27 @@ def _tolerance_use(got, ref):
     return float((np.abs(got - ref) / (atol + rtol * np.abs(ref))).max())
 
 
-@pytest.mark.parametrize("case", ["prefill", "prefill_v4", "chunk512", "steep", "gentle"])
+CASES = {"prefill": ([200, 150, 64], [200, 150, 64], None, 1.0),
+         "prefill_v1.5": ([200, 150, 64], [200, 150, 64], None, 1.5),
+         "prefill_v4": ([200, 150], [200, 150], None, 4.0),
+         "prefill_v10": ([200, 150, 64], [200, 150, 64], None, 10.0),
+         "prefill_v100": ([200, 150], [200, 150], None, 100.0),
+         "chunk512": ([4096, 3000], [512, 512], None, 1.0),
+         "steep": ([700, 1500, 2100], [160] * 3, 1.5, 1.0),
+         "gentle": ([700, 1500, 2100], [160] * 3, 0.25, 1.0),
+         "gentle_v30": ([200, 180], [200, 180], 0.25, 30.0)}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
 def test_tiled_kernel_tolerance_margin(dev, case):
-    """The fp16 weights of the tiled kernel on the cases most sensitive to
-    them: whole prompts (rows of 1 to 200 positions), the same with V scaled
-    by 4, a 512-token chunk over 4096 positions, and scores that rise along
-    the context (steeply and gently). The worst element must use at most
-    three quarters of the tolerance (it is printed)."""
-    lens, tqs, ramp, vscale = {"prefill": ([200, 150, 64], [200, 150, 64], None, 1.0),
-                               "prefill_v4": ([200, 150], [200, 150], None, 4.0),
-                               "chunk512": ([4096, 3000], [512, 512], None, 1.0),
-                               "steep": ([700, 1500, 2100], [160] * 3, 1.5, 1.0),
-                               "gentle": ([700, 1500, 2100], [160] * 3, 0.25, 1.0)}[case]
+    """The tiled kernel on the cases most sensitive to the precision of its
+    weights: whole prompts (rows of 1 to 200 positions), with V at unit scale
+    (the fp16 pass) and scaled by 1.5 (mostly the fp16 pass), 4, 10 and 100
+    (the exact pass: fp16 weights alone would miss the tolerance from about
+    10 on), a 512-token chunk over 4096 positions, and scores that rise along
+    the context (steeply, gently, gently with V x 30). The worst element must
+    use at most three quarters of the tolerance (it is printed)."""
+    lens, tqs, ramp, vscale = CASES[case]
     c, rng, qs = _tiled_case(dev, 351, lens, tqs)
     kp = O.as_f64(c.ok_pool, "bf16").astype(np.float32)
     vp = O.as_f64(c.ov_pool, "bf16").astype(np.float32) * vscale
