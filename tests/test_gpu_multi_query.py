@@ -295,3 +295,87 @@ def test_tiled_kernel_tolerance_margin(dev, case):
     use = _tolerance_use(got, ref)
     print(f"{case}: worst element uses {use:.3f} of the tolerance")
     assert use <= 0.75, use
+
+
+def _tiled_inputs(dev, seed, big_at=None):
+    """A 3-sequence batch on the tiled kernel; big_at = (value, seq, position)
+    puts one V value of that size into the context."""
+    lens, tqs = [300, 1100, 700], [40, 64, 33]
+    c, rng, qs = _tiled_case(dev, seed, lens, tqs)
+    q_np = W.normal_values((int(qs[-1]), 32, 128), rng, "bf16")
+    vp = to_storage_np(c.v_pool).copy()
+    vbig = vp.copy()
+    if big_at is not None:
+        val, seq, pos = big_at
+        phys, off = O.positions_to_rows(c.otables[seq], lens[seq], 16)
+        vbig[phys[pos], 2, off[pos], 5] = W.to_bf16_bits(np.array([val], np.float32))[0]
+    return c, q_np, qs, vp, vbig
+
+
+def _ref(c, q_np, qs, vp):
+    return O.multi_query(O.as_f64(q_np, "bf16"), O.as_f64(c.ok_pool, "bf16"), O.as_f64(vp, "bf16"),
+                         c.otables, c.olens, qs, c.scale)
+
+
+def test_tiled_kernel_calls_on_two_streams(dev):
+    """Calls on two streams at once, one of them with a V value of 100 in its
+    context (its tiles go to the exact pass), the other without: a call's
+    exact pass runs when the device ticket is at least its own, so a later
+    call's ticket can make an earlier call redo its tiles but never lets it
+    skip them. Both must match the oracle, over several rounds."""
+    ca, qa_np, qsa, _, va = _tiled_inputs(dev, 361, (100.0, 1, 600))
+    cb, qb_np, qsb, vb, _ = _tiled_inputs(dev, 362)
+    ca.v_pool.copy_(to_device(va, "bf16", dev))
+    refa, refb = _ref(ca, qa_np, qsa, va), _ref(cb, qb_np, qsb, vb)
+    qa, qb = to_device(qa_np, "bf16", dev), to_device(qb_np, "bf16", dev)
+    qsa_d, qsb_d = torch.from_numpy(qsa).to(dev), torch.from_numpy(qsb).to(dev)
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    for rnd in range(4):
+        outa = torch.full_like(qa, float("nan"))
+        outb = torch.full_like(qb, float("nan"))
+        torch.cuda.synchronize()
+        for first in ((0, 1) if rnd % 2 == 0 else (1, 0)):
+            with torch.cuda.stream(s1 if first == 0 else s2):
+                if first == 0:
+                    P.pa_multi_query(qa, ca.k_pool, ca.v_pool, ca.tables, ca.lens, qsa_d, ca.scale,
+                                     outa, max_seq_len=ca.max_len, max_query_len=64)
+                else:
+                    P.pa_multi_query(qb, cb.k_pool, cb.v_pool, cb.tables, cb.lens, qsb_d, cb.scale,
+                                     outb, max_seq_len=cb.max_len, max_query_len=64)
+        torch.cuda.synchronize()
+        assert P.pa_device_errors() == 0
+        check_close(O.as_f64(to_storage_np(outa), "bf16"), refa, "bf16", f"stream 1, round {rnd}")
+        check_close(O.as_f64(to_storage_np(outb), "bf16"), refb, "bf16", f"stream 2, round {rnd}")
+
+
+def test_tiled_kernel_graph_replays(dev):
+    """The call captured in a graph (both launches, with the ticket it had at
+    capture) and replayed with ordinary V, then with a V value of 100 placed
+    in the pool between replays (the exact pass takes over), then ordinary V
+    again (the captured ticket stays raised, so the exact pass keeps running:
+    slower, same results). Eager work and a synchronisation between replays;
+    every replay against the oracle."""
+    c, q_np, qs, vp, vbig = _tiled_inputs(dev, 371, (100.0, 2, 650))
+    q = to_device(q_np, "bf16", dev)
+    qs_d = torch.from_numpy(qs).to(dev)
+    out = torch.empty_like(q)
+    args = (q, c.k_pool, c.v_pool, c.tables, c.lens, qs_d, c.scale, out)
+    kw = dict(max_seq_len=c.max_len, max_query_len=64)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        P.pa_multi_query(*args, **kw)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        P.pa_multi_query(*args, **kw)
+    refs = {"plain": _ref(c, q_np, qs, vp), "big": _ref(c, q_np, qs, vbig)}
+    for k, name in enumerate(["plain", "big", "plain", "big", "plain"]):
+        c.v_pool.copy_(to_device(vp if name == "plain" else vbig, "bf16", dev))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert P.pa_device_errors() == 0
+        check_close(O.as_f64(to_storage_np(out), "bf16"), refs[name], "bf16", f"replay {k} ({name})")
