@@ -230,6 +230,23 @@ __device__ __forceinline__ uint32_t pack_high_halves(uint32_t lo_src, uint32_t h
   return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);
 }
 
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// Two floats as a bf16 pair (round to nearest even), low element first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+  const f32x2v_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
+}
+
+// Two floats as an fp16 pair (round to nearest even), low element first.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+  const f32x2v_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2v_t));
+}
+
 // Weight of a softmax stream with running max m when merged under max M.
 __device__ __forceinline__ float merge_weight(float m, float big_m) {
   return m == -INFINITY ? 0.0f : exp2_fast(m - big_m);
@@ -286,6 +303,76 @@ __device__ void write_zero_rows(const DecodeArgs& a, int i, int g) {
   for (int t = threadIdx.x; t < G * D; t += NW * 64) {
     const int h = t / D, d = t % D;
     Elem<T>::store(out + ((int64_t)i * a.num_q_heads + g * G + h) * D + d, 0.0f);
+  }
+}
+
+// Merges the NW waves' streams staged in LDS (s_m[w][h], s_l[w][h]: each
+// wave's (max, exp-sum) per head, s_acc[w][h][d]: its unnormalised output)
+// and writes either the final output (single-partition sequence) or the
+// partition's partials. Called by every thread after the staging barrier.
+template <typename T, int D, int G, int NW, bool PFX>
+__device__ __forceinline__ void finish_waves(const DecodeArgs& a, const PartitionWork& wk,
+                                             const float (*s_m)[G], const float (*s_l)[G],
+                                             const float (*s_acc)[G][D], float out_scale) {
+  // Merge of the NW wave streams, 4 consecutive dims per thread: one 16-byte
+  // (fp32) or 8-byte (bf16) store each.
+  constexpr int V4 = D / 4;
+  for (int t = threadIdx.x; t < G * V4; t += NW * 64) {
+    const int h = t / V4, d0 = (t % V4) * 4;
+    float big = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
+    float lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float f = merge_weight(s_m[k][h], big);
+      lsum += f * s_l[k][h];
+      const float4 sa = *reinterpret_cast<const float4*>(&s_acc[k][h][d0]);
+      o[0] += f * sa.x;
+      o[1] += f * sa.y;
+      o[2] += f * sa.z;
+      o[3] += f * sa.w;
+    }
+    const float inv = lsum > 0.0f ? out_scale / lsum : 0.0f;
+    const int64_t row = (int64_t)wk.i * a.num_q_heads + wk.g * G + h;
+    if (wk.direct) {
+      store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
+                o[3] * inv);
+    } else {
+      // the partial output of a partition holding at least
+      // kHalfPartialMinTokens positions is stored in bf16 when part_half is
+      // set (in the first half of its fp32-sized slot), other partials in
+      // fp32; the merge of the partitions runs in fp32
+      float* slot = reinterpret_cast<float*>(a.part_o) +
+                    (row * (PFX ? a.slot_stride : a.max_parts) + wk.slot) * D;
+      if (a.part_half && wk.tok1 - wk.tok0 >= kHalfPartialMinTokens)
+        store4<uint16_t>(reinterpret_cast<uint16_t*>(slot) + d0, o[0] * inv, o[1] * inv,
+                         o[2] * inv, o[3] * inv);
+      else
+        store4<float>(slot + d0, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+    }
+  }
+  // (max, exp-sum) of every head of the group: one full 128-byte record per
+  // workgroup, so the write never covers part of a cache line.
+  if (!wk.direct && threadIdx.x < kMlRecord / 4) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int f = threadIdx.x * 4 + e, h = f >> 1;
+      v[e] = 0.0f;
+      if (h < G) {
+        float big = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) lsum += merge_weight(s_m[k][h], big) * s_l[k][h];
+        v[e] = (f & 1) ? lsum : big;
+      }
+    }
+    const int64_t rec = (((int64_t)wk.i * a.num_kv_heads + wk.g) *
+                             (PFX ? a.slot_stride : a.max_parts) + wk.slot) * kMlRecord;
+    reinterpret_cast<float4*>(a.part_ml + rec)[threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -369,66 +456,7 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const Part
     }
   }
   __syncthreads();
-  // Merge of the NW wave streams, 4 consecutive dims per thread: one 16-byte
-  // (fp32) or 8-byte (bf16) store each.
-  constexpr int V4 = D / 4;
-  for (int t = threadIdx.x; t < G * V4; t += NW * 64) {
-    const int h = t / V4, d0 = (t % V4) * 4;
-    float big = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
-    float lsum = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float f = merge_weight(s_m[k][h], big);
-      lsum += f * s_l[k][h];
-      const float4 sa = *reinterpret_cast<const float4*>(&s_acc[k][h][d0]);
-      o[0] += f * sa.x;
-      o[1] += f * sa.y;
-      o[2] += f * sa.z;
-      o[3] += f * sa.w;
-    }
-    const float inv = lsum > 0.0f ? out_scale / lsum : 0.0f;
-    const int64_t row = (int64_t)wk.i * a.num_q_heads + wk.g * G + h;
-    if (wk.direct) {
-      store4<T>(reinterpret_cast<T*>(a.out) + row * D + d0, o[0] * inv, o[1] * inv, o[2] * inv,
-                o[3] * inv);
-    } else {
-      // the partial output of a partition holding at least
-      // kHalfPartialMinTokens positions is stored in bf16 when part_half is
-      // set (in the first half of its fp32-sized slot), other partials in
-      // fp32; the merge of the partitions runs in fp32
-      float* slot = reinterpret_cast<float*>(a.part_o) +
-                    (row * (PFX ? a.slot_stride : a.max_parts) + wk.slot) * D;
-      if (a.part_half && wk.tok1 - wk.tok0 >= kHalfPartialMinTokens)
-        store4<uint16_t>(reinterpret_cast<uint16_t*>(slot) + d0, o[0] * inv, o[1] * inv,
-                         o[2] * inv, o[3] * inv);
-      else
-        store4<float>(slot + d0, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-    }
-  }
-  // (max, exp-sum) of every head of the group: one full 128-byte record per
-  // workgroup, so the write never covers part of a cache line.
-  if (!wk.direct && threadIdx.x < kMlRecord / 4) {
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int f = threadIdx.x * 4 + e, h = f >> 1;
-      v[e] = 0.0f;
-      if (h < G) {
-        float big = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) big = fmaxf(big, s_m[k][h]);
-        float lsum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) lsum += merge_weight(s_m[k][h], big) * s_l[k][h];
-        v[e] = (f & 1) ? lsum : big;
-      }
-    }
-    const int64_t rec = (((int64_t)wk.i * a.num_kv_heads + wk.g) *
-                             (PFX ? a.slot_stride : a.max_parts) + wk.slot) * kMlRecord;
-    reinterpret_cast<float4*>(a.part_ml + rec)[threadIdx.x] = make_float4(v[0], v[1], v[2], v[3]);
-  }
+  finish_waves<T, D, G, NW, PFX>(a, wk, s_m, s_l, s_acc, out_scale);
 }
 
 
@@ -879,6 +907,115 @@ __device__ __forceinline__ void mfma_chunk(const CH& c, const bf16x8_t (&qop)[4]
   }
 }
 
+// P.V on the matrix cores too (v_mfma_f32_16x16x16_bf16), each lane feeding
+// its own values (used for 8-bit pools and for 2+ query heads per KV head). A = V^T for dims 8m + t (tile t = 0..7, row m
+// = lane % 16): lane (R, c) holds the codes of rows 4R .. 4R+3 at dims 8c ..
+// 8c+7, i.e. exactly A[m = c][k = 4R .. 4R+3] of every tile (8-bit codes
+// converted to bf16, exactly). B = P: lane (R, c) holds the weights of those rows
+// for head c % G, B[k = 4R .. 4R+3][n = c], as two bf16 terms. The result
+// C[m = 4R + r][n = c] of tile t is O[head c % G][dim 8 (4R + r) + t]. The
+// four row groups feed one product, so each head is one softmax stream: the
+// block maximum is shared across the row groups (two cross-lane steps) and
+// every lane keeps its own share of the exp-sum.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+template <int G, typename CH>
+__device__ __forceinline__ void mfma_chunk_pvm(const CH& c, const bf16x8_t (&qop)[4],
+                                               float qscale, int tokc, int tok1, int R, float& m,
+                                               float& lsum, f32x4_t (&acc)[8]) {
+  f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.kop(s), qop[s], sc, 0, 0, 0);
+  const bool full = tokc + 16 <= tok1;
+  float sv[4];
+  bool ok[4];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = sc[r] * qscale;
+    ok[r] = full || (tokc + 4 * R + r < tok1);
+    bm = ok[r] ? fmaxf(bm, sv[r]) : bm;
+  }
+  bm = fmaxf(bm, xor_lanes<16>(bm));
+  bm = fmaxf(bm, xor_lanes<32>(bm));
+  const float mn = bm > m + kLazyMax ? bm : m;
+  const float alpha = mn == m ? 1.0f : exp2_fast(m - mn);
+  m = mn;
+  float p[4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = ok[r] ? exp2_fast(sv[r] - mn) : 0.0f;
+    psum += p[r];
+  }
+  lsum = lsum * alpha + psum;
+  if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+  }
+  // B: the weights as two bf16 terms (hi + lo, ~16 significant bits)
+  const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+  const uint32_t l01 = pack_bf16x2(p[0] - __uint_as_float(h01 << 16), p[1] - __uint_as_float(h01 & 0xffff0000u));
+  const uint32_t l23 = pack_bf16x2(p[2] - __uint_as_float(h23 << 16), p[3] - __uint_as_float(h23 & 0xffff0000u));
+  const bf16x4_t phi = __builtin_bit_cast(bf16x4_t, make_uint2(h01, h23));
+  const bf16x4_t plo = __builtin_bit_cast(bf16x4_t, make_uint2(l01, l23));
+  // A: bf16 pairs b[jj][u] = dims 8c + 2u, 8c + 2u + 1 of row 4R + jj (code
+  // 0 for rows past the end, whose slack may hold NaN codes)
+  uint32_t b[4][4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    if constexpr (std::is_same<CH, KVChunk8>::value) {
+      const uint2 w = full || ok[jj] ? c.v[jj] : make_uint2(0, 0);
+      b[jj][0] = e4m3x2_to_bf16x2<false>(w.x);
+      b[jj][1] = e4m3x2_to_bf16x2<true>(w.x);
+      b[jj][2] = e4m3x2_to_bf16x2<false>(w.y);
+      b[jj][3] = e4m3x2_to_bf16x2<true>(w.y);
+    } else {
+      const uint4 w = full || ok[jj] ? c.v[jj] : make_uint4(0, 0, 0, 0);
+      b[jj][0] = w.x;
+      b[jj][1] = w.y;
+      b[jj][2] = w.z;
+      b[jj][3] = w.w;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int u = t >> 1;
+    const uint2 av = (t & 1) ? make_uint2(pack_high_halves(b[0][u], b[1][u]), pack_high_halves(b[2][u], b[3][u]))
+                             : make_uint2(pack_low_halves(b[0][u], b[1][u]), pack_low_halves(b[2][u], b[3][u]));
+    const bf16x4_t a = __builtin_bit_cast(bf16x4_t, av);
+    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, acc[t], 0, 0, 0);
+    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, acc[t], 0, 0, 0);
+  }
+}
+
+// The waves' streams of the matrix-core P.V (mfma_chunk_pvm) into LDS, then
+// finish_waves. Lane (R, c), c < G, holds head c: its max, the exp-sum of all
+// row groups (l_all) and dims 32R + 8r + t in acc[t][r].
+template <typename T, int D, int G, int NW, bool PFX>
+__device__ __forceinline__ void finish_partition_pvm(const DecodeArgs& a, const PartitionWork& wk,
+                                                     float m, float l_all, const f32x4_t (&acc)[8],
+                                                     float out_scale) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, R = lane >> 4, c = lane & 15;
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ __align__(16) float s_acc[NW][G][D];
+  if (c < G) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* d = &s_acc[w][c][32 * R + 8 * r];
+      *reinterpret_cast<float4*>(d) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+    }
+    if (R == 0) {
+      s_m[w][c] = m;
+      s_l[w][c] = l_all;
+    }
+  }
+  __syncthreads();
+  finish_waves<T, D, G, NW, PFX>(a, wk, s_m, s_l, s_acc, out_scale);
+}
+
 // One work unit (sequence, KV head, partition) of the matrix-core kernel.
 // F8: the pools hold FP8 E4M3 codes (q and out stay bf16); scores use
 // qscale = scale * log2(e) * k_scale and outputs are multiplied by v_scale.
@@ -920,12 +1057,19 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
   const uint32_t k_off = (uint32_t)(c * ROW + R * 16);       // + s * 64 (bf16), + h * 64 (8-bit)
   const uint32_t v_off = (uint32_t)(4 * R * ROW + c * (F8 ? 8 : 16));   // + jj * ROW
 
-  float m = -INFINITY, lsum = 0.0f;  // stream of row R, head lane % G
+  float m = -INFINITY, lsum = 0.0f;  // stream of row R (8-bit pools: of the head), head lane % G
   float acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  // P.V on the matrix cores (mfma_chunk_pvm) for 8-bit pools and for 2 or
+  // more query heads per KV head; at one head the vector form needs few
+  // instructions and stays slightly faster (Llama-2-13B shape: 570 vs 572 us)
+  constexpr bool kPvm = F8 || (G > 1 && BS != 8);
+  f32x4_t accm[8];                   // kPvm: the matrix-core P.V tiles
+#pragma unroll
+  for (int t = 0; t < 8; ++t) accm[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nch = (wk.tok1 - wk.tok0 + 15) / 16;
   const int nmine = nch > w ? (nch - w + NW - 1) / NW : 0;   // chunks of this wave
@@ -956,7 +1100,10 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
     int t = 0;
     auto stage = [&](Chunk& nxt, const Chunk& cur) {
       issue(nxt, t + NBUF - 1);
-      mfma_chunk<G>(cur, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
+      if constexpr (kPvm)
+        mfma_chunk_pvm<G>(cur, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, accm);
+      else
+        mfma_chunk<G>(cur, qop, a.qscale, chunk_tok(win + t), wk.tok1, R, m, lsum, acc);
       return ++t >= cnt;
     };
     Chunk b0, b1;
@@ -981,14 +1128,23 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, const PartitionWo
       }
     }
   }
-  float mh[G], lh[G];
-  quad_spread<G>(m, mh);
-  quad_spread<G>(lsum, lh);
-  finish_partition<uint16_t, D, G, NW, 16, 8, PFX>(a, wk, mh, lh, acc, F8 ? a.out_scale : 1.0f);
+  if constexpr (kPvm) {
+    float l_all = lsum + xor_lanes<16>(lsum);
+    l_all += xor_lanes<32>(l_all);
+    finish_partition_pvm<uint16_t, D, G, NW, PFX>(a, wk, m, l_all, accm, F8 ? a.out_scale : 1.0f);
+  } else {
+    float mh[G], lh[G];
+    quad_spread<G>(m, mh);
+    quad_spread<G>(lsum, lh);
+    finish_partition<uint16_t, D, G, NW, 16, 8, PFX>(a, wk, mh, lh, acc, 1.0f);
+  }
 }
 
 template <int BS, int G, int NW, bool F8, bool PFX = false, int POL = kKvStream>
-__global__ PA_MFMA_BOUNDS(NW * 64) __attribute__((amdgpu_waves_per_eu(PFX ? 3 : 1)))
+// at least 3 waves per SIMD for the matrix-core P.V forms (unbounded, the
+// compiler gives them 172 registers, 2 waves) and the shared-prefix walks
+__global__ PA_MFMA_BOUNDS(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PFX || F8 || (G > 1 && BS != 8) ? 3 : 1)))
 void decode_partition_mfma(DecodeArgs a) {
   PartitionWork wk;
   if (!setup_partition<uint16_t, 128, BS, G, NW, PFX>(a, wk, blockIdx.x)) return;
@@ -1424,22 +1580,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
 //     O[rows 4R .. 4R+3][dim 16t + c].
 // Each wave owns its LDS buffers and its unit, so waves never wait for one
 // another; K/V of chunk c+1 are issued before chunk c is computed.
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 
-// Two floats as a bf16 pair (round to nearest even), low element first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
-  const f32x2v_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v_t));
-}
 
-// Two floats as an fp16 pair (round to nearest even), low element first.
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  typedef float f32x2v_t __attribute__((ext_vector_type(2)));
-  typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
-  const f32x2v_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2v_t));
-}
 
 // p as two bf16 terms hi + lo (lo = the bf16 rounding of p - hi), 8 values
 // per operand: ~16 significant bits instead of bf16's 8.
