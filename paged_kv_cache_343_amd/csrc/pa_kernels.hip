@@ -35,8 +35,11 @@
 //   MFMA: q.K on the matrix cores (v_mfma_f32_16x16x32_bf16) with K as the
 //         A operand and the group's query rows, replicated over the 16
 //         columns, as B; the result leaves each lane with the scores of its
-//         own row's 4 positions, and a quad-level DPP broadcast hands each
-//         lane the other heads' probabilities; P.V on the VALU.
+//         own row's 4 positions. P.V on the matrix cores too
+//         (v_mfma_f32_16x16x16_bf16, each lane's own V rows and weights as
+//         operands) for 2+ query heads per KV head and 8-bit pools; at one
+//         head, a quad-level DPP broadcast of the probabilities and P.V on
+//         the VALU.
 // Every device-resident index is range-checked; a bad one is replaced by an
 // in-range value, its work is masked, and a bit is set in g_error_word.
 #include <hip/hip_runtime.h>
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_valu(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA partition kernel (bf16, D = 128, G in {1, 2, 4})
+// MFMA partition kernel (bf16 or 8-bit pools, D = 128, G in {1, 2, 4})
 // ---------------------------------------------------------------------------
 // Positions are taken 16 at a time ("chunk"; a 16-token block, or a 16-token
 // slice of a larger block). Lane l: R = l / 16 (row), c = l % 16.
@@ -650,7 +653,9 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_valu(DecodeArgs a) {
 //   q operand step s:    query row (l % 16) % G, same dims        -> B operand
 //   MFMA result reg r:   score of token 4 R + r for head (l % G)
 //   V load jj (0..3):    token 4 R + jj, dims [8 c, +8), coalesced 256 B rows
-// Row R is one softmax stream over tokens {4R .. 4R+3} of every chunk.
+// With P.V on the VALU (one query head per KV head) row R is one softmax
+// stream over tokens {4R .. 4R+3} of every chunk; with P.V on the matrix
+// cores the four rows share one stream per head (mfma_chunk_pvm).
 //
 // Wave w of the workgroup takes chunks w, w + NW, w + 2 NW, ... of the
 // partition. The physical block ids of those chunks are read once, one per
