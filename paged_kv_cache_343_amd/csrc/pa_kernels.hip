@@ -68,6 +68,7 @@ __device__ __forceinline__ void flag_error(uint32_t bit) { atomicOr(&g_error_wor
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
@@ -2066,34 +2067,34 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
 
 // ---------------------------------------------------------------------------
 // Multi-token queries, many rows per (sequence, KV head): one workgroup of 4
-// waves per tile of 128 query rows (32 rows = two 16-row tiles per wave).
-// Positions are walked 64 at a time (a "block"); each block's K rows and V
-// rows are read from the pool once per workgroup and staged in LDS:
-//   K as rows (272-byte stride: the 16 lanes of an operand read hit distinct
+// waves per tile of 128 query rows, 32 rows per wave, on 32x32x16 matrix
+// products. Positions are walked 64 at a time (a "block"); each block's K
+// rows and V rows are read from the pool once per workgroup and staged in LDS:
+//   K as rows (272-byte stride: the 16 lanes of a read group hit distinct
 //     banks); the A operand of S^T = K Q^T is a 16-byte LDS read;
-//   V transposed (V^T, dims as rows, 144-byte stride), with the 64
-//     positions of a block permuted inside each 32-position half so that the
-//     8 positions a lane contributes to one P.V step are contiguous: the B
-//     operand of O += P V is a 16-byte LDS read too.
-// Lane l: R = l / 16, c = l % 16. Per 16-row tile and 16-position slice the
-// S^T product leaves lane (R, c) the scores of row c at positions 4R .. 4R+3
-// of the slice; with the two slices of a 32-position step these are exactly
-// the lane's 8 k-slots (8R .. 8R+7) of the P.V step, so P goes from the
-// softmax to the matrix cores without leaving the lane: in fp16, with V^T
-// staged in fp16 (11 significant bits, 8x finer than bf16; for tiles whose V
-// values stay within +-kFaF16VMax), or, on the exact pass, as two bf16 terms
-// p = hi + lo (~16 significant bits) against bf16 V^T. The next block's K/V
-// loads are issued before the current block is computed. Workgroup ids: every
-// tile of one (sequence, KV head) lands on the same XCD (XCD = id % 8), so the
-// tiles share that XCD's L2 copy of the context; heavier (later) tiles first.
+//   V transposed (V^T, dims as rows, 144-byte stride), with the positions of
+//     each 16-position group permuted so that the 8 positions a lane
+//     contributes to one P.V step are contiguous: the A operand of
+//     O^T += V^T P^T is a 16-byte LDS read too.
+// Lane l: n = l % 32 (the wave's query row n), hh = l / 32. Each S^T tile
+// (32 positions x 32 rows) leaves lane (hh, n) 16 scores of row n, at
+// positions 8 (v / 4) + 4 hh + v % 4 (v = 0 .. 15); the 8 of them in one
+// 16-position group are exactly the lane's k-slots (8 hh ..) of the B operand
+// (P^T) of a P.V step, so P goes from the softmax to the matrix cores without
+// leaving the lane: in fp16, with V^T staged in fp16 (11 significant bits, 8x
+// finer than bf16; for tiles whose V values stay within +-kFaF16VMax), or, on
+// the exact pass, as two bf16 terms p = hi + lo (~16 significant bits) against
+// bf16 V^T. With rows in lanes the softmax is lane-local but for one 32-lane
+// swap per block (the row maximum) and one at the end (the row sum). The next
+// block's K/V loads are issued before the current block is computed.
+// Workgroup ids: every tile of one (sequence, KV head) lands on the same XCD
+// (XCD = id % 8), so the tiles share that XCD's L2 copy of the context;
+// heavier (later) tiles first.
 constexpr int kFaRows = 128;     // query rows per workgroup
 constexpr int kFaPos = 64;       // positions per block
 constexpr int kFaKRow = 136;     // bf16 elements per staged K row (128 + 8 pad)
 constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad)
-#ifndef PA_FA_BUFS
-#define PA_FA_BUFS 2
-#endif
-constexpr int kFaBufs = PA_FA_BUFS;   // LDS stages of K and V^T
+constexpr int kFaBufs = 2;       // LDS stages of K and V^T (one barrier per block)
 // The fp16 pass serves tiles whose context holds V values within
 // +-kFaF16VMax only (its weights' rounding then moves an output by at most
 // 2^-10 * 2 * kFaF16VMax, and in practice as little as the two-term P does);
@@ -2102,16 +2103,16 @@ constexpr float kFaF16VMax = 8.0f;
 
 
 // Slot of position j (0..63) of a block in a staged V^T row: inside each
-// 32-position half, positions 16h + 4R + r go to 8R + 4h + r.
+// 16-position group, position 8q + 4h + r goes to slot 8h + 4q + r (the
+// k-slot order of the 32x32x16 operands).
 __device__ __forceinline__ int fa_vt_slot(int j) {
-  const int half = j >> 5, h = (j >> 4) & 1, R = (j >> 2) & 3, r = j & 3;
-  return 32 * half + 8 * R + 4 * h + r;
+  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
 typedef uint16_t FaKStage[kFaPos][kFaKRow];
 typedef uint16_t FaVtStage[128][kFaVRow];
 
-// One workgroup's tile. F16: P and V^T in fp16 on v_mfma_f32_16x16x32_f16;
+// One workgroup's tile. F16: P and V^T in fp16 on v_mfma_f32_32x32x16_f16;
 // returns false (and writes nothing) as soon as a staged block holds a V value
 // beyond +-kFaF16VMax (infinite ones included). Otherwise P as two bf16 terms
 // on the bf16 matrix product, for any input.
@@ -2121,12 +2122,11 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
   constexpr int D = 128, ROW = 256;
   constexpr int64_t kHeadBytes = (int64_t)BS * ROW;
   static_assert(BS % 16 == 0 && kFaRows % (2 * 16) == 0 && 16 % G == 0,
-                "whole 4-position groups per block, whole tokens per 16-row tile");
+                "whole 4-position groups per block, whole tokens per 32-row wave");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int R = lane >> 4, c = lane & 15;
 
   // workgroup id -> (tile, KV head, sequence)
   const int ntiles = (a.max_query_len * G + kFaRows - 1) / kFaRows;
@@ -2152,21 +2152,21 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
   const int npos = L - tq + t_last + 1;          // positions the tile's last token sees
   const int nblk = (npos + kFaPos - 1) / kFaPos;
 
-  // this lane's query rows (columns of S^T), one per 16-row tile
+  // this lane's query row (column n of S^T); lanes n and n + 32 share it
+  const int n = lane & 31, hh = lane >> 5;
   const int roww = row0 + 32 * w;
-  bf16x8_t qop[2][4];
-  int pos_c[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int rc = roww + 16 * rt + c;
+  bf16x8_t qop[8];
+  int pos_c;
+  {
+    const int rc = roww + n;
     const bool ok = rc < rows;
     const int tc = ok ? rc / G : 0, hc = rc % G;
-    pos_c[rt] = ok ? L - tq + tc : -1;
+    pos_c = ok ? L - tq + tc : -1;
     const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((int64_t)(q0 + tc) * a.num_q_heads + g * G + hc) * D + 8 * R) * 2;
+                     (((int64_t)(q0 + tc) * a.num_q_heads + g * G + hc) * D + 8 * hh) * 2;
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      qop[rt][s2] = __builtin_bit_cast(bf16x8_t, ok ? ld16(qp, s2 * 64) : make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < 8; ++ks)
+      qop[ks] = __builtin_bit_cast(bf16x8_t, ok ? ld16(qp, ks * 32) : make_uint4(0, 0, 0, 0));
   }
   // every row of this wave sees positions below vis_w (its first row's token)
   const int vis_w = L - tq + min(roww, rows - 1) / G + 1;
@@ -2175,16 +2175,14 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
   const float qs = fabsf(a.qscale);
   if (a.qscale < 0.0f) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        uint4 u = __builtin_bit_cast(uint4, qop[rt][s2]);
-        u.x ^= 0x80008000u;
-        u.y ^= 0x80008000u;
-        u.z ^= 0x80008000u;
-        u.w ^= 0x80008000u;
-        qop[rt][s2] = __builtin_bit_cast(bf16x8_t, u);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 u = __builtin_bit_cast(uint4, qop[ks]);
+      u.x ^= 0x80008000u;
+      u.y ^= 0x80008000u;
+      u.z ^= 0x80008000u;
+      u.w ^= 0x80008000u;
+      qop[ks] = __builtin_bit_cast(bf16x8_t, u);
+    }
   }
 
   // loaders: K thread = (token group tk, 16-byte dim chunk dk), V thread =
@@ -2275,19 +2273,12 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
     // so that weights down to 2^-21 of the reference stay normal numbers; the
     // factor cancels in O / l
     constexpr float kPBias = F16 ? 7.0f : 0.0f;
-    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
-    f32x4_t acc[2][8];
-    // fp16 path: the row sums of P come from the matrix cores too, as P times
-    // a column of ones; lane (R, c) holds the sums of rows 4R .. 4R+3, like
-    // the output accumulators
-    f32x4_t acc_l[2];
+    float m = -INFINITY, lsum = 0.0f;          // row n; lsum: this lane's positions only
+    f32x16_t acc[4];                           // O^T tiles: dims 32 dt + 8 (v/4) + 4 hh + v%4
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      acc_l[rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[rt][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      for (int v = 0; v < 16; ++v) acc[dt][v] = 0.0f;
 
     int idk, idv;
     block_ids(0, idk, idv);
@@ -2298,192 +2289,127 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
       if (tid < kFaBufs) s_big[tid] = -1;
       __syncthreads();
     }
-#if PA_FA_BUFS == 2
-    // two LDS buffers: block b + 1 is staged while others may still compute
-    // block b, so one barrier per block suffices
     stage(0, 0);
     if (nblk > 1) {
       fetch(1, idk, idv);
       if (nblk > 2) block_ids(2, idk, idv);
     }
     __syncthreads();
-#endif
     for (int blk = 0; blk < nblk; ++blk) {
-#if PA_FA_BUFS == 2
       const uint16_t(*s_k)[kFaKRow] = s_kb[blk & 1];
       const uint16_t(*s_vt)[kFaVRow] = s_vtb[blk & 1];
       const int cur = blk & 1;
-#else
-      if (blk > 0) __syncthreads();          // every wave is done with the previous block
-      stage(0, blk);
-      __syncthreads();
-      if (blk + 1 < nblk) {
-        fetch(blk + 1, idk, idv);
-        if (blk + 2 < nblk) block_ids(blk + 2, idk, idv);
-      }
-      const uint16_t(*s_k)[kFaKRow] = s_kb[0];
-      const uint16_t(*s_vt)[kFaVRow] = s_vtb[0];
-      const int cur = 0;
-#endif
       const int p0 = blk * kFaPos;
-      // fp16 pass: a V value of this block lies beyond +-kFaF16VMax. Every
-      // wave reads the same stamp after the same barrier, so the whole
-      // workgroup leaves the tile here, to the exact pass.
       if constexpr (F16) {
         if (__builtin_amdgcn_readfirstlane(s_big[cur]) == blk) return false;
       }
-
-      // S^T for the block: sc[rt][sl] = scores of row c (tile rt) at positions
-      // p0 + 16 sl + 4R + r
-      f32x4_t sc[2][4];
+      // S^T tiles: sc[pt][v] = score of row n at position p0 + 32 pt + 8 (v/4) + 4 hh + v%4
+      f32x16_t sc[2];
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        bf16x8_t kop[4];
+      for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2)
-          kop[s2] = __builtin_bit_cast(bf16x8_t,
-                                       *reinterpret_cast<const uint4*>(&s_k[16 * sl + c][8 * R + 32 * s2]));
+        for (int v = 0; v < 16; ++v) sc[pt][v] = 0.0f;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          sc[rt][sl] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2)
-            sc[rt][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[s2], qop[rt][s2], sc[rt][sl], 0, 0, 0);
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8_t kop = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(&s_k[32 * pt + n][16 * ks + 8 * hh]));
+          sc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], sc[pt], 0, 0, 0);
         }
       }
-      uint4 phi[2][2], plo[2][2];                 // [rt][32-position step]
-      bool rescale = false;
-      float alpha[2];
-      // the softmax of the block's scores, with a per-position mask (kMasked:
-      // the block reaches past some row's last position) or without
+      // B operands of the P.V steps: step st covers positions 16 st .. 16 st + 15;
+      // this lane's k-slots 8 hh + 4 q + r are positions 16 st + 8 q + 4 hh + r,
+      // i.e. its scores v = 8 (st % 2) .. + 7 of tile st / 2
+      uint4 pb[4], pl[4];
+      bool rescale;
+      float alpha;
       auto softmax = [&](auto masked_tag) {
         constexpr bool kMasked = decltype(masked_tag)::value;
+        float bm = -INFINITY;
+        if constexpr (kMasked) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          // scores stay unscaled until the exponent: qs >= 0 (a negative scale
-          // was folded into q's sign), so the row maximum scales with them
-          float bm = -INFINITY;
-          if constexpr (kMasked) {
+          for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
+            for (int v = 0; v < 16; ++v)
+              bm = p0 + 32 * pt + 8 * (v >> 2) + 4 * hh + (v & 3) <= pos_c ? fmaxf(bm, sc[pt][v]) : bm;
+        } else {
+          float b0 = -INFINITY, b1 = -INFINITY;
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                bm = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? fmaxf(bm, sc[rt][sl][r]) : bm;
+          for (int v = 0; v < 16; v += 2) {
+            b0 = max3f(b0, sc[0][v], sc[0][v + 1]);
+            b1 = max3f(b1, sc[1][v], sc[1][v + 1]);
+          }
+          bm = fmaxf(b0, b1);
+        }
+        bm = fmaxf(bm, xor_lanes<32>(bm));
+        const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
+        const float mn = bms > m + kLazyMax ? bms : m;
+        alpha = mn == m ? 1.0f : exp2_fast(m - mn);
+        rescale = alpha != 1.0f;
+        m = mn;
+        const float mo = kPBias - mn;
+        float p[2][16];
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            p[pt][v] = exp2_fast(fmaf(sc[pt][v], qs, mo));
+            if constexpr (kMasked)
+              p[pt][v] = p0 + 32 * pt + 8 * (v >> 2) + 4 * hh + (v & 3) <= pos_c ? p[pt][v] : 0.0f;
+          }
+        float ps = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float* f = &p[st >> 1][8 * (st & 1)];
+          if constexpr (F16) {
+            pb[st] = make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
+                                pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7]));
+            // row sum of the weights as the matrix cores see them (fp16)
+            const f16x2_t one2 = {1, 1};
+            ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pb[st].x), one2, ps, false);
+            ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pb[st].y), one2, ps, false);
+            ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pb[st].z), one2, ps, false);
+            ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pb[st].w), one2, ps, false);
           } else {
-            float b0 = -INFINITY, b1 = -INFINITY;
+            uint32_t hb[4], lb[4];
 #pragma unroll
-            for (int sl = 0; sl < 4; sl += 2) {
-              b0 = max3f(b0, sc[rt][sl][0], sc[rt][sl][1]);
-              b0 = max3f(b0, sc[rt][sl][2], sc[rt][sl][3]);
-              b1 = max3f(b1, sc[rt][sl + 1][0], sc[rt][sl + 1][1]);
-              b1 = max3f(b1, sc[rt][sl + 1][2], sc[rt][sl + 1][3]);
+            for (int e = 0; e < 4; ++e) {
+              hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+              lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
+                                  f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
+              ps += f[2 * e] + f[2 * e + 1];
             }
-            bm = fmaxf(b0, b1);
-          }
-          bm = fmaxf(bm, xor_lanes<16>(bm));
-          bm = fmaxf(bm, xor_lanes<32>(bm));
-          // lazy reference maximum (kLazyMax): rows rarely need rescaling
-          // after the first block
-          const float bms = bm == -INFINITY ? -INFINITY : bm * qs;
-          const float mn = bms > m[rt] + kLazyMax ? bms : m[rt];
-          alpha[rt] = mn == m[rt] ? 1.0f : exp2_fast(m[rt] - mn);
-          rescale |= alpha[rt] != 1.0f;
-          m[rt] = mn;
-          const float mo = kPBias - mn;
-          float p[16];
-#pragma unroll
-          for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[4 * sl + r] = exp2_fast(fmaf(sc[rt][sl][r], qs, mo));
-          if constexpr (kMasked) {
-            // masked positions (and every position while the row has none) get 0
-#pragma unroll
-            for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                p[4 * sl + r] = p0 + 16 * sl + 4 * R + r <= pos_c[rt] ? p[4 * sl + r] : 0.0f;
-          }
-          if constexpr (!F16) {
-            float ps = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) ps += p[e];
-            lsum[rt] = lsum[rt] * alpha[rt] + ps;
-          }
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            // k-slots 8R + 4h + r <- position 32 st + 16 h + 4R + r = p[4 (2 st + h) + r]
-            const float* f = p + 8 * st;
-            if constexpr (F16) {
-              phi[rt][st] = make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
-                                       pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7]));
-            } else {
-              uint32_t hb[4], lb[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                hb[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-                lb[e] = pack_bf16x2(f[2 * e] - __uint_as_float(hb[e] << 16),
-                                    f[2 * e + 1] - __uint_as_float(hb[e] & 0xffff0000u));
-              }
-              phi[rt][st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-              plo[rt][st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
-            }
+            pb[st] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+            pl[st] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
           }
         }
+        lsum = lsum * alpha + ps;
       };
-      // no position of the block is masked for this wave
       if (p0 + kFaPos <= vis_w)
         softmax(std::false_type{});
       else
         softmax(std::true_type{});
-      // rescale output rows 4R + r of each tile by their rows' alpha (row c's
-      // alpha sits in lane c); skipped when no row's maximum moved
       if (__ballot(rescale) != 0) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float ar = __shfl(alpha[rt], 4 * R + r);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) acc[rt][t][r] *= ar;
-            if constexpr (F16) acc_l[rt][r] *= ar;
-          }
+        for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
       }
-      // O += P V over 8 tiles of 16 dims and two 32-position steps
-      if constexpr (F16) {
+      // O^T += V^T P^T: A = V^T (dim 32 dt + n, k-slots 8 hh ..), B = P^T (row n)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-            acc_l[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, phi[rt][st]),
-                                                               ones, acc_l[rt], 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const f16x8_t vb = __builtin_bit_cast(
-                f16x8_t, *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]));
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, phi[rt][st]),
-                                                                  vb, acc[rt][t], 0, 0, 0);
+        for (int st = 0; st < 4; ++st) {
+          const uint4 vraw = *reinterpret_cast<const uint4*>(&s_vt[32 * dt + n][16 * st + 8 * hh]);
+          if constexpr (F16) {
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, vraw),
+                                                             __builtin_bit_cast(f16x8_t, pb[st]),
+                                                             acc[dt], 0, 0, 0);
+          } else {
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vraw);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, pb[st]),
+                                                              acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8_t, pl[st]),
+                                                              acc[dt], 0, 0, 0);
           }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const bf16x8_t vb = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const uint4*>(&s_vt[16 * t + c][32 * st + 8 * R]));
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, phi[rt][st]), vb, acc[rt][t], 0, 0, 0);
-              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, plo[rt][st]), vb, acc[rt][t], 0, 0, 0);
-            }
-          }
-      }
-#if PA_FA_BUFS == 2
+        }
       if (blk + 1 < nblk) {
         // every wave finished block b - 1 before the barrier that ended it, so
         // its buffer ((b + 1) & 1) is free
@@ -2494,28 +2420,25 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
         }
       }
       __syncthreads();
-#endif
     }
-    // out[row] = O[row] / l[row]; lane holds rows 4R + r of each tile, dims 16 t + c
+    // out[row n] = O[row n] / l; lane holds dims 32 dt + 8 gq + 4 hh + (0..3)
+    const float l = lsum + xor_lanes<32>(lsum);
+    const int row = roww + n;
+    if (row < rows) {
+      const int t = row / G, h = row % G;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                      ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + 4 * hh;
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float l = lsum[rt];
-      if constexpr (!F16) {
-        l += xor_lanes<16>(l);
-        l += xor_lanes<32>(l);
-      }
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float lr = F16 ? acc_l[rt][r] : __shfl(l, 4 * R + r);
-        const int row = roww + 16 * rt + 4 * R + r;
-        if (row >= rows) continue;
-        const int t = row / G, h = row % G;
-        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
-                        ((int64_t)(q0 + t) * a.num_q_heads + g * G + h) * D + c;
-        const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-#pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2) dst[16 * t2] = bf16_bits(acc[rt][t2][r] * inv);
-      }
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint32_t lo = (uint32_t)bf16_bits(acc[dt][4 * gq] * inv) |
+                              ((uint32_t)bf16_bits(acc[dt][4 * gq + 1] * inv) << 16);
+          const uint32_t hi = (uint32_t)bf16_bits(acc[dt][4 * gq + 2] * inv) |
+                              ((uint32_t)bf16_bits(acc[dt][4 * gq + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * gq) = make_uint2(lo, hi);
+        }
     }
   }
   return true;
