@@ -71,6 +71,24 @@ def pin_contiguous_sdpa(O):
             np.testing.assert_allclose(got[i, h], ref.view(-1).numpy(), rtol=1e-12, atol=1e-13)
 
 
+def pin_negative_scale_sdpa(O):
+    # any finite scale is accepted; a negative one turns the largest dot
+    # product into the smallest weight (library routine: SDPA in float64)
+    rng = np.random.default_rng(12)
+    B, hq, hkv, d, bs = 2, 4, 1, 8, 4
+    lens = [7, 18]
+    q, kp, vp, tab, sl, ks, vs = _case(rng, B, hq, hkv, d, bs, lens)
+    for scale in (-1.0 / math.sqrt(d), -2.5):
+        got = O.decode(q, kp, vp, tab, sl, scale)
+        for i in range(B):
+            for h in range(hq):
+                qq = torch.tensor(q[i, h]).view(1, 1, 1, d)
+                kk = torch.tensor(ks[i][0]).view(1, 1, -1, d)
+                vv = torch.tensor(vs[i][0]).view(1, 1, -1, d)
+                ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+                np.testing.assert_allclose(got[i, h], ref.view(-1).numpy(), rtol=1e-12, atol=1e-13)
+
+
 def pin_contiguous_dense(O):
     # same layout check with an arbitrary scale and an MHA shape
     rng = np.random.default_rng(12)
@@ -142,7 +160,7 @@ def pin_bruteforce(O):
                     assert abs(got[i, h, e] - ref) <= 1e-12 * (1 + abs(ref))
 
 
-ALL_PINS = [pin_contiguous_sdpa, pin_contiguous_dense, pin_gqa_mapping, pin_closed_forms, pin_bruteforce]
+ALL_PINS = [pin_contiguous_sdpa, pin_negative_scale_sdpa, pin_contiguous_dense, pin_gqa_mapping, pin_closed_forms, pin_bruteforce]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
