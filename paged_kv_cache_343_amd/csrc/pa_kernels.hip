@@ -2066,10 +2066,12 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Multi-token queries, many rows per (sequence, KV head): one workgroup of 4
-// waves per tile of 128 query rows, 32 rows per wave, on 32x32x16 matrix
-// products. Positions are walked 64 at a time (a "block"); each block's K
-// rows and V rows are read from the pool once per workgroup and staged in LDS:
+// Multi-token queries, many rows per (sequence, KV head): one workgroup of 8
+// waves (one per CU: 2 per SIMD) per tile of 256 query rows, 32 rows per wave,
+// on 32x32x16 matrix products. Positions are walked 64 at a time (a "block");
+// each block's K rows and V rows are read from the pool once per workgroup and
+// staged in LDS, each of the 512 threads loading and staging 2 positions of
+// one 16-byte column of K and of V:
 //   K as rows (272-byte stride: the 16 lanes of a read group hit distinct
 //     banks); the A operand of S^T = K Q^T is a 16-byte LDS read;
 //   V transposed (V^T, dims as rows, 144-byte stride), with the positions of
@@ -2090,8 +2092,16 @@ __global__ __launch_bounds__(kMqWaves * 64) void multi_query_reduce(MqArgs a) {
 // Workgroup ids: every tile of one (sequence, KV head) lands on the same XCD
 // (XCD = id % 8), so the tiles share that XCD's L2 copy of the context;
 // heavier (later) tiles first.
-constexpr int kFaRows = 128;     // query rows per workgroup
+#ifndef PA_FA_WAVES
+#define PA_FA_WAVES 8
+#endif
+constexpr int kFaWaves = PA_FA_WAVES;   // waves per workgroup, 32 query rows each
+constexpr int kFaRows = 32 * kFaWaves;  // query rows per workgroup
+constexpr int kFaMinRows = 128;         // rows per KV head from which calls take this kernel
 constexpr int kFaPos = 64;       // positions per block
+// positions of one staged block per loader thread (16-byte pieces of K and V)
+constexpr int kFaNp = kFaPos * 16 / (kFaWaves * 64);
+static_assert(kFaNp == 2 || kFaNp == 4, "4 or 8 waves per workgroup");
 constexpr int kFaKRow = 136;     // bf16 elements per staged K row (128 + 8 pad)
 constexpr int kFaVRow = 72;      // bf16 elements per staged V^T row (64 + 8 pad)
 constexpr int kFaBufs = 2;       // LDS stages of K and V^T (one barrier per block)
@@ -2187,24 +2197,25 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
 
   // loaders: K thread = (token group tk, 16-byte dim chunk dk), V thread =
   // (token group tv, dim chunk dv); each moves 4 consecutive positions
+  constexpr int kTg = kFaPos / kFaNp;    // V loaders per dim chunk
   const int dk = tid & 15, tk = tid >> 4;
-  const int tv = tid & 15, dv = tid >> 4;
+  const int tv = tid % kTg, dv = tid / kTg;
   const int64_t blk_bytes = kHeadBytes * a.num_kv_heads;
   const char* kbase = reinterpret_cast<const char*>(a.k_pool) + g * kHeadBytes;
   const char* vbase = reinterpret_cast<const char*>(a.v_pool) + g * kHeadBytes;
   const int64_t trow = (int64_t)i * a.max_blocks;
-  uint4 kreg[4], vreg[4];
+  uint4 kreg[kFaNp], vreg[kFaNp];
   // physical blocks of this thread's K and V positions in block `blk`, read
   // one block ahead of the K/V loads that use them and range-checked only
   // there (a check at the read would make the wave wait for every load
   // issued before it)
   auto block_ids = [&](int blk, int& idk, int& idv) {
-    const int pk = blk * kFaPos + 4 * tk, pv = blk * kFaPos + 4 * tv;
+    const int pk = blk * kFaPos + kFaNp * tk, pv = blk * kFaPos + kFaNp * tv;
     idk = pk < npos ? a.block_tables[trow + pk / BS] : 0;
     idv = pv < npos ? a.block_tables[trow + pv / BS] : 0;
   };
   auto fetch = [&](int blk, int idk, int idv) {
-    const int pk = blk * kFaPos + 4 * tk, pv = blk * kFaPos + 4 * tv;
+    const int pk = blk * kFaPos + kFaNp * tk, pv = blk * kFaPos + kFaNp * tv;
     if ((unsigned)idk >= (unsigned)a.num_blocks || (unsigned)idv >= (unsigned)a.num_blocks) {
       flag_error(kErrBlockId);
       idk = (unsigned)idk >= (unsigned)a.num_blocks ? 0 : idk;
@@ -2214,13 +2225,13 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
     const char* vp = vbase + (int64_t)idv * blk_bytes + (pv % BS) * ROW + 16 * dv;
     if ((blk + 1) * kFaPos <= npos) {      // every position of the block is cached
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kFaNp; ++r) {
         kreg[r] = ld16(kp, r * ROW);
         vreg[r] = ld16(vp, r * ROW);
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kFaNp; ++r) {
         kreg[r] = pk + r < npos ? ld16(kp, r * ROW) : make_uint4(0, 0, 0, 0);
         vreg[r] = pv + r < npos ? ld16(vp, r * ROW) : make_uint4(0, 0, 0, 0);
       }
@@ -2235,12 +2246,38 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
     uint16_t(*s_vt)[kFaVRow] = s_vtb[buf];
     float vmax = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(&s_k[4 * tk + r][8 * dk]) = kreg[r];
-    const int slot = fa_vt_slot(4 * tv);
+    for (int r = 0; r < kFaNp; ++r)
+      *reinterpret_cast<uint4*>(&s_k[kFaNp * tk + r][8 * dk]) = kreg[r];
+    const int slot = fa_vt_slot(kFaNp * tv);
+    if constexpr (kFaNp == 2) {
+      // dims 8 dv + 2e (low halves) and + 2e + 1 (high halves) of 2 positions
+      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[kFaNp - 1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t lo, hi;
+        if constexpr (F16) {
+          const float a0 = __uint_as_float(v0[e] << 16), a1 = __uint_as_float(v1[e] << 16);
+          const float b0 = __uint_as_float(v0[e] & 0xffff0000u), b1 = __uint_as_float(v1[e] & 0xffff0000u);
+          lo = pack_f16x2(a0, a1);
+          hi = pack_f16x2(b0, b1);
+          vmax = max3_abs(vmax, a0, a1);
+          vmax = max3_abs(vmax, b0, b1);
+        } else {
+          lo = pack_low_halves(v0[e], v1[e]);
+          hi = pack_high_halves(v0[e], v1[e]);
+        }
+        *reinterpret_cast<uint32_t*>(&s_vt[8 * dv + 2 * e][slot]) = lo;
+        *reinterpret_cast<uint32_t*>(&s_vt[8 * dv + 2 * e + 1][slot]) = hi;
+      }
+      if constexpr (F16) {
+        if (vmax > kFaF16VMax) s_big[buf] = b;
+      }
+    } else {
     const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1 % kFaNp]);
+    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2 % kFaNp]);
+    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3 % kFaNp]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // dims 8 dv + 2e (low halves) and + 2e + 1 (high halves) of positions 0..3
@@ -2265,6 +2302,7 @@ __device__ __forceinline__ bool multi_query_fa_tile(const MqArgs& a, FaKStage* s
     }
     if constexpr (F16) {
       if (vmax > kFaF16VMax) s_big[buf] = b;
+    }
     }
   };
 
@@ -2454,7 +2492,7 @@ __device__ unsigned long long g_fa_exact_ticket;
 // ticket shows that some fp16 tile of this call (or of a later one, which
 // costs a redundant pass and nothing else) gave up.
 template <int BS, int G, bool F16>
-__global__ __launch_bounds__(256, 2) void multi_query_fa(MqArgs a) {
+__global__ __launch_bounds__(kFaRows * 2, 2) void multi_query_fa(MqArgs a) {
   __shared__ __align__(16) uint16_t s_kb[kFaBufs][kFaPos][kFaKRow];
   __shared__ __align__(16) uint16_t s_vtb[kFaBufs][128][kFaVRow];
   __shared__ int s_big[kFaBufs];
@@ -2693,10 +2731,10 @@ hipError_t launch_multi_query(int block_size, int group, const MqArgs& args, hip
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     MqArgs a = args;
     a.fa_ticket = ++g_fa_tickets;
-    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx), dim3(64 * kFaWaves), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(exact, dim3((unsigned)gx), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(exact, dim3((unsigned)gx), dim3(64 * kFaWaves), 0, stream, a);
     return hipGetLastError();
   }
   hipError_t e = launch_multi_query_tiles(block_size, group, args, stream);
@@ -2794,7 +2832,7 @@ hipError_t launch_shared_prefix_decode(int block_size, int group, const MqArgs& 
 }
 
 bool multi_query_tiled(int group, int max_query_len) {
-  return (int64_t)max_query_len * group >= kFaRows;
+  return (int64_t)max_query_len * group >= kFaMinRows;
 }
 
 // Copy of the error word taken by take_errors_kernel.
